@@ -1,0 +1,231 @@
+/*
+ * qk_oracle.c - plain, slow CPU oracle for ggml block-quantized dequantize,
+ * GEMV and GEMM (formats Q4_0, Q4_1, Q8_0).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference the GPU
+ * library is checked against.  Only the test suite, the package smoke check
+ * and the benchmark's CPU-baseline leg may load it.  It shares no code,
+ * header, table or constant with the GPU library, and the GPU library never
+ * calls it.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * (contraction off: every fp32 multiply and add below is rounded on its own,
+ * in the order written).
+ *
+ * Sources (the pages this follows):
+ *  - "llama_cpp 0.12.1 -> 0.12.2" diff of vendored ggml-cuda.cu (diffend page 4):
+ *      hunk adding dequantize_block_q4_0 / dequantize_block_q4_1: block
+ *      fields d (fp16 scale), dm (fp16 pair d, m), qs (16 nibble bytes);
+ *      byte j holds element j in its low nibble and element j+16 in its high
+ *      nibble; value computed in fp32 as d*q + (-8*d) (Q4_0) and
+ *      d.x*q + d.y (Q4_1), then stored to the fp32 or fp16 destination.
+ *    - hunk adding dequantize_block_q8_0_f16: a Q8_0 block is an fp16 d
+ *      followed by 32 signed bytes (64 blocks fill 2176 bytes, so 34 bytes a
+ *      block); value q*d.
+ *    - the dequantize_row_*_cuda launchers: 32 weights per block (nb32 = k/32).
+ *  - The dot-product definition y[i,j] = sum_c W[i,c] * X[c,j] is the plain
+ *    matrix-vector / matrix-matrix product that dequantize_mul_mat_vec and the
+ *    mul_mat path compute (same diff page, ggml_cuda_op_mul_mat and the
+ *    dmmv tuning block); the oracle evaluates it in fp64.
+ */
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+
+/* Format ids used by this oracle's C entry points (its own numbering). */
+#define ORC_Q4_0 0
+#define ORC_Q4_1 1
+#define ORC_Q8_0 2
+
+/* ---------------------------------------------------------------------
+ * IEEE-754 binary16 codec, written from the format definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * ------------------------------------------------------------------- */
+
+/* Exact decode of binary16 bits to fp32 (every binary16 value is an fp32). */
+float orc_half_to_float(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int e = (h >> 10) & 31;
+    const int f = h & 1023;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);              /* zero or subnormal: f * 2^-24 */
+    } else if (e == 31) {
+        v = (f == 0) ? INFINITY : NAN;          /* infinity or NaN */
+    } else {
+        v = ldexp((double)(1024 + f), e - 25);  /* normal: (1 + f/1024) * 2^(e-15) */
+    }
+    if (isnan(v)) {
+        return sign ? -NAN : NAN;
+    }
+    return (float)(sign ? -v : v);
+}
+
+/* Round a non-negative double holding an exact multiple of 2^-k (k small)
+ * to the nearest integer, ties to even.  All steps are exact in double. */
+static double orc_round_half_even(double q)
+{
+    const double fl = floor(q);
+    const double frac = q - fl;
+    if (frac > 0.5) return fl + 1.0;
+    if (frac < 0.5) return fl;
+    return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+/* fp32 -> binary16, round to nearest even, overflow to infinity, subnormals
+ * kept.  NaN maps to a quiet NaN of the same sign. */
+uint16_t orc_float_to_half(float v)
+{
+    const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return (uint16_t)(sign | 0x7E00u);
+    const double a = fabs((double)v);
+    if (a == 0.0) return sign;
+    if (isinf(v)) return (uint16_t)(sign | 0x7C00u);
+    int ex;
+    frexp(a, &ex);                 /* a = m * 2^ex, m in [0.5, 1) */
+    int e = ex - 1;                /* a in [2^e, 2^(e+1)) */
+    if (e < -14) {
+        /* subnormal range: quantum 2^-24 */
+        const double r = orc_round_half_even(ldexp(a, 24));
+        return (uint16_t)(sign | (uint16_t)r);   /* r == 1024 is the smallest normal */
+    }
+    double r = orc_round_half_even(ldexp(a, 10 - e));  /* in [1024, 2048] */
+    if (r == 2048.0) {
+        r = 1024.0;
+        e += 1;
+    }
+    if (e > 15) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(r - 1024.0));
+}
+
+/* ---------------------------------------------------------------------
+ * Block layout
+ * ------------------------------------------------------------------- */
+
+int orc_block_bytes(int fmt)
+{
+    switch (fmt) {
+    case ORC_Q4_0: return 2 + 16;        /* d, qs[16] */
+    case ORC_Q4_1: return 2 + 2 + 16;    /* d, m, qs[16] */
+    case ORC_Q8_0: return 2 + 32;        /* d, qs[32] (int8) */
+    default: return 0;
+    }
+}
+
+static uint16_t orc_le16(const uint8_t *p)
+{
+    return (uint16_t)(p[0] | (p[1] << 8));
+}
+
+/* Integer code of element t (0..31) of one block. */
+int orc_code(int fmt, const uint8_t *blk, int t)
+{
+    switch (fmt) {
+    case ORC_Q4_0:
+    case ORC_Q4_1: {
+        const uint8_t *qs = blk + (fmt == ORC_Q4_0 ? 2 : 4);
+        return (t < 16) ? (qs[t] & 0x0F) : (qs[t - 16] >> 4);
+    }
+    case ORC_Q8_0:
+        return (int)(int8_t)blk[2 + t];
+    default:
+        return 0;
+    }
+}
+
+/* fp32 value of element t of one block, in the pages' operation order,
+ * each operation rounded separately (no contraction). */
+float orc_value(int fmt, const uint8_t *blk, int t)
+{
+    const float d = orc_half_to_float(orc_le16(blk));
+    const float c = (float)orc_code(fmt, blk, t);
+    switch (fmt) {
+    case ORC_Q4_0: {
+        const float dm = -8.0f * d;
+        const float p = d * c;
+        return p + dm;
+    }
+    case ORC_Q4_1: {
+        const float m = orc_half_to_float(orc_le16(blk + 2));
+        const float p = d * c;
+        return p + m;
+    }
+    case ORC_Q8_0:
+        return d * c;
+    default:
+        return NAN;
+    }
+}
+
+/* Element (i, c) of a rows x k matrix stored row after row, each row k/32
+ * blocks back to back, no padding. */
+static float orc_weight(int fmt, const uint8_t *w, int64_t k, int64_t i, int64_t c)
+{
+    const int64_t bs = orc_block_bytes(fmt);
+    const uint8_t *blk = w + (i * (k / 32) + c / 32) * bs;
+    return orc_value(fmt, blk, (int)(c % 32));
+}
+
+/* ---------------------------------------------------------------------
+ * Dequantize: out[i*k + c] = W[i, c]
+ * ------------------------------------------------------------------- */
+
+void orc_dequantize_f32(int fmt, const uint8_t *w, int64_t rows, int64_t k, float *out)
+{
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t c = 0; c < k; ++c)
+            out[i * k + c] = orc_weight(fmt, w, k, i, c);
+}
+
+/* fp16 output: one round-to-nearest-even of the fp32 value. */
+void orc_dequantize_f16(int fmt, const uint8_t *w, int64_t rows, int64_t k, uint16_t *out)
+{
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t c = 0; c < k; ++c)
+            out[i * k + c] = orc_float_to_half(orc_weight(fmt, w, k, i, c));
+}
+
+/* ---------------------------------------------------------------------
+ * Products.  Activations X are n columns of length k, column j starting at
+ * element j*ldx; either fp32 (x_is_f16 == 0) or binary16 bits (x_is_f16 == 1).
+ * Result y[j*m + i] = sum_c W[i,c] * X[c,j] accumulated in fp64 from the
+ * fp32 weight values, and s[j*m + i] = sum_c |W[i,c] * X[c,j]| (the
+ * tolerance scale).
+ * ------------------------------------------------------------------- */
+
+static double orc_x(const void *x, int x_is_f16, int64_t idx)
+{
+    if (x_is_f16) return (double)orc_half_to_float(((const uint16_t *)x)[idx]);
+    return (double)((const float *)x)[idx];
+}
+
+static void orc_dot_one(int fmt, const uint8_t *w, int64_t k, const void *x, int x_is_f16,
+                        int64_t ldx, int64_t i, int64_t j, double *y, double *s)
+{
+    double acc = 0.0, mag = 0.0;
+    for (int64_t c = 0; c < k; ++c) {
+        const double p = (double)orc_weight(fmt, w, k, i, c) * orc_x(x, x_is_f16, j * ldx + c);
+        acc += p;
+        mag += fabs(p);
+    }
+    *y = acc;
+    *s = mag;
+}
+
+void orc_dot(int fmt, const uint8_t *w, int64_t m, int64_t k, const void *x, int x_is_f16,
+             int64_t ldx, int64_t n, double *y, double *s)
+{
+    for (int64_t j = 0; j < n; ++j)
+        for (int64_t i = 0; i < m; ++i)
+            orc_dot_one(fmt, w, k, x, x_is_f16, ldx, i, j, &y[j * m + i], &s[j * m + i]);
+}
+
+/* Selected entries only: (ii[e], jj[e]) for e < count. */
+void orc_dot_entries(int fmt, const uint8_t *w, int64_t k, const void *x, int x_is_f16,
+                     int64_t ldx, const int64_t *ii, const int64_t *jj, int64_t count,
+                     double *y, double *s)
+{
+    for (int64_t e = 0; e < count; ++e)
+        orc_dot_one(fmt, w, k, x, x_is_f16, ldx, ii[e], jj[e], &y[e], &s[e]);
+}

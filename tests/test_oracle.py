@@ -1,0 +1,331 @@
+"""Pins for the CPU oracle against facts fixed outside it.
+
+Each test ties the oracle to something it does not compute itself: numpy's
+binary16 conversion (a library routine), hand-worked blocks and exact dot
+products (tests/golden/hand_blocks.json, derived by hand from the block
+definitions), exact rational arithmetic, closed forms and invariants.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from dequant_quantized_gemv_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_blocks.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _hex_bytes(s):
+    return np.frombuffer(bytes.fromhex(s.replace(" ", "")), dtype=np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# binary16 codec
+# ---------------------------------------------------------------------------
+
+def test_half_decode_exhaustive_matches_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.halves_to_float(bits)
+    ref = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    # sign of NaN kept
+    assert np.array_equal(np.signbit(got[nan]), np.signbit(ref[nan]))
+
+
+def _encode_cases():
+    rng = np.random.default_rng(1234)
+    halves = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    fin = halves[np.isfinite(halves)].astype(np.float64)
+    fin = np.unique(fin)
+    mids = (fin[:-1] + fin[1:]) / 2.0                      # exact ties (in double)
+    mids32 = mids.astype(np.float32)
+    ties = mids32[mids32.astype(np.float64) == mids]       # ties exactly representable in fp32
+    up = np.nextafter(ties, np.float32(np.inf))
+    dn = np.nextafter(ties, np.float32(-np.inf))
+    rnd = rng.integers(0, 2**32, size=200_000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    special = np.array([65504.0, 65519.996, 65520.0, 65536.0, 1e6, 2.0**-24, 2.0**-25,
+                        2.0**-25 * 1.0000001, 3 * 2.0**-26, 2.0**-14, 2.0**-14 - 2.0**-25,
+                        0.0, -0.0, np.inf, -np.inf, np.nan], dtype=np.float32)
+    return np.concatenate([fin.astype(np.float32), ties, up, dn, rnd, special,
+                           -ties, -up, -dn])
+
+
+def test_half_encode_matches_numpy_rne():
+    v = _encode_cases()
+    got = oracle.floats_to_half(v)
+    ref = v.astype(np.float16).view(np.uint16)
+    nan = np.isnan(v)
+    assert np.array_equal(got[~nan], ref[~nan])
+    g = got[nan]
+    assert np.all(((g & 0x7C00) == 0x7C00) & ((g & 0x3FF) != 0))
+
+
+# ---------------------------------------------------------------------------
+# hand-worked blocks
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("blk", _golden()["blocks"], ids=lambda b: b["name"])
+def test_hand_worked_block(blk):
+    fmt = blk["fmt"]
+    raw = _hex_bytes(blk["bytes_hex"])
+    assert raw.size == oracle.block_bytes(fmt) == synth.BLOCK_BYTES[fmt]
+    want = np.array([float(v) for v in blk["values"]], dtype=np.float32)
+    got = oracle.dequantize_f32(fmt, raw, 1, 32).ravel()
+    assert np.array_equal(got, want)
+    for t in blk["positive_zero_at"]:
+        assert got[t].view(np.uint32) == 0, f"element {t} must be +0.0"
+    # per-element entry point agrees with the matrix one
+    assert all(oracle.value(fmt, raw, t) == want[t] for t in range(32))
+    # fp16 output: every value here is exactly representable
+    h = oracle.dequantize_f16(fmt, raw, 1, 32).ravel()
+    assert np.array_equal(h, want.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("case", _golden()["dots"], ids=lambda c: c["name"])
+def test_hand_worked_dot(case):
+    g = _golden()
+    byname = {b["name"]: b for b in g["blocks"]}
+    fmt, m, k = case["fmt"], case["m"], case["k"]
+    if "rows_hex" in case:
+        w = np.concatenate([_hex_bytes(r) for r in case["rows_hex"]])
+    else:
+        w = np.concatenate([_hex_bytes(byname[b]["bytes_hex"]) for b in case["blocks"]])
+    t = np.arange(k)
+    x = {"t+1": t + 1.0, "(t mod 7) - 3": (t % 7) - 3.0}[case["x_rule"]].astype(np.float32)
+    y, s = oracle.dot(fmt, w, m, k, x, 1)
+    assert list(y[0]) == [float(Fraction(v)) for v in case["y"]]
+    assert list(s[0]) == [float(Fraction(v)) for v in case["s"]]
+
+
+# ---------------------------------------------------------------------------
+# layout, exact values, round trip
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+def test_nibble_and_byte_index_layout(fmt):
+    # one marked code per block, at every position in turn; d = 1 (0x3C00), m = 0
+    base = 8 if fmt == "q4_0" else 0
+    codes = np.full((32, 32), base, dtype=np.int64)
+    for t in range(32):
+        codes[t, t] = base + 5
+    w = synth.pack_blocks(fmt, np.full(32, 0x3C00), codes, m_bits=np.zeros(32))
+    got = oracle.dequantize_f32(fmt, w, 32, 32)
+    assert np.array_equal(got, 5.0 * np.eye(32, dtype=np.float32))
+    # raw placement: element t < 16 in the low nibble of qs[t], t >= 16 in the
+    # high nibble of qs[t-16]; Q8_0 element t in qs[t]
+    blk = w.reshape(32, -1)
+    off = synth.QS_OFFSET[fmt]
+    for t in range(32):
+        if fmt == "q8_0":
+            assert blk[t, off + t] == 5
+        elif t < 16:
+            assert blk[t, off + t] == (base + 5) | (base << 4)
+        else:
+            assert blk[t, off + t - 16] == base | ((base + 5) << 4)
+
+
+def _d_values():
+    # normals across the range, fp16 subnormals, negatives, +-0
+    bits = [0x3C00, 0x3800, 0x2000, 0x1400, 0x0400, 0x03FF, 0x0001, 0x0200, 0x7BFF,
+            0xBC00, 0xB800, 0x8001, 0x83FF, 0x0000, 0x8000, 0x211F, 0x1E3B, 0x5A00]
+    return np.array(bits, dtype=np.uint16)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+def test_every_code_exact_against_rationals(fmt):
+    dbits = _d_values()
+    if fmt == "q4_0":
+        code_set = np.arange(16)
+    else:
+        code_set = np.arange(-128, 128)
+    nb = dbits.size * ((code_set.size + 31) // 32)
+    codes = np.resize(code_set, (nb, 32)) if code_set.size >= 32 else np.tile(code_set, (nb, 2))
+    d_rep = np.repeat(dbits, nb // dbits.size)
+    w = synth.pack_blocks(fmt, d_rep, codes)
+    got = oracle.dequantize_f32(fmt, w, nb, 32)
+    dv = d_rep.view(np.float16).astype(np.float64)
+    for b in range(nb):
+        d = Fraction(float(dv[b]))
+        for t in range(32):
+            c = int(codes[b, t])
+            exact = d * (c - 8) if fmt == "q4_0" else d * c
+            assert Fraction(float(got[b, t])) == exact
+
+
+def test_q4_1_exact_where_representable():
+    # d*c is always exact in fp32; d*c + m is exact whenever the rational sum
+    # fits in 24 bits -- pick such d, m
+    dbits = np.array([0x3C00, 0x3400, 0x2000, 0x0400, 0x0001, 0xB800], dtype=np.uint16)
+    mbits = np.array([0xBC00, 0x0000, 0x2E66, 0xAE66, 0x0001, 0x3555], dtype=np.uint16)
+    codes = np.tile(np.arange(16), (dbits.size, 2))
+    w = synth.pack_blocks("q4_1", dbits, codes, m_bits=mbits)
+    got = oracle.dequantize_f32("q4_1", w, dbits.size, 32)
+    d = dbits.view(np.float16).astype(np.float64)
+    m = mbits.view(np.float16).astype(np.float64)
+    for b in range(dbits.size):
+        for t in range(32):
+            exact = Fraction(d[b]) * int(codes[b, t]) + Fraction(m[b])
+            # the fp32 result is the correctly rounded (RNE) value of the exact sum
+            assert Fraction(float(got[b, t])) == Fraction(float(np.float32(float(exact))))
+            if exact.denominator & (exact.denominator - 1) == 0 and \
+                    abs(exact) < 2**24 * Fraction(1, exact.denominator):
+                assert Fraction(float(got[b, t])) == exact
+
+
+def test_q4_1_single_rounding_generic():
+    # d = 1000, m = fp16(1e-7): d*c + m is not an fp32; one RNE of the exact sum
+    d = np.float16(1000.0).view(np.uint16)
+    m = np.float16(1e-7).view(np.uint16)
+    codes = np.tile(np.arange(16), (1, 2))
+    w = synth.pack_blocks("q4_1", [d], codes, m_bits=[m])
+    got = oracle.dequantize_f32("q4_1", w, 1, 32).ravel()
+    mv = float(np.float16(1e-7))
+    for t in range(32):
+        assert got[t] == np.float32(1000.0 * int(codes[0, t]) + mv)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+def test_round_trip_exactly_representable(fmt):
+    rng = np.random.default_rng(7)
+    nb = 64
+    # power-of-two d, m so every value and every inverse step is exact
+    dbits = (np.float16(2.0) ** rng.integers(-12, 4, size=nb)).astype(np.float16).view(np.uint16)
+    mbits = (-np.float16(2.0) ** rng.integers(-8, 2, size=nb)).astype(np.float16).view(np.uint16)
+    if fmt == "q8_0":
+        codes = rng.integers(-128, 128, size=(nb, 32))
+    else:
+        codes = rng.integers(0, 16, size=(nb, 32))
+    w = synth.pack_blocks(fmt, dbits, codes, m_bits=mbits)
+    vals = oracle.dequantize_f32(fmt, w, nb, 32).astype(np.float64)
+    d = dbits.view(np.float16).astype(np.float64)[:, None]
+    m = mbits.view(np.float16).astype(np.float64)[:, None]
+    if fmt == "q4_0":
+        rec = vals / d + 8
+    elif fmt == "q4_1":
+        rec = (vals - m) / d
+    else:
+        rec = vals / d
+    assert np.array_equal(rec, codes.astype(np.float64))
+    w2 = synth.pack_blocks(fmt, dbits, rec.astype(np.int64), m_bits=mbits)
+    assert np.array_equal(w2, w)
+
+
+def test_f16_output_is_one_rne_of_f32():
+    # random blocks plus overflow cases: fp16 max d with extreme codes -> +-inf
+    for fmt in ("q4_0", "q4_1", "q8_0"):
+        w = synth.quant_matrix(fmt, 8, 256, seed=99, tensor_id=1, d_range=(1e-3, 2e-2))
+        f32 = oracle.dequantize_f32(fmt, w, 8, 256)
+        f16 = oracle.dequantize_f16(fmt, w, 8, 256)
+        assert np.array_equal(f16, f32.astype(np.float16).view(np.uint16))
+    big = np.array([0x7BFF, 0xFBFF, 0x0001, 0x03FF], dtype=np.uint16)
+    for fmt, codes in (("q4_0", np.tile(np.arange(16), (4, 2))),
+                       ("q8_0", np.tile(np.array([-128, 127, -1, 1] * 8), (4, 1)))):
+        w = synth.pack_blocks(fmt, big, codes)
+        f32 = oracle.dequantize_f32(fmt, w, 4, 32)
+        f16 = oracle.dequantize_f16(fmt, w, 4, 32)
+        assert np.array_equal(f16, f32.astype(np.float16).view(np.uint16))
+        assert np.isinf(f16.view(np.float16)).any()
+
+
+# ---------------------------------------------------------------------------
+# products
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+def test_dot_matches_numpy_fp64_matmul(fmt):
+    m, k, n = 13, 320, 3
+    w = synth.quant_matrix(fmt, m, k, seed=5, tensor_id=2, d_range=(1e-3, 2e-2))
+    x = synth.activations(k, n, seed=5, tensor_id=3)
+    y, s = oracle.dot(fmt, w, m, k, x, n)
+    W = oracle.dequantize_f32(fmt, w, m, k).astype(np.float64)
+    X = x.astype(np.float64)
+    np.testing.assert_allclose(y, X @ W.T, rtol=0, atol=1e-12 * s.max())
+    np.testing.assert_allclose(s, np.abs(X) @ np.abs(W).T, rtol=1e-13)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+def test_dot_unit_vectors_give_columns(fmt):
+    m, k = 5, 96
+    w = synth.quant_matrix(fmt, m, k, seed=6, tensor_id=2, d_range=(1e-3, 2e-2))
+    W = oracle.dequantize_f32(fmt, w, m, k)
+    cols = [0, 15, 16, 31, 32, 95]
+    x = np.zeros((len(cols), k), dtype=np.float32)
+    for j, c in enumerate(cols):
+        x[j, c] = 1.0
+    y, _ = oracle.dot(fmt, w, m, k, x, len(cols))
+    for j, c in enumerate(cols):
+        assert np.array_equal(y[j], W[:, c].astype(np.float64))
+    y0, s0 = oracle.dot(fmt, w, m, k, np.zeros(k, np.float32), 1)
+    assert np.all(y0 == 0) and np.all(s0 == 0)
+
+
+def test_dot_all_code8_row_is_zero_and_linear():
+    k = 128
+    codes = np.full((4, 32), 8)
+    w = synth.pack_blocks("q4_0", np.full(4, 0x2A00), codes)
+    x = synth.activations(k, 1, seed=1, tensor_id=1)
+    y, s = oracle.dot("q4_0", w, 1, k, x, 1)
+    assert y[0, 0] == 0.0 and s[0, 0] == 0.0
+    m = 7
+    w = synth.quant_matrix("q4_1", m, k, seed=2, tensor_id=4, d_range=(1e-3, 2e-2))
+    x2 = synth.activations(k, 2, seed=2, tensor_id=5)
+    ya, sa = oracle.dot("q4_1", w, m, k, x2[0], 1)
+    yb, sb = oracle.dot("q4_1", w, m, k, x2[1], 1)
+    comb = (np.float32(0.5) * x2[0] + np.float32(0.25) * x2[1]).astype(np.float32)
+    yc, _ = oracle.dot("q4_1", w, m, k, comb, 1)
+    np.testing.assert_allclose(yc, 0.5 * ya + 0.25 * yb, atol=1e-6 * (sa + sb).max())
+
+
+def test_dot_strided_columns_and_fp16_activations():
+    m, k, n, ldx = 6, 64, 3, 80
+    w = synth.quant_matrix("q8_0", m, k, seed=3, tensor_id=1, d_range=(1e-3, 1e-2))
+    xs = synth.activations(ldx, n, seed=3, tensor_id=2)   # rows of length ldx
+    y, s = oracle.dot("q8_0", w, m, k, xs.ravel(), n, ldx=ldx)
+    W = oracle.dequantize_f32("q8_0", w, m, k).astype(np.float64)
+    np.testing.assert_allclose(y, xs[:, :k].astype(np.float64) @ W.T, atol=1e-12 * s.max())
+    xh = xs.astype(np.float16)
+    yh, sh = oracle.dot("q8_0", w, m, k, xh.view(np.uint16).ravel(), n, ldx=ldx, x_is_f16=True)
+    np.testing.assert_allclose(yh, xh[:, :k].astype(np.float64) @ W.T, atol=1e-12 * sh.max())
+
+
+def test_dot_entries_agree_with_full():
+    m, k, n = 9, 160, 4
+    w = synth.quant_matrix("q4_0", m, k, seed=4, tensor_id=1, d_range=(1e-3, 2e-2))
+    x = synth.activations(k, n, seed=4, tensor_id=2)
+    y, s = oracle.dot("q4_0", w, m, k, x, n)
+    ii = np.array([0, 8, 3, 3, 5])
+    jj = np.array([0, 3, 1, 2, 0])
+    ye, se = oracle.dot_entries("q4_0", w, m, k, x.ravel(), k, ii, jj)
+    assert np.array_equal(ye, y[jj, ii]) and np.array_equal(se, s[jj, ii])
+
+
+def test_mistakes_are_caught_by_pins():
+    """Planted mistakes (in a copy of the oracle's steps, on the CPU) are
+    rejected by the hand-worked values: swapping nibble halves, dropping the
+    -8 offset, or the d*(q-8) order (sign of zero)."""
+    g = {b["name"]: b for b in _golden()["blocks"]}
+    blk = _hex_bytes(g["q4_0_ramp"]["bytes_hex"])
+    want = np.array([float(v) for v in g["q4_0_ramp"]["values"]], dtype=np.float32)
+    d = np.float32(blk[:2].view("<u2").view(np.float16)[0])
+    qs = blk[2:]
+    lo, hi = (qs & 15).astype(np.float32), (qs >> 4).astype(np.float32)
+    swapped = np.concatenate([hi, lo]) * d + np.float32(-8) * d
+    no_offset = np.concatenate([lo, hi]) * d
+    assert not np.array_equal(swapped, want)
+    assert not np.array_equal(no_offset, want)
+    z = g["q4_0_sign_of_zero"]
+    zb = _hex_bytes(z["bytes_hex"])
+    dz = np.float32(zb[:2].view("<u2").view(np.float16)[0])
+    mul_form = dz * (np.float32(zb[2] & 15) - np.float32(8))
+    assert np.signbit(mul_form)          # the other order gives -0.0 ...
+    assert not np.signbit(oracle.dequantize_f32("q4_0", zb, 1, 32)[0, 0])  # ... the oracle +0.0
