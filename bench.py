@@ -1,0 +1,365 @@
+"""Benchmark of the quantized GEMV hot path on one MI355X.
+
+Default workload: Q8_0 GEMV, W 4096 x 4096 times one fp32 activation column
+(x ~ N(0,1)), y = W x in fp32.  A step is one qk_mul_mat_vec call: block
+decode, fused dequantize + dot products, wave/workgroup reduction, dispatch.
+
+Measurement
+  * Inputs live in HBM before the timed region.  Every working set here fits
+    in the 256 MB Infinity Cache, so the benchmark rotates through R copies of
+    the weights (R * |W| >= 1 GiB): launch i reads copy i % R, which is never
+    cache-resident.
+  * Launches are captured into a HIP graph (torch.cuda.CUDAGraph) so host
+    launch overhead is out of the way; the timed region is one replay of K
+    launches, bracketed by synchronization, timed with HIP events recorded on
+    the stream the kernels run on.
+  * Before timing, the output is checked against the CPU oracle (every row).
+  * metric value = weight bytes per launch * K / elapsed  (effective weight GB/s)
+  * roofline.achieved = algorithmic bytes per launch (W + x + y) / average
+    launch time; peak = 8 TB/s HBM.
+  * cpu_baseline: the oracle (plain C, fp64, one thread) on the same matrix.
+
+Options: --workload NAME runs another of the five workloads as the headline;
+--configs also measures all five and adds them under "configs".
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+COLD_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "dequant_quantized_gemv_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel_key, sources):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, or None if
+    they were taken on a different version of the kernel source."""
+    path = os.path.join(PROFILES, f"traffic_{kernel_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(sources):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+class Timer:
+    """Graph-captured launches timed with HIP events on the launch stream."""
+
+    def __init__(self, torch):
+        self.t = torch
+
+    def capture(self, fn, count):
+        t = self.t
+        g = t.cuda.CUDAGraph()
+        s = t.cuda.Stream()
+        s.wait_stream(t.cuda.current_stream())
+        with t.cuda.stream(s):
+            with t.cuda.graph(g, stream=s):
+                for i in range(count):
+                    fn(i)
+        t.cuda.current_stream().wait_stream(s)
+        t.cuda.synchronize()
+        return g
+
+    def time_graph(self, g):
+        t = self.t
+        t.cuda.synchronize()
+        st = t.cuda.current_stream()
+        e0 = t.cuda.Event(enable_timing=True)
+        e1 = t.cuda.Event(enable_timing=True)
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        t.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3  # seconds
+
+
+def copies_for(nbytes, minimum=2):
+    return max(minimum, math.ceil(COLD_BYTES / max(nbytes, 1)))
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def setup_gemv(torch, qk, synth, oracle, fmt, m, k, n, seed, wtid, xtid, d, mr=None,
+               check="full", rng_seed=0):
+    """Device copies of one GEMV problem plus the parity check of one launch."""
+    w = synth.quant_matrix(fmt, m, k, seed=seed, tensor_id=wtid, d_range=d,
+                           **({"m_range": mr} if mr else {}))
+    x = synth.activations(k, 8 if n > 1 else 1, seed=seed, tensor_id=xtid)[:n]
+    wd = torch.from_numpy(w).cuda()
+    xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    y = torch.empty((n, m), dtype=torch.float32, device="cuda")
+    qk.mul_mat_vec(fmt, wd, m, k, xd, y=y)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy().astype(np.float64)
+    if check == "full":
+        yr, s = oracle.dot(fmt, w, m, k, x, n)
+        ok = bool(np.all(np.abs(yh - yr) <= 1e-4 * s))
+        worst = float(np.max(np.abs(yh - yr) / np.where(s > 0, s, 1)))
+    else:
+        rng = np.random.default_rng(rng_seed)
+        ii = rng.integers(0, m, size=256)
+        jj = rng.integers(0, n, size=256)
+        yr, s = oracle.dot_entries(fmt, w, m, k, x.ravel(), k, ii, jj)
+        got = yh[jj, ii]
+        ok = bool(np.all(np.abs(got - yr) <= 1e-4 * s))
+        worst = float(np.max(np.abs(got - yr) / np.where(s > 0, s, 1)))
+    return dict(w=w, x=x, wd=wd, xd=xd, y=y, ok=ok, worst=worst)
+
+
+def gemv_bytes(fmt, m, k, n):
+    bs = {"q4_0": 18, "q4_1": 20, "q8_0": 34}[fmt]
+    wb = m * (k // 32) * bs
+    return wb, wb + 4 * n * (k + m)
+
+
+def bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup):
+    wb, algo = gemv_bytes(fmt, m, k, n)
+    R = copies_for(wb)
+    copies = [prob["wd"]] + [prob["wd"].clone() for _ in range(R - 1)]
+    xd, y = prob["xd"], prob["y"]
+    lib = qk.load()
+    code = qk.FORMATS[fmt]
+    ptrs = [c.data_ptr() for c in copies]
+    xp, yp = xd.data_ptr(), y.data_ptr()
+
+    def launch(i):
+        st = lib.qk_mul_mat_vec(code, ptrs[i % R], m, k, xp, n, k, yp, m,
+                                torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"qk_mul_mat_vec: {qk.status_string(st)}")
+
+    gw = timer.capture(launch, max(warmup, 1))
+    gk = timer.capture(lambda i: launch(i + warmup), steps)
+    timer.time_graph(gw)
+    sec = timer.time_graph(gk)
+    del gw, gk, copies
+    return dict(seconds=sec, per_launch_s=sec / steps, weight_bytes=wb, algo_bytes=algo, copies=R)
+
+
+def cpu_baseline_gemv(oracle, prob, fmt, m, k, n, budget_s=10.0):
+    wb, _ = gemv_bytes(fmt, m, k, n)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.dot(fmt, prob["w"], m, k, prob["x"], n)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or passes >= 200:
+            break
+    return dict(value=round(wb * passes / el / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"full {m}x{k} {fmt} matrix x {n} column(s), {passes} passes, "
+                       f"{el:.1f} s, one thread")
+
+
+def run_headline(torch, qk, synth, oracle, timer, name, steps, warmup, with_cpu):
+    cfg = synth.WORKLOADS[name]
+    seed = synth.workload_seed(cfg["id"])
+    fmt = cfg["fmt"]
+    if "layer" in cfg or name.startswith("dequant") or name.startswith("gemm"):
+        raise SystemExit(f"--workload {name}: the headline is a single GEMV; use --configs")
+    n = cfg["n"] if isinstance(cfg["n"], int) else cfg["n"][0]
+    m, k = cfg["m"], cfg["k"]
+    prob = setup_gemv(torch, qk, synth, oracle, fmt, m, k, n, seed, 0, 100, cfg["d"],
+                      cfg.get("mr"))
+    if not prob["ok"]:
+        raise SystemExit(f"parity check failed before timing (max err/S {prob['worst']:.3g})")
+    log(f"parity ok: max |y-ref|/S = {prob['worst']:.3g}")
+    r = bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup)
+    gbps = r["weight_bytes"] * steps / r["seconds"] / 1e9
+    achieved = r["algo_bytes"] / r["per_launch_s"] / 1e9
+    traffic = stored_traffic(f"gemv_{fmt}_{m}x{k}_n{n}", ["gemv.hip", "qk_common.h"])
+    out = {
+        "metric": "effective weight GB/s (% of HBM peak) for Q4_0/Q8_0 GEMV; batched TFLOP/s",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(r["seconds"] * 1e3 / steps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "format": fmt, "m": m, "k": k, "n": n,
+                   "cold_weight_copies": r["copies"], "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
+    }
+    if with_cpu:
+        log("timing the CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline_gemv(oracle, prob, fmt, m, k, n)
+    return out
+
+
+def run_configs(torch, qk, synth, oracle, timer, steps, warmup):
+    """All five workloads, each parity-checked before it is timed."""
+    res = {}
+    # C0: dequantize Q4_0 4096x4096 -> fp32
+    cfg = synth.WORKLOADS["dequant_q4_0_4096x4096_f32"]
+    seed = synth.workload_seed(cfg["id"])
+    m, k = cfg["m"], cfg["k"]
+    w = synth.quant_matrix("q4_0", m, k, seed=seed, tensor_id=0, d_range=cfg["d"])
+    wd = torch.from_numpy(w).cuda()
+    out = qk.dequantize("q4_0", wd, m, k, "f32")
+    ok = np.array_equal(out.cpu().numpy().view(np.uint32),
+                        oracle.dequantize_f32("q4_0", w, m, k).view(np.uint32))
+    inb, outb = w.size, m * k * 4
+    R = copies_for(inb + outb)
+    ins = [wd] + [wd.clone() for _ in range(R - 1)]
+    outs = [out] + [torch.empty_like(out) for _ in range(R - 1)]
+    lib = qk.load()
+
+    def dq(i):
+        lib.qk_dequantize(qk.QK_Q4_0, ins[i % R].data_ptr(), m, k, qk.QK_F32,
+                          outs[i % R].data_ptr(), torch.cuda.current_stream().cuda_stream)
+
+    st = max(steps // 4, 20)
+    gw, gk = timer.capture(dq, warmup), timer.capture(lambda i: dq(i + warmup), st)
+    timer.time_graph(gw)
+    sec = timer.time_graph(gk) / st
+    res["dequant_q4_0_4096x4096_f32"] = {
+        "parity": "bit-exact" if ok else "FAILED", "us_per_launch": round(sec * 1e6, 3),
+        "total_GBps": round((inb + outb) / sec / 1e9, 1),
+        "weight_GBps": round(inb / sec / 1e9, 1),
+        "pct_of_hbm_peak": round(100 * (inb + outb) / sec / 1e9 / HBM_PEAK_GBPS, 1)}
+    del ins, outs, gw, gk
+
+    # C1 and C2: single GEMVs
+    for name, ns in (("gemv_q8_0_4096x4096_n1", (1,)), ("gemv_q4_1_11008x4096", (1, 2, 4, 8))):
+        cfg = synth.WORKLOADS[name]
+        seed = synth.workload_seed(cfg["id"])
+        for n in ns:
+            prob = setup_gemv(torch, qk, synth, oracle, cfg["fmt"], cfg["m"], cfg["k"], n, seed, 0,
+                              100, cfg["d"], cfg.get("mr"), check="sampled", rng_seed=n)
+            r = bench_gemv(torch, qk, timer, prob, cfg["fmt"], cfg["m"], cfg["k"], n, steps, warmup)
+            gbps = r["weight_bytes"] / r["per_launch_s"] / 1e9
+            res[f"{name}" + ("" if len(ns) == 1 else f"_n{n}")] = {
+                "parity": "ok" if prob["ok"] else "FAILED", "max_err_over_S": prob["worst"],
+                "us_per_launch": round(r["per_launch_s"] * 1e6, 3),
+                "weight_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
+            del prob
+
+    # C3: the decode layer, 7 GEMVs per step
+    cfg = synth.WORKLOADS["gemv_q4_0_decode_layer"]
+    seed = synth.workload_seed(cfg["id"])
+    probs, wtot = [], 0
+    for tid, (nm, m, k) in enumerate(cfg["layer"]):
+        p = setup_gemv(torch, qk, synth, oracle, "q4_0", m, k, 1, seed, tid, 100 + tid, cfg["d"],
+                       check="sampled", rng_seed=tid)
+        p.update(m=m, k=k)
+        probs.append(p)
+        wtot += gemv_bytes("q4_0", m, k, 1)[0]
+    R = copies_for(wtot)
+    layer_copies = [[p["wd"]] + [p["wd"].clone() for _ in range(R - 1)] for p in probs]
+
+    def layer(i):
+        s = torch.cuda.current_stream().cuda_stream
+        for p, cps in zip(probs, layer_copies):
+            lib.qk_mul_mat_vec(qk.QK_Q4_0, cps[i % R].data_ptr(), p["m"], p["k"], p["xd"].data_ptr(),
+                               1, p["k"], p["y"].data_ptr(), p["m"], s)
+
+    st = max(steps // 7, 20)
+    gw, gk = timer.capture(layer, warmup), timer.capture(lambda i: layer(i + warmup), st)
+    timer.time_graph(gw)
+    sec = timer.time_graph(gk) / st
+    res["gemv_q4_0_decode_layer"] = {
+        "parity": "ok" if all(p["ok"] for p in probs) else "FAILED",
+        "us_per_layer": round(sec * 1e6, 3), "weight_GBps": round(wtot / sec / 1e9, 1),
+        "pct_of_hbm_peak": round(100 * wtot / sec / 1e9 / HBM_PEAK_GBPS, 1)}
+    del probs, layer_copies, gw, gk
+
+    # C4: GEMM
+    cfg = synth.WORKLOADS["gemm_q4_0_14336x4096_n512"]
+    seed = synth.workload_seed(cfg["id"])
+    m, k, n = cfg["m"], cfg["k"], cfg["n"]
+    w = synth.quant_matrix("q4_0", m, k, seed=seed, tensor_id=0, d_range=cfg["d"])
+    xh = synth.activations(k, n, seed=seed, tensor_id=100, dtype=np.float16)
+    wd = torch.from_numpy(w).cuda()
+    xd = torch.from_numpy(xh).cuda()
+    y = qk.mul_mat("q4_0", wd, m, k, xd)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    ii, jj = rng.integers(0, m, 256), rng.integers(0, n, 256)
+    yr, s = oracle.dot_entries("q4_0", w, m, k, xh.view(np.uint16).ravel(), k, ii, jj, x_is_f16=True)
+    got = y.cpu().numpy()[jj, ii].astype(np.float64)
+    ok = bool(np.all(np.abs(got - yr) <= 1e-2 * s))
+    R = copies_for(w.size, minimum=4)
+    wc = [wd] + [wd.clone() for _ in range(R - 1)]
+
+    def gm(i):
+        lib.qk_mul_mat(qk.QK_Q4_0, wc[i % R].data_ptr(), m, k, xd.data_ptr(), n, k, y.data_ptr(), m,
+                       torch.cuda.current_stream().cuda_stream)
+
+    st = max(steps // 20, 20)
+    gw, gk = timer.capture(gm, max(warmup // 10, 2)), timer.capture(gm, st)
+    timer.time_graph(gw)
+    sec = timer.time_graph(gk) / st
+    tf = 2.0 * m * n * k / sec / 1e12
+    res["gemm_q4_0_14336x4096_n512"] = {
+        "parity": "ok" if ok else "FAILED", "us_per_launch": round(sec * 1e6, 2),
+        "TFLOPs": round(tf, 1), "pct_of_mfma_f16_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 1)}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="gemv_q8_0_4096x4096_n1")
+    ap.add_argument("--configs", action="store_true", help="also measure all five workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import oracle
+    from dequant_quantized_gemv_amd import qk, synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    qk.load()  # fails loudly if libqk.so is not built
+    torch.cuda.set_device(0)
+    timer = Timer(torch)
+    out = run_headline(torch, qk, synth, oracle, timer, args.workload, args.steps, args.warmup,
+                       not args.no_cpu)
+    if args.configs:
+        log("measuring all five workloads")
+        out["configs"] = run_configs(torch, qk, synth, oracle, timer, args.steps, args.warmup)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

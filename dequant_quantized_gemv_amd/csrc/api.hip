@@ -1,0 +1,110 @@
+// api.hip - the C ABI: argument validation, then dispatch to the launchers.
+//
+// Validation happens entirely on the host before any HIP call, so every error
+// path returns a status with nothing enqueued.
+#include <stdint.h>
+#include <stddef.h>
+
+#include "qk.h"
+#include "qk_common.h"
+#include "qk_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = INT32_MAX;  // kernels index rows and columns in 32 bits
+
+bool fmt_ok(int fmt) { return qk::block_bytes_host(fmt) != 0; }
+
+// Half-open byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Bytes spanned by n columns of length len with stride ld (elements of size es).
+size_t span_bytes(int64_t n, int64_t ld, int64_t len, size_t es) {
+    if (n <= 0 || len <= 0) return 0;
+    return (size_t)((n - 1) * ld + len) * es;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qk_block_bytes(int fmt) { return (size_t)qk::block_bytes_host(fmt); }
+
+size_t qk_row_bytes(int fmt, int64_t k) {
+    if (!fmt_ok(fmt) || k < 0 || k % 32 != 0) return 0;
+    return (size_t)(k / 32) * (size_t)qk::block_bytes_host(fmt);
+}
+
+const char *qk_status_string(int status) {
+    switch (status) {
+    case QK_OK: return "ok";
+    case QK_ERR_INVALID_ARG: return "invalid argument";
+    case QK_ERR_UNSUPPORTED: return "unsupported format or dtype";
+    case QK_ERR_ALIGNMENT: return "misaligned pointer";
+    case QK_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int qk_version(void) { return 100; }
+
+int qk_dequantize(int fmt, const void *w, int64_t rows, int64_t k, int out_dtype, void *out,
+                  void *stream) {
+    if (!fmt_ok(fmt)) return QK_ERR_UNSUPPORTED;
+    if (out_dtype != QK_F32 && out_dtype != QK_F16) return QK_ERR_UNSUPPORTED;
+    if (rows < 0 || k < 0 || k % 32 != 0) return QK_ERR_INVALID_ARG;
+    if (rows == 0 || k == 0) return QK_OK;
+    if (k > kMaxDim || rows > INT64_MAX / (k / 32)) return QK_ERR_INVALID_ARG;
+    // one workgroup per 256 blocks, one grid dimension
+    if ((rows * (k / 32) + 255) / 256 > (int64_t)INT32_MAX) return QK_ERR_INVALID_ARG;
+    if (w == nullptr || out == nullptr) return QK_ERR_INVALID_ARG;
+    const size_t es = out_dtype == QK_F32 ? 4 : 2;
+    if ((uintptr_t)w % 2 != 0 || (uintptr_t)out % es != 0) return QK_ERR_ALIGNMENT;
+    const int64_t nblocks = rows * (k / 32);
+    const size_t wbytes = (size_t)nblocks * qk::block_bytes_host(fmt);
+    const size_t obytes = (size_t)(rows * k) * es;
+    if (overlaps(w, wbytes, out, obytes)) return QK_ERR_INVALID_ARG;
+    return qk::launch_dequantize(fmt, w, nblocks, out_dtype, out,
+                                 static_cast<hipStream_t>(stream));
+}
+
+int qk_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k, const float *x, int64_t n,
+                   int64_t ldx, float *y, int64_t ldy, void *stream) {
+    if (!fmt_ok(fmt)) return QK_ERR_UNSUPPORTED;
+    if (m < 0 || k < 0 || k % 32 != 0 || n < 0 || n > 8) return QK_ERR_INVALID_ARG;
+    if (m == 0 || n == 0) return QK_OK;
+    if (m > kMaxDim || k > kMaxDim || ldx < k || ldy < m) return QK_ERR_INVALID_ARG;
+    if (y == nullptr || (k > 0 && (w == nullptr || x == nullptr))) return QK_ERR_INVALID_ARG;
+    if ((uintptr_t)w % 2 != 0 || (uintptr_t)x % 4 != 0 || (uintptr_t)y % 4 != 0)
+        return QK_ERR_ALIGNMENT;
+    const size_t wbytes = (size_t)m * (size_t)(k / 32) * qk::block_bytes_host(fmt);
+    const size_t xbytes = span_bytes(n, ldx, k, 4);
+    const size_t ybytes = span_bytes(n, ldy, m, 4);
+    if (overlaps(y, ybytes, w, wbytes) || overlaps(y, ybytes, x, xbytes)) return QK_ERR_INVALID_ARG;
+    return qk::launch_mul_mat_vec(fmt, w, m, k, x, n, ldx, y, ldy, static_cast<hipStream_t>(stream));
+}
+
+int qk_mul_mat(int fmt, const void *w, int64_t m, int64_t k, const void *x_f16, int64_t n,
+               int64_t ldx, float *y, int64_t ldy, void *stream) {
+    if (!fmt_ok(fmt)) return QK_ERR_UNSUPPORTED;
+    if (m < 0 || k < 0 || k % 32 != 0 || n < 0) return QK_ERR_INVALID_ARG;
+    if (m == 0 || n == 0) return QK_OK;
+    if (m > kMaxDim || k > kMaxDim || n > kMaxDim || ldx < k || ldy < m) return QK_ERR_INVALID_ARG;
+    // the tile grid is one dimension of 128 x 128 tiles
+    if (((m + 127) / 128) * ((n + 127) / 128) > (int64_t)INT32_MAX) return QK_ERR_INVALID_ARG;
+    if (y == nullptr || (k > 0 && (w == nullptr || x_f16 == nullptr))) return QK_ERR_INVALID_ARG;
+    if ((uintptr_t)w % 2 != 0 || (uintptr_t)x_f16 % 2 != 0 || (uintptr_t)y % 4 != 0)
+        return QK_ERR_ALIGNMENT;
+    const size_t wbytes = (size_t)m * (size_t)(k / 32) * qk::block_bytes_host(fmt);
+    const size_t xbytes = span_bytes(n, ldx, k, 2);
+    const size_t ybytes = span_bytes(n, ldy, m, 4);
+    if (overlaps(y, ybytes, w, wbytes) || overlaps(y, ybytes, x_f16, xbytes)) return QK_ERR_INVALID_ARG;
+    return qk::launch_mul_mat(fmt, w, m, k, static_cast<const uint16_t *>(x_f16), n, ldx, y, ldy,
+                              static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

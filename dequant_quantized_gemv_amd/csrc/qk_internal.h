@@ -1,0 +1,40 @@
+// qk_internal.h - launchers behind the C ABI (validated arguments only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+#include "qk.h"
+
+namespace qk {
+
+// Launch a kernel with hipLaunchKernel and map the runtime's answer to a
+// status code (no global error state is read or cleared).
+template <typename... KArgs, typename... Args>
+inline int launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                  Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel arity");
+    std::tuple<KArgs...> vals(static_cast<KArgs>(args)...);
+    void *argv[sizeof...(KArgs)];
+    std::apply([&](auto &...v) {
+        int i = 0;
+        ((argv[i++] = static_cast<void *>(&v)), ...);
+    }, vals);
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kern), grid, block,
+                                         argv, 0, stream);
+    return e == hipSuccess ? QK_OK : QK_ERR_LAUNCH;
+}
+
+int launch_dequantize(int fmt, const void *w, int64_t nblocks, int out_dtype, void *out,
+                      hipStream_t stream);
+
+int launch_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k, const float *x,
+                       int64_t n, int64_t ldx, float *y, int64_t ldy, hipStream_t stream);
+
+int launch_mul_mat(int fmt, const void *w, int64_t m, int64_t k, const uint16_t *x,
+                   int64_t n, int64_t ldx, float *y, int64_t ldy, hipStream_t stream);
+
+}  // namespace qk

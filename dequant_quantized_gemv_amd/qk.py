@@ -1,0 +1,153 @@
+"""Thin Python binding of libqk (include/qk.h).
+
+Argument marshalling only: tensors are passed as device pointers with the
+current HIP stream; every step of the computation runs in the library's gfx950
+kernels.  The library must be built (``python -m dequant_quantized_gemv_amd.build``
+or ``__graft_entry__.build()``); loading fails loudly otherwise, and there is no
+CPU fallback.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqk.so")
+
+# enum qk_format / qk_dtype / qk_status (include/qk.h)
+QK_Q4_0, QK_Q4_1, QK_Q8_0 = 1, 2, 3
+QK_F32, QK_F16 = 0, 1
+QK_OK, QK_ERR_INVALID_ARG, QK_ERR_UNSUPPORTED, QK_ERR_ALIGNMENT, QK_ERR_LAUNCH = 0, 1, 2, 3, 4
+
+FORMATS = {"q4_0": QK_Q4_0, "q4_1": QK_Q4_1, "q8_0": QK_Q8_0}
+SYMBOLS = ("qk_block_bytes", "qk_row_bytes", "qk_status_string", "qk_version",
+           "qk_dequantize", "qk_mul_mat_vec", "qk_mul_mat")
+
+
+class QKError(RuntimeError):
+    def __init__(self, status, call):
+        self.status = status
+        super().__init__(f"{call} failed: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load():
+    """Load libqk.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "or python -m dequant_quantized_gemv_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.qk_block_bytes.argtypes = [ci]
+    lib.qk_block_bytes.restype = ctypes.c_size_t
+    lib.qk_row_bytes.argtypes = [ci, i64]
+    lib.qk_row_bytes.restype = ctypes.c_size_t
+    lib.qk_status_string.argtypes = [ci]
+    lib.qk_status_string.restype = ctypes.c_char_p
+    lib.qk_version.argtypes = []
+    lib.qk_version.restype = ci
+    lib.qk_dequantize.argtypes = [ci, vp, i64, i64, ci, vp, vp]
+    lib.qk_dequantize.restype = ci
+    lib.qk_mul_mat_vec.argtypes = [ci, vp, i64, i64, vp, i64, i64, vp, i64, vp]
+    lib.qk_mul_mat_vec.restype = ci
+    lib.qk_mul_mat.argtypes = [ci, vp, i64, i64, vp, i64, i64, vp, i64, vp]
+    lib.qk_mul_mat.restype = ci
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load().qk_status_string(int(status)).decode()
+
+
+def block_bytes(fmt):
+    return load().qk_block_bytes(_fmt(fmt))
+
+
+def row_bytes(fmt, k):
+    return load().qk_row_bytes(_fmt(fmt), int(k))
+
+
+def _fmt(fmt):
+    if isinstance(fmt, str):
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown format {fmt!r}")
+        return FORMATS[fmt]
+    return int(fmt)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return int(stream) if not hasattr(stream, "cuda_stream") else stream.cuda_stream
+
+
+def _check(status, call):
+    if status != QK_OK:
+        raise QKError(status, call)
+
+
+# ---------------------------------------------------------------------------
+# Raw entry points (pointers and sizes, same names and argument order as C)
+# ---------------------------------------------------------------------------
+
+def qk_dequantize(fmt, w_ptr, rows, k, out_dtype, out_ptr, stream=0):
+    return load().qk_dequantize(_fmt(fmt), w_ptr, rows, k, out_dtype, out_ptr, stream)
+
+
+def qk_mul_mat_vec(fmt, w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream=0):
+    return load().qk_mul_mat_vec(_fmt(fmt), w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream)
+
+
+def qk_mul_mat(fmt, w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream=0):
+    return load().qk_mul_mat(_fmt(fmt), w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream)
+
+
+# ---------------------------------------------------------------------------
+# torch-tensor conveniences (allocation by torch, compute by libqk)
+# ---------------------------------------------------------------------------
+
+def dequantize(fmt, w, rows, k, out_dtype="f32", out=None, stream=None):
+    """Dequantize a rows x k matrix held as block bytes in a uint8 CUDA tensor."""
+    import torch
+    dt = {"f32": (QK_F32, torch.float32), "f16": (QK_F16, torch.float16)}[out_dtype]
+    if out is None:
+        out = torch.empty((rows, k), dtype=dt[1], device=w.device)
+    st = qk_dequantize(fmt, w.data_ptr(), rows, k, dt[0], out.data_ptr(), _stream(stream))
+    _check(st, "qk_dequantize")
+    return out
+
+
+def mul_mat_vec(fmt, w, m, k, x, y=None, stream=None):
+    """y (n, m) = x (n, k) @ W^T for 1..8 fp32 columns; rows of x and y are the
+    ggml columns (contiguous, ldx = x.stride(0), ldy = y.stride(0))."""
+    import torch
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    n = x.shape[0]
+    if x.dtype != torch.float32 or x.stride(1) != 1:
+        raise TypeError("x must be float32 with contiguous columns")
+    if y is None:
+        y = torch.empty((n, m), dtype=torch.float32, device=x.device)
+    st = qk_mul_mat_vec(fmt, w.data_ptr(), m, k, x.data_ptr(), n, x.stride(0),
+                        y.data_ptr(), y.stride(0), _stream(stream))
+    _check(st, "qk_mul_mat_vec")
+    return y
+
+
+def mul_mat(fmt, w, m, k, x, y=None, stream=None):
+    """y (n, m) = x (n, k, fp16) @ f16(W)^T on the matrix cores."""
+    import torch
+    n = x.shape[0]
+    if x.dtype != torch.float16 or x.stride(1) != 1:
+        raise TypeError("x must be float16 with contiguous columns")
+    if y is None:
+        y = torch.empty((n, m), dtype=torch.float32, device=x.device)
+    st = qk_mul_mat(fmt, w.data_ptr(), m, k, x.data_ptr(), n, x.stride(0),
+                    y.data_ptr(), y.stride(0), _stream(stream))
+    _check(st, "qk_mul_mat")
+    return y

@@ -1,0 +1,150 @@
+/*
+ * qk.h - C ABI of libqk: ggml block-quantized dequantize, GEMV and GEMM on
+ * AMD gfx950 (MI355X).
+ *
+ * Block formats (32 weights per block, little-endian binary16 fields, blocks
+ * packed back to back, a matrix stored row after row with k/32 blocks per row
+ * and no padding):
+ *   QK_Q4_0  d[2] qs[16]       18 bytes  w = d*q + (-8*d),  q = nibble 0..15
+ *   QK_Q4_1  d[2] m[2] qs[16]  20 bytes  w = d*q + m
+ *   QK_Q8_0  d[2] qs[32]       34 bytes  w = d*q,           q = int8
+ * For Q4_x, quant byte j holds element j in its low nibble and element j+16 in
+ * its high nibble.  Source: "llama_cpp 0.12.1 -> 0.12.2" diff of ggml-cuda.cu
+ * (diffend, page 4), hunks adding dequantize_block_q4_0, dequantize_block_q4_1
+ * and dequantize_block_q8_0_f16; the row launchers dequantize_row_q4_*_cuda
+ * give the 32-weight block (nb32 = k/32).
+ *
+ * Matrix layout follows ggml (ne0 is the contiguous dimension):
+ *   W  m rows of k weights (row-major blocks as above);
+ *   X  n activation columns of length k, column j starting at element j*ldx;
+ *   Y  n output columns of length m, column j starting at element j*ldy.
+ *
+ * Conventions shared by every call:
+ *   - Pointers are device pointers (or host-registered/managed memory the GPU
+ *     can read) owned by the caller; they are borrowed until the enqueued work
+ *     completes.  The library allocates, frees and synchronizes nothing and
+ *     keeps no state, so calls are re-entrant.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.  Work
+ *     is enqueued on it and the call returns without waiting.
+ *   - The return value is QK_OK or an error code.  When validation fails,
+ *     nothing is enqueued.  The library never aborts or prints.
+ *   - m == 0, rows == 0 or n == 0 is a no-op returning QK_OK.
+ *   - k must be a non-negative multiple of 32 (QK_ERR_INVALID_ARG otherwise).
+ *   - Output ranges must not overlap input ranges (QK_ERR_INVALID_ARG).
+ */
+#ifndef QK_H
+#define QK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Block formats (this library's own numbering). */
+enum qk_format {
+    QK_Q4_0 = 1,
+    QK_Q4_1 = 2,
+    QK_Q8_0 = 3
+};
+
+/* Output element types of qk_dequantize. */
+enum qk_dtype {
+    QK_F32 = 0,
+    QK_F16 = 1
+};
+
+/* Status codes. */
+enum qk_status {
+    QK_OK = 0,
+    QK_ERR_INVALID_ARG = 1,   /* null pointer, bad size, k % 32 != 0, n out of
+                                 range, ld too small, overlapping in/out */
+    QK_ERR_UNSUPPORTED = 2,   /* unknown format or output dtype */
+    QK_ERR_ALIGNMENT = 3,     /* w not 2-byte aligned, or x / y / out not
+                                 aligned to their element size */
+    QK_ERR_LAUNCH = 4         /* the HIP runtime refused the kernel launch */
+};
+
+/* Bytes per 32-weight block: 18, 20 or 34; 0 for an unknown format. */
+size_t qk_block_bytes(int fmt);
+
+/* Bytes of one row of k weights (k a multiple of 32); 0 on a bad argument. */
+size_t qk_row_bytes(int fmt, int64_t k);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *qk_status_string(int status);
+
+/* Library version as an integer (major*10000 + minor*100 + patch). */
+int qk_version(void);
+
+/*
+ * qk_dequantize - convert a rows x k quantized matrix to fp32 or fp16.
+ *
+ *   out[r*k + c] = W[r, c]   for r < rows, c < k.
+ *
+ * fp32: the value is computed in fp32 in the order shown in the format table
+ * (multiply, then add; no fused multiply-add), which is exact for Q4_0 and
+ * Q8_0 and one round-to-nearest-even for Q4_1.  Q4_0 with q = 8 gives +0.0.
+ * fp16: one round-to-nearest-even of that fp32 value (overflow to +-inf,
+ * subnormals kept).
+ * Source: dequantize_block_q4_0 / _q4_1 / _q8_0_f16 hunks and the
+ * ggml_get_to_fp16_cuda / ggml_get_to_fp32_cuda dispatch in the same diff.
+ *
+ *   fmt        QK_Q4_0, QK_Q4_1 or QK_Q8_0
+ *   w          rows*k/32 blocks; 2-byte aligned
+ *   rows, k    rows >= 0, k >= 0, k % 32 == 0
+ *   out_dtype  QK_F32 or QK_F16
+ *   out        rows*k elements of out_dtype, aligned to the element size
+ *   stream     hipStream_t or NULL
+ */
+int qk_dequantize(int fmt, const void *w, int64_t rows, int64_t k,
+                  int out_dtype, void *out, void *stream);
+
+/*
+ * qk_mul_mat_vec - fused quantized GEMV for decode: dequantize in registers
+ * and multiply by 1..8 fp32 activation vectors, accumulating in fp32.
+ *
+ *   y[j*ldy + i] = sum_c W[i, c] * x[j*ldx + c]   for i < m, j < n   (overwrite)
+ *
+ * Each product uses the exact fp32 weight value, so the result is within a
+ * few fp32 roundings per term of the exact sum: |y - exact| is a small
+ * multiple of 2^-24 * sum_c |W[i,c] x[j*ldx+c]|.
+ * Source: dequantize_mul_mat_vec (the "dmmv" tuning block) and the
+ * ggml_cuda_op_mul_mat row-range x column-count driver in the same diff,
+ * which use it when the right operand is a vector.
+ *
+ *   w          m rows of k/32 blocks; 2-byte aligned
+ *   m, k       m >= 0, k >= 0, k % 32 == 0
+ *   x          fp32, 4-byte aligned; n columns, stride ldx >= k
+ *   n          0..8 (0 is a no-op; above 8: QK_ERR_INVALID_ARG)
+ *   y          fp32, 4-byte aligned; n columns, stride ldy >= m
+ */
+int qk_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k,
+                   const float *x, int64_t n, int64_t ldx,
+                   float *y, int64_t ldy, void *stream);
+
+/*
+ * qk_mul_mat - batched GEMM: weights dequantized to fp16 tiles in LDS and
+ * multiplied by fp16 activations on the matrix cores, accumulating in fp32.
+ *
+ *   y[j*ldy + i] = sum_c f16(W[i, c]) * x[j*ldx + c]   for i < m, j < n
+ *
+ * f16(W) is the qk_dequantize fp16 value (one RNE of the fp32 weight).
+ * Source: the dequantize-to-fp16 then GEMM path (ggml_get_to_fp16_cuda feeding
+ * the BLAS mul_mat) and ggml_cuda_mul_mat's choice of a batched kernel when
+ * the right operand has more than one column, in the same diff.
+ *
+ *   x          binary16, 2-byte aligned; n columns, stride ldx >= k
+ *   n          n >= 0
+ *   y          fp32, 4-byte aligned; n columns, stride ldy >= m
+ */
+int qk_mul_mat(int fmt, const void *w, int64_t m, int64_t k,
+               const void *x_f16, int64_t n, int64_t ldx,
+               float *y, int64_t ldy, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QK_H */

@@ -1,0 +1,128 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status before
+touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dequant_quantized_gemv_amd import qk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qk.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qk_\w+)\s*\(", text)))
+
+
+def _declared_enums():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"\b(QK_\w+)\s*=\s*(\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return qk.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    funcs = _declared_functions()
+    assert set(funcs) == set(qk.SYMBOLS)
+    for name in funcs:
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_binding_constants_match_header():
+    enums = _declared_enums()
+    for name in ("QK_Q4_0", "QK_Q4_1", "QK_Q8_0", "QK_F32", "QK_F16", "QK_OK",
+                 "QK_ERR_INVALID_ARG", "QK_ERR_UNSUPPORTED", "QK_ERR_ALIGNMENT",
+                 "QK_ERR_LAUNCH"):
+        assert getattr(qk, name) == enums[name], name
+
+
+def test_sizes_and_strings(lib):
+    assert qk.block_bytes("q4_0") == 18
+    assert qk.block_bytes("q4_1") == 20
+    assert qk.block_bytes("q8_0") == 34
+    assert lib.qk_block_bytes(0) == 0 and lib.qk_block_bytes(99) == 0
+    assert qk.row_bytes("q4_0", 4096) == 2304
+    assert qk.row_bytes("q8_0", 11008) == 344 * 34
+    assert qk.row_bytes("q4_1", 33) == 0 and qk.row_bytes("q4_1", -32) == 0
+    for s in range(6):
+        assert isinstance(qk.status_string(s), str) and qk.status_string(s)
+    assert qk.status_string(0) == "ok"
+    assert lib.qk_version() >= 100
+
+
+# Fake, never-dereferenced device addresses: every call below fails validation.
+W, X, Y, OUT = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+E = qk
+
+
+@pytest.mark.parametrize("args,want", [
+    ((0, W, 4, 64, E.QK_F32, OUT), E.QK_ERR_UNSUPPORTED),           # bad format
+    ((E.QK_Q4_0, W, 4, 64, 7, OUT), E.QK_ERR_UNSUPPORTED),          # bad dtype
+    ((E.QK_Q4_0, W, 4, 63, E.QK_F32, OUT), E.QK_ERR_INVALID_ARG),   # k % 32
+    ((E.QK_Q4_0, W, -1, 64, E.QK_F32, OUT), E.QK_ERR_INVALID_ARG),  # negative rows
+    ((E.QK_Q4_0, None, 4, 64, E.QK_F32, OUT), E.QK_ERR_INVALID_ARG),  # null w
+    ((E.QK_Q4_0, W, 4, 64, E.QK_F32, None), E.QK_ERR_INVALID_ARG),  # null out
+    ((E.QK_Q4_0, W + 1, 4, 64, E.QK_F32, OUT), E.QK_ERR_ALIGNMENT),  # odd w
+    ((E.QK_Q4_0, W, 4, 64, E.QK_F32, OUT + 2), E.QK_ERR_ALIGNMENT),  # f32 out not 4-aligned
+    ((E.QK_Q4_0, W, 4, 64, E.QK_F16, OUT + 1), E.QK_ERR_ALIGNMENT),  # f16 out odd
+    ((E.QK_Q4_0, W, 4, 64, E.QK_F32, W + 8), E.QK_ERR_INVALID_ARG),  # overlap
+    ((E.QK_Q4_0, W, 2**40, 2**31 - 32, E.QK_F32, OUT), E.QK_ERR_INVALID_ARG),  # too big
+    ((E.QK_Q4_0, W, 2**30, 2**10, E.QK_F32, OUT), E.QK_ERR_INVALID_ARG),  # grid too big
+    ((E.QK_Q4_0, None, 0, 64, E.QK_F32, None), E.QK_OK),            # empty: no-op
+    ((E.QK_Q4_0, None, 5, 0, E.QK_F32, None), E.QK_OK),             # k == 0: no-op
+])
+def test_dequantize_validation(args, want):
+    assert qk.qk_dequantize(*args, 0) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((9, W, 8, 64, X, 1, 64, Y, 8), E.QK_ERR_UNSUPPORTED),
+    ((E.QK_Q8_0, W, 8, 48, X, 1, 64, Y, 8), E.QK_ERR_INVALID_ARG),   # k % 32
+    ((E.QK_Q8_0, W, 8, 64, X, 9, 64, Y, 8), E.QK_ERR_INVALID_ARG),   # n > 8
+    ((E.QK_Q8_0, W, 8, 64, X, -1, 64, Y, 8), E.QK_ERR_INVALID_ARG),  # n < 0
+    ((E.QK_Q8_0, W, 8, 64, X, 2, 63, Y, 8), E.QK_ERR_INVALID_ARG),   # ldx < k
+    ((E.QK_Q8_0, W, 8, 64, X, 2, 64, Y, 7), E.QK_ERR_INVALID_ARG),   # ldy < m
+    ((E.QK_Q8_0, None, 8, 64, X, 1, 64, Y, 8), E.QK_ERR_INVALID_ARG),
+    ((E.QK_Q8_0, W, 8, 64, None, 1, 64, Y, 8), E.QK_ERR_INVALID_ARG),
+    ((E.QK_Q8_0, W, 8, 64, X, 1, 64, None, 8), E.QK_ERR_INVALID_ARG),
+    ((E.QK_Q8_0, W + 1, 8, 64, X, 1, 64, Y, 8), E.QK_ERR_ALIGNMENT),
+    ((E.QK_Q8_0, W, 8, 64, X + 2, 1, 64, Y, 8), E.QK_ERR_ALIGNMENT),
+    ((E.QK_Q8_0, W, 8, 64, X, 1, 64, Y + 2, 8), E.QK_ERR_ALIGNMENT),
+    ((E.QK_Q8_0, W, 8, 64, X, 1, 64, W + 4, 8), E.QK_ERR_INVALID_ARG),   # y overlaps w
+    ((E.QK_Q8_0, W, 8, 64, X, 2, 64, X + 256, 8), E.QK_ERR_INVALID_ARG),  # y overlaps x
+    ((E.QK_Q8_0, W, 0, 64, X, 1, 64, Y, 8), E.QK_OK),                # m == 0
+    ((E.QK_Q8_0, W, 8, 64, X, 0, 64, Y, 8), E.QK_OK),                # n == 0
+])
+def test_mul_mat_vec_validation(args, want):
+    assert qk.qk_mul_mat_vec(*args, 0) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((4, W, 8, 64, X, 16, 64, Y, 8), E.QK_ERR_UNSUPPORTED),
+    ((E.QK_Q4_0, W, 8, 40, X, 16, 64, Y, 8), E.QK_ERR_INVALID_ARG),
+    ((E.QK_Q4_0, W, 8, 64, X, -3, 64, Y, 8), E.QK_ERR_INVALID_ARG),
+    ((E.QK_Q4_0, W, 8, 64, X, 16, 32, Y, 8), E.QK_ERR_INVALID_ARG),
+    ((E.QK_Q4_0, W, 8, 64, X, 16, 64, Y, 4), E.QK_ERR_INVALID_ARG),
+    ((E.QK_Q4_0, W, 8, 64, X + 1, 16, 64, Y, 8), E.QK_ERR_ALIGNMENT),
+    ((E.QK_Q4_0, W, 8, 64, X, 16, 64, Y + 1, 8), E.QK_ERR_ALIGNMENT),
+    ((E.QK_Q4_0, W, 8, 64, X, 16, 64, X + 64, 8), E.QK_ERR_INVALID_ARG),  # y overlaps x
+    ((E.QK_Q4_0, None, 8, 64, X, 16, 64, Y, 8), E.QK_ERR_INVALID_ARG),
+    ((E.QK_Q4_0, W, 8, 64, X, 0, 64, Y, 8), E.QK_OK),
+    ((E.QK_Q4_0, W, 0, 64, X, 16, 64, Y, 8), E.QK_OK),
+])
+def test_mul_mat_validation(args, want):
+    assert qk.qk_mul_mat(*args, 0) == want
+
+
+def test_binding_raises_on_error_status():
+    err = qk.QKError(qk.QK_ERR_ALIGNMENT, "qk_mul_mat")
+    assert "misaligned" in str(err) and err.status == qk.QK_ERR_ALIGNMENT
