@@ -66,11 +66,25 @@ __device__ __forceinline__ uint32_t lds_u32_a2(const uint8_t *base, int byte_off
     return (uint32_t)p[0] | ((uint32_t)p[1] << 16);
 }
 
-// Sum over the 64 lanes of a wave; every lane gets the total.
+// DPP lane-shuffle of a float (rows of 16 lanes; lanes outside row_mask
+// read 0).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 ROW_MASK, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave with DPP, returned to every lane:
+// xor 1 and xor 2 within quads, half-row and row mirrors give every lane its
+// 16-lane row sum, then two row broadcasts fold rows 0..3 into lane 63.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += dpp<0xB1>(v);         // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);         // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);        // row_half_mirror
+    v += dpp<0x140>(v);        // row_mirror
+    v += dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 }  // namespace qk
