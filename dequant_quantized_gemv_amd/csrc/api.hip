@@ -72,20 +72,58 @@ int qk_dequantize(int fmt, const void *w, int64_t rows, int64_t k, int out_dtype
                                  static_cast<hipStream_t>(stream));
 }
 
+// Checks one GEMV problem (n already known to be 1..8); QK_OK if valid.
+static int check_gemv_item(int fmt, const qk_mat_vec_item &it, int64_t n) {
+    if (it.m < 0 || it.k < 0 || it.k % 32 != 0) return QK_ERR_INVALID_ARG;
+    if (it.m == 0) return QK_OK;
+    if (it.m > kMaxDim || it.k > kMaxDim || it.ldx < it.k || it.ldy < it.m) return QK_ERR_INVALID_ARG;
+    if (it.y == nullptr || (it.k > 0 && (it.w == nullptr || it.x == nullptr))) return QK_ERR_INVALID_ARG;
+    if ((uintptr_t)it.w % 2 != 0 || (uintptr_t)it.x % 4 != 0 || (uintptr_t)it.y % 4 != 0)
+        return QK_ERR_ALIGNMENT;
+    const size_t wbytes = (size_t)it.m * (size_t)(it.k / 32) * qk::block_bytes_host(fmt);
+    const size_t xbytes = span_bytes(n, it.ldx, it.k, 4);
+    const size_t ybytes = span_bytes(n, it.ldy, it.m, 4);
+    if (overlaps(it.y, ybytes, it.w, wbytes) || overlaps(it.y, ybytes, it.x, xbytes))
+        return QK_ERR_INVALID_ARG;
+    return QK_OK;
+}
+
 int qk_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k, const float *x, int64_t n,
                    int64_t ldx, float *y, int64_t ldy, void *stream) {
     if (!fmt_ok(fmt)) return QK_ERR_UNSUPPORTED;
     if (m < 0 || k < 0 || k % 32 != 0 || n < 0 || n > 8) return QK_ERR_INVALID_ARG;
     if (m == 0 || n == 0) return QK_OK;
-    if (m > kMaxDim || k > kMaxDim || ldx < k || ldy < m) return QK_ERR_INVALID_ARG;
-    if (y == nullptr || (k > 0 && (w == nullptr || x == nullptr))) return QK_ERR_INVALID_ARG;
-    if ((uintptr_t)w % 2 != 0 || (uintptr_t)x % 4 != 0 || (uintptr_t)y % 4 != 0)
-        return QK_ERR_ALIGNMENT;
-    const size_t wbytes = (size_t)m * (size_t)(k / 32) * qk::block_bytes_host(fmt);
-    const size_t xbytes = span_bytes(n, ldx, k, 4);
-    const size_t ybytes = span_bytes(n, ldy, m, 4);
-    if (overlaps(y, ybytes, w, wbytes) || overlaps(y, ybytes, x, xbytes)) return QK_ERR_INVALID_ARG;
+    const qk_mat_vec_item it{w, m, k, x, ldx, y, ldy};
+    const int st = check_gemv_item(fmt, it, n);
+    if (st != QK_OK) return st;
     return qk::launch_mul_mat_vec(fmt, w, m, k, x, n, ldx, y, ldy, static_cast<hipStream_t>(stream));
+}
+
+int qk_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count, int64_t n,
+                           void *stream) {
+    if (!fmt_ok(fmt)) return QK_ERR_UNSUPPORTED;
+    if (count < 0 || count > QK_MAX_BATCH || n < 0 || n > 8) return QK_ERR_INVALID_ARG;
+    if (count == 0 || n == 0) return QK_OK;
+    if (items == nullptr) return QK_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i) {
+        const int st = check_gemv_item(fmt, items[i], n);
+        if (st != QK_OK) return st;
+    }
+    // no output may overlap another item's inputs or output
+    for (int i = 0; i < count; ++i) {
+        const qk_mat_vec_item &a = items[i];
+        if (a.m == 0) continue;
+        const size_t ya = span_bytes(n, a.ldy, a.m, 4);
+        for (int j = 0; j < count; ++j) {
+            const qk_mat_vec_item &b = items[j];
+            if (j == i || b.m == 0) continue;
+            const size_t wb = (size_t)b.m * (size_t)(b.k / 32) * qk::block_bytes_host(fmt);
+            if (overlaps(a.y, ya, b.w, wb) || overlaps(a.y, ya, b.x, span_bytes(n, b.ldx, b.k, 4)) ||
+                overlaps(a.y, ya, b.y, span_bytes(n, b.ldy, b.m, 4)))
+                return QK_ERR_INVALID_ARG;
+        }
+    }
+    return qk::launch_mul_mat_vec_batched(fmt, items, count, n, static_cast<hipStream_t>(stream));
 }
 
 int qk_mul_mat(int fmt, const void *w, int64_t m, int64_t k, const void *x_f16, int64_t n,

@@ -37,11 +37,12 @@
 #include "qk_common.h"
 #include "qk_internal.h"
 
+#include <type_traits>
+
 namespace qk {
 
 constexpr int kGvChunkPairs = 64;                   // pairs per chunk (one per lane)
 constexpr int kGvChunkElems = kGvChunkPairs * 64;   // 4096 weights per chunk
-constexpr int kGvXPitch = kGvChunkElems + kGvChunkElems / 16;  // floats per column in LDS (padded)
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
@@ -209,279 +210,487 @@ __device__ __forceinline__ float group_q4_1(uint32_t qw, float d, float mm, cons
     return a;
 }
 
-// float4 of x (column j) at chunk-relative element e (e % 4 == 0) from LDS.
-__device__ __forceinline__ float4 x_lds(const float *xs, int j, int e) {
-    return *reinterpret_cast<const float4 *>(xs + j * kGvXPitch + e + (e >> 6) * 4);
+// float4 of x (column j) at window-relative element e (e % 4 == 0) from LDS;
+// column pitch xp floats.
+__device__ __forceinline__ float4 x_lds(const float *xs, int xp, int j, int e) {
+    return *reinterpret_cast<const float4 *>(xs + j * xp + e + (e >> 6) * 4);
 }
 
-// FAST: w 4-byte aligned, an even number of blocks per row, x 16-byte aligned
-// and ldx % 4 == 0.
-//
-// The grid walks row groups of 4*RWV rows: workgroup g takes groups g,
-// g + gridDim.x, ...  When K fits in one chunk, x is staged once and reused by
-// every group the workgroup takes.
-template <int FMT, int NC, int RWV, int WPG, bool FAST>
-__global__ __launch_bounds__(64 * WPG) void gemv_kernel(
-    const uint8_t *__restrict__ w, int m, int nb, const float *__restrict__ x, int64_t ldx,
-    float *__restrict__ y, int64_t ldy) {
-    constexpr int BS = Format<FMT>::kBytes;
-    constexpr int ND = Pair<FMT>::kDwords;
-    constexpr int RG = WPG * RWV;  // rows per group
-    constexpr int NT = 64 * WPG;   // lanes per workgroup
-    __shared__ __attribute__((aligned(16))) float xs[NC * kGvXPitch];
+// One problem of a (possibly grouped) launch: y = W x for NC columns.
+struct GemvItem {
+    const uint8_t *w;
+    const float *x;
+    float *y;
+    int64_t ldx;
+    int64_t ldy;
+    int m;
+    int nb;  // blocks per row
+};
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int npairs = (nb + 1) >> 1;
-    const int k = nb * 32;
-    const int64_t row_bytes = (int64_t)nb * BS;
-    const int ngroups = (m + RG - 1) / RG;
-    int staged = -1;  // chunk currently in LDS (uniform across the workgroup)
+constexpr int kGvMaxItems = 16;
 
-    for (int g = blockIdx.x; g < ngroups; g += gridDim.x) {
-        const int row0 = g * RG + wave * RWV;
-        const int nrows = max(0, min(RWV, m - row0));  // rows of this wave (uniform)
-        const uint8_t *__restrict__ wr0 = w + (int64_t)row0 * row_bytes;
+// Launch arguments (passed by value in the kernel argument segment).
+// Row groups of all items are numbered consecutively: item i owns groups
+// gbase[i] .. gbase[i+1]-1.
+struct GemvArgs {
+    GemvItem item[kGvMaxItems];
+    int gbase[kGvMaxItems + 1];
+    int count;
+};
 
-        float acc[RWV][NC];
-#pragma unroll
-        for (int r = 0; r < RWV; ++r)
-#pragma unroll
-            for (int j = 0; j < NC; ++j) acc[r][j] = 0.0f;
+// Split of the launch's `total` row groups over the grid: workgroup b takes
+// per groups, plus one more if b < rem (computed on the host; no division on
+// the device).
+struct GemvSplit {
+    int total;
+    int per;
+    int rem;
+};
 
-        for (int p0 = 0; p0 < npairs; p0 += kGvChunkPairs) {
-            const int pp = p0 + lane;  // this lane's pair
-            const bool have = pp < npairs;
-            const bool second = FAST || (2 * pp + 1 < nb);
-
-            // Activations of this chunk go to LDS once per workgroup and chunk.
-            // Their loads are issued before the weight loads, so writing them
-            // to LDS does not wait for the weights (loads complete in order).
-            const int chunk = p0 / kGvChunkPairs;
-            const bool stage = staged != chunk;
-            const int e0 = p0 * 64;
-            const int ce4 = min(kGvChunkElems, k - e0) / 4;  // float4s in this chunk
-            constexpr int XR = NC <= 2 ? NC : 0;  // columns staged through registers
-            constexpr int XU = (kGvChunkElems / 4 + NT - 1) / NT;  // float4s per lane and column
-            f32x4_t xr[XR > 0 ? XR : 1][XU];
-            if (stage) {
-                if (staged >= 0) __syncthreads();  // readers of the previous chunk are done
+// Dot products of one wave's RWV rows with this lane's pair, added to acc.
+template <int FMT, int NC, int RWV, bool FAST>
+__device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDwords], int nrows,
+                                         bool second, const float *xs, int xp, int el,
+                                         float (&acc)[RWV][NC]) {
 #pragma unroll
-                for (int j = 0; j < XR; ++j) {
-                    const float *xj = x + j * ldx + e0;
+    for (int b = 0; b < 2; ++b) {
+        if (!FAST && b == 1 && !second) break;
+        if constexpr (FMT == QK_Q4_1) {
 #pragma unroll
-                    for (int u = 0; u < XU; ++u) {
-                        // clamped so every lane loads (a tail lane repeats the
-                        // last float4 and does not store it)
-                        const int t = min(tid + u * NT, ce4 - 1);
-                        if (FAST) {
-                            xr[j][u] = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
-                        } else {
-                            xr[j][u] = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
-                        }
-                    }
-                }
-            }
-
-            // weights of this chunk for the wave's rows, straight to registers
-            uint32_t v[RWV][ND];
-#pragma unroll
-            for (int r = 0; r < RWV; ++r) {
-                if (r < nrows && have) {
-                    const uint8_t *p = wr0 + r * row_bytes + (int64_t)pp * (2 * BS);
-                    if (FAST) load_pair_fast<FMT>(p, v[r]);
-                    else load_pair_generic<FMT>(p, second, v[r]);
-                }
-            }
-
-            if (stage) {
-#pragma unroll
-                for (int j = 0; j < XR; ++j)
-#pragma unroll
-                    for (int u = 0; u < XU; ++u) {
-                        const int t = tid + u * NT;
-                        if (t < ce4) *reinterpret_cast<f32x4_t *>(xs + j * kGvXPitch + 4 * t + (t >> 4) * 4) = xr[j][u];
-                    }
-#pragma unroll
-                for (int j = XR; j < NC; ++j) {
-                    const float *xj = x + j * ldx + e0;
-                    for (int t = tid; t < ce4; t += NT) {
-                        float4 val;
-                        if (FAST) {
-                            val = *reinterpret_cast<const float4 *>(xj + 4 * t);
-                        } else {
-                            val = make_float4(xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]);
-                        }
-                        *reinterpret_cast<float4 *>(xs + j * kGvXPitch + 4 * t + (t >> 4) * 4) = val;
-                    }
-                }
-                __syncthreads();
-                staged = chunk;
-            }
-
-            if (have && nrows > 0) {
-                const int el = lane * 64;  // chunk-relative element of this lane's pair
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    if (!FAST && b == 1 && !second) break;
-                    if constexpr (FMT == QK_Q4_1) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            float4 xa[NC], xb[NC];
-#pragma unroll
-                            for (int j = 0; j < NC; ++j) {
-                                xa[j] = x_lds(xs, j, el + 32 * b + 4 * i);
-                                xb[j] = x_lds(xs, j, el + 32 * b + 16 + 4 * i);
-                            }
-#pragma unroll
-                            for (int r = 0; r < RWV; ++r) {
-                                if (r < nrows) {
-                                    const float d = h2f(pair_d<FMT>(v[r], b));
-                                    const float mm = h2f(pair_m_q41(v[r], b));
-                                    const uint32_t qw = pair_qs<FMT>(v[r], b, i);
-                                    const uint32_t lo = qw & 0x0F0F0F0Fu;
-                                    const uint32_t hi = (qw >> 4) & 0x0F0F0F0Fu;
-                                    const float w0 = wval(d, ubyte_f<0>(lo), mm), w1 = wval(d, ubyte_f<1>(lo), mm);
-                                    const float w2 = wval(d, ubyte_f<2>(lo), mm), w3 = wval(d, ubyte_f<3>(lo), mm);
-                                    const float w4 = wval(d, ubyte_f<0>(hi), mm), w5 = wval(d, ubyte_f<1>(hi), mm);
-                                    const float w6 = wval(d, ubyte_f<2>(hi), mm), w7 = wval(d, ubyte_f<3>(hi), mm);
-#pragma unroll
-                                    for (int j = 0; j < NC; ++j) {
-                                        float a = acc[r][j];
-                                        a = __builtin_fmaf(w0, xa[j].x, a);
-                                        a = __builtin_fmaf(w1, xa[j].y, a);
-                                        a = __builtin_fmaf(w2, xa[j].z, a);
-                                        a = __builtin_fmaf(w3, xa[j].w, a);
-                                        a = __builtin_fmaf(w4, xb[j].x, a);
-                                        a = __builtin_fmaf(w5, xb[j].y, a);
-                                        a = __builtin_fmaf(w6, xb[j].z, a);
-                                        a = __builtin_fmaf(w7, xb[j].w, a);
-                                        acc[r][j] = a;
-                                    }
-                                }
-                            }
-                            // keep the next group's LDS reads from being hoisted
-                            // above this one (bounds the live activations)
-                            if constexpr (NC >= 2) __builtin_amdgcn_sched_barrier(0);
-                        }
-                    } else {
-                        float s[RWV][NC];
-#pragma unroll
-                        for (int r = 0; r < RWV; ++r)
-#pragma unroll
-                            for (int j = 0; j < NC; ++j) s[r][j] = 0.0f;
-                        constexpr int NGRP = (FMT == QK_Q8_0) ? 8 : 4;
-#pragma unroll
-                        for (int i = 0; i < NGRP; ++i) {
-                            float4 xa[NC], xb[NC];
-#pragma unroll
-                            for (int j = 0; j < NC; ++j) {
-                                xa[j] = x_lds(xs, j, el + 32 * b + 4 * i);
-                                if (FMT == QK_Q4_0) xb[j] = x_lds(xs, j, el + 32 * b + 16 + 4 * i);
-                            }
-#pragma unroll
-                            for (int r = 0; r < RWV; ++r) {
-                                if (r < nrows) {
-#pragma unroll
-                                    for (int j = 0; j < NC; ++j) {
-                                        if constexpr (FMT == QK_Q4_0) {
-                                            s[r][j] = group_q4_0(pair_qs<FMT>(v[r], b, i), xa[j], xb[j], s[r][j]);
-                                        } else if (b == 0) {
-                                            s[r][j] = group_q8_0_split(v[r][i], v[r][i + 1], xa[j], s[r][j]);
-                                        } else {
-                                            s[r][j] = group_q8_0(v[r][9 + i], xa[j], s[r][j]);
-                                        }
-                                    }
-                                }
-                            }
-                            if constexpr (NC >= 3) __builtin_amdgcn_sched_barrier(0);
-                        }
-#pragma unroll
-                        for (int r = 0; r < RWV; ++r) {
-                            if (r < nrows) {
-                                const float d = h2f(pair_d<FMT>(v[r], b));
-#pragma unroll
-                                for (int j = 0; j < NC; ++j) acc[r][j] = __builtin_fmaf(d, s[r][j], acc[r][j]);
-                            }
-                        }
-                    }
-                }
-            }
-        }
-
-#pragma unroll
-        for (int r = 0; r < RWV; ++r) {
-            if (r < nrows) {
+            for (int i = 0; i < 4; ++i) {
+                float4 xa[NC], xb[NC];
 #pragma unroll
                 for (int j = 0; j < NC; ++j) {
-                    const float sum = wave_sum(acc[r][j]);
-                    if (lane == 0) y[j * ldy + row0 + r] = sum;
+                    xa[j] = x_lds(xs, xp, j, el + 32 * b + 4 * i);
+                    xb[j] = x_lds(xs, xp, j, el + 32 * b + 16 + 4 * i);
+                }
+#pragma unroll
+                for (int r = 0; r < RWV; ++r) {
+                    if (r < nrows) {
+                        const float d = h2f(pair_d<FMT>(v[r], b));
+                        const float mm = h2f(pair_m_q41(v[r], b));
+                        const uint32_t qw = pair_qs<FMT>(v[r], b, i);
+                        const uint32_t lo = qw & 0x0F0F0F0Fu;
+                        const uint32_t hi = (qw >> 4) & 0x0F0F0F0Fu;
+                        const float w0 = wval(d, ubyte_f<0>(lo), mm), w1 = wval(d, ubyte_f<1>(lo), mm);
+                        const float w2 = wval(d, ubyte_f<2>(lo), mm), w3 = wval(d, ubyte_f<3>(lo), mm);
+                        const float w4 = wval(d, ubyte_f<0>(hi), mm), w5 = wval(d, ubyte_f<1>(hi), mm);
+                        const float w6 = wval(d, ubyte_f<2>(hi), mm), w7 = wval(d, ubyte_f<3>(hi), mm);
+#pragma unroll
+                        for (int j = 0; j < NC; ++j) {
+                            float a = acc[r][j];
+                            a = __builtin_fmaf(w0, xa[j].x, a);
+                            a = __builtin_fmaf(w1, xa[j].y, a);
+                            a = __builtin_fmaf(w2, xa[j].z, a);
+                            a = __builtin_fmaf(w3, xa[j].w, a);
+                            a = __builtin_fmaf(w4, xb[j].x, a);
+                            a = __builtin_fmaf(w5, xb[j].y, a);
+                            a = __builtin_fmaf(w6, xb[j].z, a);
+                            a = __builtin_fmaf(w7, xb[j].w, a);
+                            acc[r][j] = a;
+                        }
+                    }
+                }
+                // keep the next group's LDS reads from being hoisted above
+                // this one (bounds the live activations)
+                if constexpr (NC >= 2) __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            float s[RWV][NC];
+#pragma unroll
+            for (int r = 0; r < RWV; ++r)
+#pragma unroll
+                for (int j = 0; j < NC; ++j) s[r][j] = 0.0f;
+            constexpr int NGRP = (FMT == QK_Q8_0) ? 8 : 4;
+#pragma unroll
+            for (int i = 0; i < NGRP; ++i) {
+                float4 xa[NC], xb[NC];
+#pragma unroll
+                for (int j = 0; j < NC; ++j) {
+                    xa[j] = x_lds(xs, xp, j, el + 32 * b + 4 * i);
+                    if (FMT == QK_Q4_0) xb[j] = x_lds(xs, xp, j, el + 32 * b + 16 + 4 * i);
+                }
+#pragma unroll
+                for (int r = 0; r < RWV; ++r) {
+                    if (r < nrows) {
+#pragma unroll
+                        for (int j = 0; j < NC; ++j) {
+                            if constexpr (FMT == QK_Q4_0) {
+                                s[r][j] = group_q4_0(pair_qs<FMT>(v[r], b, i), xa[j], xb[j], s[r][j]);
+                            } else if (b == 0) {
+                                s[r][j] = group_q8_0_split(v[r][i], v[r][i + 1], xa[j], s[r][j]);
+                            } else {
+                                s[r][j] = group_q8_0(v[r][9 + i], xa[j], s[r][j]);
+                            }
+                        }
+                    }
+                }
+                if constexpr (NC >= 3) __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int r = 0; r < RWV; ++r) {
+                if (r < nrows) {
+                    const float d = h2f(pair_d<FMT>(v[r], b));
+#pragma unroll
+                    for (int j = 0; j < NC; ++j) acc[r][j] = __builtin_fmaf(d, s[r][j], acc[r][j]);
                 }
             }
         }
     }
 }
 
-// Launch shape by column count: RWV rows per wave (registers hold RWV pairs
-// of weights and RWV * NC partial sums), WPG waves per workgroup sharing one
-// LDS copy of the activations.
+// FAST: for every item, w 4-byte aligned, an even number of blocks per row,
+// x 16-byte aligned and ldx % 4 == 0.
+//
+// The launch's row groups (WPG*RWV rows each, all items numbered in a row) are
+// split into gridDim.x contiguous ranges, one per workgroup.  A workgroup walks
+// its range as a sequence of steps (row group, K chunk); each step's weights
+// were requested during the previous step, and x is re-staged only when the
+// item or the chunk changes.
+// The activation window staged in LDS: `xw` weights (a multiple of 4096) per
+// column, each run of 64 floats followed by 4 floats of padding.
+__host__ __device__ constexpr int xw_pitch(int xw) { return xw + xw / 16; }
+
+// FAST: for every item, w 4-byte aligned, an even number of blocks per row,
+// x 16-byte aligned and ldx % 4 == 0.
+//
+// The launch's row groups (WPG*RWV rows each, all items numbered in a row)
+// are split into gridDim.x contiguous ranges, one per workgroup.  A workgroup
+// walks its range as a sequence of steps (row group, chunk of 4096 weights);
+// in a step lane p takes pair p of the chunk.  Each step's weights were
+// requested during the previous step (two register sets used in turn).  The
+// activations are staged into LDS in windows of `xw` weights (the whole row
+// when K <= xw), only when the item or the window changes.
+// SINGLE: one item, passed in its own argument (fixed offsets, no indexed
+// reads of the item table before the first weight load).
+template <int FMT, int NC, int RWV, int WPG, bool FAST, bool SINGLE>
+__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 1 || (NC == 2 && FMT != QK_Q8_0) ? 4 : (NC == 2 ? 2 : 1)))) void gemv_kernel(const GemvArgs args, const GemvItem one,
+                                                        const GemvSplit split, const int xw) {
+    constexpr int BS = Format<FMT>::kBytes;
+    constexpr int ND = Pair<FMT>::kDwords;
+    constexpr int RG = WPG * RWV;               // rows per group
+    constexpr int NT = 64 * WPG;                // lanes per workgroup
+    constexpr int CP = kGvChunkPairs;           // pairs per step
+    constexpr int CE = kGvChunkElems;           // weights per step
+    extern __shared__ __attribute__((aligned(16))) float xs[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int b = blockIdx.x;
+    const int gbeg = b * split.per + min(b, split.rem);
+    const int gend = gbeg + split.per + (b < split.rem ? 1 : 0);
+    if (gbeg >= gend) return;  // whole workgroup, before any barrier
+    const int xp = xw_pitch(xw);
+    const int cpw = xw / CE;  // steps per activation window
+
+    const int count = SINGLE ? 1 : args.count;
+    auto gbase = [&](int i) { return SINGLE ? (i == 0 ? 0 : split.total) : args.gbase[i]; };
+    auto item = [&](int i) -> const GemvItem & { return SINGLE ? one : args.item[i]; };
+
+    // step state (uniform across the workgroup)
+    int g = gbeg, mi = 0, c = 0;
+    while (g >= gbase(mi + 1)) ++mi;
+    int staged_mi = -1, staged_w = -1;
+
+    float acc[RWV][NC];
+#pragma unroll
+    for (int r = 0; r < RWV; ++r)
+#pragma unroll
+        for (int j = 0; j < NC; ++j) acc[r][j] = 0.0f;
+
+    // Weight loads of step (sg, smi, sc) into dst.  On the fast path every lane
+    // issues the same loads with no branch around them (a lane past the last
+    // pair or row reads a clamped, valid address and ignores the data), so the
+    // compiler counts them and waits for exactly the loads a computation needs
+    // while the prefetch stays in flight.
+    auto load_step = [&](int sg, int smi, int sc, uint32_t (&dst)[RWV][ND]) {
+        const GemvItem &it = item(smi);
+        const int row0 = (sg - gbase(smi)) * RG + wave * RWV;
+        const int npairs = (it.nb + 1) >> 1;
+        const int64_t row_bytes = (int64_t)it.nb * BS;
+        const int pp = sc * CP + lane;
+        if (FAST) {
+            const int ppc = min(pp, npairs - 1);
+#pragma unroll
+            for (int r = 0; r < RWV; ++r) {
+                const int row = min(row0 + r, it.m - 1);
+                load_pair_fast<FMT>(it.w + (int64_t)row * row_bytes + (int64_t)ppc * (2 * BS), dst[r]);
+            }
+        } else if (pp < npairs) {
+            const int nrows = max(0, min(RWV, it.m - row0));
+            const uint8_t *p = it.w + (int64_t)row0 * row_bytes + (int64_t)pp * (2 * BS);
+            const bool second = 2 * pp + 1 < it.nb;
+#pragma unroll
+            for (int r = 0; r < RWV; ++r)
+                if (r < nrows) load_pair_generic<FMT>(p + r * row_bytes, second, dst[r]);
+        }
+    };
+
+    constexpr int XR = NC <= 2 ? NC : 0;  // columns staged through registers (first window)
+
+    // Copy window `wi` of item `it`'s activations into LDS (whole workgroup).
+    auto stage_x = [&](const GemvItem &it, int wi) {
+        const int e0 = wi * xw;
+        const int ce4 = min(xw, it.nb * 32 - e0) / 4;  // float4s in this window
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const float *xj = it.x + j * it.ldx + e0;
+            for (int t = tid; t < ce4; t += NT) {
+                f32x4_t val;
+                if (FAST) val = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
+                else val = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
+                *reinterpret_cast<f32x4_t *>(xs + j * xp + 4 * t + (t >> 4) * 4) = val;
+            }
+        }
+    };
+
+    // Steps in this workgroup's range.
+    int nsteps = 0;
+    {
+        int gg = gbeg, ii = mi;
+        while (gg < gend) {
+            while (gg >= gbase(ii + 1)) ++ii;
+            const int nxt = min(gend, gbase(ii + 1));
+            nsteps += (nxt - gg) * ((((item(ii).nb + 1) >> 1) + CP - 1) / CP);
+            gg = nxt;
+        }
+    }
+
+    // One step computing with cur.  PREFETCH: the next step's weights are
+    // requested into nxt before this step's computation.  Each (FIRST,
+    // PREFETCH) combination is its own straight-line code, so the compiler
+    // waits for exactly the loads the computation needs and the prefetch stays
+    // in flight.  FIRST issues the activation loads before any weight load, so
+    // copying them to LDS does not wait for the weights (loads complete in
+    // order).
+    auto step = [&](auto first_tag, auto prefetch_tag, uint32_t (&cur)[RWV][ND],
+                    uint32_t (&nxt)[RWV][ND]) {
+        constexpr bool FIRST = decltype(first_tag)::value;
+        constexpr bool PREFETCH = decltype(prefetch_tag)::value;
+        const GemvItem &it = item(mi);
+        const int npairs = (it.nb + 1) >> 1;
+        const int nchunks = (npairs + CP - 1) / CP;
+        const int wi = c / cpw;  // activation window of this step
+
+        int g2 = g, mi2 = mi, c2 = c + 1;
+        if (c2 >= nchunks) {
+            c2 = 0;
+            ++g2;
+            while (mi2 < count && g2 >= gbase(mi2 + 1)) ++mi2;
+        }
+
+        if constexpr (FIRST) {
+            // activation loads, then this step's and the next step's weights,
+            // then the LDS copy (waits only for the activations)
+            constexpr int XU = (CE / 4 + NT - 1) / NT;  // registers cover the first 4096
+            const int e0 = wi * xw;
+            const int ce4 = min(xw, it.nb * 32 - e0) / 4;
+            const int cr4 = min(CE / 4, ce4);
+            f32x4_t xr[XR > 0 ? XR : 1][XU];
+#pragma unroll
+            for (int j = 0; j < XR; ++j) {
+                const float *xj = it.x + j * it.ldx + e0;
+#pragma unroll
+                for (int u = 0; u < XU; ++u) {
+                    // clamped so every lane loads (a tail lane repeats the last
+                    // float4 and stores it again)
+                    const int t = min(tid + u * NT, cr4 - 1);
+                    if (FAST) xr[j][u] = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
+                    else xr[j][u] = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
+                }
+            }
+            load_step(g, mi, c, cur);
+            if constexpr (PREFETCH) load_step(g2, mi2, c2, nxt);
+            // unconditional stores (a tail lane rewrites the last float4 with
+            // the same value), so no load is moved behind the weight loads
+#pragma unroll
+            for (int j = 0; j < XR; ++j)
+#pragma unroll
+                for (int u = 0; u < XU; ++u) {
+                    const int t = min(tid + u * NT, cr4 - 1);
+                    *reinterpret_cast<f32x4_t *>(xs + j * xp + 4 * t + (t >> 4) * 4) = xr[j][u];
+                }
+            // the rest of the window (and wider activation sets) directly
+#pragma unroll
+            for (int j = 0; j < NC; ++j) {
+                const float *xj = it.x + j * it.ldx + e0;
+                for (int t = (j < XR ? cr4 : 0) + tid; t < ce4; t += NT) {
+                    f32x4_t val;
+                    if (FAST) val = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
+                    else val = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
+                    *reinterpret_cast<f32x4_t *>(xs + j * xp + 4 * t + (t >> 4) * 4) = val;
+                }
+            }
+            __syncthreads();
+            staged_mi = mi;
+            staged_w = wi;
+        } else {
+            // a new item or window: restage the activations before the prefetch
+            if (staged_mi != mi || staged_w != wi) {
+                __syncthreads();  // readers of the previous window are done
+                stage_x(it, wi);
+                __syncthreads();
+                staged_mi = mi;
+                staged_w = wi;
+            }
+            if constexpr (PREFETCH) load_step(g2, mi2, c2, nxt);
+        }
+
+        // compute this step
+        const int row0 = (g - gbase(mi)) * RG + wave * RWV;
+        const int nrows = max(0, min(RWV, it.m - row0));
+        const int pp = c * CP + lane;
+        if (nrows > 0 && pp < npairs)
+            pair_dot<FMT, NC, RWV, FAST>(cur, nrows, FAST || (2 * pp + 1 < it.nb), xs, xp,
+                                         (c - wi * cpw) * CE + lane * 64, acc);
+
+        // last chunk of the group: reduce across the wave and store
+        if (c == nchunks - 1) {
+#pragma unroll
+            for (int r = 0; r < RWV; ++r) {
+                if (r < nrows) {
+#pragma unroll
+                    for (int j = 0; j < NC; ++j) {
+                        const float sum = wave_sum(acc[r][j]);
+                        if (lane == 0) it.y[j * it.ldy + row0 + r] = sum;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < NC; ++j) acc[r][j] = 0.0f;
+            }
+        }
+        g = g2;
+        mi = mi2;
+        c = c2;
+    };
+
+    using T = std::true_type;
+    using F = std::false_type;
+    uint32_t va[RWV][ND], vb[RWV][ND];
+    if (nsteps == 1) {
+        step(T{}, F{}, va, vb);
+        return;
+    }
+    step(T{}, T{}, va, vb);
+    int left = nsteps - 1;  // steps still to compute; the next one's weights are in vb
+    while (true) {
+        if (left == 1) {
+            step(F{}, F{}, vb, va);
+            break;
+        }
+        step(F{}, T{}, vb, va);
+        if (--left == 1) {
+            step(F{}, F{}, va, vb);
+            break;
+        }
+        step(F{}, T{}, va, vb);
+        --left;
+    }
+}
+
+// Launch shape by column count: RWV rows per wave, WPG waves per workgroup
+// sharing one LDS copy of the activations.
 template <int NC> struct GemvShape {
     static constexpr int kRWV = 1;
     static constexpr int kWPG = NC <= 4 ? 8 : 4;
 };
 
+static int device_cus() {
+    int cus = 256, dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+        cus = v;
+    return cus;
+}
+
 template <int FMT, int NC>
-static int dispatch_gemv_nc(const uint8_t *w, int m, int nb, const float *x, int64_t ldx,
-                            float *y, int64_t ldy, hipStream_t stream) {
+static int dispatch_gemv_nc(GemvArgs &a, bool fast, hipStream_t stream) {
     constexpr int RWV = GemvShape<NC>::kRWV;
     constexpr int WPG = GemvShape<NC>::kWPG;
     constexpr int RG = WPG * RWV;
-    const int ngroups = (m + RG - 1) / RG;
-    // Enough workgroups to cover the chip several times over; beyond that a
-    // workgroup takes several row groups and reuses its staged activations.
-    int cus = 256;
-    int dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    a.gbase[0] = 0;
+    int kmax = 0;
+    for (int i = 0; i < a.count; ++i) {
+        a.gbase[i + 1] = a.gbase[i] + (a.item[i].m + RG - 1) / RG;
+        kmax = max(kmax, a.item[i].nb * 32);
     }
-    const int per_cu = NC <= 2 ? 4 : (NC <= 4 ? 2 : 1);  // LDS holds NC * 17 KiB of activations
-    const dim3 grid((unsigned)min(ngroups, cus * per_cu));
+    const int total = a.gbase[a.count];
+    if (total == 0) return QK_OK;
+    // Activation window: the longest row rounded up to 4096 weights, capped so
+    // the window stays within 64 KiB of LDS (always at least 4096 weights).
+    const int cap = max(1, (64 * 1024) / (NC * xw_pitch(kGvChunkElems) * (int)sizeof(float))) * kGvChunkElems;
+    const int xw = max(kGvChunkElems, min(cap, (kmax + kGvChunkElems - 1) / kGvChunkElems * kGvChunkElems));
+    const size_t lds = (size_t)NC * xw_pitch(xw) * sizeof(float);
+    const int per_cu = max(1, min(4, (int)((160 * 1024) / lds)));
+    const int nwg = min(total, device_cus() * per_cu);
+    const GemvSplit split{total, total / nwg, total % nwg};
+    const dim3 grid((unsigned)nwg);
     const dim3 block(64 * WPG);
-    const bool fast = ((uintptr_t)w % 4) == 0 && (nb % 2) == 0 &&
-                      ((uintptr_t)x % 16) == 0 && (ldx % 4) == 0;
-    if (fast)
-        return launch(gemv_kernel<FMT, NC, RWV, WPG, true>, grid, block, stream, w, m, nb, x, ldx, y, ldy);
-    return launch(gemv_kernel<FMT, NC, RWV, WPG, false>, grid, block, stream, w, m, nb, x, ldx, y, ldy);
+    auto go = [&](auto kern, const GemvArgs &args) -> int {
+        if (lds > 64 * 1024 &&
+            hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return QK_ERR_LAUNCH;
+        return launch_lds(kern, grid, block, lds, stream, args, a.item[0], split, xw);
+    };
+    static const GemvArgs none{};
+    if (a.count == 1) {
+        if (fast) return go(gemv_kernel<FMT, NC, RWV, WPG, true, true>, none);
+        return go(gemv_kernel<FMT, NC, RWV, WPG, false, true>, none);
+    }
+    if (fast) return go(gemv_kernel<FMT, NC, RWV, WPG, true, false>, a);
+    return go(gemv_kernel<FMT, NC, RWV, WPG, false, false>, a);
 }
 
 template <int FMT>
-static int dispatch_gemv(const uint8_t *w, int m, int nb, const float *x, int n, int64_t ldx,
-                         float *y, int64_t ldy, hipStream_t stream) {
+static int dispatch_gemv(GemvArgs &a, int n, bool fast, hipStream_t stream) {
     switch (n) {
-    case 1: return dispatch_gemv_nc<FMT, 1>(w, m, nb, x, ldx, y, ldy, stream);
-    case 2: return dispatch_gemv_nc<FMT, 2>(w, m, nb, x, ldx, y, ldy, stream);
-    case 3: return dispatch_gemv_nc<FMT, 3>(w, m, nb, x, ldx, y, ldy, stream);
-    case 4: return dispatch_gemv_nc<FMT, 4>(w, m, nb, x, ldx, y, ldy, stream);
-    case 5: return dispatch_gemv_nc<FMT, 5>(w, m, nb, x, ldx, y, ldy, stream);
-    case 6: return dispatch_gemv_nc<FMT, 6>(w, m, nb, x, ldx, y, ldy, stream);
-    case 7: return dispatch_gemv_nc<FMT, 7>(w, m, nb, x, ldx, y, ldy, stream);
-    case 8: return dispatch_gemv_nc<FMT, 8>(w, m, nb, x, ldx, y, ldy, stream);
+    case 1: return dispatch_gemv_nc<FMT, 1>(a, fast, stream);
+    case 2: return dispatch_gemv_nc<FMT, 2>(a, fast, stream);
+    case 3: return dispatch_gemv_nc<FMT, 3>(a, fast, stream);
+    case 4: return dispatch_gemv_nc<FMT, 4>(a, fast, stream);
+    case 5: return dispatch_gemv_nc<FMT, 5>(a, fast, stream);
+    case 6: return dispatch_gemv_nc<FMT, 6>(a, fast, stream);
+    case 7: return dispatch_gemv_nc<FMT, 7>(a, fast, stream);
+    case 8: return dispatch_gemv_nc<FMT, 8>(a, fast, stream);
+    default: return QK_ERR_INVALID_ARG;
+    }
+}
+
+int launch_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count, int64_t n,
+                               hipStream_t stream) {
+    GemvArgs a{};
+    bool fast = true;
+    int used = 0;
+    for (int i = 0; i < count; ++i) {
+        const qk_mat_vec_item &src = items[i];
+        if (src.m == 0) continue;
+        GemvItem &d = a.item[used++];
+        d.w = static_cast<const uint8_t *>(src.w);
+        d.x = src.x;
+        d.y = src.y;
+        d.ldx = src.ldx;
+        d.ldy = src.ldy;
+        d.m = (int)src.m;
+        d.nb = (int)(src.k / kBlockElems);
+        fast = fast && ((uintptr_t)d.w % 4) == 0 && (d.nb % 2) == 0 &&
+               ((uintptr_t)d.x % 16) == 0 && (d.ldx % 4) == 0;
+    }
+    a.count = used;
+    if (used == 0) return QK_OK;
+    switch (fmt) {
+    case QK_Q4_0: return dispatch_gemv<QK_Q4_0>(a, (int)n, fast, stream);
+    case QK_Q4_1: return dispatch_gemv<QK_Q4_1>(a, (int)n, fast, stream);
+    case QK_Q8_0: return dispatch_gemv<QK_Q8_0>(a, (int)n, fast, stream);
     default: return QK_ERR_INVALID_ARG;
     }
 }
 
 int launch_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k, const float *x,
                        int64_t n, int64_t ldx, float *y, int64_t ldy, hipStream_t stream) {
-    const uint8_t *wb = static_cast<const uint8_t *>(w);
-    const int nb = (int)(k / kBlockElems);
-    switch (fmt) {
-    case QK_Q4_0: return dispatch_gemv<QK_Q4_0>(wb, (int)m, nb, x, (int)n, ldx, y, ldy, stream);
-    case QK_Q4_1: return dispatch_gemv<QK_Q4_1>(wb, (int)m, nb, x, (int)n, ldx, y, ldy, stream);
-    case QK_Q8_0: return dispatch_gemv<QK_Q8_0>(wb, (int)m, nb, x, (int)n, ldx, y, ldy, stream);
-    default: return QK_ERR_INVALID_ARG;
-    }
+    qk_mat_vec_item item{w, m, k, x, ldx, y, ldy};
+    return launch_mul_mat_vec_batched(fmt, &item, 1, n, stream);
 }
 
 }  // namespace qk

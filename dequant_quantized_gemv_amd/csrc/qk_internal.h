@@ -14,8 +14,8 @@ namespace qk {
 // Launch a kernel with hipLaunchKernel and map the runtime's answer to a
 // status code (no global error state is read or cleared).
 template <typename... KArgs, typename... Args>
-inline int launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
-                  Args... args) {
+inline int launch_lds(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t lds_bytes,
+                      hipStream_t stream, Args... args) {
     static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel arity");
     std::tuple<KArgs...> vals(static_cast<KArgs>(args)...);
     void *argv[sizeof...(KArgs)];
@@ -24,8 +24,14 @@ inline int launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t str
         ((argv[i++] = static_cast<void *>(&v)), ...);
     }, vals);
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kern), grid, block,
-                                         argv, 0, stream);
+                                         argv, lds_bytes, stream);
     return e == hipSuccess ? QK_OK : QK_ERR_LAUNCH;
+}
+
+template <typename... KArgs, typename... Args>
+inline int launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                  Args... args) {
+    return launch_lds(kern, grid, block, 0, stream, args...);
 }
 
 int launch_dequantize(int fmt, const void *w, int64_t nblocks, int out_dtype, void *out,
@@ -33,6 +39,9 @@ int launch_dequantize(int fmt, const void *w, int64_t nblocks, int out_dtype, vo
 
 int launch_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k, const float *x,
                        int64_t n, int64_t ldx, float *y, int64_t ldy, hipStream_t stream);
+
+int launch_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count, int64_t n,
+                               hipStream_t stream);
 
 int launch_mul_mat(int fmt, const void *w, int64_t m, int64_t k, const uint16_t *x,
                    int64_t n, int64_t ldx, float *y, int64_t ldy, hipStream_t stream);

@@ -19,7 +19,15 @@ QK_OK, QK_ERR_INVALID_ARG, QK_ERR_UNSUPPORTED, QK_ERR_ALIGNMENT, QK_ERR_LAUNCH =
 
 FORMATS = {"q4_0": QK_Q4_0, "q4_1": QK_Q4_1, "q8_0": QK_Q8_0}
 SYMBOLS = ("qk_block_bytes", "qk_row_bytes", "qk_status_string", "qk_version",
-           "qk_dequantize", "qk_mul_mat_vec", "qk_mul_mat")
+           "qk_dequantize", "qk_mul_mat_vec", "qk_mul_mat_vec_batched", "qk_mul_mat")
+QK_MAX_BATCH = 16
+
+
+class MatVecItem(ctypes.Structure):
+    """struct qk_mat_vec_item (include/qk.h)."""
+    _fields_ = [("w", ctypes.c_void_p), ("m", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64),
+                ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
 
 
 class QKError(RuntimeError):
@@ -53,6 +61,8 @@ def load():
     lib.qk_dequantize.restype = ci
     lib.qk_mul_mat_vec.argtypes = [ci, vp, i64, i64, vp, i64, i64, vp, i64, vp]
     lib.qk_mul_mat_vec.restype = ci
+    lib.qk_mul_mat_vec_batched.argtypes = [ci, ctypes.POINTER(MatVecItem), ci, i64, vp]
+    lib.qk_mul_mat_vec_batched.restype = ci
     lib.qk_mul_mat.argtypes = [ci, vp, i64, i64, vp, i64, i64, vp, i64, vp]
     lib.qk_mul_mat.restype = ci
     _lib = lib
@@ -103,6 +113,19 @@ def qk_mul_mat_vec(fmt, w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream=0):
     return load().qk_mul_mat_vec(_fmt(fmt), w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream)
 
 
+def make_items(items):
+    """ctypes array of MatVecItem from (w_ptr, m, k, x_ptr, ldx, y_ptr, ldy) tuples."""
+    arr = (MatVecItem * max(len(items), 1))()
+    for i, it in enumerate(items):
+        arr[i] = MatVecItem(*it)
+    return arr
+
+
+def qk_mul_mat_vec_batched(fmt, items, count, n, stream=0):
+    """items: a ctypes MatVecItem array (see make_items) or None."""
+    return load().qk_mul_mat_vec_batched(_fmt(fmt), items, count, n, stream)
+
+
 def qk_mul_mat(fmt, w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream=0):
     return load().qk_mul_mat(_fmt(fmt), w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream)
 
@@ -137,6 +160,27 @@ def mul_mat_vec(fmt, w, m, k, x, y=None, stream=None):
                         y.data_ptr(), y.stride(0), _stream(stream))
     _check(st, "qk_mul_mat_vec")
     return y
+
+
+def mul_mat_vec_batched(fmt, problems, ys=None, stream=None):
+    """One launch for several GEMVs of one format and column count.
+    problems: list of (w, m, k, x) with x shaped (n, k) fp32; returns the ys."""
+    import torch
+    if not problems:
+        return []
+    n = problems[0][3].shape[0] if problems[0][3].dim() == 2 else 1
+    if ys is None:
+        ys = [torch.empty((n, m), dtype=torch.float32, device=x.device) for (_, m, _, x) in problems]
+    tup = []
+    for (w, m, k, x), y in zip(problems, ys):
+        x2 = x.view(1, -1) if x.dim() == 1 else x
+        if x2.dtype != torch.float32 or x2.stride(1) != 1 or x2.shape[0] != n:
+            raise TypeError("every x must be float32 (n, k) with contiguous columns and the same n")
+        tup.append((w.data_ptr(), m, k, x2.data_ptr(), x2.stride(0), y.data_ptr(), y.stride(0)))
+    arr = make_items(tup)
+    st = qk_mul_mat_vec_batched(fmt, arr, len(tup), n, _stream(stream))
+    _check(st, "qk_mul_mat_vec_batched")
+    return ys
 
 
 def mul_mat(fmt, w, m, k, x, y=None, stream=None):

@@ -124,6 +124,39 @@ int qk_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k,
                    const float *x, int64_t n, int64_t ldx,
                    float *y, int64_t ldy, void *stream);
 
+/* One problem of a grouped GEMV: y = W x (layout as in qk_mul_mat_vec). */
+typedef struct qk_mat_vec_item {
+    const void *w;      /* m rows of k/32 blocks, 2-byte aligned */
+    int64_t m;          /* rows, m >= 0 (0: skipped) */
+    int64_t k;          /* weights per row, k >= 0, k % 32 == 0 */
+    const float *x;     /* n fp32 columns of length k, stride ldx >= k */
+    int64_t ldx;
+    float *y;           /* n fp32 columns of length m, stride ldy >= m */
+    int64_t ldy;
+} qk_mat_vec_item;
+
+/* Largest `count` qk_mul_mat_vec_batched accepts. */
+#define QK_MAX_BATCH 16
+
+/*
+ * qk_mul_mat_vec_batched - several independent GEMVs of one format and one
+ * column count n in a single launch (for example the q/k/v/o, gate/up and down
+ * projections of one decode step, or a set of expert matrices).  Each item is
+ * computed exactly as qk_mul_mat_vec would compute it; one launch amortizes
+ * the fixed launch cost over all items' weights.
+ * Source: as qk_mul_mat_vec (dequantize_mul_mat_vec under ggml_cuda_op_mul_mat,
+ * "llama_cpp 0.12.1 -> 0.12.2" ggml-cuda.cu diff), applied per item.
+ *
+ *   items      host array of `count` problems (read during the call only)
+ *   count      0..QK_MAX_BATCH (0 is a no-op)
+ *   n          1..8 columns for every item (0 is a no-op)
+ * Errors as qk_mul_mat_vec for each item; additionally QK_ERR_INVALID_ARG for
+ * count out of range, items == NULL with count > 0, or an output overlapping
+ * any input or any other item's output.
+ */
+int qk_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count, int64_t n,
+                           void *stream);
+
 /*
  * qk_mul_mat - batched GEMM: weights dequantized to fp16 tiles in LDS and
  * multiplied by fp16 activations on the matrix cores, accumulating in fp32.

@@ -126,3 +126,29 @@ def test_mul_mat_validation(args, want):
 def test_binding_raises_on_error_status():
     err = qk.QKError(qk.QK_ERR_ALIGNMENT, "qk_mul_mat")
     assert "misaligned" in str(err) and err.status == qk.QK_ERR_ALIGNMENT
+
+
+def _items(*tups):
+    return qk.make_items(list(tups))
+
+
+@pytest.mark.parametrize("fmt,items,count,n,want", [
+    (9, [(W, 8, 64, X, 64, Y, 8)], 1, 1, E.QK_ERR_UNSUPPORTED),
+    (E.QK_Q4_0, [(W, 8, 64, X, 64, Y, 8)], 17, 1, E.QK_ERR_INVALID_ARG),     # count > 16
+    (E.QK_Q4_0, [(W, 8, 64, X, 64, Y, 8)], -1, 1, E.QK_ERR_INVALID_ARG),
+    (E.QK_Q4_0, [(W, 8, 64, X, 64, Y, 8)], 1, 9, E.QK_ERR_INVALID_ARG),      # n > 8
+    (E.QK_Q4_0, [(W, 8, 64, X, 64, Y, 8), (W, 8, 48, X, 64, Y + 64, 8)], 2, 1, E.QK_ERR_INVALID_ARG),
+    (E.QK_Q4_0, [(W, 8, 64, X, 64, Y, 8), (W + 1, 8, 64, X, 64, Y + 64, 8)], 2, 1, E.QK_ERR_ALIGNMENT),
+    (E.QK_Q4_0, [(W, 8, 64, X, 64, Y, 8), (W, 8, 64, X, 64, Y + 16, 8)], 2, 1, E.QK_ERR_INVALID_ARG),  # outputs overlap
+    (E.QK_Q4_0, [(W, 8, 64, X, 64, Y, 8), (W, 8, 64, X, 64, W + 8, 8)], 2, 1, E.QK_ERR_INVALID_ARG),   # y overlaps other w
+    (E.QK_Q4_0, [(W, 8, 64, X, 64, Y, 8), (W, 8, 64, X, 64, X + 4, 8)], 2, 1, E.QK_ERR_INVALID_ARG),   # y overlaps x
+    (E.QK_Q4_0, [(W, 8, 64, X, 64, Y, 8)], 0, 1, E.QK_OK),
+    (E.QK_Q4_0, [(W, 8, 64, X, 64, Y, 8)], 1, 0, E.QK_OK),
+    (E.QK_Q4_0, [(W, 0, 64, X, 64, Y, 8)], 1, 1, E.QK_OK),                    # only empty items
+])
+def test_mul_mat_vec_batched_validation(fmt, items, count, n, want):
+    assert qk.qk_mul_mat_vec_batched(fmt, _items(*items), count, n, 0) == want
+
+
+def test_mul_mat_vec_batched_null_items():
+    assert qk.qk_mul_mat_vec_batched(qk.QK_Q4_0, None, 2, 1, 0) == qk.QK_ERR_INVALID_ARG

@@ -378,3 +378,90 @@ def test_gemm_full_config4_sampled():
     y = _gpu_gemm("q4_0", w, cfg["m"], cfg["k"], xh)
     _sampled_check("q4_0", w, cfg["m"], cfg["k"], xh, y, np.random.default_rng(4), 1024,
                    GEMM_TOL, x_is_f16=True, what="config4")
+
+
+# ---------------------------------------------------------------------------
+# grouped GEMV (one launch, several problems)
+# ---------------------------------------------------------------------------
+
+def _gpu_gemv_batched(fmt, probs, n, w_offs=None, x_offs=None):
+    """probs: list of (w_bytes, m, k, x2d); returns list of (n, m) outputs."""
+    holds, tups, outs = [], [], []
+    for i, (w, m, k, x2d) in enumerate(probs):
+        hw, wp = to_dev_bytes(w, (w_offs or [0] * len(probs))[i])
+        hx, xp = x_dev(x2d, k, np.float32, (x_offs or [0] * len(probs))[i])
+        out = Guarded(max(((n - 1) * m + m) * 4, 4))
+        holds += [hw, hx]
+        outs.append(out)
+        tups.append((wp, m, k, xp, k, out.ptr, m))
+    arr = qk.make_items(tups)
+    st = qk.qk_mul_mat_vec_batched(fmt, arr, len(tups), n, _stream())
+    assert st == qk.QK_OK, qk.status_string(st)
+    res = []
+    for (w, m, k, x2d), out in zip(probs, outs):
+        y = out.host(np.float32)
+        assert out.guards_intact(), "mul_mat_vec_batched wrote outside an output"
+        res.append(np.stack([y[j * m:(j + 1) * m] for j in range(n)]) if m else np.zeros((n, 0)))
+    del holds
+    return res
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n", [1, 3, 8])
+def test_gemv_batched_mixed_shapes(fmt, n):
+    shapes = [(37, 2048), (1, 32), (0, 64), (300, 4096), (16, 11008), (5, 96), (64, 256)]
+    _say("gemv batched", fmt, n)
+    probs = []
+    for i, (m, k) in enumerate(shapes):
+        w = _weights(fmt, m, k, seed=60 + i) if m else np.zeros(0, np.uint8)
+        x = synth.activations(k, n, seed=60 + i, tensor_id=7)
+        probs.append((w, m, k, x))
+    ys = _gpu_gemv_batched(fmt, probs, n)
+    for (w, m, k, x), y in zip(probs, ys):
+        if m == 0:
+            continue
+        yref, s = oracle.dot(fmt, w, m, k, x, n)
+        assert_within(y, yref, s, GEMV_TOL, f"batched {fmt} {m}x{k} n={n}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_batched_matches_single_calls_bitwise(fmt):
+    """A grouped launch computes every row exactly as a single call does."""
+    shapes = [(130, 4096), (77, 2048), (9, 11008)]
+    probs = []
+    for i, (m, k) in enumerate(shapes):
+        probs.append((_weights(fmt, m, k, seed=70 + i), m, k, synth.activations(k, 2, seed=70 + i, tensor_id=3)))
+    ys = _gpu_gemv_batched(fmt, probs, 2)
+    for (w, m, k, x), y in zip(probs, ys):
+        assert np.array_equal(y.view(np.uint32), _gpu_gemv(fmt, w, m, k, x).view(np.uint32))
+
+
+def test_gemv_batched_generic_path_and_sixteen_items():
+    """16 items, one of them misaligned (forces the 2-byte generic path for the
+    whole launch) and one with an odd block count."""
+    probs = []
+    for i in range(16):
+        m, k = 20 + 3 * i, (96 if i == 5 else 1024)
+        probs.append((_weights("q4_0", m, k, seed=80 + i), m, k, synth.activations(k, 1, seed=80 + i, tensor_id=2)))
+    _say("gemv batched 16 generic")
+    w_offs = [0] * 16
+    w_offs[3] = 2
+    ys = _gpu_gemv_batched("q4_0", probs, 1, w_offs=w_offs)
+    for (w, m, k, x), y in zip(probs, ys):
+        yref, s = oracle.dot("q4_0", w, m, k, x, 1)
+        assert_within(y, yref, s, GEMV_TOL, f"batched generic {m}x{k}")
+
+
+def test_gemv_batched_full_config3_sampled():
+    """The whole 7B-shaped decode layer in one launch (Q4_0, batch 1)."""
+    cfg = synth.WORKLOADS["gemv_q4_0_decode_layer"]
+    seed = synth.workload_seed(cfg["id"])
+    _say("gemv batched config3")
+    probs = []
+    for tid, (name, m, k) in enumerate(cfg["layer"]):
+        w = synth.quant_matrix("q4_0", m, k, seed=seed, tensor_id=tid, d_range=cfg["d"])
+        probs.append((w, m, k, synth.activations(k, 1, seed=seed, tensor_id=100 + tid)))
+    ys = _gpu_gemv_batched("q4_0", probs, 1)
+    for tid, ((w, m, k, x), y) in enumerate(zip(probs, ys)):
+        _sampled_check("q4_0", w, m, k, x, y, np.random.default_rng(50 + tid), 256, GEMV_TOL,
+                       what=f"batched config3 item {tid}")
