@@ -40,6 +40,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 COLD_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
+GEMV_SOURCES = ["gemv.hip", "qk_common.h", "qk_internal.h"]
 
 
 def log(*a):
@@ -55,16 +56,37 @@ def kernel_source_hash(names):
 
 
 def stored_traffic(kernel_key, sources):
-    """HBM bytes per launch from committed rocprofv3 --pmc counters, or None if
-    they were taken on a different version of the kernel source."""
-    path = os.path.join(PROFILES, f"traffic_{kernel_key}.json")
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (profiles/<kernel_key>_traffic.md, lines `source_hash: ...` and
+    `traffic_bytes_per_launch: ...`), or None when those counters were taken
+    on a different version of the kernel source."""
+    path = os.path.join(PROFILES, f"{kernel_key}_traffic.md")
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as f:
-        rec = json.load(f)
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                rec[k.strip().strip("`* -")] = v.strip().strip("`* ")
     if rec.get("source_hash") != kernel_source_hash(sources):
         return None
-    return rec.get("traffic_bytes_per_launch")
+    try:
+        return int(float(rec["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, mib):
+    """A plain device copy of a known size (for scaling rocprofv3 FETCH_SIZE /
+    WRITE_SIZE): reads and writes `mib` MiB, five times."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {mib} MiB read + {mib} MiB written per copy, 5 copies")
 
 
 class Timer:
@@ -194,7 +216,7 @@ def run_headline(torch, qk, synth, oracle, timer, name, steps, warmup, with_cpu)
     r = bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup)
     gbps = r["weight_bytes"] * steps / r["seconds"] / 1e9
     achieved = r["algo_bytes"] / r["per_launch_s"] / 1e9
-    traffic = stored_traffic(f"gemv_{fmt}_{m}x{k}_n{n}", ["gemv.hip", "qk_common.h"])
+    traffic = stored_traffic(f"gemv_{fmt}_{m}x{k}_n{n}", GEMV_SOURCES)
     out = {
         "metric": "effective weight GB/s (% of HBM peak) for Q4_0/Q8_0 GEMV; batched TFLOP/s",
         "value": round(gbps, 2),
@@ -364,6 +386,8 @@ def main():
     ap.add_argument("--workload", default="gemv_q8_0_4096x4096_n1")
     ap.add_argument("--configs", action="store_true", help="also measure all five workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -381,6 +405,8 @@ def main():
     timer = Timer(torch)
     out = run_headline(torch, qk, synth, oracle, timer, args.workload, args.steps, args.warmup,
                        not args.no_cpu)
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
     if args.configs:
         log("measuring all five workloads")
         out["configs"] = run_configs(torch, qk, synth, oracle, timer, args.steps, args.warmup)
@@ -388,4 +414,7 @@ def main():
 
 
 if __name__ == "__main__":
+    if len(sys.argv) > 1 and sys.argv[1] == "--print-source-hash":
+        print(kernel_source_hash(GEMV_SOURCES))
+        sys.exit(0)
     main()
