@@ -3,31 +3,39 @@
 // The reference path for more than one activation column dequantizes the
 // weights to fp16 (ggml_get_to_fp16_cuda) and hands them to a BLAS GEMM;
 // ggml_cuda_mul_mat picks it by the column count ("llama_cpp 0.12.1 -> 0.12.2"
-// ggml-cuda.cu diff).  Here the two steps are fused: each 128 x 128 output tile
-// dequantizes its weight rows straight into LDS as fp16 and feeds them, with
-// the fp16 activation tile, to v_mfma_f32_16x16x32_f16, accumulating in fp32.
-// The fp16 weight is one round-to-nearest-even of the exact weight value, i.e.
-// the value qk_dequantize(..., QK_F16, ...) produces (a Q4_0 code 8 with
-// negative d gives -0 here, +0 there: the same number).
+// ggml-cuda.cu diff).  Here the two steps are fused: weights are dequantized to
+// fp16 straight into the registers that feed v_mfma_f32_16x16x32_f16, and the
+// products accumulate in fp32.  The fp16 weight is one round-to-nearest-even
+// of the exact weight value, i.e. the value qk_dequantize(..., QK_F16, ...)
+// produces (a Q4_0 code 8 with negative d gives -0 here, +0 there: the same
+// number).
 //
-// Workgroup: 256 lanes = 4 waves in a 2 x 2 grid, each wave a 64 x 64 sub-tile
-// (4 x 4 MFMA tiles of 16 x 16).  K advances 64 (two quant blocks, one "pair")
-// per step.  Lane t stages row t/2 of the weight tile: it loads the row's pair
-// (36 / 40 / 68 bytes, dword aligned when the block count is even) and
-// dequantizes block t%2 of it; it also loads 64 bytes of activations (column
-// t/2, k-half t%2).  The next step's loads are issued into registers before the
-// matrix cores work on the current step.
+// Tile: 256 rows x 128 columns per workgroup of 4 waves; wave v owns rows
+// 64v..64v+63 and all 128 columns (4 x 8 MFMA tiles of 16 x 16, 128 fp32
+// accumulators per lane).  K advances 64 (two quant blocks, one "pair") per
+// step.  In the MFMA A operand, lane l holds row l%16 of a 16-row tile and
+// elements 8(l/16)..8(l/16)+7 of a 32-element block, so each 16 x 32 operand
+// is exactly one quant block of 16 rows.  Each lane loads only the bytes of
+// its own 8 weights (plus the scales) with dword loads, so the weights never
+// pass through LDS; the activation tile (128 columns x 64) is staged through a
+// double-buffered LDS tile read by all four waves.  Quant words are loaded
+// two steps ahead; the next step's weights are dequantized while the matrix
+// cores work on the current one.
 //
 // Dequantization to fp16 (Q4_0, Q8_0), packed two at a time and exact: the
 // integer code is placed in the mantissa of an fp16 (0x64XX is 1024 + XX) with
-// a byte permute, the bias removed with one packed add (q - 8, or q, exactly),
-// and one packed multiply by (d, d) rounds d * (q - 8) or d * q to fp16 once.
-// Q4_1 (d*q + m is one fp32 rounding) goes through fp32 so that the fp16 is
-// rounded from exactly the fp32 dequantized value.
+// a byte permute, the bias removed with one packed fma or add (giving q - 8,
+// or q, exactly), and one packed multiply by (d, d) rounds d * (q - 8) or
+// d * q to fp16 once.  A lane that takes high nibbles keeps them in place
+// (0x64XX with XX = 16q) and scales by 1/16 in the same fma.  Q4_1
+// (d*q + m is one fp32 rounding) goes through fp32 so that the fp16 is rounded
+// from exactly the fp32 dequantized value.
 //
 // Tiles are assigned so that the workgroups of one XCD (the hardware sends
 // workgroup i to XCD i % 8) cover consecutive tiles, column tile fastest, so
 // the workgroups sharing a weight row tile share that XCD's L2.
+#include <type_traits>
+
 #include "qk_common.h"
 #include "qk_internal.h"
 
@@ -37,18 +45,44 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2g_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4g_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3g_a4 __attribute__((ext_vector_type(3), aligned(4)));
+typedef uint32_t u32x2g_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef uint32_t u32x4g_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2g_t __attribute__((ext_vector_type(2)));
 
-constexpr int kGmThreads = 256;
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kBK = 64;
-constexpr int kPitch = kBK + 8;  // halves per LDS row (144 bytes: spreads rows over banks)
+constexpr int kGmThreads = 512;  // 8 waves: 4 row slices x 2 k groups
+constexpr int kBM = 256;         // rows per tile (64 per row slice)
+constexpr int kBN = 128;         // columns per tile
+constexpr int kBK = 64;          // elements of K per step (one pair of blocks)
+constexpr int kPitch = kBK + 8;  // halves per LDS column (144 bytes: spreads columns over banks)
+constexpr int kRT = 4;           // 16-row MFMA tiles per wave
+constexpr int kCT = 8;           // 16-column MFMA tiles per wave
 
-template <int FMT> struct GmPair;
-template <> struct GmPair<QK_Q4_0> { static constexpr int kDwords = 9; };
-template <> struct GmPair<QK_Q4_1> { static constexpr int kDwords = 10; };
-template <> struct GmPair<QK_Q8_0> { static constexpr int kDwords = 17; };
+// Quant dwords one lane loads per 16-row tile and step.  Byte offsets from the
+// start of the pair (g = lane/16, h = g % 2 picks the half of a block's quant
+// bytes):
+//   Q4_0 (36-byte pair): 8h, 8h+4, 8h+8 | 20+8h, 24+8h | (h ? 0 : 16)
+//   Q4_1 (40-byte pair): 0 | 4+8h, 8+8h | 20 | 24+8h, 28+8h
+//   Q8_0 (68-byte pair): 8g, 8g+4, 8g+8 | 36+8g, 40+8g | 0 | 32
+template <int FMT> struct GmQ;
+template <> struct GmQ<QK_Q4_0> { static constexpr int kN = 6; };
+template <> struct GmQ<QK_Q4_1> { static constexpr int kN = 6; };
+template <> struct GmQ<QK_Q8_0> { static constexpr int kN = 7; };
+
+template <int FMT>
+__device__ __forceinline__ int gm_offset(int slot, int g) {
+    const int h = g & 1;
+    if constexpr (FMT == QK_Q4_0) {
+        constexpr int base[6] = {0, 4, 8, 20, 24, 0};
+        return slot < 5 ? base[slot] + 8 * h : (h ? 0 : 16);
+    } else if constexpr (FMT == QK_Q4_1) {
+        constexpr int base[6] = {0, 4, 8, 20, 24, 28};
+        return (slot == 0 || slot == 3) ? base[slot] : base[slot] + 8 * h;
+    } else {
+        constexpr int base[7] = {0, 4, 8, 36, 40, 0, 32};
+        return slot < 5 ? base[slot] + 8 * g : base[slot];
+    }
+}
 
 __device__ __forceinline__ uint32_t gm_perm_lo(uint32_t src) {
     return __builtin_amdgcn_perm(0x64646464u, src, 0x04010400u);  // [b0, 64, b1, 64]
@@ -56,13 +90,13 @@ __device__ __forceinline__ uint32_t gm_perm_lo(uint32_t src) {
 __device__ __forceinline__ uint32_t gm_perm_hi(uint32_t src) {
     return __builtin_amdgcn_perm(0x64646464u, src, 0x04030402u);  // [b2, 64, b3, 64]
 }
-__device__ __forceinline__ uint32_t gm_pk_add(uint32_t a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2g_t, a) + half2g_t{(_Float16)b, (_Float16)b});
+__device__ __forceinline__ uint32_t gm_pk_add(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2g_t, a) + __builtin_bit_cast(half2g_t, b));
 }
-__device__ __forceinline__ uint32_t gm_pk_fma(uint32_t a, float s, float t) {
+__device__ __forceinline__ uint32_t gm_pk_fma(uint32_t a, uint32_t s, uint32_t t) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2g_t, a),
-                                                                  half2g_t{(_Float16)s, (_Float16)s},
-                                                                  half2g_t{(_Float16)t, (_Float16)t}));
+                                                                  __builtin_bit_cast(half2g_t, s),
+                                                                  __builtin_bit_cast(half2g_t, t)));
 }
 __device__ __forceinline__ uint32_t gm_pk_mul(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2g_t, a) * __builtin_bit_cast(half2g_t, b));
@@ -70,76 +104,111 @@ __device__ __forceinline__ uint32_t gm_pk_mul(uint32_t a, uint32_t b) {
 __device__ __forceinline__ uint32_t gm_pack2(float a, float b) {
     return (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
 }
-
-// Block b (0/1) of a pair held in registers: d bits, m bits, quant word i.
-template <int FMT>
-__device__ __forceinline__ uint32_t gm_d(const uint32_t (&v)[GmPair<FMT>::kDwords], int b) {
-    if constexpr (FMT == QK_Q4_0) return b == 0 ? (v[0] & 0xFFFFu) : (v[4] >> 16);
-    if constexpr (FMT == QK_Q4_1) return b == 0 ? (v[0] & 0xFFFFu) : (v[5] & 0xFFFFu);
-    return b == 0 ? (v[0] & 0xFFFFu) : (v[8] >> 16);
-}
-template <int FMT>
-__device__ __forceinline__ uint32_t gm_qs(const uint32_t (&v)[GmPair<FMT>::kDwords], int b, int i) {
-    if constexpr (FMT == QK_Q4_0) return b == 0 ? __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2) : v[5 + i];
-    if constexpr (FMT == QK_Q4_1) return b == 0 ? v[1 + i] : v[6 + i];
-    return b == 0 ? __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2) : v[9 + i];
+__device__ __forceinline__ uint32_t gm_h2(float v) {
+    const uint32_t b = f2h(v);
+    return b | (b << 16);
 }
 
-// Dequantize block b of the pair to 32 fp16 (out[g] = elements 8g..8g+7).
+// Per-lane constants of the dequantization.
+struct GmLaneConst {
+    uint32_t mask;   // Q4_x: nibble mask of this lane's half (low, or high in place)
+    uint32_t s, t;   // Q4_0: packed fp16 scale and offset taking 0x64XX to q - 8
+    uint32_t sel0;   // Q4_0: perm selector giving (d, d) of block 0
+    uint32_t sel1;   // Q4_0: perm selector giving (d, d) of block 1
+    float dscale;    // Q4_1: 1, or 1/16 for high nibbles kept in place (16q)
+};
+
 template <int FMT>
-__device__ __forceinline__ void gm_dequant(const uint32_t (&v)[GmPair<FMT>::kDwords], int b, u32x4g_t (&out)[4]) {
-    const uint32_t db = gm_d<FMT>(v, b);
-    if constexpr (FMT == QK_Q4_1) {
-        const float d = h2f(db);
-        const float mm = h2f(b == 0 ? (v[0] >> 16) : (v[5] >> 16));
-        // word i: low nibbles -> elements 4i..4i+3, high -> 16+4i..16+4i+3
-        uint32_t lo[4][2], hi[4][2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t q = gm_qs<FMT>(v, b, i);
-            const uint32_t l = q & 0x0F0F0F0Fu, h = (q >> 4) & 0x0F0F0F0Fu;
-            lo[i][0] = gm_pack2(d * ubyte_f<0>(l) + mm, d * ubyte_f<1>(l) + mm);
-            lo[i][1] = gm_pack2(d * ubyte_f<2>(l) + mm, d * ubyte_f<3>(l) + mm);
-            hi[i][0] = gm_pack2(d * ubyte_f<0>(h) + mm, d * ubyte_f<1>(h) + mm);
-            hi[i][1] = gm_pack2(d * ubyte_f<2>(h) + mm, d * ubyte_f<3>(h) + mm);
-        }
-        out[0] = u32x4g_t{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
-        out[1] = u32x4g_t{lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
-        out[2] = u32x4g_t{hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
-        out[3] = u32x4g_t{hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
-    } else if constexpr (FMT == QK_Q4_0) {
-        const uint32_t dd = db | (db << 16);
-        uint32_t lo[4][2], hi[4][2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t q = gm_qs<FMT>(v, b, i);
-            const uint32_t l = q & 0x0F0F0F0Fu, h = q & 0xF0F0F0F0u;
-            // 1024 + c - 1032 = c - 8; (1024 + 16c) / 16 - 72 = c - 8; then * d
-            lo[i][0] = gm_pk_mul(gm_pk_add(gm_perm_lo(l), -1032.0f), dd);
-            lo[i][1] = gm_pk_mul(gm_pk_add(gm_perm_hi(l), -1032.0f), dd);
-            hi[i][0] = gm_pk_mul(gm_pk_fma(gm_perm_lo(h), 0.0625f, -72.0f), dd);
-            hi[i][1] = gm_pk_mul(gm_pk_fma(gm_perm_hi(h), 0.0625f, -72.0f), dd);
-        }
-        out[0] = u32x4g_t{lo[0][0], lo[0][1], lo[1][0], lo[1][1]};
-        out[1] = u32x4g_t{lo[2][0], lo[2][1], lo[3][0], lo[3][1]};
-        out[2] = u32x4g_t{hi[0][0], hi[0][1], hi[1][0], hi[1][1]};
-        out[3] = u32x4g_t{hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
+__device__ __forceinline__ GmLaneConst gm_lane_const(int g) {
+    GmLaneConst c;
+    const bool hi = (g >> 1) != 0;
+    const bool h = (g & 1) != 0;
+    c.mask = hi ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+    c.s = hi ? gm_h2(0.0625f) : gm_h2(1.0f);
+    c.t = hi ? gm_h2(-72.0f) : gm_h2(-1032.0f);
+    // Q4_0: d of block 0 is pair bytes 0-1, d of block 1 bytes 18-19.  With
+    // h = 0 they sit in slot 0 (offset 0, low half) and slot 5 (offset 16,
+    // high half); with h = 1 in slot 5 (offset 0, low) and slot 2 (offset 16,
+    // high).  perm(src0, src1, sel) takes selector values 4-7 from src0.
+    c.sel0 = h ? 0x05040504u : 0x01000100u;  // perm(q5, q0)
+    c.sel1 = h ? 0x07060706u : 0x03020302u;  // perm(q2, q5)
+    c.dscale = hi ? 0.0625f : 1.0f;
+    return c;
+}
+
+// Two quant dwords (8 weights of this lane) -> 4 packed fp16 (one A operand).
+template <int FMT>
+__device__ __forceinline__ u32x4g_t gm_decode8(uint32_t qa, uint32_t qb, uint32_t dd, float d, float mm,
+                                               const GmLaneConst &c) {
+    if constexpr (FMT == QK_Q4_0) {
+        const uint32_t ua = qa & c.mask, ub = qb & c.mask;
+        return u32x4g_t{gm_pk_mul(gm_pk_fma(gm_perm_lo(ua), c.s, c.t), dd),
+                        gm_pk_mul(gm_pk_fma(gm_perm_hi(ua), c.s, c.t), dd),
+                        gm_pk_mul(gm_pk_fma(gm_perm_lo(ub), c.s, c.t), dd),
+                        gm_pk_mul(gm_pk_fma(gm_perm_hi(ub), c.s, c.t), dd)};
+    } else if constexpr (FMT == QK_Q8_0) {
+        // c + 128 is the byte of (c ^ 0x80): 1024 + c + 128 - 1152 = c
+        const uint32_t ua = qa ^ 0x80808080u, ub = qb ^ 0x80808080u;
+        const uint32_t bias = 0xE480E480u;  // (-1152, -1152)
+        return u32x4g_t{gm_pk_mul(gm_pk_add(gm_perm_lo(ua), bias), dd),
+                        gm_pk_mul(gm_pk_add(gm_perm_hi(ua), bias), dd),
+                        gm_pk_mul(gm_pk_add(gm_perm_lo(ub), bias), dd),
+                        gm_pk_mul(gm_pk_add(gm_perm_hi(ub), bias), dd)};
     } else {
-        const uint32_t dd = db | (db << 16);
-        uint32_t p[8][2];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            // c + 128 is the byte of (c ^ 0x80): 1024 + c + 128 - 1152 = c; then * d
-            const uint32_t u = gm_qs<FMT>(v, b, i) ^ 0x80808080u;
-            p[i][0] = gm_pk_mul(gm_pk_add(gm_perm_lo(u), -1152.0f), dd);
-            p[i][1] = gm_pk_mul(gm_pk_add(gm_perm_hi(u), -1152.0f), dd);
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) out[g] = u32x4g_t{p[2 * g][0], p[2 * g][1], p[2 * g + 1][0], p[2 * g + 1][1]};
+        // d here is d or d/16 (exact in fp32); times the in-place code it is
+        // d * q exactly, so the fma rounds d*q + m once, as the definition does
+        const uint32_t ua = qa & c.mask, ub = qb & c.mask;
+        return u32x4g_t{gm_pack2(__builtin_fmaf(d, ubyte_f<0>(ua), mm), __builtin_fmaf(d, ubyte_f<1>(ua), mm)),
+                        gm_pack2(__builtin_fmaf(d, ubyte_f<2>(ua), mm), __builtin_fmaf(d, ubyte_f<3>(ua), mm)),
+                        gm_pack2(__builtin_fmaf(d, ubyte_f<0>(ub), mm), __builtin_fmaf(d, ubyte_f<1>(ub), mm)),
+                        gm_pack2(__builtin_fmaf(d, ubyte_f<2>(ub), mm), __builtin_fmaf(d, ubyte_f<3>(ub), mm))};
     }
 }
 
-// FAST: w 4-byte aligned and an even number of blocks per row (so every pair
+// The lane's A operands of one 16-row tile and step: block 0 -> a0, block 1 -> a1.
+template <int FMT>
+__device__ __forceinline__ void gm_decode(const uint32_t (&q)[GmQ<FMT>::kN], const GmLaneConst &c,
+                                          u32x4g_t &a0, u32x4g_t &a1) {
+    if constexpr (FMT == QK_Q4_0) {
+        const uint32_t dd0 = __builtin_amdgcn_perm(q[5], q[0], c.sel0);
+        const uint32_t dd1 = __builtin_amdgcn_perm(q[2], q[5], c.sel1);
+        a0 = gm_decode8<FMT>(__builtin_amdgcn_alignbyte(q[1], q[0], 2), __builtin_amdgcn_alignbyte(q[2], q[1], 2),
+                             dd0, 0.0f, 0.0f, c);
+        a1 = gm_decode8<FMT>(q[3], q[4], dd1, 0.0f, 0.0f, c);
+    } else if constexpr (FMT == QK_Q8_0) {
+        const uint32_t dd0 = __builtin_amdgcn_perm(0u, q[5], 0x01000100u);
+        const uint32_t dd1 = __builtin_amdgcn_perm(0u, q[6], 0x03020302u);
+        a0 = gm_decode8<FMT>(__builtin_amdgcn_alignbyte(q[1], q[0], 2), __builtin_amdgcn_alignbyte(q[2], q[1], 2),
+                             dd0, 0.0f, 0.0f, c);
+        a1 = gm_decode8<FMT>(q[3], q[4], dd1, 0.0f, 0.0f, c);
+    } else {
+        const float d0 = h2f(q[0] & 0xFFFFu) * c.dscale, m0 = h2f(q[0] >> 16);
+        const float d1 = h2f(q[3] & 0xFFFFu) * c.dscale, m1 = h2f(q[3] >> 16);
+        a0 = gm_decode8<FMT>(q[1], q[2], 0u, d0, m0, c);
+        a1 = gm_decode8<FMT>(q[4], q[5], 0u, d1, m1, c);
+    }
+}
+
+// LDS bytes per weight row and step in the quant stage (the pair, padded so
+// that rows start on 16 bytes; the pitch in dwords is 4 mod 8 or 8 mod 16,
+// which spreads 16 consecutive rows over distinct banks).
+template <int FMT> struct GmStage;
+template <> struct GmStage<QK_Q4_0> { static constexpr int kPitch = 48; };
+template <> struct GmStage<QK_Q4_1> { static constexpr int kPitch = 48; };
+template <> struct GmStage<QK_Q8_0> { static constexpr int kPitch = 80; };
+
+template <int FMT>
+constexpr size_t gm_group_lds() {
+    return 2 * (size_t)kBN * kPitch * 2 + 2 * (size_t)kBM * GmStage<FMT>::kPitch;
+}
+template <int FMT>
+constexpr size_t gm_lds_bytes() {
+    // two k groups; the partial-sum exchange (8 waves x 8 tiles x 64 lanes x
+    // 16 bytes) reuses the same memory after the k loop
+    return 2 * gm_group_lds<FMT>() > 8 * 8 * 64 * 16 ? 2 * gm_group_lds<FMT>() : 8 * 8 * 64 * 16;
+}
+
+// FAST: w 4-byte aligned and an even number of blocks per row (every pair
 // starts on 4 bytes and both of its blocks exist), x 16-byte aligned and
 // ldx % 8 == 0.  YALIGNED: y 16-byte aligned and ldy % 4 == 0.
 template <int FMT, bool FAST, bool YALIGNED>
@@ -147,9 +216,13 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
     const uint8_t *__restrict__ w, int m, int nb, const uint16_t *__restrict__ x, int64_t ldx,
     int n, float *__restrict__ y, int64_t ldy, int mtiles, int ntiles) {
     using F = Format<FMT>;
-    constexpr int ND = GmPair<FMT>::kDwords;
-    __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kPitch];
+    constexpr int NQ = GmQ<FMT>::kN;
+    constexpr int kPairBytes = 2 * F::kBytes;
+    constexpr int kNC = kPairBytes / 16;        // 16-byte chunks of a pair
+    constexpr int kTail = kPairBytes % 16;      // remaining 4 or 8 bytes
+    constexpr int kAP = GmStage<FMT>::kPitch;
+    constexpr int kBufHalves = kBN * kPitch;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     // XCD-aware tile order: XCD x (= id % 8) takes a contiguous range of tiles.
     const int ntot = mtiles * ntiles;
@@ -165,124 +238,255 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int wr = wave >> 1;
-    const int wc = wave & 1;
+    const int g = lane >> 4;
+    const int wm = wave & 3;     // 64-row slice of the tile
+    const int kg = wave >> 2;    // k group: first or second half of the pairs
+    const int gtid = tid & 255;  // thread index within the k group
     const int k = nb * 32;
-
-    // loader roles
-    const int lr = tid >> 1;   // weight row / activation column within the tile
-    const int lh = tid & 1;    // block of the pair / k-half of the step
+    const int npairs = (nb + 1) / 2;
+    const int nsteps = (npairs + 1) / 2;   // steps of group 0; group 1 has npairs - nsteps
+    const int pbase = kg * nsteps;
+    const int gsteps = kg ? npairs - nsteps : nsteps;
     const int64_t row_bytes = (int64_t)nb * F::kBytes;
-    // Rows and columns past the matrix load a clamped, valid row or column.
-    // Output (i, j) depends only on weight row i and activation column j, and
-    // such rows and columns are never stored, so their values do not matter.
-    const uint8_t *__restrict__ wrow = w + (int64_t)min(row0 + lr, m - 1) * row_bytes;
-    const uint16_t *__restrict__ xcol = x + (int64_t)min(col0 + lr, n - 1) * ldx;
+    const GmLaneConst lc = gm_lane_const<FMT>(g);
 
-    uint32_t wv[ND];
-    u32x4g_t xv[4];
+    // this group's LDS: activation tiles [2][kBN][kPitch] halves, then the
+    // quant stages [2][kBM][kAP] bytes
+    uint8_t *const glds = lds + kg * gm_group_lds<FMT>();
+    uint16_t *const bsm = reinterpret_cast<uint16_t *>(glds);
+    uint8_t *const asm_ = glds + 2 * (size_t)kBufHalves * 2;
 
-    auto load_step = [&](int it) {
-        const uint8_t *p = wrow + (int64_t)it * (2 * F::kBytes);
-        if (FAST) {
+    // Quant staging role: 16-byte chunk u of thread gtid is chunk c of row r
+    // (e = gtid + 256u, r = e / kNC, c = e % kNC), and the tail of row gtid.
+    // Rows past the matrix read a clamped, valid row: output (i, j) depends
+    // only on weight row i and activation column j, and such rows are never
+    // stored.
+    const uint8_t *arow[kNC + 1];
 #pragma unroll
-            for (int i = 0; i + 4 <= ND; i += 4) {
-                const u32x4g_a4 t = *reinterpret_cast<const u32x4g_a4 *>(p + 4 * i);
-                wv[i] = t.x; wv[i + 1] = t.y; wv[i + 2] = t.z; wv[i + 3] = t.w;
+    for (int u = 0; u < kNC; ++u) {
+        const int e = gtid + 256 * u;
+        arow[u] = w + (int64_t)min(row0 + e / kNC, m - 1) * row_bytes + 16 * (e % kNC);
+    }
+    arow[kNC] = w + (int64_t)min(row0 + gtid, m - 1) * row_bytes + 16 * kNC;
+
+    // activation staging role: column gtid/2 of the tile, k-half gtid%2 of the step
+    const int bcol = gtid >> 1, bhalf = gtid & 1;
+    const uint16_t *__restrict__ xcol = x + (int64_t)min(col0 + bcol, n - 1) * ldx + 32 * bhalf;
+
+    typedef u32x4g_t ASet[kRT][2];
+    typedef uint32_t QStage[kNC * 4 + kTail / 4];
+    typedef u32x4g_t XSet[4];
+
+    // Global -> registers: the quant bytes and activations of local step s
+    // (clamped to the group's last pair; the data of a clamped step is unused).
+    auto load_a = [&](int s, QStage &qa) __attribute__((always_inline)) {
+        const int pair = pbase + min(s, gsteps - 1);
+        const int64_t off = (int64_t)pair * kPairBytes;
+        if constexpr (FAST) {
+#pragma unroll
+            for (int u = 0; u < kNC; ++u) {
+                const u32x4g_a4 t = *reinterpret_cast<const u32x4g_a4 *>(arow[u] + off);
+                qa[4 * u] = t.x; qa[4 * u + 1] = t.y; qa[4 * u + 2] = t.z; qa[4 * u + 3] = t.w;
             }
-#pragma unroll
-            for (int i = ND & ~3; i < ND; ++i) wv[i] = *reinterpret_cast<const uint32_t *>(p + 4 * i);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xv[i] = *reinterpret_cast<const u32x4g_t *>(xcol + it * kBK + 32 * lh + 8 * i);
+            if constexpr (kTail == 8) {
+                const u32x2g_a4 t = *reinterpret_cast<const u32x2g_a4 *>(arow[kNC] + off);
+                qa[4 * kNC] = t.x; qa[4 * kNC + 1] = t.y;
+            } else {
+                qa[4 * kNC] = *reinterpret_cast<const uint32_t *>(arow[kNC] + off);
+            }
         } else {
             // 2-byte loads; a missing second block (odd block count) reads as
-            // zeros (d = m = 0, weights 0), activations past K as 0
-            const bool second = 2 * it + 1 < nb;
-            const uint16_t *h = reinterpret_cast<const uint16_t *>(p);
+            // zeros (scale 0, weights 0)
+            const bool second = 2 * pair + 1 < nb;
 #pragma unroll
-            for (int i = 0; i < ND; ++i) {
-                const uint32_t a = (4 * i < F::kBytes || second) ? (uint32_t)h[2 * i] : 0u;
-                const uint32_t b = (4 * i + 2 < F::kBytes || second) ? (uint32_t)h[2 * i + 1] : 0u;
-                wv[i] = a | (b << 16);
-            }
+            for (int u = 0; u <= kNC; ++u) {
+                const int nd = u < kNC ? 4 : kTail / 4;
+                const int pos0 = u < kNC ? 16 * ((gtid + 256 * u) % kNC) : 16 * kNC;
+                const uint16_t *hp = reinterpret_cast<const uint16_t *>(arow[u] + off);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kk = it * kBK + 32 * lh + 8 * i;
-                uint32_t e[4] = {0u, 0u, 0u, 0u};
-                if (kk < k) {
-                    const uint16_t *q = xcol + kk;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) e[u] = (uint32_t)q[2 * u] | ((uint32_t)q[2 * u + 1] << 16);
+                for (int d = 0; d < 4; ++d) {
+                    if (d < nd) {
+                        const int o = pos0 + 4 * d;
+                        const uint32_t lo = (o < F::kBytes || second) ? (uint32_t)hp[2 * d] : 0u;
+                        const uint32_t hi = (o + 2 < F::kBytes || second) ? (uint32_t)hp[2 * d + 1] : 0u;
+                        qa[4 * u + d] = lo | (hi << 16);
+                    }
                 }
-                xv[i] = u32x4g_t{e[0], e[1], e[2], e[3]};
+            }
+        }
+    };
+    auto store_a = [&](const QStage &qa, int buf) __attribute__((always_inline)) {
+        uint8_t *st = asm_ + buf * (kBM * kAP);
+#pragma unroll
+        for (int u = 0; u < kNC; ++u) {
+            const int e = gtid + 256 * u;
+            *reinterpret_cast<u32x4g_t *>(st + (e / kNC) * kAP + 16 * (e % kNC)) =
+                u32x4g_t{qa[4 * u], qa[4 * u + 1], qa[4 * u + 2], qa[4 * u + 3]};
+        }
+        if constexpr (kTail == 8)
+            *reinterpret_cast<u32x2g_t *>(st + gtid * kAP + 16 * kNC) = u32x2g_t{qa[4 * kNC], qa[4 * kNC + 1]};
+        else
+            *reinterpret_cast<uint32_t *>(st + gtid * kAP + 16 * kNC) = qa[4 * kNC];
+    };
+
+    auto load_b = [&](int s, XSet &xb) __attribute__((always_inline)) {
+        const int pair = pbase + min(s, gsteps - 1);
+        const uint16_t *p = xcol + pair * kBK;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if constexpr (FAST) {
+                xb[u] = *reinterpret_cast<const u32x4g_t *>(p + 8 * u);
+            } else {
+                uint32_t e[4] = {0u, 0u, 0u, 0u};
+                if (pair * kBK + 32 * bhalf + 8 * u < k) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        e[v] = (uint32_t)p[8 * u + 2 * v] | ((uint32_t)p[8 * u + 2 * v + 1] << 16);
+                }
+                xb[u] = u32x4g_t{e[0], e[1], e[2], e[3]};
+            }
+        }
+    };
+    auto store_b = [&](const XSet &xb, int buf) __attribute__((always_inline)) {
+        u32x4g_t *dst = reinterpret_cast<u32x4g_t *>(bsm + buf * kBufHalves + bcol * kPitch + 32 * bhalf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[u] = xb[u];
+    };
+
+    // LDS quant stage -> this lane's A operands (16-row tile i: rows
+    // 64wm + 16i + lane%16, the lane's 8 elements of each block).
+    auto decode = [&](int buf, ASet &a) __attribute__((always_inline)) {
+        const uint8_t *st = asm_ + buf * (kBM * kAP) + (wm * 64 + (lane & 15)) * kAP;
+#pragma unroll
+        for (int i = 0; i < kRT; ++i) {
+            uint32_t q[NQ];
+#pragma unroll
+            for (int t = 0; t < NQ; ++t) q[t] = *reinterpret_cast<const uint32_t *>(st + i * 16 * kAP + gm_offset<FMT>(t, g));
+            gm_decode<FMT>(q, lc, a[i][0], a[i][1]);
+        }
+    };
+
+    floatx4_t acc[kRT][kCT];
+#pragma unroll
+    for (int i = 0; i < kRT; ++i)
+#pragma unroll
+        for (int j = 0; j < kCT; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto mma = [&](const ASet &a, int buf) __attribute__((always_inline)) {
+        const uint16_t *bb = bsm + buf * kBufHalves + (lane & 15) * kPitch + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int j = 0; j < kCT; ++j) {
+                const half8_t bf = *reinterpret_cast<const half8_t *>(bb + j * 16 * kPitch + 32 * ks);
+#pragma unroll
+                for (int i = 0; i < kRT; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a[i][ks]), bf,
+                                                                       acc[i][j], 0, 0, 0);
             }
         }
     };
 
-    floatx4_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const int nsteps = (nb + 1) / 2;
-    if (nsteps > 0) load_step(0);
-    for (int it = 0; it < nsteps; ++it) {
-        // stage: dequantized weights and activations of this step into LDS
-        u32x4g_t a4[4];
-        // (a block missing from the last pair of an odd row was loaded as
-        // zeros: its weights are 0 and the activations past K are 0 too)
-        gm_dequant<FMT>(wv, lh, a4);
-        u32x4g_t *adst = reinterpret_cast<u32x4g_t *>(As + lr * kPitch + 32 * lh);
-        u32x4g_t *bdst = reinterpret_cast<u32x4g_t *>(Bs + lr * kPitch + 32 * lh);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            adst[g] = a4[g];
-            bdst[g] = xv[g];
-        }
+    if (nsteps > 0) {
+        QStage qa;
+        XSet xb;
+        load_a(0, qa);
+        load_b(0, xb);
+        store_a(qa, 0);
+        store_b(xb, 0);
         __syncthreads();
-        if (it + 1 < nsteps) load_step(it + 1);
-
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            half8_t af[4], bf[4];
-            const int kofs = ks * 32 + (lane >> 4) * 8;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const half8_t *>(As + (wr * 64 + i * 16 + (lane & 15)) * kPitch + kofs);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bf[j] = *reinterpret_cast<const half8_t *>(Bs + (wc * 64 + j * 16 + (lane & 15)) * kPitch + kofs);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        // Local step s (both groups step together; group 1 skips the multiply
+        // of a step past its last pair): prefetch step s+1 into registers,
+        // dequantize step s from LDS, multiply, then stage step s+1 into the
+        // other LDS buffers.
+        for (int s = 0; s < nsteps; ++s) {
+            const int buf = s & 1;
+            load_a(s + 1, qa);
+            load_b(s + 1, xb);
+            if (s < gsteps) {
+                ASet f;
+                decode(buf, f);
+                mma(f, buf);
+            }
+            store_a(qa, buf ^ 1);
+            store_b(xb, buf ^ 1);
+            __syncthreads();
         }
-        __syncthreads();
     }
 
-    // Epilogue: acc[i][j][e] is row wr*64 + 16i + 4*(lane/16) + e, column
-    // wc*64 + 16j + lane%16 of the tile.
+    // Combine the two k groups: group kg finishes columns 64kg..64kg+63 of
+    // the tile.  In two rounds (row tiles 0-1, then 2-3), each wave hands the
+    // partial sums of the other group's columns to its partner through LDS.
+    // (Column indices must be compile-time constants so that the
+    // accumulators stay in registers, hence one copy per group.)
+    float4 *red = reinterpret_cast<float4 *>(lds);
+    auto finish = [&](auto kgc) __attribute__((always_inline)) {
+        constexpr int KG = decltype(kgc)::value;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int col = col0 + wc * 64 + j * 16 + (lane & 15);
-        if (col >= n) continue;
-        float *ycol = y + (int64_t)col * ldy;
+        for (int r = 0; r < 2; ++r) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = row0 + wr * 64 + i * 16 + 4 * (lane >> 4);
-            if (YALIGNED && row + 3 < m) {
-                *reinterpret_cast<float4 *>(ycol + row) =
-                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-            } else {
+            for (int il = 0; il < 2; ++il)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (row + e < m) ycol[row + e] = acc[i][j][e];
+                for (int jl = 0; jl < 4; ++jl) {
+                    const int i = 2 * r + il;
+                    constexpr int jo = 4 * (1 - KG);
+                    const int owner = (1 - KG) * 4 + wm;
+                    red[((owner * 2 + il) * 4 + jl) * 64 + lane] =
+                        make_float4(acc[i][jo + jl][0], acc[i][jo + jl][1], acc[i][jo + jl][2], acc[i][jo + jl][3]);
+                }
+            __syncthreads();
+#pragma unroll
+            for (int il = 0; il < 2; ++il)
+#pragma unroll
+                for (int jl = 0; jl < 4; ++jl) {
+                    const int i = 2 * r + il;
+                    constexpr int jm = 4 * KG;
+                    const float4 o = red[((wave * 2 + il) * 4 + jl) * 64 + lane];
+                    acc[i][jm + jl][0] += o.x;
+                    acc[i][jm + jl][1] += o.y;
+                    acc[i][jm + jl][2] += o.z;
+                    acc[i][jm + jl][3] += o.w;
+                }
+            __syncthreads();
+        }
+
+        // acc[i][j][e] is row 64*wm + 16i + 4*(lane/16) + e, column
+        // 16j + lane%16 of the tile; this group stores j = 4KG..4KG+3.
+#pragma unroll
+        for (int jl = 0; jl < 4; ++jl) {
+            constexpr int jm = 4 * KG;
+            const int col = col0 + (jm + jl) * 16 + (lane & 15);
+            if (col >= n) continue;
+            float *ycol = y + (int64_t)col * ldy;
+#pragma unroll
+            for (int i = 0; i < kRT; ++i) {
+                const int row = row0 + wm * 64 + i * 16 + 4 * g;
+                const floatx4_t v = acc[i][jm + jl];
+                if (YALIGNED && row + 3 < m) {
+                    *reinterpret_cast<float4 *>(ycol + row) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (row + e < m) ycol[row + e] = v[e];
+                }
             }
         }
-    }
+    };
+    if (kg == 0)
+        finish(std::integral_constant<int, 0>{});
+    else
+        finish(std::integral_constant<int, 1>{});
+}
+
+template <int FMT, bool FAST, bool YA>
+static int launch_gemm(const uint8_t *w, int m, int nb, const uint16_t *x, int64_t ldx, int n,
+                       float *y, int64_t ldy, int mtiles, int ntiles, hipStream_t stream) {
+    auto kern = gemm_kernel<FMT, FAST, YA>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)gm_lds_bytes<FMT>()) != hipSuccess)
+        return QK_ERR_LAUNCH;
+    return launch_lds(kern, dim3((unsigned)(mtiles * ntiles)), dim3(kGmThreads), gm_lds_bytes<FMT>(), stream, w, m, nb,
+                      x, ldx, n, y, ldy, mtiles, ntiles);
 }
 
 template <int FMT>
@@ -290,18 +494,13 @@ static int dispatch_gemm(const uint8_t *w, int m, int nb, const uint16_t *x, int
                          float *y, int64_t ldy, hipStream_t stream) {
     const int mtiles = (m + kBM - 1) / kBM;
     const int ntiles = (n + kBN - 1) / kBN;
-    const dim3 grid((unsigned)(mtiles * ntiles));
-    const dim3 block(kGmThreads);
     const bool fast = ((uintptr_t)w % 4) == 0 && (nb % 2) == 0 && ((uintptr_t)x % 16) == 0 &&
                       (ldx % 8) == 0;
     const bool ya = ((uintptr_t)y % 16) == 0 && (ldy % 4) == 0;
-    if (fast && ya)
-        return launch(gemm_kernel<FMT, true, true>, grid, block, stream, w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles);
-    if (fast)
-        return launch(gemm_kernel<FMT, true, false>, grid, block, stream, w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles);
-    if (ya)
-        return launch(gemm_kernel<FMT, false, true>, grid, block, stream, w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles);
-    return launch(gemm_kernel<FMT, false, false>, grid, block, stream, w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles);
+    if (fast && ya) return launch_gemm<FMT, true, true>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
+    if (fast) return launch_gemm<FMT, true, false>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
+    if (ya) return launch_gemm<FMT, false, true>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
+    return launch_gemm<FMT, false, false>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
 }
 
 int launch_mul_mat(int fmt, const void *w, int64_t m, int64_t k, const uint16_t *x, int64_t n,

@@ -368,6 +368,39 @@ def test_gemm_matches_exact_fp16_weight_products():
         assert np.array_equal(y[j], W16[:, c])
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k", [(300, 256), (77, 160), (129, 32)])
+def test_gemm_identity_gives_fp16_weights(fmt, m, k):
+    """With X = I (n = k one-hot columns) every output is one fp16 weight:
+    Y[j] == f16(W)[:, j] exactly, which pins the placement of every element
+    of every block (k = 160 has an odd block count)."""
+    _say("gemm identity", fmt, m, k)
+    w = _weights(fmt, m, k, seed=44)
+    xh = np.eye(k, dtype=np.float16)
+    y = _gpu_gemm(fmt, w, m, k, xh)
+    W16 = oracle.dequantize_f16(fmt, w, m, k).view(np.float16).astype(np.float32)
+    assert np.array_equal(y, W16.T), f"gemm identity {fmt} {m}x{k}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k,n", [(257, 640, 129), (300, 2080, 17), (512, 4096, 256)])
+def test_gemm_against_fp16_weight_product(fmt, m, k, n):
+    """Against the exact product of the oracle's fp16 weights and the fp16
+    activations (fp64): each product is exact in fp32, so only the fp32
+    accumulation rounds, at most k+1 times: |y - ref| <= (k+1) 2^-24 S16."""
+    _say("gemm fp16-weight product", fmt, m, k, n)
+    w = _weights(fmt, m, k, seed=45)
+    xh = synth.activations(k, n, seed=45, tensor_id=2, dtype=np.float16)
+    y = _gpu_gemm(fmt, w, m, k, xh)
+    W16 = oracle.dequantize_f16(fmt, w, m, k).view(np.float16).astype(np.float64)
+    X = xh.astype(np.float64)
+    ref = X @ W16.T
+    s16 = np.abs(X) @ np.abs(W16).T
+    bound = (k + 1) * 2.0 ** -24 * s16
+    err = np.abs(y.astype(np.float64) - ref)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}"
+
+
 def test_gemm_full_config4_sampled():
     """Q4_0 14336 x 4096 times fp16 4096 x 512: sampled outputs against the oracle."""
     cfg = synth.WORKLOADS["gemm_q4_0_14336x4096_n512"]
