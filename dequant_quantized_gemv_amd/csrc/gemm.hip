@@ -189,6 +189,69 @@ __device__ __forceinline__ void gm_decode(const uint32_t (&q)[GmQ<FMT>::kN], con
     }
 }
 
+// Combine the two k groups of a 256 x 128 tile and store it: group KG
+// finishes columns 64KG..64KG+63.  In two rounds (row tiles 0-1, then 2-3),
+// each wave hands the partial sums of the other group's columns to its
+// partner through LDS (8 waves x 8 tiles x 64 lanes x 16 bytes).  Column
+// indices are compile-time constants so that the accumulators stay in
+// registers, hence one instance per group.
+template <int KG, bool YALIGNED>
+__device__ __forceinline__ void gm_finish(floatx4_t (&acc)[kRT][kCT], uint8_t *lds, int wave, int lane,
+                                          int row0, int col0, int m, int n, float *__restrict__ y,
+                                          int64_t ldy) {
+    const int wm = wave & 3, g = lane >> 4;
+    float4 *red = reinterpret_cast<float4 *>(lds);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+        for (int il = 0; il < 2; ++il)
+#pragma unroll
+            for (int jl = 0; jl < 4; ++jl) {
+                const int i = 2 * r + il;
+                constexpr int jo = 4 * (1 - KG);
+                const int owner = (1 - KG) * 4 + wm;
+                red[((owner * 2 + il) * 4 + jl) * 64 + lane] =
+                    make_float4(acc[i][jo + jl][0], acc[i][jo + jl][1], acc[i][jo + jl][2], acc[i][jo + jl][3]);
+            }
+        __syncthreads();
+#pragma unroll
+        for (int il = 0; il < 2; ++il)
+#pragma unroll
+            for (int jl = 0; jl < 4; ++jl) {
+                const int i = 2 * r + il;
+                constexpr int jm = 4 * KG;
+                const float4 o = red[((wave * 2 + il) * 4 + jl) * 64 + lane];
+                acc[i][jm + jl][0] += o.x;
+                acc[i][jm + jl][1] += o.y;
+                acc[i][jm + jl][2] += o.z;
+                acc[i][jm + jl][3] += o.w;
+            }
+        __syncthreads();
+    }
+
+    // acc[i][j][e] is row 64*wm + 16i + 4*(lane/16) + e, column 16j + lane%16
+    // of the tile; this group stores j = 4KG..4KG+3.
+#pragma unroll
+    for (int jl = 0; jl < 4; ++jl) {
+        constexpr int jm = 4 * KG;
+        const int col = col0 + (jm + jl) * 16 + (lane & 15);
+        if (col >= n) continue;
+        float *ycol = y + (int64_t)col * ldy;
+#pragma unroll
+        for (int i = 0; i < kRT; ++i) {
+            const int row = row0 + wm * 64 + i * 16 + 4 * g;
+            const floatx4_t v = acc[i][jm + jl];
+            if (YALIGNED && row + 3 < m) {
+                *reinterpret_cast<float4 *>(ycol + row) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (row + e < m) ycol[row + e] = v[e];
+            }
+        }
+    }
+}
+
 // LDS bytes per weight row and step in the quant stage (the pair, padded so
 // that rows start on 16 bytes; the pitch in dwords is 4 mod 8 or 8 mod 16,
 // which spreads 16 consecutive rows over distinct banks).
@@ -414,68 +477,230 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
         }
     }
 
-    // Combine the two k groups: group kg finishes columns 64kg..64kg+63 of
-    // the tile.  In two rounds (row tiles 0-1, then 2-3), each wave hands the
-    // partial sums of the other group's columns to its partner through LDS.
-    // (Column indices must be compile-time constants so that the
-    // accumulators stay in registers, hence one copy per group.)
-    float4 *red = reinterpret_cast<float4 *>(lds);
-    auto finish = [&](auto kgc) __attribute__((always_inline)) {
-        constexpr int KG = decltype(kgc)::value;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-#pragma unroll
-            for (int il = 0; il < 2; ++il)
-#pragma unroll
-                for (int jl = 0; jl < 4; ++jl) {
-                    const int i = 2 * r + il;
-                    constexpr int jo = 4 * (1 - KG);
-                    const int owner = (1 - KG) * 4 + wm;
-                    red[((owner * 2 + il) * 4 + jl) * 64 + lane] =
-                        make_float4(acc[i][jo + jl][0], acc[i][jo + jl][1], acc[i][jo + jl][2], acc[i][jo + jl][3]);
-                }
-            __syncthreads();
-#pragma unroll
-            for (int il = 0; il < 2; ++il)
-#pragma unroll
-                for (int jl = 0; jl < 4; ++jl) {
-                    const int i = 2 * r + il;
-                    constexpr int jm = 4 * KG;
-                    const float4 o = red[((wave * 2 + il) * 4 + jl) * 64 + lane];
-                    acc[i][jm + jl][0] += o.x;
-                    acc[i][jm + jl][1] += o.y;
-                    acc[i][jm + jl][2] += o.z;
-                    acc[i][jm + jl][3] += o.w;
-                }
-            __syncthreads();
-        }
+    if (kg == 0)
+        gm_finish<0, YALIGNED>(acc, lds, wave, lane, row0, col0, m, n, y, ldy);
+    else
+        gm_finish<1, YALIGNED>(acc, lds, wave, lane, row0, col0, m, n, y, ldy);
+}
 
-        // acc[i][j][e] is row 64*wm + 16i + 4*(lane/16) + e, column
-        // 16j + lane%16 of the tile; this group stores j = 4KG..4KG+3.
+// ---------------------------------------------------------------------------
+// Aligned path: the same tile, waves and arithmetic, with the operands copied
+// global -> LDS by the gfx950 direct loads (global_load_lds, no registers in
+// between) into a ring of stages, kDmaLead super-steps ahead of their use.
+// A super-step is two consecutive pairs: k group 0 multiplies the first and
+// k group 1 the second, so one stage holds, per weight row, 72 / 80 / 136
+// contiguous quant bytes, and two 128 x 64 activation tiles.
+//
+// Quant stage: the row's bytes as 16-byte chunks, row pitch 16 * kDmaChunks;
+// a row length that is not a multiple of 16 (Q4_0 72, Q8_0 136) is covered by
+// a last chunk that overlaps the one before it (global bytes R-16..R-1), so
+// global byte o >= 16 (kDmaChunks - 1) sits at o + kDmaPad in LDS.
+// Activation tile: column c's eight 16-byte chunks at c*128 + 16 (q ^ ((c/2)
+// % 8)) (an XOR swizzle in place of padding: the direct loads write lane after
+// lane, and 16 consecutive columns of a fragment read then fall on distinct
+// banks).
+// ---------------------------------------------------------------------------
+template <int FMT> struct GmDma {
+    static constexpr int kRow = 4 * Format<FMT>::kBytes;            // quant bytes per row and super-step
+    static constexpr int kChunks = (kRow + 15) / 16;
+    static constexpr int kPad = 16 * kChunks - kRow;
+    static constexpr int kAStage = kBM * 16 * kChunks;              // bytes
+    static constexpr int kBStage = 2 * kBN * kBK * 2;               // bytes (two tiles)
+    static constexpr int kStage = kAStage + kBStage;
+    static constexpr int kStages = 3 * kStage <= 160 * 1024 ? 3 : 2;
+    static constexpr int kLead = kStages - 1;                       // super-steps loaded ahead
+    static constexpr int kAPerThread = (kBM * kChunks + kGmThreads - 1) / kGmThreads;
+    static constexpr int kBPerThread = kBStage / 16 / kGmThreads;  // 4
+    // Direct loads a wave issues per stage.  Wave v issues quant chunk u when
+    // 512u + 64v < kBM * kChunks, so the last waves may issue one fewer; the
+    // count used in the waits is the smallest one (wave 7's): leaving that
+    // many newer loads outstanding completes the older stage for every wave
+    // (a wave with more newer loads merely waits for one of them as well).
+    static constexpr int kAMin = (kBM * kChunks - 64 * 7 + kGmThreads - 1) / kGmThreads;
+    static constexpr int kLoadsPerStage = kAMin + kBPerThread;
+};
+
+template <int FMT>
+constexpr size_t gm_dma_lds_bytes() {
+    return (size_t)GmDma<FMT>::kStages * GmDma<FMT>::kStage > 8 * 8 * 64 * 16
+               ? (size_t)GmDma<FMT>::kStages * GmDma<FMT>::kStage
+               : 8 * 8 * 64 * 16;
+}
+
+typedef __attribute__((address_space(3))) void gm_lds_void;
+typedef __attribute__((address_space(1))) void gm_glb_void;
+
+__device__ __forceinline__ void gm_dma16(const void *src, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds((gm_glb_void *)src, (gm_lds_void *)lds_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), then the workgroup barrier; a
+// compiler-level memory barrier as well.
+template <int N>
+__device__ __forceinline__ void gm_wait_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int FMT, bool YALIGNED>
+__global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
+    const uint8_t *__restrict__ w, int m, int nb, const uint16_t *__restrict__ x, int64_t ldx,
+    int n, float *__restrict__ y, int64_t ldy, int mtiles, int ntiles) {
+    using F = Format<FMT>;
+    using D = GmDma<FMT>;
+    constexpr int NQ = GmQ<FMT>::kN;
+    constexpr int kPairBytes = 2 * F::kBytes;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    // XCD-aware tile order: XCD x (= id % 8) takes a contiguous range of tiles.
+    const int ntot = mtiles * ntiles;
+    const int id = blockIdx.x;
+    const int xcd = id & 7, slot = id >> 3;
+    const int per = ntot >> 3, rem = ntot & 7;
+    const int L = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+    const int mt = L / ntiles;
+    const int nt = L - mt * ntiles;
+    const int row0 = mt * kBM;
+    const int col0 = nt * kBN;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int g = lane >> 4;
+    const int wm = wave & 3;   // 64-row slice of the tile
+    const int kg = wave >> 2;  // k group: first or second pair of each super-step
+    const int npairs = nb / 2;                 // nb % 4 == 0 here: whole super-steps
+    const int nsup = (npairs + 1) / 2;         // super-steps
+    const int64_t row_bytes = (int64_t)nb * F::kBytes;
+    const GmLaneConst lc = gm_lane_const<FMT>(g);
+
+    // Direct-load roles.  Quant chunk u of this thread: linear chunk
+    // e = 512u + tid of the stage, row e / kChunks, chunk e % kChunks (rows
+    // past the matrix are clamped: their outputs are never stored).
+    const uint8_t *asrc[D::kAPerThread];
 #pragma unroll
-        for (int jl = 0; jl < 4; ++jl) {
-            constexpr int jm = 4 * KG;
-            const int col = col0 + (jm + jl) * 16 + (lane & 15);
-            if (col >= n) continue;
-            float *ycol = y + (int64_t)col * ldy;
+    for (int u = 0; u < D::kAPerThread; ++u) {
+        const int e = min(kGmThreads * u + tid, kBM * D::kChunks - 1);
+        const int r = e / D::kChunks, c = e % D::kChunks;
+        const int off = c < D::kChunks - 1 ? 16 * c : D::kRow - 16;
+        asrc[u] = w + (int64_t)min(row0 + r, m - 1) * row_bytes + off;
+    }
+    // Activation chunk u: linear chunk e = 512u + tid, tile e / 1024 (the
+    // k group), column (e / 8) % 128, stored slot e % 8 holding logical
+    // 16-byte chunk (e % 8) ^ ((column / 2) % 8).
+    const uint16_t *bsrc[D::kBPerThread];
+    int bgrp[D::kBPerThread];
 #pragma unroll
-            for (int i = 0; i < kRT; ++i) {
-                const int row = row0 + wm * 64 + i * 16 + 4 * g;
-                const floatx4_t v = acc[i][jm + jl];
-                if (YALIGNED && row + 3 < m) {
-                    *reinterpret_cast<float4 *>(ycol + row) = make_float4(v[0], v[1], v[2], v[3]);
-                } else {
+    for (int u = 0; u < D::kBPerThread; ++u) {
+        const int e = kGmThreads * u + tid;
+        const int grp = e >> 10, col = (e >> 3) & (kBN - 1), p = e & 7;
+        const int q = p ^ ((col >> 1) & 7);
+        bgrp[u] = grp;
+        bsrc[u] = x + (int64_t)min(col0 + col, n - 1) * ldx + 8 * q;
+    }
+
+    // Issue the direct loads of super-step t (clamped to the last one) into
+    // stage buffer `buf`.
+    auto issue = [&](int t, int buf) __attribute__((always_inline)) {
+        t = min(t, nsup - 1);
+        uint8_t *st = lds + buf * D::kStage;
+        const int64_t aoff = (int64_t)(2 * t) * kPairBytes;
+        // quant bytes of the second pair of a super-step past the last pair
+        // are never used (that step's k group 1 skips its multiply)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (row + e < m) ycol[row + e] = v[e];
-                }
-            }
+        for (int u = 0; u < D::kAPerThread; ++u) {
+            if (kGmThreads * u + wave * 64 < kBM * D::kChunks)  // wave-uniform
+                gm_dma16(asrc[u] + aoff, st + 16 * (kGmThreads * u + wave * 64));
+        }
+        uint8_t *bst = st + D::kAStage;
+#pragma unroll
+        for (int u = 0; u < D::kBPerThread; ++u) {
+            const int pair = min(2 * t + bgrp[u], npairs - 1);
+            gm_dma16(bsrc[u] + pair * kBK, bst + 16 * (kGmThreads * u + wave * 64));
         }
     };
+
+    // LDS byte offset of quant byte o (of the super-step's row bytes)
+    auto aoff_lds = [&](int o) __attribute__((always_inline)) {
+        return o < 16 * (D::kChunks - 1) ? o : o + D::kPad;
+    };
+    int qoff[NQ];
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) qoff[t] = aoff_lds(kg * kPairBytes + gm_offset<FMT>(t, g));
+    const int arow = (wm * 64 + (lane & 15)) * 16 * D::kChunks;
+    // activation fragment: column 16j + lane%16 of this group's tile, logical
+    // chunk 4ks + g, stored at slot (4ks + g) ^ ((lane%16) / 2)
+    const int bcol = (lane & 15) * 128;
+    const int bslot0 = 16 * ((0 * 4 + g) ^ ((lane & 15) >> 1));
+    const int bslot1 = 16 * ((1 * 4 + g) ^ ((lane & 15) >> 1));
+
+    typedef u32x4g_t ASet[kRT][2];
+    floatx4_t acc[kRT][kCT];
+#pragma unroll
+    for (int i = 0; i < kRT; ++i)
+#pragma unroll
+        for (int j = 0; j < kCT; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (nsup > 0) {
+#pragma unroll
+        for (int t = 0; t < D::kLead; ++t) issue(t, t);
+        gm_wait_barrier<(D::kLead - 1) * D::kLoadsPerStage>();
+
+        int buf = 0;
+        for (int t = 0; t < nsup; ++t) {
+            int nbuf = buf + D::kLead;
+            if (nbuf >= D::kStages) nbuf -= D::kStages;
+            issue(t + D::kLead, nbuf);
+            const uint8_t *st = lds + buf * D::kStage;
+            if (kg == 0 || 2 * t + 1 < npairs) {
+                ASet f;
+#pragma unroll
+                for (int i = 0; i < kRT; ++i) {
+                    const uint8_t *ar = st + arow + i * 16 * (16 * D::kChunks);
+                    uint32_t q[NQ];
+#pragma unroll
+                    for (int t2 = 0; t2 < NQ; ++t2) q[t2] = *reinterpret_cast<const uint32_t *>(ar + qoff[t2]);
+                    gm_decode<FMT>(q, lc, f[i][0], f[i][1]);
+                }
+                const uint8_t *bb = st + D::kAStage + kg * (kBN * kBK * 2) + bcol;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int bslot = ks ? bslot1 : bslot0;
+#pragma unroll
+                    for (int j = 0; j < kCT; ++j) {
+                        const half8_t bf = *reinterpret_cast<const half8_t *>(bb + j * 16 * 128 + bslot);
+#pragma unroll
+                        for (int i = 0; i < kRT; ++i)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(half8_t, f[i][ks]), bf, acc[i][j], 0, 0, 0);
+                    }
+                }
+            }
+            // stage t+1 (issued kLead-1 super-steps ago) complete for every
+            // wave before anyone reads it; the kLead-1 newer stages may still
+            // be in flight
+            gm_wait_barrier<(D::kLead - 1) * D::kLoadsPerStage>();
+            buf = buf + 1 == D::kStages ? 0 : buf + 1;
+        }
+        // drain the clamped prefetches before the LDS is reused
+        gm_wait_barrier<0>();
+    }
+
     if (kg == 0)
-        finish(std::integral_constant<int, 0>{});
+        gm_finish<0, YALIGNED>(acc, lds, wave, lane, row0, col0, m, n, y, ldy);
     else
-        finish(std::integral_constant<int, 1>{});
+        gm_finish<1, YALIGNED>(acc, lds, wave, lane, row0, col0, m, n, y, ldy);
+}
+
+template <int FMT, bool YA>
+static int launch_gemm_dma(const uint8_t *w, int m, int nb, const uint16_t *x, int64_t ldx, int n,
+                           float *y, int64_t ldy, int mtiles, int ntiles, hipStream_t stream) {
+    auto kern = gemm_dma_kernel<FMT, YA>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)gm_dma_lds_bytes<FMT>()) != hipSuccess)
+        return QK_ERR_LAUNCH;
+    return launch_lds(kern, dim3((unsigned)(mtiles * ntiles)), dim3(kGmThreads), gm_dma_lds_bytes<FMT>(), stream,
+                      w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles);
 }
 
 template <int FMT, bool FAST, bool YA>
@@ -497,6 +722,10 @@ static int dispatch_gemm(const uint8_t *w, int m, int nb, const uint16_t *x, int
     const bool fast = ((uintptr_t)w % 4) == 0 && (nb % 2) == 0 && ((uintptr_t)x % 16) == 0 &&
                       (ldx % 8) == 0;
     const bool ya = ((uintptr_t)y % 16) == 0 && (ldy % 4) == 0;
+    // the direct-load path moves whole super-steps (two pairs): k % 128 == 0
+    const bool dma = fast && (nb % 4) == 0;
+    if (dma && ya) return launch_gemm_dma<FMT, true>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
+    if (dma) return launch_gemm_dma<FMT, false>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
     if (fast && ya) return launch_gemm<FMT, true, true>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
     if (fast) return launch_gemm<FMT, true, false>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
     if (ya) return launch_gemm<FMT, false, true>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
