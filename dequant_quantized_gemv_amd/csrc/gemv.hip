@@ -266,7 +266,7 @@ __device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDw
                 }
 #pragma unroll
                 for (int r = 0; r < RWV; ++r) {
-                    if (r < nrows) {
+                    if (FAST || r < nrows) {  // fast path: rows clamped, stores guarded
                         const float d = h2f(pair_d<FMT>(v[r], b));
                         const float mm = h2f(pair_m_q41(v[r], b));
                         const uint32_t qw = pair_qs<FMT>(v[r], b, i);
@@ -293,7 +293,7 @@ __device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDw
                 }
                 // keep the next group's LDS reads from being hoisted above
                 // this one (bounds the live activations)
-                if constexpr (NC >= 2) __builtin_amdgcn_sched_barrier(0);
+                if constexpr (NC >= 2) asm volatile("" ::: "memory");
             }
         } else {
             float s[RWV][NC];
@@ -312,7 +312,7 @@ __device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDw
                 }
 #pragma unroll
                 for (int r = 0; r < RWV; ++r) {
-                    if (r < nrows) {
+                    if (FAST || r < nrows) {  // fast path: rows clamped, stores guarded
 #pragma unroll
                         for (int j = 0; j < NC; ++j) {
                             if constexpr (FMT == QK_Q4_0) {
@@ -325,11 +325,11 @@ __device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDw
                         }
                     }
                 }
-                if constexpr (NC >= 3) __builtin_amdgcn_sched_barrier(0);
+                if constexpr (NC >= 3) asm volatile("" ::: "memory");
             }
 #pragma unroll
             for (int r = 0; r < RWV; ++r) {
-                if (r < nrows) {
+                if (FAST || r < nrows) {
                     const float d = h2f(pair_d<FMT>(v[r], b));
 #pragma unroll
                     for (int j = 0; j < NC; ++j) acc[r][j] = __builtin_fmaf(d, s[r][j], acc[r][j]);
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
     // pair or row reads a clamped, valid address and ignores the data), so the
     // compiler counts them and waits for exactly the loads a computation needs
     // while the prefetch stays in flight.
-    auto load_step = [&](int sg, int smi, int sc, uint32_t (&dst)[RWV][ND]) {
+    auto load_step = [&](int sg, int smi, int sc, uint32_t (&dst)[RWV][ND]) __attribute__((always_inline)) {
         const GemvItem &it = item(smi);
         const int row0 = (sg - gbase(smi)) * RG + wave * RWV;
         const int npairs = (it.nb + 1) >> 1;
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
     constexpr int XR = NC <= 2 ? NC : 0;  // columns staged through registers (first window)
 
     // Copy window `wi` of item `it`'s activations into LDS (whole workgroup).
-    auto stage_x = [&](const GemvItem &it, int wi) {
+    auto stage_x = [&](const GemvItem &it, int wi) __attribute__((always_inline)) {
         const int e0 = wi * xw;
         const int ce4 = min(xw, it.nb * 32 - e0) / 4;  // float4s in this window
 #pragma unroll
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
     // copying them to LDS does not wait for the weights (loads complete in
     // order).
     auto step = [&](auto first_tag, auto prefetch_tag, uint32_t (&cur)[RWV][ND],
-                    uint32_t (&nxt)[RWV][ND]) {
+                    uint32_t (&nxt)[RWV][ND]) __attribute__((always_inline)) {
         constexpr bool FIRST = decltype(first_tag)::value;
         constexpr bool PREFETCH = decltype(prefetch_tag)::value;
         const GemvItem &it = item(mi);
@@ -479,6 +479,9 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
             ++g2;
             while (mi2 < count && g2 >= gbase(mi2 + 1)) ++mi2;
         }
+        // past the workgroup's last step a prefetch repeats this step's loads
+        const bool more = g2 < gend;
+        const int pg = more ? g2 : g, pmi = more ? mi2 : mi, pc = more ? c2 : c;
 
         if constexpr (FIRST) {
             // activation loads, then this step's and the next step's weights,
@@ -501,7 +504,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
                 }
             }
             load_step(g, mi, c, cur);
-            if constexpr (PREFETCH) load_step(g2, mi2, c2, nxt);
+            if constexpr (PREFETCH) load_step(pg, pmi, pc, nxt);
             // unconditional stores (a tail lane rewrites the last float4 with
             // the same value), so no load is moved behind the weight loads
 #pragma unroll
@@ -534,7 +537,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
                 staged_mi = mi;
                 staged_w = wi;
             }
-            if constexpr (PREFETCH) load_step(g2, mi2, c2, nxt);
+            if constexpr (PREFETCH) load_step(pg, pmi, pc, nxt);
         }
 
         // compute this step
@@ -573,6 +576,19 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         return;
     }
     step(T{}, T{}, va, vb);
+    if constexpr (NC >= 4) {
+        // one steady-state step body (a single copy of the wide code keeps
+        // register allocation tractable); the last step's prefetch repeats
+        // its own loads (clamped), and the next set is copied into place
+        for (int left = nsteps - 1; left > 0; --left) {
+#pragma unroll
+            for (int r = 0; r < RWV; ++r)
+#pragma unroll
+                for (int d = 0; d < ND; ++d) va[r][d] = vb[r][d];
+            step(F{}, T{}, va, vb);
+        }
+        return;
+    }
     int left = nsteps - 1;  // steps still to compute; the next one's weights are in vb
     while (true) {
         if (left == 1) {
@@ -591,9 +607,12 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
 
 // Launch shape by column count: RWV rows per wave, WPG waves per workgroup
 // sharing one LDS copy of the activations.
-template <int NC> struct GemvShape {
-    static constexpr int kRWV = 1;
-    static constexpr int kWPG = NC <= 4 ? 8 : 4;
+// Above 4 columns the staged activations (NC x 4096 floats) leave room for
+// one workgroup per CU, so the workgroup itself is as wide as registers
+// allow: 12 waves (3 per SIMD) for Q4_1, 8 for Q4_0, 4 for Q8_0.
+template <int FMT, int NC> struct GemvShape {
+    static constexpr int kRWV = NC >= 4 && FMT != QK_Q8_0 ? 2 : 1;
+    static constexpr int kWPG = NC <= 4 ? 8 : (FMT == QK_Q4_1 ? 12 : (FMT == QK_Q4_0 ? 8 : 4));
 };
 
 static int device_cus() {
@@ -606,8 +625,8 @@ static int device_cus() {
 
 template <int FMT, int NC>
 static int dispatch_gemv_nc(GemvArgs &a, bool fast, hipStream_t stream) {
-    constexpr int RWV = GemvShape<NC>::kRWV;
-    constexpr int WPG = GemvShape<NC>::kWPG;
+    constexpr int RWV = GemvShape<FMT, NC>::kRWV;
+    constexpr int WPG = GemvShape<FMT, NC>::kWPG;
     constexpr int RG = WPG * RWV;
     a.gbase[0] = 0;
     int kmax = 0;
