@@ -615,6 +615,15 @@ template <int FMT, int NC> struct GemvShape {
     static constexpr int kWPG = NC <= 4 ? 8 : (FMT == QK_Q4_1 ? 12 : (FMT == QK_Q4_0 ? 8 : 4));
 };
 
+// Workgroups launched per CU at most (when LDS allows).  Above what can be
+// resident at once, the hardware dispatcher starts a workgroup as another
+// finishes, which balances row groups better than giving each resident
+// workgroup a longer range.
+#ifndef QK_GEMV_WG_PER_CU
+#define QK_GEMV_WG_PER_CU 8
+#endif
+constexpr int kGvMaxWgPerCu = QK_GEMV_WG_PER_CU;
+
 static int device_cus() {
     int cus = 256, dev = 0, v = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
@@ -641,7 +650,7 @@ static int dispatch_gemv_nc(GemvArgs &a, bool fast, hipStream_t stream) {
     const int cap = max(1, (64 * 1024) / (NC * xw_pitch(kGvChunkElems) * (int)sizeof(float))) * kGvChunkElems;
     const int xw = max(kGvChunkElems, min(cap, (kmax + kGvChunkElems - 1) / kGvChunkElems * kGvChunkElems));
     const size_t lds = (size_t)NC * xw_pitch(xw) * sizeof(float);
-    const int per_cu = max(1, min(4, (int)((160 * 1024) / lds)));
+    const int per_cu = max(1, min(kGvMaxWgPerCu, (int)((160 * 1024) / lds)));
     const int nwg = min(total, device_cus() * per_cu);
     const GemvSplit split{total, total / nwg, total % nwg};
     const dim3 grid((unsigned)nwg);
