@@ -384,13 +384,52 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
     const int xp = xw_pitch(xw);
     const int cpw = xw / CE;  // steps per activation window
 
-    const int count = SINGLE ? 1 : args.count;
     auto gbase = [&](int i) { return SINGLE ? (i == 0 ? 0 : split.total) : args.gbase[i]; };
     auto item = [&](int i) -> const GemvItem & { return SINGLE ? one : args.item[i]; };
 
-    // step state (uniform across the workgroup)
-    int g = gbeg, mi = 0, c = 0;
-    while (g >= gbase(mi + 1)) ++mi;
+    // Step position (uniform across the workgroup): row group g of item mi,
+    // chunk c, with the item's descriptor held in registers.  It is read from
+    // the argument table only when a step enters a new item.
+    struct Pos {
+        int g, mi, c;
+        int gb0, gb1;   // the item's first row group and one past its last
+        int nchunks;    // steps per row group
+        GemvItem it;
+    };
+    // (field by field: a whole-struct copy out of the argument table is
+    // lowered through scratch memory)
+    auto enter = [&](Pos &q, int i) __attribute__((always_inline)) {
+        q.mi = i;
+        const GemvItem &src = item(i);
+        q.it.w = src.w;
+        q.it.x = src.x;
+        q.it.y = src.y;
+        q.it.ldx = src.ldx;
+        q.it.ldy = src.ldy;
+        q.it.m = src.m;
+        q.it.nb = src.nb;
+        q.gb0 = gbase(i);
+        q.gb1 = gbase(i + 1);
+        q.nchunks = (((q.it.nb + 1) >> 1) + CP - 1) / CP;
+    };
+    Pos P;
+    P.g = gbeg;
+    P.c = 0;
+    {
+        int i = 0;
+        while (gbeg >= gbase(i + 1)) ++i;
+        enter(P, i);
+    }
+    // The step after q within this workgroup's range (items have at least one
+    // row group each, so a step enters at most one new item).
+    auto advance = [&](const Pos &q) __attribute__((always_inline)) {
+        Pos r = q;
+        if (++r.c >= r.nchunks) {
+            r.c = 0;
+            if (++r.g >= r.gb1 && r.g < gend) enter(r, r.mi + 1);
+        }
+        return r;
+    };
     int staged_mi = -1, staged_w = -1;
 
     float acc[RWV][NC];
@@ -404,12 +443,12 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
     // pair or row reads a clamped, valid address and ignores the data), so the
     // compiler counts them and waits for exactly the loads a computation needs
     // while the prefetch stays in flight.
-    auto load_step = [&](int sg, int smi, int sc, uint32_t (&dst)[RWV][ND]) __attribute__((always_inline)) {
-        const GemvItem &it = item(smi);
-        const int row0 = (sg - gbase(smi)) * RG + wave * RWV;
+    auto load_step = [&](const Pos &q, uint32_t (&dst)[RWV][ND]) __attribute__((always_inline)) {
+        const GemvItem &it = q.it;
+        const int row0 = (q.g - q.gb0) * RG + wave * RWV;
         const int npairs = (it.nb + 1) >> 1;
         const int64_t row_bytes = (int64_t)it.nb * BS;
-        const int pp = sc * CP + lane;
+        const int pp = q.c * CP + lane;
         if (FAST) {
             const int ppc = min(pp, npairs - 1);
 #pragma unroll
@@ -448,7 +487,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
     // Steps in this workgroup's range.
     int nsteps = 0;
     {
-        int gg = gbeg, ii = mi;
+        int gg = gbeg, ii = P.mi;
         while (gg < gend) {
             while (gg >= gbase(ii + 1)) ++ii;
             const int nxt = min(gend, gbase(ii + 1));
@@ -468,20 +507,13 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
                     uint32_t (&nxt)[RWV][ND]) __attribute__((always_inline)) {
         constexpr bool FIRST = decltype(first_tag)::value;
         constexpr bool PREFETCH = decltype(prefetch_tag)::value;
-        const GemvItem &it = item(mi);
+        const GemvItem &it = P.it;
         const int npairs = (it.nb + 1) >> 1;
-        const int nchunks = (npairs + CP - 1) / CP;
-        const int wi = c / cpw;  // activation window of this step
+        const int wi = P.c / cpw;  // activation window of this step
 
-        int g2 = g, mi2 = mi, c2 = c + 1;
-        if (c2 >= nchunks) {
-            c2 = 0;
-            ++g2;
-            while (mi2 < count && g2 >= gbase(mi2 + 1)) ++mi2;
-        }
+        const Pos Q = advance(P);
         // past the workgroup's last step a prefetch repeats this step's loads
-        const bool more = g2 < gend;
-        const int pg = more ? g2 : g, pmi = more ? mi2 : mi, pc = more ? c2 : c;
+        const Pos PF = Q.g < gend ? Q : P;
 
         if constexpr (FIRST) {
             // activation loads, then this step's and the next step's weights,
@@ -503,8 +535,8 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
                     else xr[j][u] = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
                 }
             }
-            load_step(g, mi, c, cur);
-            if constexpr (PREFETCH) load_step(pg, pmi, pc, nxt);
+            load_step(P, cur);
+            if constexpr (PREFETCH) load_step(PF, nxt);
             // unconditional stores (a tail lane rewrites the last float4 with
             // the same value), so no load is moved behind the weight loads
 #pragma unroll
@@ -526,30 +558,30 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
                 }
             }
             __syncthreads();
-            staged_mi = mi;
+            staged_mi = P.mi;
             staged_w = wi;
         } else {
             // a new item or window: restage the activations before the prefetch
-            if (staged_mi != mi || staged_w != wi) {
+            if (staged_mi != P.mi || staged_w != wi) {
                 __syncthreads();  // readers of the previous window are done
                 stage_x(it, wi);
                 __syncthreads();
-                staged_mi = mi;
+                staged_mi = P.mi;
                 staged_w = wi;
             }
-            if constexpr (PREFETCH) load_step(pg, pmi, pc, nxt);
+            if constexpr (PREFETCH) load_step(PF, nxt);
         }
 
         // compute this step
-        const int row0 = (g - gbase(mi)) * RG + wave * RWV;
+        const int row0 = (P.g - P.gb0) * RG + wave * RWV;
         const int nrows = max(0, min(RWV, it.m - row0));
-        const int pp = c * CP + lane;
+        const int pp = P.c * CP + lane;
         if (nrows > 0 && pp < npairs)
             pair_dot<FMT, NC, RWV, FAST>(cur, nrows, FAST || (2 * pp + 1 < it.nb), xs, xp,
-                                         (c - wi * cpw) * CE + lane * 64, acc);
+                                         (P.c - wi * cpw) * CE + lane * 64, acc);
 
         // last chunk of the group: reduce across the wave and store
-        if (c == nchunks - 1) {
+        if (P.c == P.nchunks - 1) {
 #pragma unroll
             for (int r = 0; r < RWV; ++r) {
                 if (r < nrows) {
@@ -563,9 +595,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
                 for (int j = 0; j < NC; ++j) acc[r][j] = 0.0f;
             }
         }
-        g = g2;
-        mi = mi2;
-        c = c2;
+        P = Q;
     };
 
     using T = std::true_type;
