@@ -503,10 +503,12 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
     // in flight.  FIRST issues the activation loads before any weight load, so
     // copying them to LDS does not wait for the weights (loads complete in
     // order).
-    auto step = [&](auto first_tag, auto prefetch_tag, uint32_t (&cur)[RWV][ND],
+    // DEPTH: 0 no prefetch, 1 the next step's weights requested into nxt.
+    auto step = [&](auto first_tag, auto depth_tag, uint32_t (&cur)[RWV][ND],
                     uint32_t (&nxt)[RWV][ND]) __attribute__((always_inline)) {
         constexpr bool FIRST = decltype(first_tag)::value;
-        constexpr bool PREFETCH = decltype(prefetch_tag)::value;
+        constexpr int DEPTH = decltype(depth_tag)::value;
+        constexpr bool PREFETCH = DEPTH > 0;
         const GemvItem &it = P.it;
         const int npairs = (it.nb + 1) >> 1;
         const int wi = P.c / cpw;  // activation window of this step
@@ -600,39 +602,25 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
 
     using T = std::true_type;
     using F = std::false_type;
+    using D0 = std::integral_constant<int, 0>;
+    using D1 = std::integral_constant<int, 1>;
     uint32_t va[RWV][ND], vb[RWV][ND];
     if (nsteps == 1) {
-        step(T{}, F{}, va, vb);
+        step(T{}, D0{}, va, vb);
         return;
     }
-    step(T{}, T{}, va, vb);
-    if constexpr (NC >= 4) {
-        // one steady-state step body (a single copy of the wide code keeps
-        // register allocation tractable); the last step's prefetch repeats
-        // its own loads (clamped), and the next set is copied into place
-        for (int left = nsteps - 1; left > 0; --left) {
-#pragma unroll
-            for (int r = 0; r < RWV; ++r)
-#pragma unroll
-                for (int d = 0; d < ND; ++d) va[r][d] = vb[r][d];
-            step(F{}, T{}, va, vb);
-        }
-        return;
-    }
+    step(T{}, D1{}, va, vb);
+    // Two steps per iteration with the register sets in swapped roles and no
+    // branch between them, so the two bodies stay distinct: a merged body
+    // would copy the prefetched registers into place, and that copy waits for
+    // every outstanding load (the new prefetch included).  The final step's
+    // prefetch repeats its own loads (clamped).
     int left = nsteps - 1;  // steps still to compute; the next one's weights are in vb
-    while (true) {
-        if (left == 1) {
-            step(F{}, F{}, vb, va);
-            break;
-        }
-        step(F{}, T{}, vb, va);
-        if (--left == 1) {
-            step(F{}, F{}, va, vb);
-            break;
-        }
-        step(F{}, T{}, va, vb);
-        --left;
+    for (; left >= 2; left -= 2) {
+        step(F{}, D1{}, vb, va);
+        step(F{}, D1{}, va, vb);
     }
+    if (left == 1) step(F{}, D0{}, vb, va);
 }
 
 // Launch shape by column count: RWV rows per wave, WPG waves per workgroup
@@ -675,10 +663,12 @@ static int dispatch_gemv_nc(GemvArgs &a, bool fast, hipStream_t stream) {
     }
     const int total = a.gbase[a.count];
     if (total == 0) return QK_OK;
-    // Activation window: the longest row rounded up to 4096 weights, capped so
-    // the window stays within 64 KiB of LDS (always at least 4096 weights).
-    const int cap = max(1, (64 * 1024) / (NC * xw_pitch(kGvChunkElems) * (int)sizeof(float))) * kGvChunkElems;
-    const int xw = max(kGvChunkElems, min(cap, (kmax + kGvChunkElems - 1) / kGvChunkElems * kGvChunkElems));
+    // Activation window: one chunk of 4096 weights per column (17 KiB at one
+    // column).  Longer rows restage it per chunk; the small window lets more
+    // workgroups share a CU, which measured faster than holding whole rows of
+    // 11008 weights.
+    const int xw = kGvChunkElems;
+    (void)kmax;
     const size_t lds = (size_t)NC * xw_pitch(xw) * sizeof(float);
     const int per_cu = max(1, min(kGvMaxWgPerCu, (int)((160 * 1024) / lds)));
     const int nwg = min(total, device_cus() * per_cu);
