@@ -727,6 +727,16 @@ int launch_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count,
     }
     a.count = used;
     if (used == 0) return QK_OK;
+    // Longest rows first: items are independent, and a row group of a long
+    // row is several steps, so starting those first keeps them from being the
+    // stragglers at the end of the launch (insertion sort, at most 16 items,
+    // stable so equal lengths keep the caller's order).
+    for (int i = 1; i < used; ++i) {
+        const GemvItem t = a.item[i];
+        int j = i;
+        for (; j > 0 && a.item[j - 1].nb < t.nb; --j) a.item[j] = a.item[j - 1];
+        a.item[j] = t;
+    }
     switch (fmt) {
     case QK_Q4_0: return dispatch_gemv<QK_Q4_0>(a, (int)n, fast, stream);
     case QK_Q4_1: return dispatch_gemv<QK_Q4_1>(a, (int)n, fast, stream);
