@@ -20,8 +20,9 @@
 // there by all of its rows; its global loads are issued before the weight
 // loads so the copy never waits behind HBM.  In LDS each run of 64 floats is
 // followed by 4 floats of padding, so the 16-byte reads of lanes p = 0..15 (at
-// float offset 68p + 4t) fall in distinct banks.  A workgroup may take several
-// row groups (grid-stride) and keeps its staged x when K fits one chunk.
+// float offset 68p + 4t) fall in distinct banks.  A workgroup takes a range
+// of consecutive row groups (of one or several items of a grouped launch) and
+// restages x only when a step enters a new item or chunk.
 //
 // Arithmetic, exact per term (every term is the exact weight times x):
 //  * Q4_0: the nibble becomes the exact fp16 number q - 8 by placing it in

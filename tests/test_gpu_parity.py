@@ -469,6 +469,25 @@ def test_gemv_batched_matches_single_calls_bitwise(fmt):
         assert np.array_equal(y.view(np.uint32), _gpu_gemv(fmt, w, m, k, x).view(np.uint32))
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_batched_item_order_does_not_matter(fmt):
+    """The launcher reorders items (longest rows first); any order of the same
+    items gives bitwise the same outputs."""
+    shapes = [(40, 4096), (25, 11008), (64, 2048), (7, 8192)]
+    probs = []
+    for i, (m, k) in enumerate(shapes):
+        probs.append((_weights(fmt, m, k, seed=90 + i), m, k, synth.activations(k, 1, seed=90 + i, tensor_id=4)))
+    _say("gemv batched order", fmt)
+    ys = _gpu_gemv_batched(fmt, probs, 1)
+    order = [2, 0, 3, 1]
+    ys2 = _gpu_gemv_batched(fmt, [probs[i] for i in order], 1)
+    for pos, i in enumerate(order):
+        assert np.array_equal(ys[i].view(np.uint32), ys2[pos].view(np.uint32))
+    for (w, m, k, x), y in zip(probs, ys):
+        yref, s = oracle.dot(fmt, w, m, k, x, 1)
+        assert_within(y, yref, s, GEMV_TOL, f"batched order {fmt} {m}x{k}")
+
+
 def test_gemv_batched_generic_path_and_sixteen_items():
     """16 items, one of them misaligned (forces the 2-byte generic path for the
     whole launch) and one with an odd block count."""
