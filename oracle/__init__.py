@@ -57,6 +57,9 @@ def _load():
     lib.orc_dot_entries.argtypes = [ctypes.c_int, vp, i64, vp, ctypes.c_int, i64,
                                     vp, vp, i64, vp, vp]
     lib.orc_dot_entries.restype = None
+    lib.orc_dot_id.argtypes = [ctypes.c_int, vp, i64, i64, i64, i64, vp, i64, i64, i64,
+                               vp, i64, i64, vp, vp]
+    lib.orc_dot_id.restype = None
     _lib = lib
     return lib
 
@@ -178,3 +181,33 @@ def dot_entries(fmt, w, m, k, x, ldx, ii, jj, x_is_f16=False):
     _load().orc_dot_entries(_fmt(fmt), _ptr(w), k, _ptr(x), int(bool(x_is_f16)), ldx,
                             _ptr(ii), _ptr(jj), ii.size, _ptr(y), _ptr(s))
     return y, s
+
+
+def dot_id(fmt, w, n_experts, expert_stride, m, k, ids, n_used, n_tokens, x,
+           x_slot, x_tok, ld_ids=None):
+    """Expert-indexed products (mixture-of-experts decode).
+
+    For token t and slot s, expert e = ids[t*ld_ids + s] (matrix at byte
+    e*expert_stride of ``w``) times the fp32 vector x[t*x_tok + s*x_slot :][:k].
+    Returns (y, s) of shape (n_tokens, n_used, m), float64; an id outside
+    [0, n_experts) gives NaN rows.
+    """
+    ld_ids = n_used if ld_ids is None else ld_ids
+    w = np.ascontiguousarray(np.asarray(w, dtype=np.uint8).ravel())
+    if k % 32 != 0:
+        raise ValueError("k must be a multiple of 32")
+    if expert_stride < m * (k // 32) * block_bytes(fmt):
+        raise ValueError("expert_stride smaller than one expert matrix")
+    if n_experts > 0 and w.size < (n_experts - 1) * expert_stride + m * (k // 32) * block_bytes(fmt):
+        raise ValueError("weight buffer too small for the expert stack")
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).ravel())
+    if n_tokens > 0 and ids.size < (n_tokens - 1) * ld_ids + n_used:
+        raise ValueError("ids buffer too small")
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32).ravel())
+    if n_tokens > 0 and n_used > 0 and x.size < (n_tokens - 1) * x_tok + (n_used - 1) * x_slot + k:
+        raise ValueError("x buffer too small")
+    y = np.empty(n_tokens * n_used * m, dtype=np.float64)
+    s = np.empty(n_tokens * n_used * m, dtype=np.float64)
+    _load().orc_dot_id(_fmt(fmt), _ptr(w), n_experts, expert_stride, m, k, _ptr(ids), ld_ids,
+                       n_used, n_tokens, _ptr(x), x_slot, x_tok, _ptr(y), _ptr(s))
+    return y.reshape(n_tokens, n_used, m), s.reshape(n_tokens, n_used, m)

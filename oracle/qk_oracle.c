@@ -229,3 +229,45 @@ void orc_dot_entries(int fmt, const uint8_t *w, int64_t k, const void *x, int x_
     for (int64_t e = 0; e < count; ++e)
         orc_dot_one(fmt, w, k, x, x_is_f16, ldx, ii[e], jj[e], &y[e], &s[e]);
 }
+
+/* ---------------------------------------------------------------------
+ * Expert-indexed products (mixture-of-experts decode).
+ *
+ * The tensor-parallel compare names ggml_cuda_mul_mat_id (a hunk of
+ * ggml-cuda.cu) and the PR's commit list a Q4_0 expert model with an
+ * intermediate dimension of 768; what the op computes is not printed on the
+ * pages.  Reading taken (ggml's mul_mat_id): a stack of n_experts matrices of
+ * the same shape, expert e at byte offset e*expert_stride; for token t and
+ * slot s the selected expert is e = ids[t*ld_ids + s] and the output is the
+ * plain product of that expert's matrix with that slot's activation vector,
+ * x + t*x_tok + s*x_slot (x_slot = 0: every slot of a token reads the same
+ * vector).
+ *
+ * Results go to y[(t*n_used + s)*m + i] and the tolerance scale to
+ * s[(t*n_used + s)*m + i].  An id outside [0, n_experts) selects nothing:
+ * its m outputs and scales are NaN.
+ * ------------------------------------------------------------------- */
+void orc_dot_id(int fmt, const uint8_t *w, int64_t n_experts, int64_t expert_stride,
+                int64_t m, int64_t k, const int32_t *ids, int64_t ld_ids, int64_t n_used,
+                int64_t n_tokens, const float *x, int64_t x_slot, int64_t x_tok,
+                double *y, double *s)
+{
+    for (int64_t t = 0; t < n_tokens; ++t) {
+        for (int64_t u = 0; u < n_used; ++u) {
+            const int64_t e = ids[t * ld_ids + u];
+            double *yo = y + (t * n_used + u) * m;
+            double *so = s + (t * n_used + u) * m;
+            if (e < 0 || e >= n_experts) {
+                for (int64_t i = 0; i < m; ++i) {
+                    yo[i] = NAN;
+                    so[i] = NAN;
+                }
+                continue;
+            }
+            const uint8_t *we = w + e * expert_stride;
+            const float *xv = x + t * x_tok + u * x_slot;
+            for (int64_t i = 0; i < m; ++i)
+                orc_dot_one(fmt, we, k, xv, 0, k, i, 0, &yo[i], &so[i]);
+        }
+    }
+}

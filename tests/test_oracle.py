@@ -329,3 +329,92 @@ def test_mistakes_are_caught_by_pins():
     mul_form = dz * (np.float32(zb[2] & 15) - np.float32(8))
     assert np.signbit(mul_form)          # the other order gives -0.0 ...
     assert not np.signbit(oracle.dequantize_f32("q4_0", zb, 1, 32)[0, 0])  # ... the oracle +0.0
+
+
+# ---------------------------------------------------------------------------
+# expert-indexed products
+# ---------------------------------------------------------------------------
+
+def _expert_case():
+    case = _golden()["expert_dots"][0]
+    w = np.concatenate([_hex_bytes(r) for e in case["experts_hex"] for r in e])
+    m, k = case["m"], case["k"]
+    ids = np.array(case["ids"], dtype=np.int32)
+    n_tokens, n_used = ids.shape
+    tau = np.arange(k)
+    base = ((tau % 7) - 3).astype(np.float32)
+    x = np.stack([np.stack([(2 * t + s + 1) * base for s in range(n_used)])
+                  for t in range(n_tokens)]).astype(np.float32)
+    return case, w, m, k, ids, x
+
+
+def test_hand_worked_expert_dot():
+    case, w, m, k, ids, x = _expert_case()
+    n_tokens, n_used = ids.shape
+    stride = m * (k // 32) * 18
+    y, s = oracle.dot_id("q4_0", w, case["n_experts"], stride, m, k, ids, n_used, n_tokens,
+                         x, k, n_used * k)
+    want_y = np.array([[[float(Fraction(v)) for v in r] for r in tt] for tt in case["y"]])
+    want_s = np.array([[[float(Fraction(v)) for v in r] for r in tt] for tt in case["s"]])
+    assert np.array_equal(y, want_y) and np.array_equal(s, want_s)
+
+
+def test_expert_dot_stride_padding_and_id_stride():
+    """Padding between experts and a row stride in ids change nothing."""
+    case, w, m, k, ids, x = _expert_case()
+    n_tokens, n_used = ids.shape
+    stride = m * (k // 32) * 18
+    y0, s0 = oracle.dot_id("q4_0", w, 3, stride, m, k, ids, n_used, n_tokens, x, k, n_used * k)
+    pad = 40
+    wp = np.zeros(3 * (stride + pad), dtype=np.uint8)
+    for e in range(3):
+        wp[e * (stride + pad):e * (stride + pad) + stride] = w[e * stride:(e + 1) * stride]
+    idp = np.full((n_tokens, 5), 77, dtype=np.int32)
+    idp[:, :n_used] = ids
+    y1, s1 = oracle.dot_id("q4_0", wp, 3, stride + pad, m, k, idp, n_used, n_tokens, x, k,
+                           n_used * k, ld_ids=5)
+    assert np.array_equal(y0, y1) and np.array_equal(s0, s1)
+
+
+def test_expert_dot_permutation_and_broadcast():
+    """Relabelling the experts (stack permuted, ids mapped) gives identical
+    results; x_slot = 0 equals every slot holding a copy of the token's x."""
+    fmt, m, k, ne = "q4_1", 5, 96, 6
+    one = m * (k // 32) * 20
+    w = synth.quant_matrix(fmt, ne * m, k, seed=9, tensor_id=1, d_range=(1e-3, 2e-2))
+    ids = np.array([[4, 0, 5], [1, 1, 3]], dtype=np.int32)
+    xt = synth.activations(k, 2, seed=9, tensor_id=2)          # one vector per token
+    y0, s0 = oracle.dot_id(fmt, w, ne, one, m, k, ids, 3, 2, xt, 0, k)
+    perm = np.array([3, 5, 0, 1, 2, 4])                         # new expert p holds old perm[p]
+    wp = np.concatenate([w[perm[p] * one:(perm[p] + 1) * one] for p in range(ne)])
+    inv = np.argsort(perm).astype(np.int32)
+    y1, s1 = oracle.dot_id(fmt, wp, ne, one, m, k, inv[ids], 3, 2, xt, 0, k)
+    assert np.array_equal(y0, y1) and np.array_equal(s0, s1)
+    xc = np.repeat(xt[:, None, :], 3, axis=1)                   # copies per slot
+    y2, s2 = oracle.dot_id(fmt, w, ne, one, m, k, ids, 3, 2, xc, k, 3 * k)
+    assert np.array_equal(y0, y2) and np.array_equal(s0, s2)
+    # each slot is the plain product of its expert with its vector
+    want, _ = oracle.dot(fmt, w[ids[1, 2] * one:], m, k, xt[1], 1)
+    assert np.array_equal(y0[1, 2], want[0])
+
+
+def test_expert_dot_bad_id_gives_nan():
+    case, w, m, k, ids, x = _expert_case()
+    bad = np.array([[1, 3], [-1, 0]], dtype=np.int32)
+    y, s = oracle.dot_id("q4_0", w, 3, m * (k // 32) * 18, m, k, bad, 2, 2, x, k, 2 * k)
+    assert np.isnan(y[0, 1]).all() and np.isnan(y[1, 0]).all()
+    assert np.isnan(s[0, 1]).all() and np.isnan(s[1, 0]).all()
+    assert np.array_equal(y[0, 0], [27.25, 50.625]) and np.array_equal(y[1, 1], [0.0, 0.0])
+
+
+def test_expert_index_mistakes_are_caught():
+    """Planted indexing mistakes (on the CPU, through the oracle's own
+    entry point) fail the hand-worked expert values: ids read with tokens and
+    slots swapped, or every slot reading its token's first vector."""
+    case, w, m, k, ids, x = _expert_case()
+    want = np.array([[[float(Fraction(v)) for v in r] for r in tt] for tt in case["y"]])
+    stride = m * (k // 32) * 18
+    y_t, _ = oracle.dot_id("q4_0", w, 3, stride, m, k, ids.T.copy(), 2, 2, x, k, 2 * k)
+    y_b, _ = oracle.dot_id("q4_0", w, 3, stride, m, k, ids, 2, 2, x, 0, 2 * k)
+    assert not np.array_equal(y_t, want)
+    assert not np.array_equal(y_b, want)
