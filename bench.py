@@ -19,8 +19,8 @@ Measurement
     launch time; peak = 8 TB/s HBM.
   * cpu_baseline: the oracle (plain C, fp64, one thread) on the same matrix.
 
-Options: --workload NAME runs another of the five workloads as the headline;
---configs also measures all five and adds them under "configs".
+Options: --workload NAME runs another single-GEMV workload as the headline;
+--configs also measures every workload and adds them under "configs".
 """
 import argparse
 import hashlib
@@ -40,7 +40,8 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 COLD_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
-GEMV_SOURCES = ["gemv.hip", "qk_common.h", "qk_internal.h"]
+GEMV_SOURCES = ["gemv.hip", "gemv.h", "gemv_impl.h", "gemv_n1.hip", "qk_common.h",
+                "qk_internal.h"]
 
 
 def log(*a):
@@ -243,7 +244,7 @@ def run_headline(torch, qk, synth, oracle, timer, name, steps, warmup, with_cpu)
 
 
 def run_configs(torch, qk, synth, oracle, timer, steps, warmup):
-    """All five workloads, each parity-checked before it is timed."""
+    """Every workload, each parity-checked before it is timed."""
     res = {}
     # C0: dequantize Q4_0 4096x4096 -> fp32
     cfg = synth.WORKLOADS["dequant_q4_0_4096x4096_f32"]
@@ -375,7 +376,74 @@ def run_configs(torch, qk, synth, oracle, timer, steps, warmup):
     res["gemm_q4_0_14336x4096_n512"] = {
         "parity": "ok" if ok else "FAILED", "us_per_launch": round(sec * 1e6, 2),
         "TFLOPs": round(tf, 1), "pct_of_mfma_f16_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 1)}
+    del wc, gw, gk
+
+    log("expert-indexed decode")
+    res["gemv_q4_0_moe_experts"] = run_moe(torch, qk, synth, oracle, timer, steps, warmup)
     return res
+
+
+def run_moe(torch, qk, synth, oracle, timer, steps, warmup):
+    """Expert-indexed decode: per token, the gate, up and down projections of
+    8 of 128 Q4_0 experts (768 x 2048, 768 x 2048, 2048 x 768), three
+    qk_mul_mat_vec_id calls.  Expert choices change every step and the stacks
+    rotate over copies, so the experts a step reads are never cache-resident."""
+    cfg = synth.WORKLOADS["gemv_q4_0_moe_experts"]
+    seed = synth.workload_seed(cfg["id"])
+    ne, nu, nt = cfg["n_experts"], cfg["n_used"], cfg["n_tokens"]
+    lib = qk.load()
+    stacks, ok = [], True
+    for tid, (nm, m, k) in enumerate(cfg["layer"]):
+        w = synth.quant_matrix("q4_0", ne * m, k, seed=seed, tensor_id=tid, d_range=cfg["d"])
+        shared = nm != "down"
+        x = synth.activations(k, nt * (1 if shared else nu), seed=seed, tensor_id=100 + tid)
+        stacks.append(dict(nm=nm, m=m, k=k, w=w, wd=torch.from_numpy(w).cuda(), x=x,
+                           xd=torch.from_numpy(np.ascontiguousarray(x)).cuda(), shared=shared,
+                           y=torch.empty((nt, nu, m), dtype=torch.float32, device="cuda"),
+                           one=m * (k // 32) * 18))
+    n_sets = 64
+    ids = np.stack([synth.expert_ids(nt, nu, ne, seed=seed, tensor_id=50 + i) for i in range(n_sets)])
+    ids_d = torch.from_numpy(ids).cuda()
+    sel_bytes = sum(nt * nu * p["one"] for p in stacks)
+    R = copies_for(sum(p["w"].size for p in stacks))
+    for p in stacks:
+        p["copies"] = [p["wd"]] + [p["wd"].clone() for _ in range(R - 1)]
+
+    def call(p, wptr, idp):
+        x_slot = 0 if p["shared"] else p["k"]
+        x_tok = p["k"] if p["shared"] else nu * p["k"]
+        return lib.qk_mul_mat_vec_id(qk.QK_Q4_0, wptr, ne, p["one"], p["m"],
+                                     p["k"], idp, nu, nu, nt, p["xd"].data_ptr(), x_slot, x_tok,
+                                     p["y"].data_ptr(), p["m"], nu * p["m"],
+                                     torch.cuda.current_stream().cuda_stream)
+
+    def layer(i):
+        idp = ids_d[i % n_sets].data_ptr()
+        for p in stacks:
+            st = call(p, p["copies"][i % R].data_ptr(), idp)
+            if st != 0:
+                raise RuntimeError(f"qk_mul_mat_vec_id: {qk.status_string(st)}")
+
+    layer(0)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for p in stacks:
+        xs = p["x"].reshape(nt, p["k"]) if p["shared"] else p["x"].reshape(nt, nu, p["k"])
+        yr, sr = oracle.dot_id("q4_0", p["w"], ne, p["one"], p["m"], p["k"], ids[0], nu, nt, xs,
+                               0 if p["shared"] else p["k"], p["k"] if p["shared"] else nu * p["k"])
+        got = p["y"].cpu().numpy().astype(np.float64)
+        ok = ok and bool(np.all(np.abs(got - yr) <= 1e-4 * sr))
+        worst = max(worst, float(np.max(np.abs(got - yr) / np.where(sr > 0, sr, 1))))
+    st = max(steps // 3, 20)
+    gw, gk = timer.capture(layer, warmup), timer.capture(lambda i: layer(i + warmup), st)
+    timer.time_graph(gw)
+    sec = timer.time_graph(gk) / st
+    del gw, gk
+    return {"parity": "ok" if ok else "FAILED", "max_err_over_S": worst,
+            "us_per_token": round(sec * 1e6, 3), "launches_per_token": len(stacks),
+            "selected_weight_bytes": sel_bytes,
+            "weight_GBps": round(sel_bytes / sec / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * sel_bytes / sec / 1e9 / HBM_PEAK_GBPS, 1)}
 
 
 def main():
@@ -384,7 +452,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="gemv_q8_0_4096x4096_n1")
-    ap.add_argument("--configs", action="store_true", help="also measure all five workloads")
+    ap.add_argument("--configs", action="store_true", help="also measure every workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (counter calibration)")
@@ -408,7 +476,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
     if args.configs:
-        log("measuring all five workloads")
+        log("measuring every workload")
         out["configs"] = run_configs(torch, qk, synth, oracle, timer, args.steps, args.warmup)
     print(json.dumps(out), flush=True)
 

@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqk.so")
-SOURCES = ["api.hip", "dequant.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.hip", "dequant.hip", "gemv.hip", "gemv_n1.hip", "gemv_n2.hip", "gemv_n34.hip",
+           "gemv_n56.hip", "gemv_n78.hip", "gemv_id.hip", "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

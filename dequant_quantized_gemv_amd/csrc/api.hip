@@ -126,6 +126,59 @@ int qk_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count, int
     return qk::launch_mul_mat_vec_batched(fmt, items, count, n, static_cast<hipStream_t>(stream));
 }
 
+// (n - 1) * ld stays below 2^58, so a sum of a few such spans (and its size
+// in bytes) cannot overflow.
+static bool span_fits(int64_t n, int64_t ld) {
+    return n <= 1 || ld == 0 || (n - 1) <= (int64_t(1) << 58) / ld;
+}
+
+// Outputs [p, p+m) at p = i*inner_ld + o*outer_ld (i < inner_n, o < outer_n)
+// are pairwise disjoint when each inner run fits inside one outer stride.
+static bool nested_disjoint(int64_t m, int64_t inner_n, int64_t inner_ld, int64_t outer_n,
+                            int64_t outer_ld) {
+    const int64_t inner_span = inner_n > 1 ? (inner_n - 1) * inner_ld + m : m;
+    return (inner_n <= 1 || inner_ld >= m) && (outer_n <= 1 || outer_ld >= inner_span);
+}
+
+int qk_mul_mat_vec_id(int fmt, const void *w, int64_t n_experts, int64_t expert_stride,
+                      int64_t m, int64_t k, const int32_t *ids, int64_t ld_ids,
+                      int64_t n_used, int64_t n_tokens, const float *x, int64_t x_slot,
+                      int64_t x_tok, float *y, int64_t y_slot, int64_t y_tok, void *stream) {
+    if (!fmt_ok(fmt)) return QK_ERR_UNSUPPORTED;
+    if (m < 0 || k < 0 || k % 32 != 0 || n_used < 0 || n_tokens < 0) return QK_ERR_INVALID_ARG;
+    if (m == 0 || n_used == 0 || n_tokens == 0) return QK_OK;
+    if (m > kMaxDim || k > kMaxDim || n_experts < 1 || n_experts > kMaxDim ||
+        n_used > kMaxDim || n_tokens > kMaxDim)
+        return QK_ERR_INVALID_ARG;
+    const int64_t es = n_experts > 1 ? expert_stride : 0;
+    const int64_t li = n_tokens > 1 ? ld_ids : 0;
+    const int64_t xs = n_used > 1 ? x_slot : 0, xt = n_tokens > 1 ? x_tok : 0;
+    const int64_t ys = n_used > 1 ? y_slot : 0, yt = n_tokens > 1 ? y_tok : 0;
+    if (es < 0 || li < 0 || xs < 0 || xt < 0 || ys < 0 || yt < 0) return QK_ERR_INVALID_ARG;
+    if (!span_fits(n_experts, es) || !span_fits(n_tokens, li) || !span_fits(n_tokens, xt) ||
+        !span_fits(n_used, xs) || !span_fits(n_tokens, yt) || !span_fits(n_used, ys))
+        return QK_ERR_INVALID_ARG;
+    const size_t ebytes = (size_t)m * (size_t)(k / 32) * qk::block_bytes_host(fmt);
+    if (n_experts > 1 && (size_t)es < ebytes) return QK_ERR_INVALID_ARG;
+    if (n_tokens > 1 && li < n_used) return QK_ERR_INVALID_ARG;
+    if (n_used * n_tokens > (int64_t)INT32_MAX / ((m + 7) / 8)) return QK_ERR_INVALID_ARG;
+    if (!nested_disjoint(m, n_used, ys, n_tokens, yt) && !nested_disjoint(m, n_tokens, yt, n_used, ys))
+        return QK_ERR_INVALID_ARG;
+    if (w == nullptr || ids == nullptr || x == nullptr || y == nullptr) return QK_ERR_INVALID_ARG;
+    if ((uintptr_t)w % 2 != 0 || es % 2 != 0 || (uintptr_t)ids % 4 != 0 || (uintptr_t)x % 4 != 0 ||
+        (uintptr_t)y % 4 != 0)
+        return QK_ERR_ALIGNMENT;
+    const size_t wbytes = (size_t)(n_experts - 1) * (size_t)es + ebytes;
+    const size_t ibytes = (size_t)((n_tokens - 1) * li + n_used) * 4;
+    const size_t xbytes = (size_t)((n_tokens - 1) * xt + (n_used - 1) * xs + k) * 4;
+    const size_t ybytes = (size_t)((n_tokens - 1) * yt + (n_used - 1) * ys + m) * 4;
+    if (overlaps(y, ybytes, w, wbytes) || overlaps(y, ybytes, ids, ibytes) ||
+        overlaps(y, ybytes, x, xbytes))
+        return QK_ERR_INVALID_ARG;
+    return qk::launch_mul_mat_vec_id(fmt, w, n_experts, es, m, k, ids, li, n_used, n_tokens, x,
+                                     xs, xt, y, ys, yt, static_cast<hipStream_t>(stream));
+}
+
 int qk_mul_mat(int fmt, const void *w, int64_t m, int64_t k, const void *x_f16, int64_t n,
                int64_t ldx, float *y, int64_t ldy, void *stream) {
     if (!fmt_ok(fmt)) return QK_ERR_UNSUPPORTED;

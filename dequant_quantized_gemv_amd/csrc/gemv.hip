@@ -1,708 +1,50 @@
-// gemv.hip - fused quantized GEMV for decode: y = W x for 1..8 fp32 columns.
-//
-// What is computed follows dequantize_mul_mat_vec ("dmmv", named with its
-// tuning block in the "llama_cpp 0.12.1 -> 0.12.2" ggml-cuda.cu diff) and the
-// ggml_cuda_op_mul_mat driver (a row range times a column count): each output
-// is the dot product of one dequantized weight row with one activation column,
-// reduced across lanes (the diff's warp_reduce_sum).  That kernel's body is not
-// on the page; this one is designed for gfx950.
-//
-// Work split.  A workgroup of WPG waves owns WPG*RWV consecutive rows, RWV
-// per wave.  K is walked in chunks of 128 blocks (4096 weights).  Within a
-// chunk, lane p of every wave owns "pair" p: two consecutive blocks, 64
-// weights.  A pair of Q4_0 / Q4_1 / Q8_0 blocks is 36 / 40 / 68 bytes, a whole
-// number of dwords, so with an even block count per row every pair starts on
-// 4 bytes and comes straight into registers with dword-aligned 16-byte loads
-// (plain loads: streaming hints measured slower on this chip).
-//
-// Activations are the expensive side: every row needs all of x.  The chunk of
-// x (4096 x NC floats) is copied once per workgroup into LDS and read from
-// there by all of its rows; its global loads are issued before the weight
-// loads so the copy never waits behind HBM.  In LDS each run of 64 floats is
-// followed by 4 floats of padding, so the 16-byte reads of lanes p = 0..15 (at
-// float offset 68p + 4t) fall in distinct banks.  A workgroup takes a range
-// of consecutive row groups (of one or several items of a grouped launch) and
-// restages x only when a step enters a new item or chunk.
-//
-// Arithmetic, exact per term (every term is the exact weight times x):
-//  * Q4_0: the nibble becomes the exact fp16 number q - 8 by placing it in
-//    the mantissa of an fp16 with a byte permute (0x64XX is 1024 + XX) and
-//    removing the bias with one packed fp16 add; v_fma_mix_f32 multiplies that
-//    fp16 by the fp32 activation into an fp32 accumulator with one rounding.
-//    The block's sum is scaled by d once (d * (q - 8) is the exact weight).
-//  * Q8_0: the signed byte converts to fp32 exactly with a byte-select
-//    convert and is multiplied by x in one FMA; the block's sum is scaled by d.
-//  * Q4_1: the exact fp32 weight d*q + m is rebuilt per element (one FMA,
-//    exact because d*q is exact) and multiplied into the accumulator.
-// Reduction: a 64-lane DPP butterfly per (row, column); lane 0 writes y.
+// gemv.hip - host side of the fused quantized GEMV: builds the launch
+// descriptors (gemv.h) from validated C-ABI arguments and picks the instance
+// by column count.  The kernels are in gemv_impl.h.
+#include "gemv.h"
 #include "qk_common.h"
 #include "qk_internal.h"
 
-#include <type_traits>
+#include <algorithm>
 
 namespace qk {
 
-constexpr int kGvChunkPairs = 64;                   // pairs per chunk (one per lane)
-constexpr int kGvChunkElems = kGvChunkPairs * 64;   // 4096 weights per chunk
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-template <int FMT> struct Pair;
-template <> struct Pair<QK_Q4_0> { static constexpr int kDwords = 9; };
-template <> struct Pair<QK_Q4_1> { static constexpr int kDwords = 10; };
-template <> struct Pair<QK_Q8_0> { static constexpr int kDwords = 17; };
-
-// acc + (fp16 in the low / high half of h) * x, fused, one rounding.
-__device__ __forceinline__ float fma_mix_lo(uint32_t h, float x, float acc) {
-    float r;
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x), "v"(acc));
-    return r;
-}
-__device__ __forceinline__ float fma_mix_hi(uint32_t h, float x, float acc) {
-    float r;
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-        : "=v"(r) : "v"(h), "v"(x), "v"(acc));
-    return r;
-}
-
-// Bytes 0,1 (lo) or 2,3 (hi) of src become the low mantissa bytes of two fp16
-// numbers with high byte 0x64: value 1024 + byte.
-__device__ __forceinline__ uint32_t bytes_to_f16_lo(uint32_t src) {
-    return __builtin_amdgcn_perm(0x64646464u, src, 0x04010400u);  // [b0, 64, b1, 64]
-}
-__device__ __forceinline__ uint32_t bytes_to_f16_hi(uint32_t src) {
-    return __builtin_amdgcn_perm(0x64646464u, src, 0x04030402u);  // [b2, 64, b3, 64]
-}
-
-__device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, float b) {
-    const half2_t r = __builtin_bit_cast(half2_t, a) + half2_t{(_Float16)b, (_Float16)b};
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ uint32_t pk_fma_f16(uint32_t a, float s, float t) {
-    const half2_t r = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, a),
-                                                half2_t{(_Float16)s, (_Float16)s},
-                                                half2_t{(_Float16)t, (_Float16)t});
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-// 32-bit word starting 2 bytes into (lo, hi).
-__device__ __forceinline__ uint32_t shift2(uint32_t lo, uint32_t hi) {
-    return __builtin_amdgcn_alignbyte(hi, lo, 2);
-}
-
-// ---------------------------------------------------------------------------
-// One pair (two consecutive blocks) of a row in registers.
-// ---------------------------------------------------------------------------
-
-// FAST: the pair starts on a 4-byte boundary and both blocks exist.
-template <int FMT>
-__device__ __forceinline__ void load_pair_fast(const uint8_t *__restrict__ p,
-                                               uint32_t (&v)[Pair<FMT>::kDwords]) {
-    constexpr int N = Pair<FMT>::kDwords;
-#pragma unroll
-    for (int i = 0; i + 4 <= N; i += 4) {
-        const u32x4_a4 t = *reinterpret_cast<const u32x4_a4 *>(p + 4 * i);
-        v[i] = t.x; v[i + 1] = t.y; v[i + 2] = t.z; v[i + 3] = t.w;
-    }
-#pragma unroll
-    for (int i = N & ~3; i < N; ++i)
-        v[i] = *reinterpret_cast<const uint32_t *>(p + 4 * i);
-}
-
-// Generic: 2-byte aligned; if only the first block exists (odd block count,
-// last pair) the second block reads as d = m = 0 and codes 0, i.e. weights 0.
-template <int FMT>
-__device__ __forceinline__ void load_pair_generic(const uint8_t *__restrict__ p, bool second,
-                                                  uint32_t (&v)[Pair<FMT>::kDwords]) {
-    constexpr int N = Pair<FMT>::kDwords;
-    constexpr int BS = Format<FMT>::kBytes;
-    const uint16_t *h = reinterpret_cast<const uint16_t *>(p);
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const uint32_t a = (4 * i < BS || second) ? (uint32_t)h[2 * i] : 0u;
-        const uint32_t b = (4 * i + 2 < BS || second) ? (uint32_t)h[2 * i + 1] : 0u;
-        v[i] = a | (b << 16);
-    }
-}
-
-// fp16 bits of d (and m) of block b of the pair.
-template <int FMT>
-__device__ __forceinline__ uint32_t pair_d(const uint32_t (&v)[Pair<FMT>::kDwords], int b) {
-    if constexpr (FMT == QK_Q4_0) return b == 0 ? (v[0] & 0xFFFFu) : (v[4] >> 16);
-    if constexpr (FMT == QK_Q4_1) return b == 0 ? (v[0] & 0xFFFFu) : (v[5] & 0xFFFFu);
-    return b == 0 ? (v[0] & 0xFFFFu) : (v[8] >> 16);
-}
-__device__ __forceinline__ uint32_t pair_m_q41(const uint32_t (&v)[10], int b) {
-    return b == 0 ? (v[0] >> 16) : (v[5] >> 16);
-}
-
-// Quant word i of block b (Q4: i < 4, bytes 4i..4i+3; Q8: i < 8).
-template <int FMT>
-__device__ __forceinline__ uint32_t pair_qs(const uint32_t (&v)[Pair<FMT>::kDwords], int b, int i) {
-    if constexpr (FMT == QK_Q4_0) return b == 0 ? shift2(v[i], v[i + 1]) : v[5 + i];
-    if constexpr (FMT == QK_Q4_1) return b == 0 ? v[1 + i] : v[6 + i];
-    return b == 0 ? shift2(v[i], v[i + 1]) : v[9 + i];
-}
-
-// ---------------------------------------------------------------------------
-// Per-group products.  A group is quant word i of block b: Q4 elements
-// 4i..4i+3 (low nibbles) and 16+4i..16+4i+3 (high nibbles); Q8 elements
-// 4i..4i+3 (i < 8).  xa / xb are the matching activations.
-// ---------------------------------------------------------------------------
-
-// Q4_0 group: sum over the 8 elements of (q - 8) * x, added to s.
-__device__ __forceinline__ float group_q4_0(uint32_t qw, const float4 &xa, const float4 &xb, float s) {
-    // low nibbles: 1024 + c - 1032 = c - 8; high nibbles left in place:
-    // (1024 + 16c) / 16 - 72 = c - 8 (one fused, exact operation)
-    const uint32_t lo = qw & 0x0F0F0F0Fu;
-    const uint32_t hi = qw & 0xF0F0F0F0u;
-    const uint32_t l01 = pk_add_f16(bytes_to_f16_lo(lo), -1032.0f);
-    const uint32_t l23 = pk_add_f16(bytes_to_f16_hi(lo), -1032.0f);
-    const uint32_t h01 = pk_fma_f16(bytes_to_f16_lo(hi), 0.0625f, -72.0f);
-    const uint32_t h23 = pk_fma_f16(bytes_to_f16_hi(hi), 0.0625f, -72.0f);
-    s = fma_mix_lo(l01, xa.x, s);
-    s = fma_mix_hi(l01, xa.y, s);
-    s = fma_mix_lo(l23, xa.z, s);
-    s = fma_mix_hi(l23, xa.w, s);
-    s = fma_mix_lo(h01, xb.x, s);
-    s = fma_mix_hi(h01, xb.y, s);
-    s = fma_mix_lo(h23, xb.z, s);
-    s = fma_mix_hi(h23, xb.w, s);
-    return s;
-}
-
-// Q8_0 group: sum over 4 elements of q * x, added to s.  A signed byte
-// converts to fp32 exactly in one instruction (byte-select SDWA), and the
-// product q * x is rounded once inside the FMA.
-__device__ __forceinline__ float group_q8_0(uint32_t qw, const float4 &xa, float s) {
-    s = __builtin_fmaf((float)(int8_t)(qw), xa.x, s);
-    s = __builtin_fmaf((float)(int8_t)(qw >> 8), xa.y, s);
-    s = __builtin_fmaf((float)(int8_t)(qw >> 16), xa.z, s);
-    s = __builtin_fmaf((float)(int8_t)(qw >> 24), xa.w, s);
-    return s;
-}
-
-// Q8_0 group of block 0 of a pair: its quant word straddles two dwords
-// (bytes 2, 3 of lo and 0, 1 of hi), which byte selects read directly.
-__device__ __forceinline__ float group_q8_0_split(uint32_t lo, uint32_t hi, const float4 &xa, float s) {
-    s = __builtin_fmaf((float)(int8_t)(lo >> 16), xa.x, s);
-    s = __builtin_fmaf((float)(int8_t)(lo >> 24), xa.y, s);
-    s = __builtin_fmaf((float)(int8_t)(hi), xa.z, s);
-    s = __builtin_fmaf((float)(int8_t)(hi >> 8), xa.w, s);
-    return s;
-}
-
-// Q4_1 group: exact weights d*q + m times x, added to acc.
-__device__ __forceinline__ float group_q4_1(uint32_t qw, float d, float mm, const float4 &xa,
-                                            const float4 &xb, float a) {
-    const uint32_t lo = qw & 0x0F0F0F0Fu;
-    const uint32_t hi = (qw >> 4) & 0x0F0F0F0Fu;
-    a = __builtin_fmaf(wval(d, ubyte_f<0>(lo), mm), xa.x, a);
-    a = __builtin_fmaf(wval(d, ubyte_f<1>(lo), mm), xa.y, a);
-    a = __builtin_fmaf(wval(d, ubyte_f<2>(lo), mm), xa.z, a);
-    a = __builtin_fmaf(wval(d, ubyte_f<3>(lo), mm), xa.w, a);
-    a = __builtin_fmaf(wval(d, ubyte_f<0>(hi), mm), xb.x, a);
-    a = __builtin_fmaf(wval(d, ubyte_f<1>(hi), mm), xb.y, a);
-    a = __builtin_fmaf(wval(d, ubyte_f<2>(hi), mm), xb.z, a);
-    a = __builtin_fmaf(wval(d, ubyte_f<3>(hi), mm), xb.w, a);
-    return a;
-}
-
-// float4 of x (column j) at window-relative element e (e % 4 == 0) from LDS;
-// column pitch xp floats.
-__device__ __forceinline__ float4 x_lds(const float *xs, int xp, int j, int e) {
-    return *reinterpret_cast<const float4 *>(xs + j * xp + e + (e >> 6) * 4);
-}
-
-// One problem of a (possibly grouped) launch: y = W x for NC columns.
-struct GemvItem {
-    const uint8_t *w;
-    const float *x;
-    float *y;
-    int64_t ldx;
-    int64_t ldy;
-    int m;
-    int nb;  // blocks per row
-};
-
-constexpr int kGvMaxItems = 16;
-
-// Launch arguments (passed by value in the kernel argument segment).
-// Row groups of all items are numbered consecutively: item i owns groups
-// gbase[i] .. gbase[i+1]-1.
-struct GemvArgs {
-    GemvItem item[kGvMaxItems];
-    int gbase[kGvMaxItems + 1];
-    int count;
-};
-
-// Split of the launch's `total` row groups over the grid: workgroup b takes
-// per groups, plus one more if b < rem (computed on the host; no division on
-// the device).
-struct GemvSplit {
-    int total;
-    int per;
-    int rem;
-};
-
-// Dot products of one wave's RWV rows with this lane's pair, added to acc.
-template <int FMT, int NC, int RWV, bool FAST>
-__device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDwords], int nrows,
-                                         bool second, const float *xs, int xp, int el,
-                                         float (&acc)[RWV][NC]) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        if (!FAST && b == 1 && !second) break;
-        if constexpr (FMT == QK_Q4_1) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float4 xa[NC], xb[NC];
-#pragma unroll
-                for (int j = 0; j < NC; ++j) {
-                    xa[j] = x_lds(xs, xp, j, el + 32 * b + 4 * i);
-                    xb[j] = x_lds(xs, xp, j, el + 32 * b + 16 + 4 * i);
-                }
-#pragma unroll
-                for (int r = 0; r < RWV; ++r) {
-                    if (FAST || r < nrows) {  // fast path: rows clamped, stores guarded
-                        const float d = h2f(pair_d<FMT>(v[r], b));
-                        const float mm = h2f(pair_m_q41(v[r], b));
-                        const uint32_t qw = pair_qs<FMT>(v[r], b, i);
-                        const uint32_t lo = qw & 0x0F0F0F0Fu;
-                        const uint32_t hi = (qw >> 4) & 0x0F0F0F0Fu;
-                        const float w0 = wval(d, ubyte_f<0>(lo), mm), w1 = wval(d, ubyte_f<1>(lo), mm);
-                        const float w2 = wval(d, ubyte_f<2>(lo), mm), w3 = wval(d, ubyte_f<3>(lo), mm);
-                        const float w4 = wval(d, ubyte_f<0>(hi), mm), w5 = wval(d, ubyte_f<1>(hi), mm);
-                        const float w6 = wval(d, ubyte_f<2>(hi), mm), w7 = wval(d, ubyte_f<3>(hi), mm);
-#pragma unroll
-                        for (int j = 0; j < NC; ++j) {
-                            float a = acc[r][j];
-                            a = __builtin_fmaf(w0, xa[j].x, a);
-                            a = __builtin_fmaf(w1, xa[j].y, a);
-                            a = __builtin_fmaf(w2, xa[j].z, a);
-                            a = __builtin_fmaf(w3, xa[j].w, a);
-                            a = __builtin_fmaf(w4, xb[j].x, a);
-                            a = __builtin_fmaf(w5, xb[j].y, a);
-                            a = __builtin_fmaf(w6, xb[j].z, a);
-                            a = __builtin_fmaf(w7, xb[j].w, a);
-                            acc[r][j] = a;
-                        }
-                    }
-                }
-                // keep the next group's LDS reads from being hoisted above
-                // this one (bounds the live activations)
-                if constexpr (NC >= 2) asm volatile("" ::: "memory");
-            }
-        } else {
-            float s[RWV][NC];
-#pragma unroll
-            for (int r = 0; r < RWV; ++r)
-#pragma unroll
-                for (int j = 0; j < NC; ++j) s[r][j] = 0.0f;
-            constexpr int NGRP = (FMT == QK_Q8_0) ? 8 : 4;
-#pragma unroll
-            for (int i = 0; i < NGRP; ++i) {
-                float4 xa[NC], xb[NC];
-#pragma unroll
-                for (int j = 0; j < NC; ++j) {
-                    xa[j] = x_lds(xs, xp, j, el + 32 * b + 4 * i);
-                    if (FMT == QK_Q4_0) xb[j] = x_lds(xs, xp, j, el + 32 * b + 16 + 4 * i);
-                }
-#pragma unroll
-                for (int r = 0; r < RWV; ++r) {
-                    if (FAST || r < nrows) {  // fast path: rows clamped, stores guarded
-#pragma unroll
-                        for (int j = 0; j < NC; ++j) {
-                            if constexpr (FMT == QK_Q4_0) {
-                                s[r][j] = group_q4_0(pair_qs<FMT>(v[r], b, i), xa[j], xb[j], s[r][j]);
-                            } else if (b == 0) {
-                                s[r][j] = group_q8_0_split(v[r][i], v[r][i + 1], xa[j], s[r][j]);
-                            } else {
-                                s[r][j] = group_q8_0(v[r][9 + i], xa[j], s[r][j]);
-                            }
-                        }
-                    }
-                }
-                if constexpr (NC >= 3) asm volatile("" ::: "memory");
-            }
-#pragma unroll
-            for (int r = 0; r < RWV; ++r) {
-                if (FAST || r < nrows) {
-                    const float d = h2f(pair_d<FMT>(v[r], b));
-#pragma unroll
-                    for (int j = 0; j < NC; ++j) acc[r][j] = __builtin_fmaf(d, s[r][j], acc[r][j]);
-                }
-            }
+// Outputs of problems with no weights per row (k == 0): the empty sum, 0, or
+// NaN where an expert id falls outside the stack.  `e` describes `count`
+// columns (slots) of m outputs each; ids == nullptr marks every column valid.
+__global__ __launch_bounds__(256) void gemv_empty_kernel(const GemvExpert e, const int64_t total) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += stride) {
+        const int64_t p = idx / e.m;
+        const int i = (int)(idx - p * e.m);
+        const int t = (int)(p / e.n_used);
+        const int s = (int)(p - (int64_t)t * e.n_used);
+        bool bad = false;
+        if (e.ids != nullptr) {
+            const int id = e.ids[(int64_t)t * e.ld_ids + s];
+            bad = (unsigned)id >= (unsigned)e.nexp;
         }
+        e.y[t * e.y_tok + s * e.y_slot + i] = bad ? __builtin_nanf("") : 0.0f;
     }
 }
 
-// FAST: for every item, w 4-byte aligned, an even number of blocks per row,
-// x 16-byte aligned and ldx % 4 == 0.
-//
-// The launch's row groups (WPG*RWV rows each, all items numbered in a row) are
-// split into gridDim.x contiguous ranges, one per workgroup.  A workgroup walks
-// its range as a sequence of steps (row group, K chunk); each step's weights
-// were requested during the previous step, and x is re-staged only when the
-// item or the chunk changes.
-// The activation window staged in LDS: `xw` weights (a multiple of 4096) per
-// column, each run of 64 floats followed by 4 floats of padding.
-__host__ __device__ constexpr int xw_pitch(int xw) { return xw + xw / 16; }
-
-// FAST: for every item, w 4-byte aligned, an even number of blocks per row,
-// x 16-byte aligned and ldx % 4 == 0.
-//
-// The launch's row groups (WPG*RWV rows each, all items numbered in a row)
-// are split into gridDim.x contiguous ranges, one per workgroup.  A workgroup
-// walks its range as a sequence of steps (row group, chunk of 4096 weights);
-// in a step lane p takes pair p of the chunk.  Each step's weights were
-// requested during the previous step (two register sets used in turn).  The
-// activations are staged into LDS in windows of `xw` weights (the whole row
-// when K <= xw), only when the item or the window changes.
-// SINGLE: one item, passed in its own argument (fixed offsets, no indexed
-// reads of the item table before the first weight load).
-template <int FMT, int NC, int RWV, int WPG, bool FAST, bool SINGLE>
-__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 1 || (NC == 2 && FMT != QK_Q8_0) ? 4 : (NC == 2 ? 2 : 1)))) void gemv_kernel(const GemvArgs args, const GemvItem one,
-                                                        const GemvSplit split, const int xw) {
-    constexpr int BS = Format<FMT>::kBytes;
-    constexpr int ND = Pair<FMT>::kDwords;
-    constexpr int RG = WPG * RWV;               // rows per group
-    constexpr int NT = 64 * WPG;                // lanes per workgroup
-    constexpr int CP = kGvChunkPairs;           // pairs per step
-    constexpr int CE = kGvChunkElems;           // weights per step
-    extern __shared__ __attribute__((aligned(16))) float xs[];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int b = blockIdx.x;
-    const int gbeg = b * split.per + min(b, split.rem);
-    const int gend = gbeg + split.per + (b < split.rem ? 1 : 0);
-    if (gbeg >= gend) return;  // whole workgroup, before any barrier
-    const int xp = xw_pitch(xw);
-    const int cpw = xw / CE;  // steps per activation window
-
-    auto gbase = [&](int i) { return SINGLE ? (i == 0 ? 0 : split.total) : args.gbase[i]; };
-    auto item = [&](int i) -> const GemvItem & { return SINGLE ? one : args.item[i]; };
-
-    // Step position (uniform across the workgroup): row group g of item mi,
-    // chunk c, with the item's descriptor held in registers.  It is read from
-    // the argument table only when a step enters a new item.
-    struct Pos {
-        int g, mi, c;
-        int gb0, gb1;   // the item's first row group and one past its last
-        int nchunks;    // steps per row group
-        GemvItem it;
-    };
-    // (field by field: a whole-struct copy out of the argument table is
-    // lowered through scratch memory)
-    auto enter = [&](Pos &q, int i) __attribute__((always_inline)) {
-        q.mi = i;
-        const GemvItem &src = item(i);
-        q.it.w = src.w;
-        q.it.x = src.x;
-        q.it.y = src.y;
-        q.it.ldx = src.ldx;
-        q.it.ldy = src.ldy;
-        q.it.m = src.m;
-        q.it.nb = src.nb;
-        q.gb0 = gbase(i);
-        q.gb1 = gbase(i + 1);
-        q.nchunks = (((q.it.nb + 1) >> 1) + CP - 1) / CP;
-    };
-    Pos P;
-    P.g = gbeg;
-    P.c = 0;
-    {
-        int i = 0;
-        while (gbeg >= gbase(i + 1)) ++i;
-        enter(P, i);
-    }
-    // The step after q within this workgroup's range (items have at least one
-    // row group each, so a step enters at most one new item).
-    auto advance = [&](const Pos &q) __attribute__((always_inline)) {
-        Pos r = q;
-        if (++r.c >= r.nchunks) {
-            r.c = 0;
-            if (++r.g >= r.gb1 && r.g < gend) enter(r, r.mi + 1);
-        }
-        return r;
-    };
-    int staged_mi = -1, staged_w = -1;
-
-    float acc[RWV][NC];
-#pragma unroll
-    for (int r = 0; r < RWV; ++r)
-#pragma unroll
-        for (int j = 0; j < NC; ++j) acc[r][j] = 0.0f;
-
-    // Weight loads of step (sg, smi, sc) into dst.  On the fast path every lane
-    // issues the same loads with no branch around them (a lane past the last
-    // pair or row reads a clamped, valid address and ignores the data), so the
-    // compiler counts them and waits for exactly the loads a computation needs
-    // while the prefetch stays in flight.
-    auto load_step = [&](const Pos &q, uint32_t (&dst)[RWV][ND]) __attribute__((always_inline)) {
-        const GemvItem &it = q.it;
-        const int row0 = (q.g - q.gb0) * RG + wave * RWV;
-        const int npairs = (it.nb + 1) >> 1;
-        const int64_t row_bytes = (int64_t)it.nb * BS;
-        const int pp = q.c * CP + lane;
-        if (FAST) {
-            const int ppc = min(pp, npairs - 1);
-#pragma unroll
-            for (int r = 0; r < RWV; ++r) {
-                const int row = min(row0 + r, it.m - 1);
-                load_pair_fast<FMT>(it.w + (int64_t)row * row_bytes + (int64_t)ppc * (2 * BS), dst[r]);
-            }
-        } else if (pp < npairs) {
-            const int nrows = max(0, min(RWV, it.m - row0));
-            const uint8_t *p = it.w + (int64_t)row0 * row_bytes + (int64_t)pp * (2 * BS);
-            const bool second = 2 * pp + 1 < it.nb;
-#pragma unroll
-            for (int r = 0; r < RWV; ++r)
-                if (r < nrows) load_pair_generic<FMT>(p + r * row_bytes, second, dst[r]);
-        }
-    };
-
-    constexpr int XR = NC <= 2 ? NC : 0;  // columns staged through registers (first window)
-
-    // Copy window `wi` of item `it`'s activations into LDS (whole workgroup).
-    auto stage_x = [&](const GemvItem &it, int wi) __attribute__((always_inline)) {
-        const int e0 = wi * xw;
-        const int ce4 = min(xw, it.nb * 32 - e0) / 4;  // float4s in this window
-#pragma unroll
-        for (int j = 0; j < NC; ++j) {
-            const float *xj = it.x + j * it.ldx + e0;
-            for (int t = tid; t < ce4; t += NT) {
-                f32x4_t val;
-                if (FAST) val = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
-                else val = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
-                *reinterpret_cast<f32x4_t *>(xs + j * xp + 4 * t + (t >> 4) * 4) = val;
-            }
-        }
-    };
-
-    // Steps in this workgroup's range.
-    int nsteps = 0;
-    {
-        int gg = gbeg, ii = P.mi;
-        while (gg < gend) {
-            while (gg >= gbase(ii + 1)) ++ii;
-            const int nxt = min(gend, gbase(ii + 1));
-            nsteps += (nxt - gg) * ((((item(ii).nb + 1) >> 1) + CP - 1) / CP);
-            gg = nxt;
-        }
-    }
-
-    // One step computing with cur.  PREFETCH: the next step's weights are
-    // requested into nxt before this step's computation.  Each (FIRST,
-    // PREFETCH) combination is its own straight-line code, so the compiler
-    // waits for exactly the loads the computation needs and the prefetch stays
-    // in flight.  FIRST issues the activation loads before any weight load, so
-    // copying them to LDS does not wait for the weights (loads complete in
-    // order).
-    // DEPTH: 0 no prefetch, 1 the next step's weights requested into nxt.
-    auto step = [&](auto first_tag, auto depth_tag, uint32_t (&cur)[RWV][ND],
-                    uint32_t (&nxt)[RWV][ND]) __attribute__((always_inline)) {
-        constexpr bool FIRST = decltype(first_tag)::value;
-        constexpr int DEPTH = decltype(depth_tag)::value;
-        constexpr bool PREFETCH = DEPTH > 0;
-        const GemvItem &it = P.it;
-        const int npairs = (it.nb + 1) >> 1;
-        const int wi = P.c / cpw;  // activation window of this step
-
-        const Pos Q = advance(P);
-        // past the workgroup's last step a prefetch repeats this step's loads
-        const Pos PF = Q.g < gend ? Q : P;
-
-        if constexpr (FIRST) {
-            // activation loads, then this step's and the next step's weights,
-            // then the LDS copy (waits only for the activations)
-            constexpr int XU = (CE / 4 + NT - 1) / NT;  // registers cover the first 4096
-            const int e0 = wi * xw;
-            const int ce4 = min(xw, it.nb * 32 - e0) / 4;
-            const int cr4 = min(CE / 4, ce4);
-            f32x4_t xr[XR > 0 ? XR : 1][XU];
-#pragma unroll
-            for (int j = 0; j < XR; ++j) {
-                const float *xj = it.x + j * it.ldx + e0;
-#pragma unroll
-                for (int u = 0; u < XU; ++u) {
-                    // clamped so every lane loads (a tail lane repeats the last
-                    // float4 and stores it again)
-                    const int t = min(tid + u * NT, cr4 - 1);
-                    if (FAST) xr[j][u] = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
-                    else xr[j][u] = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
-                }
-            }
-            load_step(P, cur);
-            if constexpr (PREFETCH) load_step(PF, nxt);
-            // unconditional stores (a tail lane rewrites the last float4 with
-            // the same value), so no load is moved behind the weight loads
-#pragma unroll
-            for (int j = 0; j < XR; ++j)
-#pragma unroll
-                for (int u = 0; u < XU; ++u) {
-                    const int t = min(tid + u * NT, cr4 - 1);
-                    *reinterpret_cast<f32x4_t *>(xs + j * xp + 4 * t + (t >> 4) * 4) = xr[j][u];
-                }
-            // the rest of the window (and wider activation sets) directly
-#pragma unroll
-            for (int j = 0; j < NC; ++j) {
-                const float *xj = it.x + j * it.ldx + e0;
-                for (int t = (j < XR ? cr4 : 0) + tid; t < ce4; t += NT) {
-                    f32x4_t val;
-                    if (FAST) val = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
-                    else val = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
-                    *reinterpret_cast<f32x4_t *>(xs + j * xp + 4 * t + (t >> 4) * 4) = val;
-                }
-            }
-            __syncthreads();
-            staged_mi = P.mi;
-            staged_w = wi;
-        } else {
-            // a new item or window: restage the activations before the prefetch
-            if (staged_mi != P.mi || staged_w != wi) {
-                __syncthreads();  // readers of the previous window are done
-                stage_x(it, wi);
-                __syncthreads();
-                staged_mi = P.mi;
-                staged_w = wi;
-            }
-            if constexpr (PREFETCH) load_step(PF, nxt);
-        }
-
-        // compute this step
-        const int row0 = (P.g - P.gb0) * RG + wave * RWV;
-        const int nrows = max(0, min(RWV, it.m - row0));
-        const int pp = P.c * CP + lane;
-        if (nrows > 0 && pp < npairs)
-            pair_dot<FMT, NC, RWV, FAST>(cur, nrows, FAST || (2 * pp + 1 < it.nb), xs, xp,
-                                         (P.c - wi * cpw) * CE + lane * 64, acc);
-
-        // last chunk of the group: reduce across the wave and store
-        if (P.c == P.nchunks - 1) {
-#pragma unroll
-            for (int r = 0; r < RWV; ++r) {
-                if (r < nrows) {
-#pragma unroll
-                    for (int j = 0; j < NC; ++j) {
-                        const float sum = wave_sum(acc[r][j]);
-                        if (lane == 0) it.y[j * it.ldy + row0 + r] = sum;
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < NC; ++j) acc[r][j] = 0.0f;
-            }
-        }
-        P = Q;
-    };
-
-    using T = std::true_type;
-    using F = std::false_type;
-    using D0 = std::integral_constant<int, 0>;
-    using D1 = std::integral_constant<int, 1>;
-    uint32_t va[RWV][ND], vb[RWV][ND];
-    if (nsteps == 1) {
-        step(T{}, D0{}, va, vb);
-        return;
-    }
-    step(T{}, D1{}, va, vb);
-    // Two steps per iteration with the register sets in swapped roles and no
-    // branch between them, so the two bodies stay distinct: a merged body
-    // would copy the prefetched registers into place, and that copy waits for
-    // every outstanding load (the new prefetch included).  The final step's
-    // prefetch repeats its own loads (clamped).
-    int left = nsteps - 1;  // steps still to compute; the next one's weights are in vb
-    for (; left >= 2; left -= 2) {
-        step(F{}, D1{}, vb, va);
-        step(F{}, D1{}, va, vb);
-    }
-    if (left == 1) step(F{}, D0{}, vb, va);
+static int launch_empty(const GemvExpert &e, hipStream_t stream) {
+    const int64_t total = (int64_t)e.count * e.m;
+    if (total <= 0) return QK_OK;
+    const int64_t nwg = std::min<int64_t>((total + 255) / 256, 4096);
+    return launch(gemv_empty_kernel, dim3((unsigned)nwg), dim3(256), stream, e, total);
 }
 
-// Launch shape by column count: RWV rows per wave, WPG waves per workgroup
-// sharing one LDS copy of the activations.
-// Above 4 columns the staged activations (NC x 4096 floats) leave room for
-// one workgroup per CU, so the workgroup itself is as wide as registers
-// allow: 12 waves (3 per SIMD) for Q4_1, 8 for Q4_0, 4 for Q8_0.
-template <int FMT, int NC> struct GemvShape {
-    static constexpr int kRWV = NC >= 4 && FMT != QK_Q8_0 ? 2 : 1;
-    static constexpr int kWPG = NC <= 4 ? 8 : (FMT == QK_Q4_1 ? 12 : (FMT == QK_Q4_0 ? 8 : 4));
-};
-
-// Workgroups launched per CU at most (when LDS allows).  Above what can be
-// resident at once, the hardware dispatcher starts a workgroup as another
-// finishes, which balances row groups better than giving each resident
-// workgroup a longer range.
-#ifndef QK_GEMV_WG_PER_CU
-#define QK_GEMV_WG_PER_CU 8
-#endif
-constexpr int kGvMaxWgPerCu = QK_GEMV_WG_PER_CU;
-
-static int device_cus() {
-    int cus = 256, dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-        cus = v;
-    return cus;
-}
-
-template <int FMT, int NC>
-static int dispatch_gemv_nc(GemvArgs &a, bool fast, hipStream_t stream) {
-    constexpr int RWV = GemvShape<FMT, NC>::kRWV;
-    constexpr int WPG = GemvShape<FMT, NC>::kWPG;
-    constexpr int RG = WPG * RWV;
-    a.gbase[0] = 0;
-    int kmax = 0;
-    for (int i = 0; i < a.count; ++i) {
-        a.gbase[i + 1] = a.gbase[i] + (a.item[i].m + RG - 1) / RG;
-        kmax = max(kmax, a.item[i].nb * 32);
-    }
-    const int total = a.gbase[a.count];
-    if (total == 0) return QK_OK;
-    // Activation window: one chunk of 4096 weights per column (17 KiB at one
-    // column).  Longer rows restage it per chunk; the small window lets more
-    // workgroups share a CU, which measured faster than holding whole rows of
-    // 11008 weights.
-    const int xw = kGvChunkElems;
-    (void)kmax;
-    const size_t lds = (size_t)NC * xw_pitch(xw) * sizeof(float);
-    const int per_cu = max(1, min(kGvMaxWgPerCu, (int)((160 * 1024) / lds)));
-    const int nwg = min(total, device_cus() * per_cu);
-    const GemvSplit split{total, total / nwg, total % nwg};
-    const dim3 grid((unsigned)nwg);
-    const dim3 block(64 * WPG);
-    auto go = [&](auto kern, const GemvArgs &args) -> int {
-        if (lds > 64 * 1024 &&
-            hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-            return QK_ERR_LAUNCH;
-        return launch_lds(kern, grid, block, lds, stream, args, a.item[0], split, xw);
-    };
-    static const GemvArgs none{};
-    if (a.count == 1) {
-        if (fast) return go(gemv_kernel<FMT, NC, RWV, WPG, true, true>, none);
-        return go(gemv_kernel<FMT, NC, RWV, WPG, false, true>, none);
-    }
-    if (fast) return go(gemv_kernel<FMT, NC, RWV, WPG, true, false>, a);
-    return go(gemv_kernel<FMT, NC, RWV, WPG, false, false>, a);
-}
-
-template <int FMT>
-static int dispatch_gemv(GemvArgs &a, int n, bool fast, hipStream_t stream) {
+static int gemv_by_columns(int fmt, GemvArgs &a, int n, bool fast, hipStream_t stream) {
     switch (n) {
-    case 1: return dispatch_gemv_nc<FMT, 1>(a, fast, stream);
-    case 2: return dispatch_gemv_nc<FMT, 2>(a, fast, stream);
-    case 3: return dispatch_gemv_nc<FMT, 3>(a, fast, stream);
-    case 4: return dispatch_gemv_nc<FMT, 4>(a, fast, stream);
-    case 5: return dispatch_gemv_nc<FMT, 5>(a, fast, stream);
-    case 6: return dispatch_gemv_nc<FMT, 6>(a, fast, stream);
-    case 7: return dispatch_gemv_nc<FMT, 7>(a, fast, stream);
-    case 8: return dispatch_gemv_nc<FMT, 8>(a, fast, stream);
+    case 1: return gemv_table<1>(fmt, a, fast, stream);
+    case 2: return gemv_table<2>(fmt, a, fast, stream);
+    case 3: return gemv_table<3>(fmt, a, fast, stream);
+    case 4: return gemv_table<4>(fmt, a, fast, stream);
+    case 5: return gemv_table<5>(fmt, a, fast, stream);
+    case 6: return gemv_table<6>(fmt, a, fast, stream);
+    case 7: return gemv_table<7>(fmt, a, fast, stream);
+    case 8: return gemv_table<8>(fmt, a, fast, stream);
     default: return QK_ERR_INVALID_ARG;
     }
 }
@@ -715,6 +57,18 @@ int launch_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count,
     for (int i = 0; i < count; ++i) {
         const qk_mat_vec_item &src = items[i];
         if (src.m == 0) continue;
+        if (src.k == 0) {
+            // no weights: every output is the empty sum
+            GemvExpert z{};
+            z.y = src.y;
+            z.y_slot = src.ldy;
+            z.m = (int)src.m;
+            z.n_used = (int)n;
+            z.count = (int)n;
+            const int st = launch_empty(z, stream);
+            if (st != QK_OK) return st;
+            continue;
+        }
         GemvItem &d = a.item[used++];
         d.w = static_cast<const uint8_t *>(src.w);
         d.x = src.x;
@@ -738,18 +92,40 @@ int launch_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count,
         for (; j > 0 && a.item[j - 1].nb < t.nb; --j) a.item[j] = a.item[j - 1];
         a.item[j] = t;
     }
-    switch (fmt) {
-    case QK_Q4_0: return dispatch_gemv<QK_Q4_0>(a, (int)n, fast, stream);
-    case QK_Q4_1: return dispatch_gemv<QK_Q4_1>(a, (int)n, fast, stream);
-    case QK_Q8_0: return dispatch_gemv<QK_Q8_0>(a, (int)n, fast, stream);
-    default: return QK_ERR_INVALID_ARG;
-    }
+    return gemv_by_columns(fmt, a, (int)n, fast, stream);
 }
 
 int launch_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k, const float *x,
                        int64_t n, int64_t ldx, float *y, int64_t ldy, hipStream_t stream) {
     qk_mat_vec_item item{w, m, k, x, ldx, y, ldy};
     return launch_mul_mat_vec_batched(fmt, &item, 1, n, stream);
+}
+
+int launch_mul_mat_vec_id(int fmt, const void *w, int64_t n_experts, int64_t expert_stride,
+                          int64_t m, int64_t k, const int32_t *ids, int64_t ld_ids,
+                          int64_t n_used, int64_t n_tokens, const float *x, int64_t x_slot,
+                          int64_t x_tok, float *y, int64_t y_slot, int64_t y_tok,
+                          hipStream_t stream) {
+    GemvExpert e{};
+    e.w = static_cast<const uint8_t *>(w);
+    e.estride = n_experts > 1 ? expert_stride : 0;
+    e.ids = ids;
+    e.ld_ids = n_tokens > 1 ? ld_ids : 0;
+    e.x = x;
+    e.x_slot = n_used > 1 ? x_slot : 0;
+    e.x_tok = n_tokens > 1 ? x_tok : 0;
+    e.y = y;
+    e.y_slot = n_used > 1 ? y_slot : 0;
+    e.y_tok = n_tokens > 1 ? y_tok : 0;
+    e.m = (int)m;
+    e.nb = (int)(k / kBlockElems);
+    e.nexp = (int)n_experts;
+    e.n_used = (int)n_used;
+    e.count = (int)(n_used * n_tokens);
+    if (e.nb == 0) return launch_empty(e, stream);
+    const bool fast = (uintptr_t)e.w % 4 == 0 && e.estride % 4 == 0 && e.nb % 2 == 0 &&
+                      (uintptr_t)e.x % 16 == 0 && e.x_slot % 4 == 0 && e.x_tok % 4 == 0;
+    return gemv_expert(fmt, e, fast, stream);
 }
 
 }  // namespace qk

@@ -1,0 +1,797 @@
+// gemv_impl.h - fused quantized GEMV for decode: y = W x for 1..8 fp32 columns
+// (device code and launch templates; instantiated per column count).
+//
+// What is computed follows dequantize_mul_mat_vec ("dmmv", named with its
+// tuning block in the "llama_cpp 0.12.1 -> 0.12.2" ggml-cuda.cu diff) and the
+// ggml_cuda_op_mul_mat driver (a row range times a column count): each output
+// is the dot product of one dequantized weight row with one activation column,
+// reduced across lanes (the diff's warp_reduce_sum).  That kernel's body is not
+// on the page; this one is designed for gfx950.
+//
+// Work split.  A workgroup of WPG waves owns a group of consecutive rows.  K
+// is walked in chunks of pairs of blocks: a pair of Q4_0 / Q4_1 / Q8_0 blocks
+// is 36 / 40 / 68 bytes, a whole number of dwords, so with an even block count
+// per row every pair starts on 4 bytes and comes straight into registers with
+// dword-aligned 16-byte loads (plain loads: streaming hints measured slower on
+// this chip).  For rows of more than 32 pairs a wave owns RWV rows and lane p
+// takes pair p of each 64-pair (4096-weight) chunk; shorter rows (one column
+// only) cut the wave into 2, 4 or 8 segments of 32, 16 or 8 lanes, one row
+// each, so a row of 2048 or 768 weights does not leave most lanes idle.
+//
+// Activations are the expensive side: every row needs all of x.  The chunk of
+// x (4096 x NC floats) is copied once per workgroup into LDS and read from
+// there by all of its rows; its global loads are issued before the weight
+// loads so the copy never waits behind HBM.  In LDS each run of 64 floats is
+// followed by 4 floats of padding, so the 16-byte reads of lanes p = 0..15 (at
+// float offset 68p + 4t) fall in distinct banks.  A workgroup takes a range
+// of consecutive row groups (of one or several problems of a grouped or
+// expert-indexed launch) and restages x only when a step enters a new problem
+// or window.
+//
+// Arithmetic, exact per term (every term is the exact weight times x):
+//  * Q4_0: the nibble becomes the exact fp16 number q - 8 by placing it in
+//    the mantissa of an fp16 with a byte permute (0x64XX is 1024 + XX) and
+//    removing the bias with one packed fp16 add; v_fma_mix_f32 multiplies that
+//    fp16 by the fp32 activation into an fp32 accumulator with one rounding.
+//    The block's sum is scaled by d once (d * (q - 8) is the exact weight).
+//  * Q8_0: the signed byte converts to fp32 exactly with a byte-select
+//    convert and is multiplied by x in one FMA; the block's sum is scaled by d.
+//  * Q4_1: the exact fp32 weight d*q + m is rebuilt per element (one FMA,
+//    exact because d*q is exact) and multiplied into the accumulator.
+// Reduction: a 64-lane DPP butterfly per (row, column); lane 0 writes y.
+#pragma once
+
+#include "gemv.h"
+#include "qk_common.h"
+#include "qk_internal.h"
+
+#include <type_traits>
+
+namespace qk {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int FMT> struct Pair;
+template <> struct Pair<QK_Q4_0> { static constexpr int kDwords = 9; };
+template <> struct Pair<QK_Q4_1> { static constexpr int kDwords = 10; };
+template <> struct Pair<QK_Q8_0> { static constexpr int kDwords = 17; };
+
+// acc + (fp16 in the low / high half of h) * x, fused, one rounding.
+__device__ __forceinline__ float fma_mix_lo(uint32_t h, float x, float acc) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x), "v"(acc));
+    return r;
+}
+__device__ __forceinline__ float fma_mix_hi(uint32_t h, float x, float acc) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=v"(r) : "v"(h), "v"(x), "v"(acc));
+    return r;
+}
+
+// Bytes 0,1 (lo) or 2,3 (hi) of src become the low mantissa bytes of two fp16
+// numbers with high byte 0x64: value 1024 + byte.
+__device__ __forceinline__ uint32_t bytes_to_f16_lo(uint32_t src) {
+    return __builtin_amdgcn_perm(0x64646464u, src, 0x04010400u);  // [b0, 64, b1, 64]
+}
+__device__ __forceinline__ uint32_t bytes_to_f16_hi(uint32_t src) {
+    return __builtin_amdgcn_perm(0x64646464u, src, 0x04030402u);  // [b2, 64, b3, 64]
+}
+
+__device__ __forceinline__ uint32_t pk_add_f16(uint32_t a, float b) {
+    const half2_t r = __builtin_bit_cast(half2_t, a) + half2_t{(_Float16)b, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t pk_fma_f16(uint32_t a, float s, float t) {
+    const half2_t r = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, a),
+                                                half2_t{(_Float16)s, (_Float16)s},
+                                                half2_t{(_Float16)t, (_Float16)t});
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 32-bit word starting 2 bytes into (lo, hi).
+__device__ __forceinline__ uint32_t shift2(uint32_t lo, uint32_t hi) {
+    return __builtin_amdgcn_alignbyte(hi, lo, 2);
+}
+
+// ---------------------------------------------------------------------------
+// One pair (two consecutive blocks) of a row in registers.
+// ---------------------------------------------------------------------------
+
+// FAST: the pair starts on a 4-byte boundary and both blocks exist.
+template <int FMT>
+__device__ __forceinline__ void load_pair_fast(const uint8_t *__restrict__ p,
+                                               uint32_t (&v)[Pair<FMT>::kDwords]) {
+    constexpr int N = Pair<FMT>::kDwords;
+#pragma unroll
+    for (int i = 0; i + 4 <= N; i += 4) {
+        const u32x4_a4 t = *reinterpret_cast<const u32x4_a4 *>(p + 4 * i);
+        v[i] = t.x; v[i + 1] = t.y; v[i + 2] = t.z; v[i + 3] = t.w;
+    }
+#pragma unroll
+    for (int i = N & ~3; i < N; ++i)
+        v[i] = *reinterpret_cast<const uint32_t *>(p + 4 * i);
+}
+
+// Generic: 2-byte aligned; if only the first block exists (odd block count,
+// last pair) the second block reads as d = m = 0 and codes 0, i.e. weights 0.
+template <int FMT>
+__device__ __forceinline__ void load_pair_generic(const uint8_t *__restrict__ p, bool second,
+                                                  uint32_t (&v)[Pair<FMT>::kDwords]) {
+    constexpr int N = Pair<FMT>::kDwords;
+    constexpr int BS = Format<FMT>::kBytes;
+    const uint16_t *h = reinterpret_cast<const uint16_t *>(p);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t a = (4 * i < BS || second) ? (uint32_t)h[2 * i] : 0u;
+        const uint32_t b = (4 * i + 2 < BS || second) ? (uint32_t)h[2 * i + 1] : 0u;
+        v[i] = a | (b << 16);
+    }
+}
+
+// fp16 bits of d (and m) of block b of the pair.
+template <int FMT>
+__device__ __forceinline__ uint32_t pair_d(const uint32_t (&v)[Pair<FMT>::kDwords], int b) {
+    if constexpr (FMT == QK_Q4_0) return b == 0 ? (v[0] & 0xFFFFu) : (v[4] >> 16);
+    if constexpr (FMT == QK_Q4_1) return b == 0 ? (v[0] & 0xFFFFu) : (v[5] & 0xFFFFu);
+    return b == 0 ? (v[0] & 0xFFFFu) : (v[8] >> 16);
+}
+__device__ __forceinline__ uint32_t pair_m_q41(const uint32_t (&v)[10], int b) {
+    return b == 0 ? (v[0] >> 16) : (v[5] >> 16);
+}
+
+// Quant word i of block b (Q4: i < 4, bytes 4i..4i+3; Q8: i < 8).
+template <int FMT>
+__device__ __forceinline__ uint32_t pair_qs(const uint32_t (&v)[Pair<FMT>::kDwords], int b, int i) {
+    if constexpr (FMT == QK_Q4_0) return b == 0 ? shift2(v[i], v[i + 1]) : v[5 + i];
+    if constexpr (FMT == QK_Q4_1) return b == 0 ? v[1 + i] : v[6 + i];
+    return b == 0 ? shift2(v[i], v[i + 1]) : v[9 + i];
+}
+
+// ---------------------------------------------------------------------------
+// Per-group products.  A group is quant word i of block b: Q4 elements
+// 4i..4i+3 (low nibbles) and 16+4i..16+4i+3 (high nibbles); Q8 elements
+// 4i..4i+3 (i < 8).  xa / xb are the matching activations.
+// ---------------------------------------------------------------------------
+
+// Q4_0 group: sum over the 8 elements of (q - 8) * x, added to s.
+__device__ __forceinline__ float group_q4_0(uint32_t qw, const float4 &xa, const float4 &xb, float s) {
+    // low nibbles: 1024 + c - 1032 = c - 8; high nibbles left in place:
+    // (1024 + 16c) / 16 - 72 = c - 8 (one fused, exact operation)
+    const uint32_t lo = qw & 0x0F0F0F0Fu;
+    const uint32_t hi = qw & 0xF0F0F0F0u;
+    const uint32_t l01 = pk_add_f16(bytes_to_f16_lo(lo), -1032.0f);
+    const uint32_t l23 = pk_add_f16(bytes_to_f16_hi(lo), -1032.0f);
+    const uint32_t h01 = pk_fma_f16(bytes_to_f16_lo(hi), 0.0625f, -72.0f);
+    const uint32_t h23 = pk_fma_f16(bytes_to_f16_hi(hi), 0.0625f, -72.0f);
+    s = fma_mix_lo(l01, xa.x, s);
+    s = fma_mix_hi(l01, xa.y, s);
+    s = fma_mix_lo(l23, xa.z, s);
+    s = fma_mix_hi(l23, xa.w, s);
+    s = fma_mix_lo(h01, xb.x, s);
+    s = fma_mix_hi(h01, xb.y, s);
+    s = fma_mix_lo(h23, xb.z, s);
+    s = fma_mix_hi(h23, xb.w, s);
+    return s;
+}
+
+// Q8_0 group: sum over 4 elements of q * x, added to s.  A signed byte
+// converts to fp32 exactly in one instruction (byte-select SDWA), and the
+// product q * x is rounded once inside the FMA.
+__device__ __forceinline__ float group_q8_0(uint32_t qw, const float4 &xa, float s) {
+    s = __builtin_fmaf((float)(int8_t)(qw), xa.x, s);
+    s = __builtin_fmaf((float)(int8_t)(qw >> 8), xa.y, s);
+    s = __builtin_fmaf((float)(int8_t)(qw >> 16), xa.z, s);
+    s = __builtin_fmaf((float)(int8_t)(qw >> 24), xa.w, s);
+    return s;
+}
+
+// Q8_0 group of block 0 of a pair: its quant word straddles two dwords
+// (bytes 2, 3 of lo and 0, 1 of hi), which byte selects read directly.
+__device__ __forceinline__ float group_q8_0_split(uint32_t lo, uint32_t hi, const float4 &xa, float s) {
+    s = __builtin_fmaf((float)(int8_t)(lo >> 16), xa.x, s);
+    s = __builtin_fmaf((float)(int8_t)(lo >> 24), xa.y, s);
+    s = __builtin_fmaf((float)(int8_t)(hi), xa.z, s);
+    s = __builtin_fmaf((float)(int8_t)(hi >> 8), xa.w, s);
+    return s;
+}
+
+// Q4_1 group: exact weights d*q + m times x, added to acc.
+__device__ __forceinline__ float group_q4_1(uint32_t qw, float d, float mm, const float4 &xa,
+                                            const float4 &xb, float a) {
+    const uint32_t lo = qw & 0x0F0F0F0Fu;
+    const uint32_t hi = (qw >> 4) & 0x0F0F0F0Fu;
+    a = __builtin_fmaf(wval(d, ubyte_f<0>(lo), mm), xa.x, a);
+    a = __builtin_fmaf(wval(d, ubyte_f<1>(lo), mm), xa.y, a);
+    a = __builtin_fmaf(wval(d, ubyte_f<2>(lo), mm), xa.z, a);
+    a = __builtin_fmaf(wval(d, ubyte_f<3>(lo), mm), xa.w, a);
+    a = __builtin_fmaf(wval(d, ubyte_f<0>(hi), mm), xb.x, a);
+    a = __builtin_fmaf(wval(d, ubyte_f<1>(hi), mm), xb.y, a);
+    a = __builtin_fmaf(wval(d, ubyte_f<2>(hi), mm), xb.z, a);
+    a = __builtin_fmaf(wval(d, ubyte_f<3>(hi), mm), xb.w, a);
+    return a;
+}
+
+// float4 of x (column j) at window-relative element e (e % 4 == 0) from LDS;
+// column pitch xp floats.
+__device__ __forceinline__ float4 x_lds(const float *xs, int xp, int j, int e) {
+    return *reinterpret_cast<const float4 *>(xs + j * xp + e + (e >> 6) * 4);
+}
+
+// Split of the launch's `total` row groups over the grid: workgroup b takes
+// per groups, plus one more if b < rem (computed on the host; no division on
+// the device).
+struct GemvSplit {
+    int total;
+    int per;
+    int rem;
+    int gpi;  // row groups per problem (expert-indexed launches)
+};
+
+// Dot products of one wave's RWV rows with this lane's pair, added to acc.
+template <int FMT, int NC, int RWV, bool FAST>
+__device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDwords], int nrows,
+                                         bool second, const float *xs, int xp, int el,
+                                         float (&acc)[RWV][NC]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        if (!FAST && b == 1 && !second) break;
+        if constexpr (FMT == QK_Q4_1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float4 xa[NC], xb[NC];
+#pragma unroll
+                for (int j = 0; j < NC; ++j) {
+                    xa[j] = x_lds(xs, xp, j, el + 32 * b + 4 * i);
+                    xb[j] = x_lds(xs, xp, j, el + 32 * b + 16 + 4 * i);
+                }
+#pragma unroll
+                for (int r = 0; r < RWV; ++r) {
+                    if (FAST || r < nrows) {  // fast path: rows clamped, stores guarded
+                        const float d = h2f(pair_d<FMT>(v[r], b));
+                        const float mm = h2f(pair_m_q41(v[r], b));
+                        const uint32_t qw = pair_qs<FMT>(v[r], b, i);
+                        const uint32_t lo = qw & 0x0F0F0F0Fu;
+                        const uint32_t hi = (qw >> 4) & 0x0F0F0F0Fu;
+                        const float w0 = wval(d, ubyte_f<0>(lo), mm), w1 = wval(d, ubyte_f<1>(lo), mm);
+                        const float w2 = wval(d, ubyte_f<2>(lo), mm), w3 = wval(d, ubyte_f<3>(lo), mm);
+                        const float w4 = wval(d, ubyte_f<0>(hi), mm), w5 = wval(d, ubyte_f<1>(hi), mm);
+                        const float w6 = wval(d, ubyte_f<2>(hi), mm), w7 = wval(d, ubyte_f<3>(hi), mm);
+#pragma unroll
+                        for (int j = 0; j < NC; ++j) {
+                            float a = acc[r][j];
+                            a = __builtin_fmaf(w0, xa[j].x, a);
+                            a = __builtin_fmaf(w1, xa[j].y, a);
+                            a = __builtin_fmaf(w2, xa[j].z, a);
+                            a = __builtin_fmaf(w3, xa[j].w, a);
+                            a = __builtin_fmaf(w4, xb[j].x, a);
+                            a = __builtin_fmaf(w5, xb[j].y, a);
+                            a = __builtin_fmaf(w6, xb[j].z, a);
+                            a = __builtin_fmaf(w7, xb[j].w, a);
+                            acc[r][j] = a;
+                        }
+                    }
+                }
+                // keep the next group's LDS reads from being hoisted above
+                // this one (bounds the live activations)
+                if constexpr (NC >= 2) asm volatile("" ::: "memory");
+            }
+        } else {
+            float s[RWV][NC];
+#pragma unroll
+            for (int r = 0; r < RWV; ++r)
+#pragma unroll
+                for (int j = 0; j < NC; ++j) s[r][j] = 0.0f;
+            constexpr int NGRP = (FMT == QK_Q8_0) ? 8 : 4;
+#pragma unroll
+            for (int i = 0; i < NGRP; ++i) {
+                float4 xa[NC], xb[NC];
+#pragma unroll
+                for (int j = 0; j < NC; ++j) {
+                    xa[j] = x_lds(xs, xp, j, el + 32 * b + 4 * i);
+                    if (FMT == QK_Q4_0) xb[j] = x_lds(xs, xp, j, el + 32 * b + 16 + 4 * i);
+                }
+#pragma unroll
+                for (int r = 0; r < RWV; ++r) {
+                    if (FAST || r < nrows) {  // fast path: rows clamped, stores guarded
+#pragma unroll
+                        for (int j = 0; j < NC; ++j) {
+                            if constexpr (FMT == QK_Q4_0) {
+                                s[r][j] = group_q4_0(pair_qs<FMT>(v[r], b, i), xa[j], xb[j], s[r][j]);
+                            } else if (b == 0) {
+                                s[r][j] = group_q8_0_split(v[r][i], v[r][i + 1], xa[j], s[r][j]);
+                            } else {
+                                s[r][j] = group_q8_0(v[r][9 + i], xa[j], s[r][j]);
+                            }
+                        }
+                    }
+                }
+                if constexpr (NC >= 3) asm volatile("" ::: "memory");
+            }
+#pragma unroll
+            for (int r = 0; r < RWV; ++r) {
+                if (FAST || r < nrows) {
+                    const float d = h2f(pair_d<FMT>(v[r], b));
+#pragma unroll
+                    for (int j = 0; j < NC; ++j) acc[r][j] = __builtin_fmaf(d, s[r][j], acc[r][j]);
+                }
+            }
+        }
+    }
+}
+
+// The activation window staged in LDS: 4096 weights per column, each run of
+// 64 floats followed by 4 floats of padding.
+constexpr int kGvWindow = kGvChunkElems;
+constexpr int kGvPitch = kGvWindow + kGvWindow / 16;
+
+// Where a launch's problems come from.
+enum GemvSource {
+    kSrcOne = 0,     // one problem, passed in its own argument
+    kSrcTable = 1,   // a table of up to kGvMaxItems problems
+    kSrcExpert = 2,  // expert-indexed problems, ids read on the device
+};
+template <int SRC> struct GemvSrc;
+template <> struct GemvSrc<kSrcOne> { using Args = GemvItem; };
+template <> struct GemvSrc<kSrcTable> { using Args = GemvArgs; };
+template <> struct GemvSrc<kSrcExpert> { using Args = GemvExpert; };
+
+// Sum over aligned segments of LPR lanes (8, 16, 32 or 64) with DPP.  The
+// sum ends in every lane of a segment of 8 or 16 (and of the wave for 64),
+// and in the last lane of each 32-lane half for 32 (seg_store_lane).
+template <int LPR>
+__device__ __forceinline__ float seg_sum(float v) {
+    if constexpr (LPR == 64) {
+        return wave_sum(v);
+    } else {
+        v += dpp<0xB1>(v);                                 // quad_perm [1,0,3,2]
+        v += dpp<0x4E>(v);                                 // quad_perm [2,3,0,1]
+        v += dpp<0x141>(v);                                // row_half_mirror: 8 lanes
+        if constexpr (LPR >= 16) v += dpp<0x140>(v);       // row_mirror: 16 lanes
+        if constexpr (LPR == 32) v += dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+        return v;
+    }
+}
+__host__ __device__ constexpr int seg_store_lane(int lpr) { return lpr == 32 ? 31 : 0; }
+
+// FAST: for every problem, w 4-byte aligned, an even number of blocks per
+// row, x 16-byte aligned and ldx % 4 == 0.
+//
+// Lanes and rows.  A wave owns RPW = RWV << SUB rows of its row group: the
+// wave is cut into 2^SUB segments of LPR = 64 >> SUB lanes and segment q
+// takes RWV rows (SUB > 0 only with RWV = 1, for short rows: a row of 2048
+// weights fills half a wave).  A step covers LPR pairs of each row, lane l
+// taking pair l % LPR.
+//
+// The launch's row groups (WPG * RPW rows each, the problems numbered one
+// after another) are split into gridDim.x contiguous ranges, one per
+// workgroup.  A workgroup walks its range as a sequence of steps (row group,
+// chunk of LPR pairs).  Each step's weights were requested during the
+// previous step (two register sets used in turn).  The activations are
+// staged into LDS in windows of 4096 weights, only when the problem or the
+// window changes.
+// SRC: where the problems come from (GemvSource).  kSrcOne has fixed
+// offsets and no indexed reads of a table before the first weight load;
+// kSrcExpert reads each problem's expert id from device memory when a step
+// enters the problem (an id outside the stack reads expert 0 and stores NaN).
+template <int FMT, int NC, int RWV, int WPG, bool FAST, int SRC, int SUB>
+__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 1 || (NC == 2 && FMT != QK_Q8_0) ? 4 : (NC == 2 ? 2 : 1)))) void gemv_kernel(const typename GemvSrc<SRC>::Args args, const GemvSplit split) {
+    static_assert(SUB == 0 || RWV == 1, "several rows per wave only with one row per segment");
+    static_assert(SRC != kSrcExpert || NC == 1, "expert-indexed problems have one column");
+    constexpr int BS = Format<FMT>::kBytes;
+    constexpr int ND = Pair<FMT>::kDwords;
+    constexpr int LPR = 64 >> SUB;              // lanes per row segment
+    constexpr int RPW = RWV << SUB;             // rows per wave
+    constexpr int RG = WPG * RPW;               // rows per group
+    constexpr int NT = 64 * WPG;                // lanes per workgroup
+    constexpr int CP = LPR;                     // pairs per step
+    constexpr int CE = CP * 64;                 // weights per step
+    constexpr int XW = kGvWindow;               // weights per activation window
+    constexpr int XP = kGvPitch;                // LDS floats per staged column
+    static_assert(XW / CE == (1 << SUB), "steps per activation window");
+    // log2 of the steps per window, opaque to the optimiser: with the
+    // constant folded in, its schedule of the LDS reads of the eight-column
+    // Q4_1 kernel no longer fits in registers
+    int cpw_log = SUB;
+    asm volatile("" : "+s"(cpw_log));
+    extern __shared__ __attribute__((aligned(16))) float xs[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int seg = lane >> (6 - SUB);          // row segment of this lane
+    const int sl = lane & (LPR - 1);            // lane within the segment
+    const int b = blockIdx.x;
+    const int gbeg = b * split.per + min(b, split.rem);
+    const int gend = gbeg + split.per + (b < split.rem ? 1 : 0);
+    if (gbeg >= gend) return;  // whole workgroup, before any barrier
+
+    auto gbase = [&](int i) -> int {
+        if constexpr (SRC == kSrcOne) return i == 0 ? 0 : split.total;
+        else if constexpr (SRC == kSrcTable) return args.gbase[i];
+        else return i * split.gpi;
+    };
+    auto item = [&](int i) -> const GemvItem * {
+        if constexpr (SRC == kSrcOne) return &args;
+        else if constexpr (SRC == kSrcTable) return &args.item[i];
+        else return nullptr;  // expert problems are formed in enter()
+    };
+    auto chunks = [](int nb) { return (((nb + 1) >> 1) + CP - 1) / CP; };
+
+    // Step position (uniform across the workgroup): row group g of problem
+    // mi, chunk c, with the problem's descriptor held in registers.  It is
+    // formed only when a step enters a new problem.
+    struct Pos {
+        int g, mi, c;
+        int gb0, gb1;   // the problem's first row group and one past its last
+        int nchunks;    // steps per row group
+        int bad;        // expert id outside the stack: outputs are NaN (an int:
+                        // a bool member sends the struct through scratch)
+        GemvItem it;
+    };
+    // (field by field: a whole-struct copy out of the argument segment is
+    // lowered through scratch memory)
+    auto enter = [&](Pos &q, int i) __attribute__((always_inline)) {
+        q.mi = i;
+        if constexpr (SRC == kSrcExpert) {
+            const int t = i / args.n_used;
+            const int s = i - t * args.n_used;
+            const int e = args.ids[(int64_t)t * args.ld_ids + s];
+            q.bad = (unsigned)e >= (unsigned)args.nexp;
+            q.it.w = args.w + (q.bad ? 0 : (int64_t)e * args.estride);
+            q.it.x = args.x + t * args.x_tok + s * args.x_slot;
+            q.it.y = args.y + t * args.y_tok + s * args.y_slot;
+            q.it.ldx = 0;
+            q.it.ldy = 0;
+            q.it.m = args.m;
+            q.it.nb = args.nb;
+        } else {
+            const GemvItem &src = *item(i);
+            q.bad = 0;
+            q.it.w = src.w;
+            q.it.x = src.x;
+            q.it.y = src.y;
+            q.it.ldx = src.ldx;
+            q.it.ldy = src.ldy;
+            q.it.m = src.m;
+            q.it.nb = src.nb;
+        }
+        q.gb0 = gbase(i);
+        q.gb1 = gbase(i + 1);
+        q.nchunks = chunks(q.it.nb);
+    };
+    Pos P;
+    P.g = gbeg;
+    P.c = 0;
+    {
+        int i = 0;
+        if constexpr (SRC == kSrcExpert) i = gbeg / split.gpi;
+        else while (gbeg >= gbase(i + 1)) ++i;
+        enter(P, i);
+    }
+    // The step after q within this workgroup's range (problems have at least
+    // one row group each, so a step enters at most one new problem).
+    auto advance = [&](const Pos &q) __attribute__((always_inline)) {
+        Pos r = q;
+        if (++r.c >= r.nchunks) {
+            r.c = 0;
+            if (++r.g >= r.gb1 && r.g < gend) enter(r, r.mi + 1);
+        }
+        return r;
+    };
+    int staged_mi = -1, staged_w = -1;
+
+    float acc[RWV][NC];
+#pragma unroll
+    for (int r = 0; r < RWV; ++r)
+#pragma unroll
+        for (int j = 0; j < NC; ++j) acc[r][j] = 0.0f;
+
+    // Weight loads of step q into dst.  On the fast path every lane issues the
+    // same loads with no branch around them (a lane past the last pair or row
+    // reads a clamped, valid address and ignores the data), so the compiler
+    // counts them and waits for exactly the loads a computation needs while
+    // the prefetch stays in flight.
+    auto load_step = [&](const Pos &q, uint32_t (&dst)[RWV][ND]) __attribute__((always_inline)) {
+        const GemvItem &it = q.it;
+        const int row0 = (q.g - q.gb0) * RG + wave * RPW + seg * RWV;
+        const int npairs = (it.nb + 1) >> 1;
+        const int64_t row_bytes = (int64_t)it.nb * BS;
+        const int pp = q.c * CP + sl;
+        if (FAST) {
+            const int ppc = min(pp, npairs - 1);
+#pragma unroll
+            for (int r = 0; r < RWV; ++r) {
+                const int row = min(row0 + r, it.m - 1);
+                load_pair_fast<FMT>(it.w + (int64_t)row * row_bytes + (int64_t)ppc * (2 * BS), dst[r]);
+            }
+        } else if (pp < npairs) {
+            const int nrows = max(0, min(RWV, it.m - row0));
+            const uint8_t *p = it.w + (int64_t)row0 * row_bytes + (int64_t)pp * (2 * BS);
+            const bool second = 2 * pp + 1 < it.nb;
+#pragma unroll
+            for (int r = 0; r < RWV; ++r)
+                if (r < nrows) load_pair_generic<FMT>(p + r * row_bytes, second, dst[r]);
+        }
+    };
+
+    constexpr int XR = NC <= 2 ? NC : 0;  // columns staged through registers (first window)
+
+    // Copy window `wi` of problem `it`'s activations into LDS (whole workgroup).
+    auto stage_x = [&](const GemvItem &it, int wi) __attribute__((always_inline)) {
+        const int e0 = wi * XW;
+        const int ce4 = min(XW, it.nb * 32 - e0) / 4;  // float4s in this window
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const float *xj = it.x + j * it.ldx + e0;
+            for (int t = tid; t < ce4; t += NT) {
+                f32x4_t val;
+                if (FAST) val = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
+                else val = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
+                *reinterpret_cast<f32x4_t *>(xs + j * XP + 4 * t + (t >> 4) * 4) = val;
+            }
+        }
+    };
+
+    // Steps in this workgroup's range.
+    int nsteps = 0;
+    if constexpr (SRC == kSrcExpert) {
+        nsteps = (gend - gbeg) * P.nchunks;  // every problem has the same shape
+    } else {
+        int gg = gbeg, ii = P.mi;
+        while (gg < gend) {
+            while (gg >= gbase(ii + 1)) ++ii;
+            const int nxt = min(gend, gbase(ii + 1));
+            nsteps += (nxt - gg) * chunks(item(ii)->nb);
+            gg = nxt;
+        }
+    }
+
+    // One step computing with cur.  Each (FIRST, DEPTH) combination is its own
+    // straight-line code, so the compiler waits for exactly the loads the
+    // computation needs and the prefetch stays in flight.  FIRST issues the
+    // activation loads before any weight load, so copying them to LDS does
+    // not wait for the weights (loads complete in order).
+    // DEPTH: 0 no prefetch, 1 the next step's weights requested into nxt.
+    auto step = [&](auto first_tag, auto depth_tag, uint32_t (&cur)[RWV][ND],
+                    uint32_t (&nxt)[RWV][ND]) __attribute__((always_inline)) {
+        constexpr bool FIRST = decltype(first_tag)::value;
+        constexpr int DEPTH = decltype(depth_tag)::value;
+        constexpr bool PREFETCH = DEPTH > 0;
+        const GemvItem &it = P.it;
+        const int npairs = (it.nb + 1) >> 1;
+        const int wi = P.c >> cpw_log;  // activation window of this step
+
+        const Pos Q = advance(P);
+        // past the workgroup's last step a prefetch repeats this step's loads
+        const Pos PF = Q.g < gend ? Q : P;
+
+        if constexpr (FIRST) {
+            // activation loads, then this step's and the next step's weights,
+            // then the LDS copy (waits only for the activations)
+            constexpr int XU = (XW / 4 + NT - 1) / NT;  // registers cover the first window
+            const int e0 = wi * XW;
+            const int ce4 = min(XW, it.nb * 32 - e0) / 4;
+            const int cr4 = min(XW / 4, ce4);
+            f32x4_t xr[XR > 0 ? XR : 1][XU];
+#pragma unroll
+            for (int j = 0; j < XR; ++j) {
+                const float *xj = it.x + j * it.ldx + e0;
+#pragma unroll
+                for (int u = 0; u < XU; ++u) {
+                    // clamped so every lane loads (a tail lane repeats the last
+                    // float4 and stores it again)
+                    const int t = min(tid + u * NT, cr4 - 1);
+                    if (FAST) xr[j][u] = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
+                    else xr[j][u] = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
+                }
+            }
+            load_step(P, cur);
+            if constexpr (PREFETCH) load_step(PF, nxt);
+            // unconditional stores (a tail lane rewrites the last float4 with
+            // the same value), so no load is moved behind the weight loads
+#pragma unroll
+            for (int j = 0; j < XR; ++j)
+#pragma unroll
+                for (int u = 0; u < XU; ++u) {
+                    const int t = min(tid + u * NT, cr4 - 1);
+                    *reinterpret_cast<f32x4_t *>(xs + j * XP + 4 * t + (t >> 4) * 4) = xr[j][u];
+                }
+            // the rest of the window (and wider activation sets) directly
+#pragma unroll
+            for (int j = 0; j < NC; ++j) {
+                const float *xj = it.x + j * it.ldx + e0;
+                for (int t = (j < XR ? cr4 : 0) + tid; t < ce4; t += NT) {
+                    f32x4_t val;
+                    if (FAST) val = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
+                    else val = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
+                    *reinterpret_cast<f32x4_t *>(xs + j * XP + 4 * t + (t >> 4) * 4) = val;
+                }
+            }
+            __syncthreads();
+            staged_mi = P.mi;
+            staged_w = wi;
+        } else {
+            // a new problem or window: restage the activations before the prefetch
+            if (staged_mi != P.mi || staged_w != wi) {
+                __syncthreads();  // readers of the previous window are done
+                stage_x(it, wi);
+                __syncthreads();
+                staged_mi = P.mi;
+                staged_w = wi;
+            }
+            if constexpr (PREFETCH) load_step(PF, nxt);
+        }
+
+        // compute this step
+        const int row0 = (P.g - P.gb0) * RG + wave * RPW + seg * RWV;
+        const int nrows = max(0, min(RWV, it.m - row0));
+        const int pp = P.c * CP + sl;
+        if (nrows > 0 && pp < npairs)
+            pair_dot<FMT, NC, RWV, FAST>(cur, nrows, FAST || (2 * pp + 1 < it.nb), xs, XP,
+                                         (P.c - (wi << cpw_log)) * CE + sl * 64, acc);
+
+        // last chunk of the group: reduce across the row's lanes and store
+        if (P.c == P.nchunks - 1) {
+#pragma unroll
+            for (int r = 0; r < RWV; ++r) {
+                if (SUB > 0 || r < nrows) {  // (uniform across the wave when SUB == 0)
+#pragma unroll
+                    for (int j = 0; j < NC; ++j) {
+                        const float sum = seg_sum<LPR>(acc[r][j]);
+                        if (sl == seg_store_lane(LPR) && r < nrows)
+                            it.y[j * it.ldy + row0 + r] = P.bad ? __builtin_nanf("") : sum;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < NC; ++j) acc[r][j] = 0.0f;
+            }
+        }
+        P = Q;
+    };
+
+    using T = std::true_type;
+    using F = std::false_type;
+    using D0 = std::integral_constant<int, 0>;
+    using D1 = std::integral_constant<int, 1>;
+    uint32_t va[RWV][ND], vb[RWV][ND];
+    if (nsteps == 1) {
+        step(T{}, D0{}, va, vb);
+        return;
+    }
+    step(T{}, D1{}, va, vb);
+    // Two steps per iteration with the register sets in swapped roles and no
+    // branch between them, so the two bodies stay distinct: a merged body
+    // would copy the prefetched registers into place, and that copy waits for
+    // every outstanding load (the new prefetch included).  The final step's
+    // prefetch repeats its own loads (clamped).
+    int left = nsteps - 1;  // steps still to compute; the next one's weights are in vb
+    for (; left >= 2; left -= 2) {
+        step(F{}, D1{}, vb, va);
+        step(F{}, D1{}, va, vb);
+    }
+    if (left == 1) step(F{}, D0{}, vb, va);
+}
+
+// Launch shape by column count: RWV rows per wave, WPG waves per workgroup
+// sharing one LDS copy of the activations.
+// Above 4 columns the staged activations (NC x 4096 floats) leave room for
+// one workgroup per CU, so the workgroup itself is as wide as registers
+// allow: 12 waves (3 per SIMD) for Q4_1, 8 for Q4_0, 4 for Q8_0.
+template <int FMT, int NC> struct GemvShape {
+    static constexpr int kRWV = NC >= 4 && FMT != QK_Q8_0 ? 2 : 1;
+    static constexpr int kWPG = NC <= 4 ? 8 : (FMT == QK_Q4_1 ? 12 : (FMT == QK_Q4_0 ? 8 : 4));
+    template <int SUB> static constexpr int rows_per_group() { return kWPG * (kRWV << SUB); }
+};
+
+// Rows per wave (as 2^SUB) for one-column launches whose longest row has
+// `npairs` pairs: short rows share a wave instead of leaving lanes idle.
+inline int gemv_sub(int npairs) {
+    return npairs <= 8 ? 3 : (npairs <= 16 ? 2 : (npairs <= 32 ? 1 : 0));
+}
+
+// Workgroups launched per CU at most (when LDS allows).  Above what can be
+// resident at once, the hardware dispatcher starts a workgroup as another
+// finishes, which balances row groups better than giving each resident
+// workgroup a longer range.
+#ifndef QK_GEMV_WG_PER_CU
+#define QK_GEMV_WG_PER_CU 8
+#endif
+constexpr int kGvMaxWgPerCu = QK_GEMV_WG_PER_CU;
+
+inline int device_cus() {
+    int cus = 256, dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+        cus = v;
+    return cus;
+}
+
+// One launch over `total` row groups (gpi per problem for expert launches).
+template <int FMT, int NC, int SRC, int SUB>
+int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi, bool fast,
+                hipStream_t stream) {
+    constexpr int RWV = GemvShape<FMT, NC>::kRWV;
+    constexpr int WPG = GemvShape<FMT, NC>::kWPG;
+    if (total <= 0) return QK_OK;
+    if (total > INT32_MAX) return QK_ERR_INVALID_ARG;
+    // Activation window: 4096 weights per column (17 KiB at one column).
+    // Longer rows restage it per window; the small window lets more
+    // workgroups share a CU, which measured faster than holding whole rows of
+    // 11008 weights.
+    const size_t lds = (size_t)NC * kGvPitch * sizeof(float);
+    const int per_cu = max(1, min(kGvMaxWgPerCu, (int)((160 * 1024) / lds)));
+    const int64_t cap = (int64_t)device_cus() * per_cu;
+    const int nwg = (int)(total < cap ? total : cap);
+    const GemvSplit split{(int)total, (int)total / nwg, (int)total % nwg, gpi};
+    auto go = [&](auto kern) -> int {
+        if (lds > 64 * 1024 &&
+            hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return QK_ERR_LAUNCH;
+        return launch_lds(kern, dim3((unsigned)nwg), dim3(64 * WPG), lds, stream, args, split);
+    };
+    if (fast) return go(gemv_kernel<FMT, NC, RWV, WPG, true, SRC, SUB>);
+    return go(gemv_kernel<FMT, NC, RWV, WPG, false, SRC, SUB>);
+}
+
+template <int FMT, int NC, int SUB>
+int gemv_table_sub(GemvArgs &a, bool fast, hipStream_t stream) {
+    constexpr int RG = GemvShape<FMT, NC>::template rows_per_group<SUB>();
+    int64_t g = 0;
+    a.gbase[0] = 0;
+    for (int i = 0; i < a.count; ++i) {
+        g += (a.item[i].m + RG - 1) / RG;
+        if (g > INT32_MAX) return QK_ERR_INVALID_ARG;
+        a.gbase[i + 1] = (int)g;
+    }
+    if (a.count == 1) return gemv_launch<FMT, NC, kSrcOne, SUB>(a.item[0], g, 0, fast, stream);
+    return gemv_launch<FMT, NC, kSrcTable, SUB>(a, g, 0, fast, stream);
+}
+
+template <int FMT, int NC>
+int gemv_table_fmt(GemvArgs &a, bool fast, hipStream_t stream) {
+    if constexpr (NC == 1) {
+        int npairs = 0;
+        for (int i = 0; i < a.count; ++i) npairs = max(npairs, (a.item[i].nb + 1) / 2);
+        switch (gemv_sub(npairs)) {
+        case 3: return gemv_table_sub<FMT, NC, 3>(a, fast, stream);
+        case 2: return gemv_table_sub<FMT, NC, 2>(a, fast, stream);
+        case 1: return gemv_table_sub<FMT, NC, 1>(a, fast, stream);
+        default: break;
+        }
+    }
+    return gemv_table_sub<FMT, NC, 0>(a, fast, stream);
+}
+
+template <int NC>
+int gemv_table(int fmt, GemvArgs &a, bool fast, hipStream_t stream) {
+    switch (fmt) {
+    case QK_Q4_0: return gemv_table_fmt<QK_Q4_0, NC>(a, fast, stream);
+    case QK_Q4_1: return gemv_table_fmt<QK_Q4_1, NC>(a, fast, stream);
+    case QK_Q8_0: return gemv_table_fmt<QK_Q8_0, NC>(a, fast, stream);
+    default: return QK_ERR_INVALID_ARG;
+    }
+}
+
+template <int FMT, int SUB>
+int gemv_expert_sub(const GemvExpert &e, bool fast, hipStream_t stream) {
+    constexpr int RG = GemvShape<FMT, 1>::template rows_per_group<SUB>();
+    const int gpi = (e.m + RG - 1) / RG;
+    return gemv_launch<FMT, 1, kSrcExpert, SUB>(e, (int64_t)gpi * e.count, gpi, fast, stream);
+}
+
+template <int FMT>
+int gemv_expert_fmt(const GemvExpert &e, bool fast, hipStream_t stream) {
+    switch (gemv_sub((e.nb + 1) / 2)) {
+    case 3: return gemv_expert_sub<FMT, 3>(e, fast, stream);
+    case 2: return gemv_expert_sub<FMT, 2>(e, fast, stream);
+    case 1: return gemv_expert_sub<FMT, 1>(e, fast, stream);
+    default: return gemv_expert_sub<FMT, 0>(e, fast, stream);
+    }
+}
+
+}  // namespace qk

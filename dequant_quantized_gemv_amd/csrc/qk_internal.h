@@ -43,6 +43,12 @@ int launch_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k, const float
 int launch_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count, int64_t n,
                                hipStream_t stream);
 
+int launch_mul_mat_vec_id(int fmt, const void *w, int64_t n_experts, int64_t expert_stride,
+                          int64_t m, int64_t k, const int32_t *ids, int64_t ld_ids,
+                          int64_t n_used, int64_t n_tokens, const float *x, int64_t x_slot,
+                          int64_t x_tok, float *y, int64_t y_slot, int64_t y_tok,
+                          hipStream_t stream);
+
 int launch_mul_mat(int fmt, const void *w, int64_t m, int64_t k, const uint16_t *x,
                    int64_t n, int64_t ldx, float *y, int64_t ldy, hipStream_t stream);
 

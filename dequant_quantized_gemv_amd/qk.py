@@ -19,7 +19,8 @@ QK_OK, QK_ERR_INVALID_ARG, QK_ERR_UNSUPPORTED, QK_ERR_ALIGNMENT, QK_ERR_LAUNCH =
 
 FORMATS = {"q4_0": QK_Q4_0, "q4_1": QK_Q4_1, "q8_0": QK_Q8_0}
 SYMBOLS = ("qk_block_bytes", "qk_row_bytes", "qk_status_string", "qk_version",
-           "qk_dequantize", "qk_mul_mat_vec", "qk_mul_mat_vec_batched", "qk_mul_mat")
+           "qk_dequantize", "qk_mul_mat_vec", "qk_mul_mat_vec_batched", "qk_mul_mat_vec_id",
+           "qk_mul_mat")
 QK_MAX_BATCH = 16
 
 
@@ -63,6 +64,9 @@ def load():
     lib.qk_mul_mat_vec.restype = ci
     lib.qk_mul_mat_vec_batched.argtypes = [ci, ctypes.POINTER(MatVecItem), ci, i64, vp]
     lib.qk_mul_mat_vec_batched.restype = ci
+    lib.qk_mul_mat_vec_id.argtypes = [ci, vp, i64, i64, i64, i64, vp, i64, i64, i64,
+                                      vp, i64, i64, vp, i64, i64, vp]
+    lib.qk_mul_mat_vec_id.restype = ci
     lib.qk_mul_mat.argtypes = [ci, vp, i64, i64, vp, i64, i64, vp, i64, vp]
     lib.qk_mul_mat.restype = ci
     _lib = lib
@@ -126,6 +130,13 @@ def qk_mul_mat_vec_batched(fmt, items, count, n, stream=0):
     return load().qk_mul_mat_vec_batched(_fmt(fmt), items, count, n, stream)
 
 
+def qk_mul_mat_vec_id(fmt, w_ptr, n_experts, expert_stride, m, k, ids_ptr, ld_ids, n_used,
+                      n_tokens, x_ptr, x_slot, x_tok, y_ptr, y_slot, y_tok, stream=0):
+    return load().qk_mul_mat_vec_id(_fmt(fmt), w_ptr, n_experts, expert_stride, m, k, ids_ptr,
+                                    ld_ids, n_used, n_tokens, x_ptr, x_slot, x_tok, y_ptr,
+                                    y_slot, y_tok, stream)
+
+
 def qk_mul_mat(fmt, w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream=0):
     return load().qk_mul_mat(_fmt(fmt), w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream)
 
@@ -181,6 +192,35 @@ def mul_mat_vec_batched(fmt, problems, ys=None, stream=None):
     st = qk_mul_mat_vec_batched(fmt, arr, len(tup), n, _stream(stream))
     _check(st, "qk_mul_mat_vec_batched")
     return ys
+
+
+def mul_mat_vec_id(fmt, w, n_experts, m, k, ids, x, y=None, expert_stride=None, stream=None):
+    """Expert-indexed GEMV: y[t, s] = W[ids[t, s]] @ x[t] (x shaped (n_tokens, k),
+    shared by a token's slots) or x[t, s] (x shaped (n_tokens, n_used, k)).
+    w: uint8 CUDA tensor holding n_experts matrices, expert_stride bytes apart
+    (default: packed); ids: int32 CUDA tensor (n_tokens, n_used).  Returns y
+    shaped (n_tokens, n_used, m) fp32."""
+    import torch
+    if ids.dtype != torch.int32 or ids.dim() != 2 or ids.stride(1) != 1:
+        raise TypeError("ids must be int32 (n_tokens, n_used) with contiguous rows")
+    n_tokens, n_used = ids.shape
+    if x.dtype != torch.float32 or x.stride(-1) != 1:
+        raise TypeError("x must be float32 with contiguous vectors")
+    if x.dim() == 2:
+        x_slot, x_tok = 0, x.stride(0)
+    elif x.dim() == 3:
+        x_slot, x_tok = x.stride(1), x.stride(0)
+    else:
+        raise TypeError("x must be (n_tokens, k) or (n_tokens, n_used, k)")
+    if expert_stride is None:
+        expert_stride = m * row_bytes(fmt, k)
+    if y is None:
+        y = torch.empty((n_tokens, n_used, m), dtype=torch.float32, device=x.device)
+    st = qk_mul_mat_vec_id(fmt, w.data_ptr(), n_experts, expert_stride, m, k, ids.data_ptr(),
+                           ids.stride(0), n_used, n_tokens, x.data_ptr(), x_slot, x_tok,
+                           y.data_ptr(), y.stride(1), y.stride(0), _stream(stream))
+    _check(st, "qk_mul_mat_vec_id")
+    return y
 
 
 def mul_mat(fmt, w, m, k, x, y=None, stream=None):

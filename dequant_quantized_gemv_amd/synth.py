@@ -37,7 +37,7 @@ _M2 = np.uint64(0x94D049BB133111EB)
 BLOCK_BYTES = {"q4_0": 18, "q4_1": 20, "q8_0": 34}
 QS_OFFSET = {"q4_0": 2, "q4_1": 4, "q8_0": 2}
 
-FIELD_D, FIELD_M, FIELD_QS, FIELD_X, FIELD_X2 = 0, 1, 2, 3, 4
+FIELD_D, FIELD_M, FIELD_QS, FIELD_X, FIELD_X2, FIELD_IDS = 0, 1, 2, 3, 4, 5
 
 
 def _mix(z):
@@ -152,8 +152,25 @@ def activations(k, n, seed, tensor_id, dtype=np.float32):
     return v.astype(dtype)
 
 
+def expert_ids(n_tokens, n_used, n_experts, seed, tensor_id):
+    """Expert choices: for each token, n_used distinct ids drawn uniformly from
+    0..n_experts-1 (a partial Fisher-Yates shuffle driven by the stream);
+    returned as int32 of shape (n_tokens, n_used)."""
+    if n_used > n_experts:
+        raise ValueError("more slots than experts")
+    z = splitmix64(stream_key(seed, tensor_id, FIELD_IDS), n_tokens * n_used)
+    out = np.empty((n_tokens, n_used), dtype=np.int32)
+    for t in range(n_tokens):
+        perm = np.arange(n_experts)
+        for s in range(n_used):
+            j = s + int(z[t * n_used + s] % np.uint64(n_experts - s))
+            perm[s], perm[j] = perm[j], perm[s]
+        out[t] = perm[:n_used]
+    return out
+
+
 # ---------------------------------------------------------------------------
-# The five workloads (shapes and value distributions)
+# The workloads (shapes and value distributions)
 # ---------------------------------------------------------------------------
 
 SEED_BASE = 0x5EED0000
@@ -166,6 +183,11 @@ LAYER_SHAPES = [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096),
                 ("o", 4096, 4096), ("gate", 11008, 4096), ("up", 11008, 4096),
                 ("down", 4096, 11008)]
 
+# mixture-of-experts decode: expert matrices of intermediate width 768 (the
+# Q4_0 expert model the PR's commit list names) over a hidden width of 2048,
+# 128 experts, 8 used per token: gate and up 768 x 2048, down 2048 x 768
+MOE_SHAPES = [("gate", 768, 2048), ("up", 768, 2048), ("down", 2048, 768)]
+
 WORKLOADS = {
     "dequant_q4_0_4096x4096_f32": dict(id=0, fmt="q4_0", m=4096, k=4096, d=D_Q4),
     "gemv_q8_0_4096x4096_n1": dict(id=1, fmt="q8_0", m=4096, k=4096, n=1, d=D_Q8),
@@ -173,6 +195,8 @@ WORKLOADS = {
                                  d=D_Q4, mr=M_Q4_1),
     "gemv_q4_0_decode_layer": dict(id=3, fmt="q4_0", layer=LAYER_SHAPES, n=1, d=D_Q4),
     "gemm_q4_0_14336x4096_n512": dict(id=4, fmt="q4_0", m=14336, k=4096, n=512, d=D_Q4),
+    "gemv_q4_0_moe_experts": dict(id=5, fmt="q4_0", layer=MOE_SHAPES, n_experts=128, n_used=8,
+                                  n_tokens=1, d=D_Q4),
 }
 
 

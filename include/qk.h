@@ -158,6 +158,49 @@ int qk_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count, int
                            void *stream);
 
 /*
+ * qk_mul_mat_vec_id - expert-indexed GEMV for mixture-of-experts decode: for
+ * every token t and slot s, the GEMV of the expert matrix that ids selects,
+ * with the expert id read on the device (no host synchronisation).
+ *
+ *   e = ids[t*ld_ids + s]
+ *   y[t*y_tok + s*y_slot + i] = sum_c W_e[i, c] * x[t*x_tok + s*x_slot + c]
+ *        for i < m, s < n_used, t < n_tokens                          (overwrite)
+ *   W_e = m rows of k/32 blocks starting at byte e*expert_stride of w
+ *
+ * Each (t, s) is computed exactly as qk_mul_mat_vec computes one column.  An
+ * id outside [0, n_experts) selects nothing: its m outputs are set to NaN and
+ * no weight outside the stack is read.
+ * Source: ggml_cuda_mul_mat_id, named by a ggml-cuda.cu hunk of the
+ * "ggml: backend-agnostic tensor parallelism" compare (whose commit list
+ * mentions a Q4_0 expert model with intermediate dimension 768); its
+ * definition is not printed there, and this follows ggml's mul_mat_id: one
+ * product per (token, selected expert).
+ *
+ *   w              stack of n_experts matrices, 2-byte aligned
+ *   n_experts      >= 1
+ *   expert_stride  bytes between experts, even, >= one matrix (ignored if
+ *                  n_experts == 1)
+ *   m, k           m >= 0, k >= 0, k % 32 == 0
+ *   ids            device int32, 4-byte aligned; token t's ids at t*ld_ids
+ *   ld_ids         >= n_used (ignored if n_tokens == 1)
+ *   n_used         slots per token, >= 0 (0 is a no-op)
+ *   n_tokens       >= 0 (0 is a no-op)
+ *   x              fp32, 4-byte aligned; x_slot = 0 gives every slot of a
+ *                  token the same vector; strides >= 0, in elements
+ *   y              fp32, 4-byte aligned; the n_used*n_tokens outputs must not
+ *                  overlap: (y_slot >= m and y_tok >= (n_used-1)*y_slot + m)
+ *                  or (y_tok >= m and y_slot >= (n_tokens-1)*y_tok + m)
+ * Errors: QK_ERR_INVALID_ARG for the conditions above, n_used * n_tokens *
+ * ceil(m/8) above INT32_MAX, a null pointer, or y overlapping w, ids or x;
+ * QK_ERR_ALIGNMENT as listed; nothing is enqueued on an error.
+ */
+int qk_mul_mat_vec_id(int fmt, const void *w, int64_t n_experts, int64_t expert_stride,
+                      int64_t m, int64_t k, const int32_t *ids, int64_t ld_ids,
+                      int64_t n_used, int64_t n_tokens,
+                      const float *x, int64_t x_slot, int64_t x_tok,
+                      float *y, int64_t y_slot, int64_t y_tok, void *stream);
+
+/*
  * qk_mul_mat - batched GEMM: weights dequantized to fp16 tiles in LDS and
  * multiplied by fp16 activations on the matrix cores, accumulating in fp32.
  *

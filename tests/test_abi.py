@@ -152,3 +152,45 @@ def test_mul_mat_vec_batched_validation(fmt, items, count, n, want):
 
 def test_mul_mat_vec_batched_null_items():
     assert qk.qk_mul_mat_vec_batched(qk.QK_Q4_0, None, 2, 1, 0) == qk.QK_ERR_INVALID_ARG
+
+
+IDS = 0x50000000
+EB = 8 * 2 * 18   # one 8 x 64 Q4_0 expert
+
+
+# (fmt, w, n_experts, expert_stride, m, k, ids, ld_ids, n_used, n_tokens,
+#  x, x_slot, x_tok, y, y_slot, y_tok)
+def _id_args(**kw):
+    a = dict(fmt=E.QK_Q4_0, w=W, n_experts=4, expert_stride=EB, m=8, k=64, ids=IDS, ld_ids=2,
+             n_used=2, n_tokens=3, x=X, x_slot=64, x_tok=128, y=Y, y_slot=8, y_tok=16)
+    a.update(kw)
+    return tuple(a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(fmt=9), E.QK_ERR_UNSUPPORTED),
+    (dict(k=48), E.QK_ERR_INVALID_ARG),                         # k % 32
+    (dict(m=-1), E.QK_ERR_INVALID_ARG),
+    (dict(n_experts=0), E.QK_ERR_INVALID_ARG),                  # empty stack
+    (dict(expert_stride=EB - 2), E.QK_ERR_INVALID_ARG),         # experts overlap
+    (dict(expert_stride=EB + 1), E.QK_ERR_ALIGNMENT),           # odd stride
+    (dict(ld_ids=1), E.QK_ERR_INVALID_ARG),                     # ld_ids < n_used
+    (dict(x_slot=-64), E.QK_ERR_INVALID_ARG),                   # negative stride
+    (dict(y_slot=4), E.QK_ERR_INVALID_ARG),                     # outputs overlap
+    (dict(y_slot=16, y_tok=8), E.QK_ERR_INVALID_ARG),           # token 2 slot 0 meets token 0 slot 1
+
+    (dict(ids=None), E.QK_ERR_INVALID_ARG),
+    (dict(w=None), E.QK_ERR_INVALID_ARG),
+    (dict(ids=IDS + 2), E.QK_ERR_ALIGNMENT),
+    (dict(w=W + 1), E.QK_ERR_ALIGNMENT),
+    (dict(y=W + 16), E.QK_ERR_INVALID_ARG),                     # y overlaps the stack
+    (dict(y=IDS + 4), E.QK_ERR_INVALID_ARG),                    # y overlaps ids
+    (dict(y=X + 200), E.QK_ERR_INVALID_ARG),                    # y overlaps x
+    (dict(n_tokens=2**31), E.QK_ERR_INVALID_ARG),               # too many problems
+    (dict(x_tok=2**62), E.QK_ERR_INVALID_ARG),                  # span overflows
+    (dict(n_used=0), E.QK_OK),
+    (dict(n_tokens=0), E.QK_OK),
+    (dict(m=0), E.QK_OK),
+])
+def test_mul_mat_vec_id_validation(kw, want):
+    assert qk.qk_mul_mat_vec_id(*_id_args(**kw), 0) == want
