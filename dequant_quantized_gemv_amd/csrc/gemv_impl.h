@@ -407,7 +407,13 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
     const int b = blockIdx.x;
     const int gbeg = b * split.per + min(b, split.rem);
     const int gend = gbeg + split.per + (b < split.rem ? 1 : 0);
-    if (gbeg >= gend) return;  // whole workgroup, before any barrier
+    // The launcher never starts more workgroups than row groups (per >= 1),
+    // so no range is empty.  Expert-indexed launches state it rather than
+    // test it, so their argument loads are not split around a branch (one
+    // round trip before the id load; measured faster there, slower for the
+    // grouped table).
+    if constexpr (SRC == kSrcExpert) __builtin_assume(gbeg < gend);
+    else if (gbeg >= gend) return;  // whole workgroup, before any barrier
 
     auto gbase = [&](int i) -> int {
         if constexpr (SRC == kSrcOne) return i == 0 ? 0 : split.total;
@@ -428,8 +434,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         int g, mi, c;
         int gb0, gb1;   // the problem's first row group and one past its last
         int nchunks;    // steps per row group
-        int bad;        // expert id outside the stack: outputs are NaN (an int:
-                        // a bool member sends the struct through scratch)
+        int e;          // expert id (expert-indexed problems); it.w is the stack
         GemvItem it;
     };
     // (field by field: a whole-struct copy out of the argument segment is
@@ -439,9 +444,12 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         if constexpr (SRC == kSrcExpert) {
             const int t = i / args.n_used;
             const int s = i - t * args.n_used;
-            const int e = args.ids[(int64_t)t * args.ld_ids + s];
-            q.bad = (unsigned)e >= (unsigned)args.nexp;
-            q.it.w = args.w + (q.bad ? 0 : (int64_t)e * args.estride);
+            // a scalar load (constant address space): it is waited for only
+            // where the expert's address is first needed, so in the first
+            // step it overlaps the activation loads
+            typedef const __attribute__((address_space(4))) int32_t cid_t;
+            q.e = *(cid_t *)(uintptr_t)(args.ids + (int64_t)t * args.ld_ids + s);
+            q.it.w = args.w;
             q.it.x = args.x + t * args.x_tok + s * args.x_slot;
             q.it.y = args.y + t * args.y_tok + s * args.y_slot;
             q.it.ldx = 0;
@@ -450,7 +458,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
             q.it.nb = args.nb;
         } else {
             const GemvItem &src = *item(i);
-            q.bad = 0;
+            q.e = 0;
             q.it.w = src.w;
             q.it.x = src.x;
             q.it.y = src.y;
@@ -482,6 +490,16 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         }
         return r;
     };
+    // The problem's weights, and whether its outputs are NaN (an expert id
+    // outside the stack reads expert 0 instead).
+    auto bad = [&](const Pos &q) -> bool {
+        if constexpr (SRC == kSrcExpert) return (unsigned)q.e >= (unsigned)args.nexp;
+        else return false;
+    };
+    auto weights = [&](const Pos &q) -> const uint8_t * {
+        if constexpr (SRC == kSrcExpert) return q.it.w + (bad(q) ? 0 : (int64_t)q.e * args.estride);
+        else return q.it.w;
+    };
     int staged_mi = -1, staged_w = -1;
 
     float acc[RWV][NC];
@@ -497,6 +515,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
     // the prefetch stays in flight.
     auto load_step = [&](const Pos &q, uint32_t (&dst)[RWV][ND]) __attribute__((always_inline)) {
         const GemvItem &it = q.it;
+        const uint8_t *w = weights(q);
         const int row0 = (q.g - q.gb0) * RG + wave * RPW + seg * RWV;
         const int npairs = (it.nb + 1) >> 1;
         const int64_t row_bytes = (int64_t)it.nb * BS;
@@ -506,11 +525,11 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
 #pragma unroll
             for (int r = 0; r < RWV; ++r) {
                 const int row = min(row0 + r, it.m - 1);
-                load_pair_fast<FMT>(it.w + (int64_t)row * row_bytes + (int64_t)ppc * (2 * BS), dst[r]);
+                load_pair_fast<FMT>(w + (int64_t)row * row_bytes + (int64_t)ppc * (2 * BS), dst[r]);
             }
         } else if (pp < npairs) {
             const int nrows = max(0, min(RWV, it.m - row0));
-            const uint8_t *p = it.w + (int64_t)row0 * row_bytes + (int64_t)pp * (2 * BS);
+            const uint8_t *p = w + (int64_t)row0 * row_bytes + (int64_t)pp * (2 * BS);
             const bool second = 2 * pp + 1 < it.nb;
 #pragma unroll
             for (int r = 0; r < RWV; ++r)
@@ -565,8 +584,9 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         const int npairs = (it.nb + 1) >> 1;
         const int wi = P.c >> cpw_log;  // activation window of this step
 
+        // the next step, and what to prefetch: past the workgroup's last step
+        // a prefetch repeats this step's loads
         const Pos Q = advance(P);
-        // past the workgroup's last step a prefetch repeats this step's loads
         const Pos PF = Q.g < gend ? Q : P;
 
         if constexpr (FIRST) {
@@ -643,7 +663,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
                     for (int j = 0; j < NC; ++j) {
                         const float sum = seg_sum<LPR>(acc[r][j]);
                         if (sl == seg_store_lane(LPR) && r < nrows)
-                            it.y[j * it.ldy + row0 + r] = P.bad ? __builtin_nanf("") : sum;
+                            it.y[j * it.ldy + row0 + r] = bad(P) ? __builtin_nanf("") : sum;
                     }
                 }
 #pragma unroll
@@ -681,10 +701,14 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
 // Above 4 columns the staged activations (NC x 4096 floats) leave room for
 // one workgroup per CU, so the workgroup itself is as wide as registers
 // allow: 12 waves (3 per SIMD) for Q4_1, 8 for Q4_0, 4 for Q8_0.
-template <int FMT, int NC> struct GemvShape {
+#ifndef QK_GEMV_SHORT_WPG
+#define QK_GEMV_SHORT_WPG 4
+#endif
+template <int FMT, int NC, int SUB = 0> struct GemvShape {
     static constexpr int kRWV = NC >= 4 && FMT != QK_Q8_0 ? 2 : 1;
-    static constexpr int kWPG = NC <= 4 ? 8 : (FMT == QK_Q4_1 ? 12 : (FMT == QK_Q4_0 ? 8 : 4));
-    template <int SUB> static constexpr int rows_per_group() { return kWPG * (kRWV << SUB); }
+    static constexpr int kWPG = SUB > 0 ? QK_GEMV_SHORT_WPG
+                                        : (NC <= 4 ? 8 : (FMT == QK_Q4_1 ? 12 : (FMT == QK_Q4_0 ? 8 : 4)));
+    static constexpr int kRowsPerGroup = kWPG * (kRWV << SUB);
 };
 
 // Rows per wave (as 2^SUB) for one-column launches whose longest row has
@@ -714,8 +738,8 @@ inline int device_cus() {
 template <int FMT, int NC, int SRC, int SUB>
 int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi, bool fast,
                 hipStream_t stream) {
-    constexpr int RWV = GemvShape<FMT, NC>::kRWV;
-    constexpr int WPG = GemvShape<FMT, NC>::kWPG;
+    constexpr int RWV = GemvShape<FMT, NC, SUB>::kRWV;
+    constexpr int WPG = GemvShape<FMT, NC, SUB>::kWPG;
     if (total <= 0) return QK_OK;
     if (total > INT32_MAX) return QK_ERR_INVALID_ARG;
     // Activation window: 4096 weights per column (17 KiB at one column).
@@ -740,7 +764,7 @@ int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi,
 
 template <int FMT, int NC, int SUB>
 int gemv_table_sub(GemvArgs &a, bool fast, hipStream_t stream) {
-    constexpr int RG = GemvShape<FMT, NC>::template rows_per_group<SUB>();
+    constexpr int RG = GemvShape<FMT, NC, SUB>::kRowsPerGroup;
     int64_t g = 0;
     a.gbase[0] = 0;
     for (int i = 0; i < a.count; ++i) {
@@ -779,7 +803,7 @@ int gemv_table(int fmt, GemvArgs &a, bool fast, hipStream_t stream) {
 
 template <int FMT, int SUB>
 int gemv_expert_sub(const GemvExpert &e, bool fast, hipStream_t stream) {
-    constexpr int RG = GemvShape<FMT, 1>::template rows_per_group<SUB>();
+    constexpr int RG = GemvShape<FMT, 1, SUB>::kRowsPerGroup;
     const int gpi = (e.m + RG - 1) / RG;
     return gemv_launch<FMT, 1, kSrcExpert, SUB>(e, (int64_t)gpi * e.count, gpi, fast, stream);
 }
