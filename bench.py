@@ -291,7 +291,11 @@ def run_configs(torch, qk, synth, oracle, timer, steps, warmup):
                 "weight_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
             del prob
 
-    # C3: the decode layer, 7 GEMVs per step
+    # C3: the decode layer, 7 GEMVs per step (from a clean allocator: weight
+    # copies carved out of the previous workloads' freed blocks measured
+    # slower than fresh allocations)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     cfg = synth.WORKLOADS["gemv_q4_0_decode_layer"]
     seed = synth.workload_seed(cfg["id"])
     probs, wtot = [], 0
@@ -347,6 +351,8 @@ def run_configs(torch, qk, synth, oracle, timer, steps, warmup):
     del probs, layer_copies, gw, gk, item_sets
 
     # C4: GEMM
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     cfg = synth.WORKLOADS["gemm_q4_0_14336x4096_n512"]
     seed = synth.workload_seed(cfg["id"])
     m, k, n = cfg["m"], cfg["k"], cfg["n"]
@@ -379,6 +385,8 @@ def run_configs(torch, qk, synth, oracle, timer, steps, warmup):
     del wc, gw, gk
 
     log("expert-indexed decode")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     res["gemv_q4_0_moe_experts"] = run_moe(torch, qk, synth, oracle, timer, steps, warmup)
     return res
 

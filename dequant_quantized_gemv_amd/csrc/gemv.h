@@ -54,13 +54,13 @@ struct GemvExpert {
 };
 
 // Launch one table of problems with NC columns each (count == 1 uses the
-// single-problem kernel).  `fast`: every w 4-byte aligned with an even
-// number of blocks per row, every x 16-byte aligned with ldx % 4 == 0.
+// single-problem kernel).  `fast`: every w 4-byte aligned with an even number
+// of blocks per row.
 template <int NC>
 int gemv_table(int fmt, GemvArgs &a, bool fast, hipStream_t stream);
 
-// Launch expert-indexed problems (same `fast` condition, for every expert
-// and slot).
+// Launch expert-indexed problems (same `fast` condition, for every expert and
+// slot).
 int gemv_expert(int fmt, const GemvExpert &e, bool fast, hipStream_t stream);
 
 }  // namespace qk

@@ -77,8 +77,7 @@ int launch_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count,
         d.ldy = src.ldy;
         d.m = (int)src.m;
         d.nb = (int)(src.k / kBlockElems);
-        fast = fast && ((uintptr_t)d.w % 4) == 0 && (d.nb % 2) == 0 &&
-               ((uintptr_t)d.x % 16) == 0 && (d.ldx % 4) == 0;
+        fast = fast && ((uintptr_t)d.w % 4) == 0 && (d.nb % 2) == 0;
     }
     a.count = used;
     if (used == 0) return QK_OK;
@@ -123,8 +122,7 @@ int launch_mul_mat_vec_id(int fmt, const void *w, int64_t n_experts, int64_t exp
     e.n_used = (int)n_used;
     e.count = (int)(n_used * n_tokens);
     if (e.nb == 0) return launch_empty(e, stream);
-    const bool fast = (uintptr_t)e.w % 4 == 0 && e.estride % 4 == 0 && e.nb % 2 == 0 &&
-                      (uintptr_t)e.x % 16 == 0 && e.x_slot % 4 == 0 && e.x_tok % 4 == 0;
+    const bool fast = (uintptr_t)e.w % 4 == 0 && e.estride % 4 == 0 && e.nb % 2 == 0;
     return gemv_expert(fmt, e, fast, stream);
 }
 

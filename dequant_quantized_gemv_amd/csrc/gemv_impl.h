@@ -52,6 +52,8 @@ namespace qk {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// 16 activation bytes at a 4-byte aligned address (one dwordx4 load).
+typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 template <int FMT> struct Pair;
 template <> struct Pair<QK_Q4_0> { static constexpr int kDwords = 9; };
@@ -130,6 +132,33 @@ __device__ __forceinline__ void load_pair_generic(const uint8_t *__restrict__ p,
         const uint32_t b = (4 * i + 2 < BS || second) ? (uint32_t)h[2 * i + 1] : 0u;
         v[i] = a | (b << 16);
     }
+}
+
+// Generic, whole dwords: a pair that starts 2 bytes past a dword boundary
+// (rows of an odd block count, or a 2-byte aligned matrix) is read as the
+// ND + 1 dwords from the boundary below it and shifted into place.  Reads
+// from 2 bytes before p (inside p's own dword) to kPairReach bytes after it;
+// if only the first block exists the second block's words are junk, which
+// the caller ignores.
+template <int FMT> constexpr int kPairReach = 4 * (Pair<FMT>::kDwords + 1);
+
+template <int FMT>
+__device__ __forceinline__ void load_pair_shift(const uint8_t *__restrict__ p,
+                                                uint32_t (&v)[Pair<FMT>::kDwords]) {
+    constexpr int N = Pair<FMT>::kDwords + 1;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(a & ~uintptr_t(3));
+    const uint32_t sh = (uint32_t)(a & 3);
+    uint32_t d[N];
+#pragma unroll
+    for (int i = 0; i + 4 <= N; i += 4) {
+        const u32x4_a4 t = *reinterpret_cast<const u32x4_a4 *>(base + 4 * i);
+        d[i] = t.x; d[i + 1] = t.y; d[i + 2] = t.z; d[i + 3] = t.w;
+    }
+#pragma unroll
+    for (int i = N & ~3; i < N; ++i) d[i] = *reinterpret_cast<const uint32_t *>(base + 4 * i);
+#pragma unroll
+    for (int i = 0; i < N - 1; ++i) v[i] = __builtin_amdgcn_alignbyte(d[i + 1], d[i], sh);
 }
 
 // fp16 bits of d (and m) of block b of the pair.
@@ -357,8 +386,9 @@ __device__ __forceinline__ float seg_sum(float v) {
 }
 __host__ __device__ constexpr int seg_store_lane(int lpr) { return lpr == 32 ? 31 : 0; }
 
-// FAST: for every problem, w 4-byte aligned, an even number of blocks per
-// row, x 16-byte aligned and ldx % 4 == 0.
+// FAST: for every problem, w 4-byte aligned and an even number of blocks per
+// row (activations need only their 4-byte alignment: they are read with
+// 16-byte loads at any 4-byte boundary).
 //
 // Lanes and rows.  A wave owns RPW = RWV << SUB rows of its row group: the
 // wave is cut into 2^SUB segments of LPR = 64 >> SUB lanes and segment q
@@ -530,10 +560,17 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         } else if (pp < npairs) {
             const int nrows = max(0, min(RWV, it.m - row0));
             const uint8_t *p = w + (int64_t)row0 * row_bytes + (int64_t)pp * (2 * BS);
+            const uint8_t *wend = w + (int64_t)it.m * row_bytes;
             const bool second = 2 * pp + 1 < it.nb;
 #pragma unroll
-            for (int r = 0; r < RWV; ++r)
-                if (r < nrows) load_pair_generic<FMT>(p + r * row_bytes, second, dst[r]);
+            for (int r = 0; r < RWV; ++r) {
+                if (r < nrows) {
+                    const uint8_t *pr = p + r * row_bytes;
+                    // whole dwords unless that would read past the matrix
+                    if (pr + kPairReach<FMT> <= wend) load_pair_shift<FMT>(pr, dst[r]);
+                    else load_pair_generic<FMT>(pr, second, dst[r]);
+                }
+            }
         }
     };
 
@@ -547,9 +584,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         for (int j = 0; j < NC; ++j) {
             const float *xj = it.x + j * it.ldx + e0;
             for (int t = tid; t < ce4; t += NT) {
-                f32x4_t val;
-                if (FAST) val = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
-                else val = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
+                const f32x4_t val = *reinterpret_cast<const f32x4_a4 *>(xj + 4 * t);
                 *reinterpret_cast<f32x4_t *>(xs + j * XP + 4 * t + (t >> 4) * 4) = val;
             }
         }
@@ -605,8 +640,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
                     // clamped so every lane loads (a tail lane repeats the last
                     // float4 and stores it again)
                     const int t = min(tid + u * NT, cr4 - 1);
-                    if (FAST) xr[j][u] = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
-                    else xr[j][u] = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
+                    xr[j][u] = *reinterpret_cast<const f32x4_a4 *>(xj + 4 * t);
                 }
             }
             load_step(P, cur);
@@ -625,9 +659,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
             for (int j = 0; j < NC; ++j) {
                 const float *xj = it.x + j * it.ldx + e0;
                 for (int t = (j < XR ? cr4 : 0) + tid; t < ce4; t += NT) {
-                    f32x4_t val;
-                    if (FAST) val = *reinterpret_cast<const f32x4_t *>(xj + 4 * t);
-                    else val = f32x4_t{xj[4 * t], xj[4 * t + 1], xj[4 * t + 2], xj[4 * t + 3]};
+                    const f32x4_t val = *reinterpret_cast<const f32x4_a4 *>(xj + 4 * t);
                     *reinterpret_cast<f32x4_t *>(xs + j * XP + 4 * t + (t >> 4) * 4) = val;
                 }
             }
@@ -704,10 +736,14 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
 #ifndef QK_GEMV_SHORT_WPG
 #define QK_GEMV_SHORT_WPG 4
 #endif
-template <int FMT, int NC, int SUB = 0> struct GemvShape {
-    static constexpr int kRWV = NC >= 4 && FMT != QK_Q8_0 ? 2 : 1;
-    static constexpr int kWPG = SUB > 0 ? QK_GEMV_SHORT_WPG
-                                        : (NC <= 4 ? 8 : (FMT == QK_Q4_1 ? 12 : (FMT == QK_Q4_0 ? 8 : 4)));
+// The generic (unaligned) Q4_1 kernels above 4 columns need more registers
+// than 12 waves leave (168): they take one row per wave in 8-wave workgroups.
+template <int FMT, int NC, int SUB, bool FAST> struct GemvShape {
+    static constexpr bool kWideQ41Generic = FMT == QK_Q4_1 && NC > 4 && !FAST;
+    static constexpr int kRWV = NC >= 4 && FMT != QK_Q8_0 && !kWideQ41Generic ? 2 : 1;
+    static constexpr int kWPG =
+        SUB > 0 ? QK_GEMV_SHORT_WPG
+                : (NC <= 4 ? 8 : (FMT == QK_Q4_1 ? (FAST ? 12 : 8) : (FMT == QK_Q4_0 ? 8 : 4)));
     static constexpr int kRowsPerGroup = kWPG * (kRWV << SUB);
 };
 
@@ -735,11 +771,10 @@ inline int device_cus() {
 }
 
 // One launch over `total` row groups (gpi per problem for expert launches).
-template <int FMT, int NC, int SRC, int SUB>
-int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi, bool fast,
-                hipStream_t stream) {
-    constexpr int RWV = GemvShape<FMT, NC, SUB>::kRWV;
-    constexpr int WPG = GemvShape<FMT, NC, SUB>::kWPG;
+template <int FMT, int NC, int SRC, int SUB, bool FAST>
+int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi, hipStream_t stream) {
+    constexpr int RWV = GemvShape<FMT, NC, SUB, FAST>::kRWV;
+    constexpr int WPG = GemvShape<FMT, NC, SUB, FAST>::kWPG;
     if (total <= 0) return QK_OK;
     if (total > INT32_MAX) return QK_ERR_INVALID_ARG;
     // Activation window: 4096 weights per column (17 KiB at one column).
@@ -751,20 +786,17 @@ int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi,
     const int64_t cap = (int64_t)device_cus() * per_cu;
     const int nwg = (int)(total < cap ? total : cap);
     const GemvSplit split{(int)total, (int)total / nwg, (int)total % nwg, gpi};
-    auto go = [&](auto kern) -> int {
-        if (lds > 64 * 1024 &&
-            hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-            return QK_ERR_LAUNCH;
-        return launch_lds(kern, dim3((unsigned)nwg), dim3(64 * WPG), lds, stream, args, split);
-    };
-    if (fast) return go(gemv_kernel<FMT, NC, RWV, WPG, true, SRC, SUB>);
-    return go(gemv_kernel<FMT, NC, RWV, WPG, false, SRC, SUB>);
+    auto kern = gemv_kernel<FMT, NC, RWV, WPG, FAST, SRC, SUB>;
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return QK_ERR_LAUNCH;
+    return launch_lds(kern, dim3((unsigned)nwg), dim3(64 * WPG), lds, stream, args, split);
 }
 
-template <int FMT, int NC, int SUB>
-int gemv_table_sub(GemvArgs &a, bool fast, hipStream_t stream) {
-    constexpr int RG = GemvShape<FMT, NC, SUB>::kRowsPerGroup;
+template <int FMT, int NC, int SUB, bool FAST>
+int gemv_table_run(GemvArgs &a, hipStream_t stream) {
+    constexpr int RG = GemvShape<FMT, NC, SUB, FAST>::kRowsPerGroup;
     int64_t g = 0;
     a.gbase[0] = 0;
     for (int i = 0; i < a.count; ++i) {
@@ -772,8 +804,14 @@ int gemv_table_sub(GemvArgs &a, bool fast, hipStream_t stream) {
         if (g > INT32_MAX) return QK_ERR_INVALID_ARG;
         a.gbase[i + 1] = (int)g;
     }
-    if (a.count == 1) return gemv_launch<FMT, NC, kSrcOne, SUB>(a.item[0], g, 0, fast, stream);
-    return gemv_launch<FMT, NC, kSrcTable, SUB>(a, g, 0, fast, stream);
+    if (a.count == 1) return gemv_launch<FMT, NC, kSrcOne, SUB, FAST>(a.item[0], g, 0, stream);
+    return gemv_launch<FMT, NC, kSrcTable, SUB, FAST>(a, g, 0, stream);
+}
+
+template <int FMT, int NC, int SUB>
+int gemv_table_sub(GemvArgs &a, bool fast, hipStream_t stream) {
+    if (fast) return gemv_table_run<FMT, NC, SUB, true>(a, stream);
+    return gemv_table_run<FMT, NC, SUB, false>(a, stream);
 }
 
 template <int FMT, int NC>
@@ -801,11 +839,17 @@ int gemv_table(int fmt, GemvArgs &a, bool fast, hipStream_t stream) {
     }
 }
 
+template <int FMT, int SUB, bool FAST>
+int gemv_expert_run(const GemvExpert &e, hipStream_t stream) {
+    constexpr int RG = GemvShape<FMT, 1, SUB, FAST>::kRowsPerGroup;
+    const int gpi = (e.m + RG - 1) / RG;
+    return gemv_launch<FMT, 1, kSrcExpert, SUB, FAST>(e, (int64_t)gpi * e.count, gpi, stream);
+}
+
 template <int FMT, int SUB>
 int gemv_expert_sub(const GemvExpert &e, bool fast, hipStream_t stream) {
-    constexpr int RG = GemvShape<FMT, 1, SUB>::kRowsPerGroup;
-    const int gpi = (e.m + RG - 1) / RG;
-    return gemv_launch<FMT, 1, kSrcExpert, SUB>(e, (int64_t)gpi * e.count, gpi, fast, stream);
+    if (fast) return gemv_expert_run<FMT, SUB, true>(e, stream);
+    return gemv_expert_run<FMT, SUB, false>(e, stream);
 }
 
 template <int FMT>
