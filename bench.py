@@ -384,11 +384,66 @@ def run_configs(torch, qk, synth, oracle, timer, steps, warmup):
         "TFLOPs": round(tf, 1), "pct_of_mfma_f16_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 1)}
     del wc, gw, gk
 
+    log("decode layer, one GPU's share of 8-way tensor parallelism")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    res["gemv_q4_0_decode_layer_tp8_share"] = run_share_layer(torch, qk, synth, oracle, timer, steps,
+                                                              warmup)
+
     log("expert-indexed decode")
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     res["gemv_q4_0_moe_experts"] = run_moe(torch, qk, synth, oracle, timer, steps, warmup)
     return res
+
+
+def run_share_layer(torch, qk, synth, oracle, timer, steps, warmup):
+    """One GPU's share of the decode layer under 8-way tensor parallelism (row
+    shards of q, k, v, gate, up; K shards of o and down): the GEMVs of one
+    token as one grouped launch and as separate launches.  The all-reduce of
+    the K-shard partial sums is not part of it (one GPU)."""
+    cfg = synth.WORKLOADS["gemv_q4_0_decode_layer_tp8_share"]
+    seed = synth.workload_seed(cfg["id"])
+    lib = qk.load()
+    probs, wtot = [], 0
+    for tid, (nm, m, k) in enumerate(cfg["layer"]):
+        p = setup_gemv(torch, qk, synth, oracle, "q4_0", m, k, 1, seed, tid, 100 + tid, cfg["d"])
+        p.update(m=m, k=k)
+        probs.append(p)
+        wtot += gemv_bytes("q4_0", m, k, 1)[0]
+    R = copies_for(wtot)
+    copies = [[p["wd"]] + [p["wd"].clone() for _ in range(R - 1)] for p in probs]
+    sets = [qk.make_items([(cps[r].data_ptr(), p["m"], p["k"], p["xd"].data_ptr(), p["k"],
+                            p["y"].data_ptr(), p["m"]) for p, cps in zip(probs, copies)])
+            for r in range(R)]
+
+    def grouped(i):
+        lib.qk_mul_mat_vec_batched(qk.QK_Q4_0, sets[i % R], len(probs), 1,
+                                   torch.cuda.current_stream().cuda_stream)
+
+    def separate(i):
+        s = torch.cuda.current_stream().cuda_stream
+        for p, cps in zip(probs, copies):
+            lib.qk_mul_mat_vec(qk.QK_Q4_0, cps[i % R].data_ptr(), p["m"], p["k"], p["xd"].data_ptr(),
+                               1, p["k"], p["y"].data_ptr(), p["m"], s)
+
+    grouped(0)
+    torch.cuda.synchronize()
+    ok = all(p["ok"] for p in probs)
+    for p in probs:
+        yr, sr = oracle.dot("q4_0", p["w"], p["m"], p["k"], p["x"], 1)
+        got = p["y"].cpu().numpy().astype(np.float64)
+        ok = ok and bool(np.all(np.abs(got - yr) <= 1e-4 * sr))
+    out = {"parity": "ok" if ok else "FAILED", "weight_bytes": wtot}
+    st = max(steps // 4, 20)
+    for name, fn in (("grouped_launch", grouped), ("separate_launches", separate)):
+        gw, gk = timer.capture(fn, warmup), timer.capture(lambda i: fn(i + warmup), st)
+        timer.time_graph(gw)
+        sec = timer.time_graph(gk) / st
+        del gw, gk
+        out[name] = {"us_per_layer": round(sec * 1e6, 3), "weight_GBps": round(wtot / sec / 1e9, 1),
+                     "pct_of_hbm_peak": round(100 * wtot / sec / 1e9 / HBM_PEAK_GBPS, 1)}
+    return out
 
 
 def run_moe(torch, qk, synth, oracle, timer, steps, warmup):

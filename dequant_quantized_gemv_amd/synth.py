@@ -183,6 +183,14 @@ LAYER_SHAPES = [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096),
                 ("o", 4096, 4096), ("gate", 11008, 4096), ("up", 11008, 4096),
                 ("down", 4096, 11008)]
 
+# one GPU's share of that layer under 8-way tensor parallelism: q, k, v, gate
+# and up split by output rows, o and down by K (partial sums, to be added
+# across the 8 GPUs); every shard boundary falls on a block
+TP = 8
+LAYER_SHARE_SHAPES = [("q", 512, 4096), ("k", 512, 4096), ("v", 512, 4096),
+                      ("o", 4096, 512), ("gate", 1376, 4096), ("up", 1376, 4096),
+                      ("down", 4096, 1376)]
+
 # mixture-of-experts decode: expert matrices of intermediate width 768 (the
 # Q4_0 expert model the PR's commit list names) over a hidden width of 2048,
 # 128 experts, 8 used per token: gate and up 768 x 2048, down 2048 x 768
@@ -195,6 +203,8 @@ WORKLOADS = {
                                  d=D_Q4, mr=M_Q4_1),
     "gemv_q4_0_decode_layer": dict(id=3, fmt="q4_0", layer=LAYER_SHAPES, n=1, d=D_Q4),
     "gemm_q4_0_14336x4096_n512": dict(id=4, fmt="q4_0", m=14336, k=4096, n=512, d=D_Q4),
+    "gemv_q4_0_decode_layer_tp8_share": dict(id=6, fmt="q4_0", layer=LAYER_SHARE_SHAPES, tp=TP, n=1,
+                                             d=D_Q4),
     "gemv_q4_0_moe_experts": dict(id=5, fmt="q4_0", layer=MOE_SHAPES, n_experts=128, n_used=8,
                                   n_tokens=1, d=D_Q4),
 }
