@@ -60,6 +60,12 @@ def _load():
     lib.orc_dot_id.argtypes = [ctypes.c_int, vp, i64, i64, i64, i64, vp, i64, i64, i64,
                                vp, i64, i64, vp, vp]
     lib.orc_dot_id.restype = None
+    lib.orc_quantize_x8_block.argtypes = [vp, vp]
+    lib.orc_quantize_x8_block.restype = ctypes.c_float
+    lib.orc_quantize_x8.argtypes = [vp, i64, i64, i64, vp, vp]
+    lib.orc_quantize_x8.restype = None
+    lib.orc_dot_x8.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, i64, vp, vp]
+    lib.orc_dot_x8.restype = None
     _lib = lib
     return lib
 
@@ -211,3 +217,29 @@ def dot_id(fmt, w, n_experts, expert_stride, m, k, ids, n_used, n_tokens, x,
     _load().orc_dot_id(_fmt(fmt), _ptr(w), n_experts, expert_stride, m, k, _ptr(ids), ld_ids,
                        n_used, n_tokens, _ptr(x), x_slot, x_tok, _ptr(y), _ptr(s))
     return y.reshape(n_tokens, n_used, m), s.reshape(n_tokens, n_used, m)
+
+
+def quantize_x8(x, k, n, ldx=None):
+    """8-bit activation codes with power-of-two block scales.
+
+    Returns (q, d): q int8 of shape (n, k), d float32 of shape (n, k/32)."""
+    ldx = k if ldx is None else ldx
+    if k % 32 != 0:
+        raise ValueError("k must be a multiple of 32")
+    x = _check_x(x, k, n, ldx, False)
+    q = np.empty(n * k, dtype=np.int8)
+    d = np.empty(n * (k // 32), dtype=np.float32)
+    _load().orc_quantize_x8(_ptr(x), k, n, ldx, _ptr(q), _ptr(d))
+    return q.reshape(n, k), d.reshape(n, k // 32)
+
+
+def dot_x8(fmt, w, m, k, x, n, ldx=None):
+    """Products with the 8-bit-quantized activations (fp64) and their
+    tolerance scale; returns (y, s), each of shape (n, m)."""
+    ldx = k if ldx is None else ldx
+    w = _check_w(fmt, w, m, k)
+    x = _check_x(x, k, n, ldx, False)
+    y = np.empty(n * m, dtype=np.float64)
+    s = np.empty(n * m, dtype=np.float64)
+    _load().orc_dot_x8(_fmt(fmt), _ptr(w), m, k, _ptr(x), n, ldx, _ptr(y), _ptr(s))
+    return y.reshape(n, m), s.reshape(n, m)

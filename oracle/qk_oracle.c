@@ -271,3 +271,88 @@ void orc_dot_id(int fmt, const uint8_t *w, int64_t n_experts, int64_t expert_str
         }
     }
 }
+
+/* ---------------------------------------------------------------------
+ * Products with 8-bit activations (integer dot products).
+ *
+ * The gem diff names the integer-dot kernels (mul_mat_vec_q / MMQ, fed by a
+ * quantize_q8_1 step) but prints neither their activation layout nor their
+ * rounding.  Reading taken here (this build's own design, stated as such):
+ * each 32-element block of an activation column is quantized with a
+ * power-of-two scale d = 2^e, e the smallest integer with 127 * 2^e >= amax
+ * (amax = max |x| over the block), but at least -126; the codes are
+ * q = round-half-even(x / d), so |q| <= 127 and every decision is exact (a
+ * division by a power of two rounds nothing).  An all-zero block has d = 0
+ * and q = 0.  The product then uses the dequantized activation x^ = d * q.
+ * ------------------------------------------------------------------- */
+
+/* Quantize one block of 32 fp32 values: codes q[32], returns d. */
+float orc_quantize_x8_block(const float *x, int8_t *q)
+{
+    double amax = 0.0;
+    for (int t = 0; t < 32; ++t) {
+        const double a = fabs((double)x[t]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0) {
+        for (int t = 0; t < 32; ++t) q[t] = 0;
+        return 0.0f;
+    }
+    int e = -126;
+    while (127.0 * ldexp(1.0, e) < amax) ++e;   /* smallest e >= -126 */
+    const double d = ldexp(1.0, e);
+    for (int t = 0; t < 32; ++t) {
+        const double v = (double)x[t] / d;       /* exact: d is a power of two */
+        double r = floor(v);
+        const double frac = v - r;
+        if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+        q[t] = (int8_t)r;
+    }
+    return (float)d;
+}
+
+/* Quantize n columns of length k (stride ldx): codes qx[j*k + c] and scales
+ * dx[j*(k/32) + b]. */
+void orc_quantize_x8(const float *x, int64_t k, int64_t n, int64_t ldx, int8_t *qx, float *dx)
+{
+    for (int64_t j = 0; j < n; ++j)
+        for (int64_t b = 0; b < k / 32; ++b)
+            dx[j * (k / 32) + b] = orc_quantize_x8_block(x + j * ldx + 32 * b, qx + j * k + 32 * b);
+}
+
+/* y[j*m + i] = sum_c W[i,c] * x^[j][c] in fp64 (x^ = d * q as above), and
+ * the tolerance scale s[j*m + i]: the sum over blocks of |d_x * d * I| for
+ * Q4_0 / Q8_0 and |d_x * d * I| + |d_x * m * Q| for Q4_1, where I is the
+ * block's integer dot product of codes (Q4_0 codes taken as q - 8) and Q the
+ * sum of the activation codes: the magnitudes of the terms a kernel rounds. */
+void orc_dot_x8(int fmt, const uint8_t *w, int64_t m, int64_t k, const float *x, int64_t n,
+                int64_t ldx, double *y, double *s)
+{
+    const int64_t nb = k / 32;
+    const int64_t bs = orc_block_bytes(fmt);
+    int8_t q[32];
+    for (int64_t j = 0; j < n; ++j) {
+        for (int64_t i = 0; i < m; ++i) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                const float dx = orc_quantize_x8_block(x + j * ldx + 32 * b, q);
+                const uint8_t *blk = w + (i * nb + b) * bs;
+                const double dw = (double)orc_half_to_float(orc_le16(blk));
+                double isum = 0.0, qsum = 0.0;
+                for (int t = 0; t < 32; ++t) {
+                    int c = orc_code(fmt, blk, t);
+                    if (fmt == ORC_Q4_0) c -= 8;
+                    isum += (double)c * (double)q[t];
+                    qsum += (double)q[t];
+                    /* the plain product with the dequantized activation */
+                    acc += (double)orc_value(fmt, blk, t) * ((double)dx * (double)q[t]);
+                }
+                mag += fabs((double)dx * dw * isum);
+                if (fmt == ORC_Q4_1)
+                    mag += fabs((double)dx * (double)orc_half_to_float(orc_le16(blk + 2)) * qsum);
+            }
+            y[j * m + i] = acc;
+            s[j * m + i] = mag;
+        }
+    }
+}

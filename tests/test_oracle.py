@@ -418,3 +418,95 @@ def test_expert_index_mistakes_are_caught():
     y_b, _ = oracle.dot_id("q4_0", w, 3, stride, m, k, ids, 2, 2, x, 0, 2 * k)
     assert not np.array_equal(y_t, want)
     assert not np.array_equal(y_b, want)
+
+
+# ---------------------------------------------------------------------------
+# 8-bit activations (integer-dot products)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("blk", _golden()["x8_blocks"], ids=lambda b: b["name"])
+def test_x8_hand_worked_blocks(blk):
+    x = np.array([np.float32(v) for v in blk["x"]], dtype=np.float32)
+    q, d = oracle.quantize_x8(x, 32, 1)
+    assert d[0, 0] == float(Fraction(blk["d"]))
+    assert list(q[0]) == blk["q"]
+
+
+def test_x8_rule_invariants():
+    """On random columns of widely varying magnitude: d is zero or a power of
+    two, the smallest (down to 2^-126) with 127 d >= max|x|; |q| <= 127 and
+    q is x / d rounded half to even (so |x - d q| <= d / 2)."""
+    rng = np.random.default_rng(5)
+    k, n = 32 * 64, 3
+    x = (rng.standard_normal((n, k)) * np.exp2(rng.integers(-30, 30, (n, k // 32)).repeat(32, 1)))
+    x = x.astype(np.float32)
+    x[1, 32:64] = 0.0
+    x[2, 64:96] = np.float32(1e-40)          # fp32 subnormals
+    q, d = oracle.quantize_x8(x, k, n)
+    for j in range(n):
+        for b in range(k // 32):
+            xb = x[j, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.abs(xb).max()
+            db = float(d[j, b])
+            if amax == 0:
+                assert db == 0 and not q[j, 32 * b:32 * b + 32].any()
+                continue
+            m, e = np.frexp(db)
+            assert m == 0.5
+            assert 127 * db >= amax and (db == 2.0 ** -126 or 127 * db / 2 < amax)
+            qb = q[j, 32 * b:32 * b + 32].astype(np.float64)
+            assert np.all(np.abs(qb) <= 127)
+            assert np.array_equal(qb, np.rint(xb / db))   # numpy's rint: half to even
+
+
+def test_x8_hand_worked_dots():
+    g = _golden()
+    dots = {c["name"]: c for c in g["dots"]}
+    byname = {b["name"]: b for b in g["blocks"]}
+    for case in g["x8_dots"]:
+        base = dots[case["dot"]]
+        fmt, m, k = base["fmt"], base["m"], base["k"]
+        if "rows_hex" in base:
+            w = np.concatenate([_hex_bytes(r) for r in base["rows_hex"]])
+        else:
+            w = np.concatenate([_hex_bytes(byname[b]["bytes_hex"]) for b in base["blocks"]])
+        t = np.arange(k)
+        x = {"t+1": t + 1.0, "(t mod 7) - 3": (t % 7) - 3.0}[base["x_rule"]].astype(np.float32)
+        y, s = oracle.dot_x8(fmt, w, m, k, x, 1)
+        assert list(y[0]) == [float(Fraction(v)) for v in case["y"]]
+        if "s" in case:
+            assert list(s[0]) == [float(Fraction(v)) for v in case["s"]]
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+def test_x8_dot_is_the_product_with_quantized_activations(fmt):
+    """dot_x8 equals the plain product with x^ = d * q (a different route
+    through the oracle: the fp64 product of dequantized weights and
+    activations), and its scale bounds the result."""
+    m, k, n = 7, 160, 3
+    w = synth.quant_matrix(fmt, m, k, seed=8, tensor_id=1, d_range=(1e-3, 2e-2))
+    x = synth.activations(k, n, seed=8, tensor_id=2)
+    q, d = oracle.quantize_x8(x, k, n)
+    xh = (q.astype(np.float64).reshape(n, k // 32, 32) * d.astype(np.float64)[:, :, None]).reshape(n, k)
+    wf = oracle.dequantize_f32(fmt, w, m, k).astype(np.float64)
+    y, s = oracle.dot_x8(fmt, w, m, k, x, n)
+    assert np.allclose(y, xh @ wf.T, rtol=0, atol=1e-12)
+    assert np.all(np.abs(y) <= s * (1 + 1e-12))
+    # and the quantization error against the unquantized product stays within
+    # sum_c |W| * d / 2 per element
+    ye, _ = oracle.dot(fmt, w, m, k, x, n)
+    half = np.repeat(d.astype(np.float64) / 2, 32, axis=1)
+    assert np.all(np.abs(y - ye) <= (np.abs(wf) @ half.T).T + 1e-12)
+
+
+def test_x8_rounding_mistakes_are_caught():
+    """Planted mistakes (on the CPU): rounding half away from zero, or a scale
+    of max|x| / 127 instead of a power of two, change the hand-worked codes."""
+    blk = _golden()["x8_blocks"][0]
+    x = np.array([np.float32(v) for v in blk["x"]], dtype=np.float64)
+    away = np.sign(x) * np.floor(np.abs(x) + 0.5)
+    assert list(away.astype(int)) != blk["q"]
+    b2 = _golden()["x8_blocks"][1]
+    x2 = np.array([np.float32(v) for v in b2["x"]], dtype=np.float64)
+    plain = np.rint(x2 / (np.abs(x2).max() / 127))
+    assert list(plain.astype(int)) != b2["q"]
