@@ -142,6 +142,8 @@ def setup_gemv(torch, qk, synth, oracle, fmt, m, k, n, seed, wtid, xtid, d, mr=N
     qk.mul_mat_vec(fmt, wd, m, k, xd, y=y)
     torch.cuda.synchronize()
     yh = y.cpu().numpy().astype(np.float64)
+    if check == "none":
+        return dict(w=w, x=x, wd=wd, xd=xd, y=y, ok=True, worst=0.0)
     if check == "full":
         yr, s = oracle.dot(fmt, w, m, k, x, n)
         ok = bool(np.all(np.abs(yh - yr) <= 1e-4 * s))
@@ -163,7 +165,7 @@ def gemv_bytes(fmt, m, k, n):
     return wb, wb + 4 * n * (k + m)
 
 
-def bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup):
+def bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup, entry="qk_mul_mat_vec"):
     wb, algo = gemv_bytes(fmt, m, k, n)
     R = copies_for(wb)
     copies = [prob["wd"]] + [prob["wd"].clone() for _ in range(R - 1)]
@@ -173,11 +175,12 @@ def bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup):
     ptrs = [c.data_ptr() for c in copies]
     xp, yp = xd.data_ptr(), y.data_ptr()
 
+    call = getattr(lib, entry)
+
     def launch(i):
-        st = lib.qk_mul_mat_vec(code, ptrs[i % R], m, k, xp, n, k, yp, m,
-                                torch.cuda.current_stream().cuda_stream)
+        st = call(code, ptrs[i % R], m, k, xp, n, k, yp, m, torch.cuda.current_stream().cuda_stream)
         if st != 0:
-            raise RuntimeError(f"qk_mul_mat_vec: {qk.status_string(st)}")
+            raise RuntimeError(f"{entry}: {qk.status_string(st)}")
 
     gw = timer.capture(launch, max(warmup, 1))
     gk = timer.capture(lambda i: launch(i + warmup), steps)
@@ -290,6 +293,29 @@ def run_configs(torch, qk, synth, oracle, timer, steps, warmup):
                 "us_per_launch": round(r["per_launch_s"] * 1e6, 3),
                 "weight_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
             del prob
+
+    # C2 again with 8-bit activations (qk_mul_mat_vec_x8), checked against the
+    # oracle's product with the same quantized activations
+    cfg = synth.WORKLOADS["gemv_q4_1_11008x4096"]
+    seed = synth.workload_seed(cfg["id"])
+    for n in (1, 2, 4, 8):
+        prob = setup_gemv(torch, qk, synth, oracle, "q4_1", cfg["m"], cfg["k"], n, seed, 0, 100,
+                          cfg["d"], cfg.get("mr"), check="none")
+        y8 = qk.mul_mat_vec_x8("q4_1", prob["wd"], cfg["m"], cfg["k"], prob["xd"])
+        torch.cuda.synchronize()
+        rows = np.sort(np.random.default_rng(n).choice(cfg["m"], 128, replace=False))
+        rb = (cfg["k"] // 32) * 20
+        wsub = np.concatenate([prob["w"][r * rb:(r + 1) * rb] for r in rows])
+        yr, sr = oracle.dot_x8("q4_1", wsub, len(rows), cfg["k"], prob["x"], n)
+        got = y8.cpu().numpy()[:, rows].astype(np.float64)
+        ok8 = bool(np.all(np.abs(got - yr) <= 1e-4 * sr))
+        r = bench_gemv(torch, qk, timer, prob, "q4_1", cfg["m"], cfg["k"], n, steps, warmup,
+                       entry="qk_mul_mat_vec_x8")
+        gbps = r["weight_bytes"] / r["per_launch_s"] / 1e9
+        res[f"gemv_q4_1_11008x4096_x8_n{n}"] = {
+            "parity": "ok" if ok8 else "FAILED", "us_per_launch": round(r["per_launch_s"] * 1e6, 3),
+            "weight_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
+        del prob
 
     # C3: the decode layer, 7 GEMVs per step (from a clean allocator: weight
     # copies carved out of the previous workloads' freed blocks measured

@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqk.so")
 SOURCES = ["api.hip", "dequant.hip", "gemv.hip", "gemv_n1.hip", "gemv_n2.hip", "gemv_n34.hip",
-           "gemv_n56.hip", "gemv_n78.hip", "gemv_id.hip", "gemm.hip"]
+           "gemv_n56.hip", "gemv_n78.hip", "gemv_id.hip", "gemv_x8_n1.hip", "gemv_x8_n24.hip",
+           "gemv_x8_n58.hip", "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -99,6 +99,17 @@ int qk_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k, const float *x,
     return qk::launch_mul_mat_vec(fmt, w, m, k, x, n, ldx, y, ldy, static_cast<hipStream_t>(stream));
 }
 
+int qk_mul_mat_vec_x8(int fmt, const void *w, int64_t m, int64_t k, const float *x, int64_t n,
+                      int64_t ldx, float *y, int64_t ldy, void *stream) {
+    if (!fmt_ok(fmt)) return QK_ERR_UNSUPPORTED;
+    if (m < 0 || k < 0 || k % 32 != 0 || n < 0 || n > 8) return QK_ERR_INVALID_ARG;
+    if (m == 0 || n == 0) return QK_OK;
+    const qk_mat_vec_item it{w, m, k, x, ldx, y, ldy};
+    const int st = check_gemv_item(fmt, it, n);
+    if (st != QK_OK) return st;
+    return qk::launch_mul_mat_vec_x8(fmt, w, m, k, x, n, ldx, y, ldy, static_cast<hipStream_t>(stream));
+}
+
 int qk_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count, int64_t n,
                            void *stream) {
     if (!fmt_ok(fmt)) return QK_ERR_UNSUPPORTED;

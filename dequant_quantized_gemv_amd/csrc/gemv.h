@@ -59,6 +59,10 @@ struct GemvExpert {
 template <int NC>
 int gemv_table(int fmt, GemvArgs &a, bool fast, hipStream_t stream);
 
+// The same with 8-bit activations (integer dot products); one problem only.
+template <int NC>
+int gemv_table_x8(int fmt, GemvArgs &a, bool fast, hipStream_t stream);
+
 // Launch expert-indexed problems (same `fast` condition, for every expert and
 // slot).
 int gemv_expert(int fmt, const GemvExpert &e, bool fast, hipStream_t stream);

@@ -94,6 +94,42 @@ int launch_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count,
     return gemv_by_columns(fmt, a, (int)n, fast, stream);
 }
 
+int launch_mul_mat_vec_x8(int fmt, const void *w, int64_t m, int64_t k, const float *x,
+                          int64_t n, int64_t ldx, float *y, int64_t ldy, hipStream_t stream) {
+    if (k == 0) {
+        // no weights: every output is the empty sum
+        GemvExpert z{};
+        z.y = y;
+        z.y_slot = ldy;
+        z.m = (int)m;
+        z.n_used = (int)n;
+        z.count = (int)n;
+        return launch_empty(z, stream);
+    }
+    GemvArgs a{};
+    GemvItem &d = a.item[0];
+    d.w = static_cast<const uint8_t *>(w);
+    d.x = x;
+    d.y = y;
+    d.ldx = ldx;
+    d.ldy = ldy;
+    d.m = (int)m;
+    d.nb = (int)(k / kBlockElems);
+    a.count = 1;
+    const bool fast = ((uintptr_t)d.w % 4) == 0 && (d.nb % 2) == 0;
+    switch (n) {
+    case 1: return gemv_table_x8<1>(fmt, a, fast, stream);
+    case 2: return gemv_table_x8<2>(fmt, a, fast, stream);
+    case 3: return gemv_table_x8<3>(fmt, a, fast, stream);
+    case 4: return gemv_table_x8<4>(fmt, a, fast, stream);
+    case 5: return gemv_table_x8<5>(fmt, a, fast, stream);
+    case 6: return gemv_table_x8<6>(fmt, a, fast, stream);
+    case 7: return gemv_table_x8<7>(fmt, a, fast, stream);
+    case 8: return gemv_table_x8<8>(fmt, a, fast, stream);
+    default: return QK_ERR_INVALID_ARG;
+    }
+}
+
 int launch_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k, const float *x,
                        int64_t n, int64_t ldx, float *y, int64_t ldy, hipStream_t stream) {
     qk_mat_vec_item item{w, m, k, x, ldx, y, ldy};

@@ -357,6 +357,109 @@ __device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDw
 constexpr int kGvWindow = kGvChunkElems;
 constexpr int kGvPitch = kGvWindow + kGvWindow / 16;
 
+// 8-bit activations in LDS, per column: the codes of pair p of the window at
+// byte 80p (64 bytes and 16 of padding, so the 16-byte reads of eight lanes
+// cover all 32 banks), then 8 bytes per block: (scale, sum of the codes).
+constexpr int kX8PairPitch = 80;
+constexpr int kX8ScaleOff = kGvChunkPairs * kX8PairPitch;
+constexpr int kX8ColBytes = kX8ScaleOff + 8 * 2 * kGvChunkPairs;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Quantize one block of 32 activations (v) to 8-bit codes with a power-of-two
+// scale d = 2^e, e the smallest integer >= -126 with 127 * 2^e >= max|x|, and
+// q = x / d rounded half to even (exact decisions: the division by a power of
+// two rounds nothing).  Writes the 32 codes to `codes` (16-byte aligned LDS)
+// and (d, sum of the codes) to `scale`.  An all-zero block has d = 0.
+__device__ __forceinline__ void x8_block(const f32x4_t (&v)[8], uint8_t *codes, uint8_t *scale) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        amax = fmaxf(fmaxf(fmaxf(amax, fabsf(v[i].x)), fmaxf(fabsf(v[i].y), fabsf(v[i].z))), fabsf(v[i].w));
+    int ex;
+    const float mant = frexpf(amax, &ex);  // amax = mant * 2^ex, mant in [0.5, 1)
+    // 127 * 2^(ex-7) >= amax  <=>  mant <= 127/128
+    const int e = max(ex - 7 + (mant > 0.9921875f ? 1 : 0), -126);
+    const float inv = ldexpf(1.0f, -e);  // exact: 2^-e (e <= 121 here, so inv >= 2^-121)
+    // x * 2^-e is exact with |.| <= 127; adding 1.5 * 2^23 rounds it to an
+    // integer half to even (one ulp is 1 there), and the low byte of the
+    // sum's bits is that integer in two's complement
+    constexpr float kMagic = 12582912.0f;
+    auto code = [&](float x) -> uint32_t { return __builtin_bit_cast(uint32_t, x * inv + kMagic); };
+    uint32_t wd[8];
+    int qsum = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = __builtin_amdgcn_perm(code(v[i].y), code(v[i].x), 0x0c0c0400u);  // [q0, q1, 0, 0]
+        const uint32_t hi = __builtin_amdgcn_perm(code(v[i].w), code(v[i].z), 0x04000c0cu);  // [0, 0, q2, q3]
+        wd[i] = lo | hi;
+        qsum = __builtin_amdgcn_sdot4((int)wd[i], 0x01010101, qsum, false);
+    }
+    *reinterpret_cast<u32x4_t *>(codes) = u32x4_t{wd[0], wd[1], wd[2], wd[3]};
+    *reinterpret_cast<u32x4_t *>(codes + 16) = u32x4_t{wd[4], wd[5], wd[6], wd[7]};
+    const float d = amax == 0.0f ? 0.0f : ldexpf(1.0f, e);
+    *reinterpret_cast<u32x2_t *>(scale) = u32x2_t{__builtin_bit_cast(uint32_t, d), (uint32_t)qsum};
+}
+
+// Integer-dot products of one wave's RWV rows with this lane's pair (pair pw
+// of the window) against 8-bit activations, added to acc: per block and
+// column, eight 4-way int8 dot products (exact), then one scaled add,
+// d_w * d_x * I (Q4_0: codes taken as q - 8 through the code sum), and for
+// Q4_1 also m_w * d_x * (sum of the activation codes).
+template <int FMT, int NC, int RWV, bool FAST>
+__device__ __forceinline__ void pair_dot_x8(const uint32_t (&v)[RWV][Pair<FMT>::kDwords], int nrows,
+                                            bool second, const uint8_t *xq, int pw,
+                                            float (&acc)[RWV][NC]) {
+    constexpr int NW = FMT == QK_Q8_0 ? 8 : 4;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        if (!FAST && b == 1 && !second) break;
+        uint32_t wq[RWV][8];
+        float dw[RWV], mw[RWV];
+#pragma unroll
+        for (int r = 0; r < RWV; ++r) {
+            dw[r] = h2f(pair_d<FMT>(v[r], b));
+            if constexpr (FMT == QK_Q4_1) mw[r] = h2f(pair_m_q41(v[r], b));
+            else mw[r] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                const uint32_t qw = pair_qs<FMT>(v[r], b, i);
+                if constexpr (FMT == QK_Q8_0) {
+                    wq[r][i] = qw;
+                } else {
+                    wq[r][i] = qw & 0x0F0F0F0Fu;             // elements 4i..4i+3
+                    wq[r][4 + i] = (qw >> 4) & 0x0F0F0F0Fu;  // elements 16+4i..16+4i+3
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const uint8_t *c = xq + j * kX8ColBytes + kX8PairPitch * pw + 32 * b;
+            const u32x4_t c0 = *reinterpret_cast<const u32x4_t *>(c);
+            const u32x4_t c1 = *reinterpret_cast<const u32x4_t *>(c + 16);
+            const u32x2_t sc = *reinterpret_cast<const u32x2_t *>(xq + j * kX8ColBytes + kX8ScaleOff +
+                                                                  8 * (2 * pw + b));
+            const uint32_t xc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const float dx = __builtin_bit_cast(float, sc.x);
+            const int qs = (int)sc.y;
+#pragma unroll
+            for (int r = 0; r < RWV; ++r) {
+                if (FAST || r < nrows) {  // fast path: rows clamped, stores guarded
+                    int isum = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        isum = __builtin_amdgcn_sdot4((int)wq[r][i], (int)xc[i], isum, false);
+                    if constexpr (FMT == QK_Q4_0) isum -= 8 * qs;
+                    acc[r][j] += (float)isum * (dw[r] * dx);
+                    if constexpr (FMT == QK_Q4_1) acc[r][j] += (float)qs * (mw[r] * dx);
+                }
+            }
+            if constexpr (NC >= 3) asm volatile("" ::: "memory");
+        }
+    }
+}
+
 // Where a launch's problems come from.
 enum GemvSource {
     kSrcOne = 0,     // one problem, passed in its own argument
@@ -407,7 +510,7 @@ __host__ __device__ constexpr int seg_store_lane(int lpr) { return lpr == 32 ? 3
 // offsets and no indexed reads of a table before the first weight load;
 // kSrcExpert reads each problem's expert id from device memory when a step
 // enters the problem (an id outside the stack reads expert 0 and stores NaN).
-template <int FMT, int NC, int RWV, int WPG, bool FAST, int SRC, int SUB>
+template <int FMT, int NC, int RWV, int WPG, bool FAST, int SRC, int SUB, bool X8>
 __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 1 || (NC == 2 && FMT != QK_Q8_0) ? 4 : (NC == 2 ? 2 : 1)))) void gemv_kernel(const typename GemvSrc<SRC>::Args args, const GemvSplit split) {
     static_assert(SUB == 0 || RWV == 1, "several rows per wave only with one row per segment");
     static_assert(SRC != kSrcExpert || NC == 1, "expert-indexed problems have one column");
@@ -428,6 +531,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
     int cpw_log = SUB;
     asm volatile("" : "+s"(cpw_log));
     extern __shared__ __attribute__((aligned(16))) float xs[];
+    uint8_t *const xq = reinterpret_cast<uint8_t *>(xs);  // 8-bit activations (X8)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -576,9 +680,35 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
 
     constexpr int XR = NC <= 2 ? NC : 0;  // columns staged through registers (first window)
 
+    // 8-bit activations: block bi of the window (columns one after another,
+    // nblk blocks each) is read from x and quantized into LDS.
+    auto x8_src = [&](const GemvItem &it, int e0, int nblk, int bi) -> const float * {
+        const int j = bi / nblk;
+        return it.x + j * it.ldx + e0 + 32 * (bi - j * nblk);
+    };
+    auto x8_load = [&](const float *src, f32x4_t (&v)[8]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const f32x4_a4 *>(src + 4 * i);
+    };
+    auto x8_put = [&](int nblk, int bi, const f32x4_t (&v)[8]) __attribute__((always_inline)) {
+        const int j = bi / nblk;
+        const int bb = bi - j * nblk;
+        uint8_t *col = xq + j * kX8ColBytes;
+        x8_block(v, col + kX8PairPitch * (bb >> 1) + 32 * (bb & 1), col + kX8ScaleOff + 8 * bb);
+    };
+
     // Copy window `wi` of problem `it`'s activations into LDS (whole workgroup).
     auto stage_x = [&](const GemvItem &it, int wi) __attribute__((always_inline)) {
         const int e0 = wi * XW;
+        if constexpr (X8) {
+            const int nblk = min(XW, it.nb * 32 - e0) / 32;
+            for (int bi = tid; bi < NC * nblk; bi += NT) {
+                f32x4_t v[8];
+                x8_load(x8_src(it, e0, nblk, bi), v);
+                x8_put(nblk, bi, v);
+            }
+            return;
+        }
         const int ce4 = min(XW, it.nb * 32 - e0) / 4;  // float4s in this window
 #pragma unroll
         for (int j = 0; j < NC; ++j) {
@@ -624,7 +754,28 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         const Pos Q = advance(P);
         const Pos PF = Q.g < gend ? Q : P;
 
-        if constexpr (FIRST) {
+        if constexpr (FIRST && X8) {
+            // one block of activations per thread loaded first, then the
+            // weights, then quantization into LDS (waits only for the
+            // activations); a tail thread repeats the last block
+            const int e0 = wi * XW;
+            const int nblk = min(XW, it.nb * 32 - e0) / 32;
+            const int tb = NC * nblk;
+            const int b0 = min(tid, tb - 1);
+            f32x4_t xr8[8];
+            x8_load(x8_src(it, e0, nblk, b0), xr8);
+            load_step(P, cur);
+            if constexpr (PREFETCH) load_step(PF, nxt);
+            x8_put(nblk, b0, xr8);
+            for (int bi = tid + NT; bi < tb; bi += NT) {
+                f32x4_t v[8];
+                x8_load(x8_src(it, e0, nblk, bi), v);
+                x8_put(nblk, bi, v);
+            }
+            __syncthreads();
+            staged_mi = P.mi;
+            staged_w = wi;
+        } else if constexpr (FIRST) {
             // activation loads, then this step's and the next step's weights,
             // then the LDS copy (waits only for the activations)
             constexpr int XU = (XW / 4 + NT - 1) / NT;  // registers cover the first window
@@ -682,9 +833,13 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         const int row0 = (P.g - P.gb0) * RG + wave * RPW + seg * RWV;
         const int nrows = max(0, min(RWV, it.m - row0));
         const int pp = P.c * CP + sl;
-        if (nrows > 0 && pp < npairs)
-            pair_dot<FMT, NC, RWV, FAST>(cur, nrows, FAST || (2 * pp + 1 < it.nb), xs, XP,
-                                         (P.c - (wi << cpw_log)) * CE + sl * 64, acc);
+        if (nrows > 0 && pp < npairs) {
+            const int el = (P.c - (wi << cpw_log)) * CE + sl * 64;  // window element of the pair
+            if constexpr (X8)
+                pair_dot_x8<FMT, NC, RWV, FAST>(cur, nrows, FAST || (2 * pp + 1 < it.nb), xq, el >> 6, acc);
+            else
+                pair_dot<FMT, NC, RWV, FAST>(cur, nrows, FAST || (2 * pp + 1 < it.nb), xs, XP, el, acc);
+        }
 
         // last chunk of the group: reduce across the row's lanes and store
         if (P.c == P.nchunks - 1) {
@@ -761,6 +916,13 @@ inline int gemv_sub(int npairs) {
 #define QK_GEMV_WG_PER_CU 8
 #endif
 constexpr int kGvMaxWgPerCu = QK_GEMV_WG_PER_CU;
+// With 8-bit activations every workgroup quantizes the whole activation
+// window it stages, so fewer workgroups, each walking more row groups, share
+// that work.
+#ifndef QK_GEMV_X8_WG_PER_CU
+#define QK_GEMV_X8_WG_PER_CU 1
+#endif
+constexpr int kGvX8MaxWgPerCu = QK_GEMV_X8_WG_PER_CU;
 
 inline int device_cus() {
     int cus = 256, dev = 0, v = 0;
@@ -771,7 +933,7 @@ inline int device_cus() {
 }
 
 // One launch over `total` row groups (gpi per problem for expert launches).
-template <int FMT, int NC, int SRC, int SUB, bool FAST>
+template <int FMT, int NC, int SRC, int SUB, bool FAST, bool X8>
 int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi, hipStream_t stream) {
     constexpr int RWV = GemvShape<FMT, NC, SUB, FAST>::kRWV;
     constexpr int WPG = GemvShape<FMT, NC, SUB, FAST>::kWPG;
@@ -781,12 +943,13 @@ int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi,
     // Longer rows restage it per window; the small window lets more
     // workgroups share a CU, which measured faster than holding whole rows of
     // 11008 weights.
-    const size_t lds = (size_t)NC * kGvPitch * sizeof(float);
-    const int per_cu = max(1, min(kGvMaxWgPerCu, (int)((160 * 1024) / lds)));
+    // (8-bit activations: 6 KiB per column)
+    const size_t lds = X8 ? (size_t)NC * kX8ColBytes : (size_t)NC * kGvPitch * sizeof(float);
+    const int per_cu = max(1, min(X8 ? kGvX8MaxWgPerCu : kGvMaxWgPerCu, (int)((160 * 1024) / lds)));
     const int64_t cap = (int64_t)device_cus() * per_cu;
     const int nwg = (int)(total < cap ? total : cap);
     const GemvSplit split{(int)total, (int)total / nwg, (int)total % nwg, gpi};
-    auto kern = gemv_kernel<FMT, NC, RWV, WPG, FAST, SRC, SUB>;
+    auto kern = gemv_kernel<FMT, NC, RWV, WPG, FAST, SRC, SUB, X8>;
     if (lds > 64 * 1024 &&
         hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
@@ -794,7 +957,7 @@ int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi,
     return launch_lds(kern, dim3((unsigned)nwg), dim3(64 * WPG), lds, stream, args, split);
 }
 
-template <int FMT, int NC, int SUB, bool FAST>
+template <int FMT, int NC, int SUB, bool FAST, bool X8>
 int gemv_table_run(GemvArgs &a, hipStream_t stream) {
     constexpr int RG = GemvShape<FMT, NC, SUB, FAST>::kRowsPerGroup;
     int64_t g = 0;
@@ -804,37 +967,48 @@ int gemv_table_run(GemvArgs &a, hipStream_t stream) {
         if (g > INT32_MAX) return QK_ERR_INVALID_ARG;
         a.gbase[i + 1] = (int)g;
     }
-    if (a.count == 1) return gemv_launch<FMT, NC, kSrcOne, SUB, FAST>(a.item[0], g, 0, stream);
-    return gemv_launch<FMT, NC, kSrcTable, SUB, FAST>(a, g, 0, stream);
+    if (a.count == 1) return gemv_launch<FMT, NC, kSrcOne, SUB, FAST, X8>(a.item[0], g, 0, stream);
+    if constexpr (X8) return QK_ERR_INVALID_ARG;  // 8-bit activations: one problem per launch
+    else return gemv_launch<FMT, NC, kSrcTable, SUB, FAST, false>(a, g, 0, stream);
 }
 
-template <int FMT, int NC, int SUB>
+template <int FMT, int NC, int SUB, bool X8>
 int gemv_table_sub(GemvArgs &a, bool fast, hipStream_t stream) {
-    if (fast) return gemv_table_run<FMT, NC, SUB, true>(a, stream);
-    return gemv_table_run<FMT, NC, SUB, false>(a, stream);
+    if (fast) return gemv_table_run<FMT, NC, SUB, true, X8>(a, stream);
+    return gemv_table_run<FMT, NC, SUB, false, X8>(a, stream);
 }
 
-template <int FMT, int NC>
+template <int FMT, int NC, bool X8>
 int gemv_table_fmt(GemvArgs &a, bool fast, hipStream_t stream) {
     if constexpr (NC == 1) {
         int npairs = 0;
         for (int i = 0; i < a.count; ++i) npairs = max(npairs, (a.item[i].nb + 1) / 2);
         switch (gemv_sub(npairs)) {
-        case 3: return gemv_table_sub<FMT, NC, 3>(a, fast, stream);
-        case 2: return gemv_table_sub<FMT, NC, 2>(a, fast, stream);
-        case 1: return gemv_table_sub<FMT, NC, 1>(a, fast, stream);
+        case 3: return gemv_table_sub<FMT, NC, 3, X8>(a, fast, stream);
+        case 2: return gemv_table_sub<FMT, NC, 2, X8>(a, fast, stream);
+        case 1: return gemv_table_sub<FMT, NC, 1, X8>(a, fast, stream);
         default: break;
         }
     }
-    return gemv_table_sub<FMT, NC, 0>(a, fast, stream);
+    return gemv_table_sub<FMT, NC, 0, X8>(a, fast, stream);
 }
 
 template <int NC>
 int gemv_table(int fmt, GemvArgs &a, bool fast, hipStream_t stream) {
     switch (fmt) {
-    case QK_Q4_0: return gemv_table_fmt<QK_Q4_0, NC>(a, fast, stream);
-    case QK_Q4_1: return gemv_table_fmt<QK_Q4_1, NC>(a, fast, stream);
-    case QK_Q8_0: return gemv_table_fmt<QK_Q8_0, NC>(a, fast, stream);
+    case QK_Q4_0: return gemv_table_fmt<QK_Q4_0, NC, false>(a, fast, stream);
+    case QK_Q4_1: return gemv_table_fmt<QK_Q4_1, NC, false>(a, fast, stream);
+    case QK_Q8_0: return gemv_table_fmt<QK_Q8_0, NC, false>(a, fast, stream);
+    default: return QK_ERR_INVALID_ARG;
+    }
+}
+
+template <int NC>
+int gemv_table_x8(int fmt, GemvArgs &a, bool fast, hipStream_t stream) {
+    switch (fmt) {
+    case QK_Q4_0: return gemv_table_fmt<QK_Q4_0, NC, true>(a, fast, stream);
+    case QK_Q4_1: return gemv_table_fmt<QK_Q4_1, NC, true>(a, fast, stream);
+    case QK_Q8_0: return gemv_table_fmt<QK_Q8_0, NC, true>(a, fast, stream);
     default: return QK_ERR_INVALID_ARG;
     }
 }
@@ -843,7 +1017,7 @@ template <int FMT, int SUB, bool FAST>
 int gemv_expert_run(const GemvExpert &e, hipStream_t stream) {
     constexpr int RG = GemvShape<FMT, 1, SUB, FAST>::kRowsPerGroup;
     const int gpi = (e.m + RG - 1) / RG;
-    return gemv_launch<FMT, 1, kSrcExpert, SUB, FAST>(e, (int64_t)gpi * e.count, gpi, stream);
+    return gemv_launch<FMT, 1, kSrcExpert, SUB, FAST, false>(e, (int64_t)gpi * e.count, gpi, stream);
 }
 
 template <int FMT, int SUB>

@@ -40,6 +40,9 @@ int launch_dequantize(int fmt, const void *w, int64_t nblocks, int out_dtype, vo
 int launch_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k, const float *x,
                        int64_t n, int64_t ldx, float *y, int64_t ldy, hipStream_t stream);
 
+int launch_mul_mat_vec_x8(int fmt, const void *w, int64_t m, int64_t k, const float *x,
+                          int64_t n, int64_t ldx, float *y, int64_t ldy, hipStream_t stream);
+
 int launch_mul_mat_vec_batched(int fmt, const qk_mat_vec_item *items, int count, int64_t n,
                                hipStream_t stream);
 

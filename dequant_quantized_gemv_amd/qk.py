@@ -19,8 +19,8 @@ QK_OK, QK_ERR_INVALID_ARG, QK_ERR_UNSUPPORTED, QK_ERR_ALIGNMENT, QK_ERR_LAUNCH =
 
 FORMATS = {"q4_0": QK_Q4_0, "q4_1": QK_Q4_1, "q8_0": QK_Q8_0}
 SYMBOLS = ("qk_block_bytes", "qk_row_bytes", "qk_status_string", "qk_version",
-           "qk_dequantize", "qk_mul_mat_vec", "qk_mul_mat_vec_batched", "qk_mul_mat_vec_id",
-           "qk_mul_mat")
+           "qk_dequantize", "qk_mul_mat_vec", "qk_mul_mat_vec_x8", "qk_mul_mat_vec_batched",
+           "qk_mul_mat_vec_id", "qk_mul_mat")
 QK_MAX_BATCH = 16
 
 
@@ -62,6 +62,8 @@ def load():
     lib.qk_dequantize.restype = ci
     lib.qk_mul_mat_vec.argtypes = [ci, vp, i64, i64, vp, i64, i64, vp, i64, vp]
     lib.qk_mul_mat_vec.restype = ci
+    lib.qk_mul_mat_vec_x8.argtypes = [ci, vp, i64, i64, vp, i64, i64, vp, i64, vp]
+    lib.qk_mul_mat_vec_x8.restype = ci
     lib.qk_mul_mat_vec_batched.argtypes = [ci, ctypes.POINTER(MatVecItem), ci, i64, vp]
     lib.qk_mul_mat_vec_batched.restype = ci
     lib.qk_mul_mat_vec_id.argtypes = [ci, vp, i64, i64, i64, i64, vp, i64, i64, i64,
@@ -117,6 +119,10 @@ def qk_mul_mat_vec(fmt, w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream=0):
     return load().qk_mul_mat_vec(_fmt(fmt), w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream)
 
 
+def qk_mul_mat_vec_x8(fmt, w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream=0):
+    return load().qk_mul_mat_vec_x8(_fmt(fmt), w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream)
+
+
 def make_items(items):
     """ctypes array of MatVecItem from (w_ptr, m, k, x_ptr, ldx, y_ptr, ldy) tuples."""
     arr = (MatVecItem * max(len(items), 1))()
@@ -170,6 +176,23 @@ def mul_mat_vec(fmt, w, m, k, x, y=None, stream=None):
     st = qk_mul_mat_vec(fmt, w.data_ptr(), m, k, x.data_ptr(), n, x.stride(0),
                         y.data_ptr(), y.stride(0), _stream(stream))
     _check(st, "qk_mul_mat_vec")
+    return y
+
+
+def mul_mat_vec_x8(fmt, w, m, k, x, y=None, stream=None):
+    """As mul_mat_vec, with the activations quantized to 8 bits per 32-element
+    block inside the kernel and integer dot products (qk_mul_mat_vec_x8)."""
+    import torch
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    n = x.shape[0]
+    if x.dtype != torch.float32 or x.stride(1) != 1:
+        raise TypeError("x must be float32 with contiguous columns")
+    if y is None:
+        y = torch.empty((n, m), dtype=torch.float32, device=x.device)
+    st = qk_mul_mat_vec_x8(fmt, w.data_ptr(), m, k, x.data_ptr(), n, x.stride(0),
+                           y.data_ptr(), y.stride(0), _stream(stream))
+    _check(st, "qk_mul_mat_vec_x8")
     return y
 
 

@@ -124,6 +124,32 @@ int qk_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k,
                    const float *x, int64_t n, int64_t ldx,
                    float *y, int64_t ldy, void *stream);
 
+/*
+ * qk_mul_mat_vec_x8 - quantized GEMV with 8-bit activations and integer dot
+ * products: as qk_mul_mat_vec, but every 32-element block of each activation
+ * column is first quantized (inside the kernel, no scratch memory) to codes
+ * q = round-half-even(x / d) with a power-of-two scale d = 2^e, e the
+ * smallest integer >= -126 with 127 * 2^e >= max|x| over the block (d = 0 for
+ * an all-zero block), and the products use x^ = d * q:
+ *
+ *   y[j*ldy + i] = sum_c W[i, c] * x^[j][c]      for i < m, j < n   (overwrite)
+ *
+ * Per block the weight and activation codes meet in exact 4-way int8 dot
+ * products; the result is scaled by d_w * d in fp32 (and Q4_1 adds
+ * m_w * d * sum q), so |y - sum_c W x^| is a few fp32 roundings of those
+ * per-block terms.  Against the fp32 activations the quantization adds at
+ * most sum_c |W[i, c]| * d / 2.
+ * Source: the integer-dot GEMV (mul_mat_vec_q, fed by a q8_1 activation
+ * quantization) that the "llama_cpp 0.12.1 -> 0.12.2" ggml-cuda.cu diff names
+ * in ggml_cuda_mul_mat's kernel choice; its activation format is not on the
+ * page, and the power-of-two block scale is this library's.
+ *
+ * Arguments, layouts and errors as qk_mul_mat_vec (n = 1..8).
+ */
+int qk_mul_mat_vec_x8(int fmt, const void *w, int64_t m, int64_t k,
+                      const float *x, int64_t n, int64_t ldx,
+                      float *y, int64_t ldy, void *stream);
+
 /* One problem of a grouped GEMV: y = W x (layout as in qk_mul_mat_vec). */
 typedef struct qk_mat_vec_item {
     const void *w;      /* m rows of k/32 blocks, 2-byte aligned */
