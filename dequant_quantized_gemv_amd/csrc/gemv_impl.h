@@ -893,12 +893,18 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
 #endif
 // The generic (unaligned) Q4_1 kernels above 4 columns need more registers
 // than 12 waves leave (168): they take one row per wave in 8-wave workgroups.
-template <int FMT, int NC, int SUB, bool FAST> struct GemvShape {
+// With 8-bit activations the Q8_0 kernels above 3 columns fit two rows per
+// wave in 8-wave workgroups (measured 15.3 -> 12.1 us at 8 columns on
+// 4096 x 4096; four rows per wave was slower for every format).
+template <int FMT, int NC, int SUB, bool FAST, bool X8 = false> struct GemvShape {
     static constexpr bool kWideQ41Generic = FMT == QK_Q4_1 && NC > 4 && !FAST;
-    static constexpr int kRWV = NC >= 4 && FMT != QK_Q8_0 && !kWideQ41Generic ? 2 : 1;
+    static constexpr bool kX8Q8Wide = X8 && FMT == QK_Q8_0 && NC >= 4 && SUB == 0;
+    static constexpr int kRWV =
+        kX8Q8Wide ? 2 : (NC >= 4 && FMT != QK_Q8_0 && !kWideQ41Generic ? 2 : 1);
     static constexpr int kWPG =
         SUB > 0 ? QK_GEMV_SHORT_WPG
-                : (NC <= 4 ? 8 : (FMT == QK_Q4_1 ? (FAST ? 12 : 8) : (FMT == QK_Q4_0 ? 8 : 4)));
+                : (kX8Q8Wide ? 8
+                             : (NC <= 4 ? 8 : (FMT == QK_Q4_1 ? (FAST ? 12 : 8) : (FMT == QK_Q4_0 ? 8 : 4))));
     static constexpr int kRowsPerGroup = kWPG * (kRWV << SUB);
 };
 
@@ -935,8 +941,8 @@ inline int device_cus() {
 // One launch over `total` row groups (gpi per problem for expert launches).
 template <int FMT, int NC, int SRC, int SUB, bool FAST, bool X8>
 int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi, hipStream_t stream) {
-    constexpr int RWV = GemvShape<FMT, NC, SUB, FAST>::kRWV;
-    constexpr int WPG = GemvShape<FMT, NC, SUB, FAST>::kWPG;
+    constexpr int RWV = GemvShape<FMT, NC, SUB, FAST, X8>::kRWV;
+    constexpr int WPG = GemvShape<FMT, NC, SUB, FAST, X8>::kWPG;
     if (total <= 0) return QK_OK;
     if (total > INT32_MAX) return QK_ERR_INVALID_ARG;
     // Activation window: 4096 weights per column (17 KiB at one column).
@@ -959,7 +965,7 @@ int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi,
 
 template <int FMT, int NC, int SUB, bool FAST, bool X8>
 int gemv_table_run(GemvArgs &a, hipStream_t stream) {
-    constexpr int RG = GemvShape<FMT, NC, SUB, FAST>::kRowsPerGroup;
+    constexpr int RG = GemvShape<FMT, NC, SUB, FAST, X8>::kRowsPerGroup;
     int64_t g = 0;
     a.gbase[0] = 0;
     for (int i = 0; i < a.count; ++i) {
