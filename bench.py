@@ -475,8 +475,9 @@ def run_share_layer(torch, qk, synth, oracle, timer, steps, warmup):
 def run_moe(torch, qk, synth, oracle, timer, steps, warmup):
     """Expert-indexed decode: per token, the gate, up and down projections of
     8 of 128 Q4_0 experts (768 x 2048, 768 x 2048, 2048 x 768), three
-    qk_mul_mat_vec_id calls.  Expert choices change every step and the stacks
-    rotate over copies, so the experts a step reads are never cache-resident."""
+    qk_mul_mat_vec_id calls; and the same with gate and up merged per expert
+    (two calls).  Expert choices change every step and the stacks rotate over
+    copies, so the experts a step reads are never cache-resident."""
     cfg = synth.WORKLOADS["gemv_q4_0_moe_experts"]
     seed = synth.workload_seed(cfg["id"])
     ne, nu, nt = cfg["n_experts"], cfg["n_used"], cfg["n_tokens"]
@@ -485,7 +486,9 @@ def run_moe(torch, qk, synth, oracle, timer, steps, warmup):
     for tid, (nm, m, k) in enumerate(cfg["layer"]):
         w = synth.quant_matrix("q4_0", ne * m, k, seed=seed, tensor_id=tid, d_range=cfg["d"])
         shared = nm != "down"
-        x = synth.activations(k, nt * (1 if shared else nu), seed=seed, tensor_id=100 + tid)
+        # gate and up read the same hidden state; down one vector per slot
+        xtid = 100 if shared else 100 + tid
+        x = synth.activations(k, nt * (1 if shared else nu), seed=seed, tensor_id=xtid)
         stacks.append(dict(nm=nm, m=m, k=k, w=w, wd=torch.from_numpy(w).cuda(), x=x,
                            xd=torch.from_numpy(np.ascontiguousarray(x)).cuda(), shared=shared,
                            y=torch.empty((nt, nu, m), dtype=torch.float32, device="cuda"),
@@ -528,11 +531,51 @@ def run_moe(torch, qk, synth, oracle, timer, steps, warmup):
     timer.time_graph(gw)
     sec = timer.time_graph(gk) / st
     del gw, gk
-    return {"parity": "ok" if ok else "FAILED", "max_err_over_S": worst,
-            "us_per_token": round(sec * 1e6, 3), "launches_per_token": len(stacks),
-            "selected_weight_bytes": sel_bytes,
-            "weight_GBps": round(sel_bytes / sec / 1e9, 1),
-            "pct_of_hbm_peak": round(100 * sel_bytes / sec / 1e9 / HBM_PEAK_GBPS, 1)}
+    out = {"parity": "ok" if ok else "FAILED", "max_err_over_S": worst,
+           "us_per_token": round(sec * 1e6, 3), "launches_per_token": len(stacks),
+           "selected_weight_bytes": sel_bytes,
+           "weight_GBps": round(sel_bytes / sec / 1e9, 1),
+           "pct_of_hbm_peak": round(100 * sel_bytes / sec / 1e9 / HBM_PEAK_GBPS, 1)}
+
+    # the same weights with gate and up merged per expert (one 1536 x 2048
+    # matrix an expert: gate rows, then up rows), so one call covers both
+    gate, up, down = stacks
+    mg = gate["m"] + up["m"]
+    layer(0)
+    torch.cuda.synchronize()
+    ref_gate, ref_up = gate["y"].clone(), up["y"].clone()
+    gate["copies"] = up["copies"] = None
+    gate["wd"] = up["wd"] = None
+    torch.cuda.empty_cache()
+    merged = np.concatenate([gate["w"].reshape(ne, -1), up["w"].reshape(ne, -1)], axis=1).ravel()
+    md = torch.from_numpy(merged).cuda()
+    mcopies = [md] + [md.clone() for _ in range(R - 1)]
+    ym = torch.empty((nt, nu, mg), dtype=torch.float32, device="cuda")
+    one_m = mg * (gate["k"] // 32) * 18
+
+    def merged_layer(i):
+        s = torch.cuda.current_stream().cuda_stream
+        idp = ids_d[i % n_sets].data_ptr()
+        st1 = lib.qk_mul_mat_vec_id(qk.QK_Q4_0, mcopies[i % R].data_ptr(), ne, one_m, mg, gate["k"],
+                                    idp, nu, nu, nt, gate["xd"].data_ptr(), 0, gate["k"],
+                                    ym.data_ptr(), mg, nu * mg, s)
+        st2 = call(down, down["copies"][i % R].data_ptr(), idp)
+        if st1 != 0 or st2 != 0:
+            raise RuntimeError("qk_mul_mat_vec_id failed")
+
+    merged_layer(0)
+    torch.cuda.synchronize()
+    # the merged call's rows are the separate calls' outputs, bit for bit
+    same = bool(torch.equal(ym[:, :, :gate["m"]], ref_gate) and torch.equal(ym[:, :, gate["m"]:], ref_up))
+    gw, gk = timer.capture(merged_layer, warmup), timer.capture(lambda i: merged_layer(i + warmup), st)
+    timer.time_graph(gw)
+    secm = timer.time_graph(gk) / st
+    del gw, gk, mcopies
+    out["merged_gate_up"] = {"parity": "bitwise equal to separate calls" if same else "FAILED",
+                             "us_per_token": round(secm * 1e6, 3), "launches_per_token": 2,
+                             "weight_GBps": round(sel_bytes / secm / 1e9, 1),
+                             "pct_of_hbm_peak": round(100 * sel_bytes / secm / 1e9 / HBM_PEAK_GBPS, 1)}
+    return out
 
 
 def main():
