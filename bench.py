@@ -18,11 +18,15 @@ Measurement
   * roofline.achieved = algorithmic bytes per launch (W + x + y) / average
     launch time; peak = 8 TB/s HBM.
   * cpu_baseline: the oracle (plain C, fp64, one thread) on the same matrix.
+  * practical_ceiling: a plain streaming-read kernel (libqk_ceiling.so) over
+    the same weight bytes, same rotation and launch pattern; --configs adds
+    it per GEMV workload and an MFMA-only loop for the GEMM.
 
 Options: --workload NAME runs another single-GEMV workload as the headline;
 --configs also measures every workload and adds them under "configs".
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -46,6 +50,53 @@ GEMV_SOURCES = ["gemv.hip", "gemv.h", "gemv_impl.h", "gemv_n1.hip", "qk_common.h
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def load_ceiling():
+    """The practical-ceiling kernels (libqk_ceiling.so, built with libqk)."""
+    path = os.path.join(ROOT, "dequant_quantized_gemv_amd", "libqk_ceiling.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.qkc_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.qkc_stream_read.restype = ctypes.c_int
+    lib.qkc_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.qkc_mfma_loop.restype = ctypes.c_int
+    return lib
+
+
+def stream_read_time(torch, timer, clib, ptrs, nbytes, steps, warmup):
+    """Seconds per streaming read of nbytes, launch i reading ptrs[i % len]
+    (the same cold rotation as the kernel it is compared with)."""
+    sink = torch.zeros(4, device="cuda")
+    R = len(ptrs)
+
+    def rd(i):
+        if clib.qkc_stream_read(ptrs[i % R], nbytes, sink.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("qkc_stream_read failed")
+
+    gw, gk = timer.capture(rd, max(warmup, 1)), timer.capture(lambda i: rd(i + warmup), steps)
+    timer.time_graph(gw)
+    sec = timer.time_graph(gk) / steps
+    del gw, gk
+    return sec
+
+
+def mfma_loop_tflops(torch, timer, clib):
+    """fp16 MFMA rate of a register-only loop over every CU (TFLOP/s)."""
+    sink = torch.zeros(4, device="cuda")
+    wgs = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 4000
+
+    def run(i):
+        if clib.qkc_mfma_loop(wgs, iters, sink.data_ptr(), torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("qkc_mfma_loop failed")
+
+    gw, gk = timer.capture(run, 2), timer.capture(run, 5)
+    timer.time_graph(gw)
+    sec = timer.time_graph(gk) / 5
+    return wgs * 8 * iters * 32 * (2.0 * 16 * 16 * 32) / sec / 1e12
 
 
 def kernel_source_hash(names):
@@ -165,7 +216,8 @@ def gemv_bytes(fmt, m, k, n):
     return wb, wb + 4 * n * (k + m)
 
 
-def bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup, entry="qk_mul_mat_vec"):
+def bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup, entry="qk_mul_mat_vec",
+               clib=None):
     wb, algo = gemv_bytes(fmt, m, k, n)
     R = copies_for(wb)
     copies = [prob["wd"]] + [prob["wd"].clone() for _ in range(R - 1)]
@@ -186,8 +238,13 @@ def bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup, entry="qk_mu
     gk = timer.capture(lambda i: launch(i + warmup), steps)
     timer.time_graph(gw)
     sec = timer.time_graph(gk)
-    del gw, gk, copies
-    return dict(seconds=sec, per_launch_s=sec / steps, weight_bytes=wb, algo_bytes=algo, copies=R)
+    del gw, gk
+    out = dict(seconds=sec, per_launch_s=sec / steps, weight_bytes=wb, algo_bytes=algo, copies=R)
+    if clib is not None:
+        # the same bytes streamed by a plain read kernel, same rotation
+        out["stream_read_s"] = stream_read_time(torch, timer, clib, ptrs, wb, steps, warmup)
+    del copies
+    return out
 
 
 def cpu_baseline_gemv(oracle, prob, fmt, m, k, n, budget_s=10.0):
@@ -204,7 +261,7 @@ def cpu_baseline_gemv(oracle, prob, fmt, m, k, n, budget_s=10.0):
                        f"{el:.1f} s, one thread")
 
 
-def run_headline(torch, qk, synth, oracle, timer, name, steps, warmup, with_cpu):
+def run_headline(torch, qk, synth, oracle, timer, name, steps, warmup, with_cpu, clib):
     cfg = synth.WORKLOADS[name]
     seed = synth.workload_seed(cfg["id"])
     fmt = cfg["fmt"]
@@ -217,7 +274,7 @@ def run_headline(torch, qk, synth, oracle, timer, name, steps, warmup, with_cpu)
     if not prob["ok"]:
         raise SystemExit(f"parity check failed before timing (max err/S {prob['worst']:.3g})")
     log(f"parity ok: max |y-ref|/S = {prob['worst']:.3g}")
-    r = bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup)
+    r = bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup, clib=clib)
     gbps = r["weight_bytes"] * steps / r["seconds"] / 1e9
     achieved = r["algo_bytes"] / r["per_launch_s"] / 1e9
     traffic = stored_traffic(f"gemv_{fmt}_{m}x{k}_n{n}", GEMV_SOURCES)
@@ -239,6 +296,11 @@ def run_headline(torch, qk, synth, oracle, timer, name, steps, warmup, with_cpu)
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},
+        # a plain streaming read of the same weight bytes (same cold rotation,
+        # same launch pattern): the practical ceiling on this chip
+        "practical_ceiling": {"stream_read_us": round(r["stream_read_s"] * 1e6, 3),
+                              "stream_read_GBps": round(r["weight_bytes"] / r["stream_read_s"] / 1e9, 1),
+                              "frac_of_stream_read": round(r["stream_read_s"] / r["per_launch_s"], 4)},
     }
     if with_cpu:
         log("timing the CPU oracle baseline")
@@ -246,7 +308,7 @@ def run_headline(torch, qk, synth, oracle, timer, name, steps, warmup, with_cpu)
     return out
 
 
-def run_configs(torch, qk, synth, oracle, timer, steps, warmup):
+def run_configs(torch, qk, synth, oracle, timer, steps, warmup, clib):
     """Every workload, each parity-checked before it is timed."""
     res = {}
     # C0: dequantize Q4_0 4096x4096 -> fp32
@@ -286,12 +348,15 @@ def run_configs(torch, qk, synth, oracle, timer, steps, warmup):
         for n in ns:
             prob = setup_gemv(torch, qk, synth, oracle, cfg["fmt"], cfg["m"], cfg["k"], n, seed, 0,
                               100, cfg["d"], cfg.get("mr"), check="sampled", rng_seed=n)
-            r = bench_gemv(torch, qk, timer, prob, cfg["fmt"], cfg["m"], cfg["k"], n, steps, warmup)
+            r = bench_gemv(torch, qk, timer, prob, cfg["fmt"], cfg["m"], cfg["k"], n, steps, warmup,
+                           clib=clib)
             gbps = r["weight_bytes"] / r["per_launch_s"] / 1e9
             res[f"{name}" + ("" if len(ns) == 1 else f"_n{n}")] = {
                 "parity": "ok" if prob["ok"] else "FAILED", "max_err_over_S": prob["worst"],
                 "us_per_launch": round(r["per_launch_s"] * 1e6, 3),
-                "weight_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
+                "weight_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+                "stream_read_us": round(r["stream_read_s"] * 1e6, 3),
+                "pct_of_stream_read": round(100 * r["stream_read_s"] / r["per_launch_s"], 1)}
             del prob
 
     # C2 again with 8-bit activations (qk_mul_mat_vec_x8), checked against the
@@ -368,12 +433,18 @@ def run_configs(torch, qk, synth, oracle, timer, steps, warmup):
     gw, gk = timer.capture(grouped, warmup), timer.capture(lambda i: grouped(i + warmup), st)
     timer.time_graph(gw)
     secg = timer.time_graph(gk) / st
+    # a streaming read of the layer's weight bytes as one buffer per copy
+    flat = [torch.empty(wtot, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    sr = stream_read_time(torch, timer, clib, [f.data_ptr() for f in flat], wtot, st, warmup)
+    del flat
     res["gemv_q4_0_decode_layer"] = {
         "parity": "ok" if all(p["ok"] for p in probs) and gok else "FAILED",
         "separate_launches": {"us_per_layer": round(sec * 1e6, 3), "weight_GBps": round(wtot / sec / 1e9, 1),
                               "pct_of_hbm_peak": round(100 * wtot / sec / 1e9 / HBM_PEAK_GBPS, 1)},
         "grouped_launch": {"us_per_layer": round(secg * 1e6, 3), "weight_GBps": round(wtot / secg / 1e9, 1),
-                           "pct_of_hbm_peak": round(100 * wtot / secg / 1e9 / HBM_PEAK_GBPS, 1)}}
+                           "pct_of_hbm_peak": round(100 * wtot / secg / 1e9 / HBM_PEAK_GBPS, 1),
+                           "stream_read_us": round(sr * 1e6, 3),
+                           "pct_of_stream_read": round(100 * sr / secg, 1)}}
     del probs, layer_copies, gw, gk, item_sets
 
     # C4: GEMM
@@ -405,9 +476,11 @@ def run_configs(torch, qk, synth, oracle, timer, steps, warmup):
     timer.time_graph(gw)
     sec = timer.time_graph(gk) / st
     tf = 2.0 * m * n * k / sec / 1e12
+    loop_tf = mfma_loop_tflops(torch, timer, clib)
     res["gemm_q4_0_14336x4096_n512"] = {
         "parity": "ok" if ok else "FAILED", "us_per_launch": round(sec * 1e6, 2),
-        "TFLOPs": round(tf, 1), "pct_of_mfma_f16_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 1)}
+        "TFLOPs": round(tf, 1), "pct_of_mfma_f16_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 1),
+        "mfma_loop_TFLOPs": round(loop_tf, 1), "pct_of_mfma_loop": round(100 * tf / loop_tf, 1)}
     del wc, gw, gk
 
     log("decode layer, one GPU's share of 8-way tensor parallelism")
@@ -601,15 +674,16 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     qk.load()  # fails loudly if libqk.so is not built
+    clib = load_ceiling()
     torch.cuda.set_device(0)
     timer = Timer(torch)
     out = run_headline(torch, qk, synth, oracle, timer, args.workload, args.steps, args.warmup,
-                       not args.no_cpu)
+                       not args.no_cpu, clib)
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
     if args.configs:
         log("measuring every workload")
-        out["configs"] = run_configs(torch, qk, synth, oracle, timer, args.steps, args.warmup)
+        out["configs"] = run_configs(torch, qk, synth, oracle, timer, args.steps, args.warmup, clib)
     print(json.dumps(out), flush=True)
 
 

@@ -13,6 +13,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqk.so")
+# The benchmark's practical-ceiling kernels (streaming read, MFMA loop): a
+# library of their own, not part of the qk C ABI.
+CEILING_SOURCE = "ceiling.hip"
+CEILING_LIB = os.path.join(PKG, "libqk_ceiling.so")
 SOURCES = ["api.hip", "dequant.hip", "gemv.hip", "gemv_n1.hip", "gemv_n2.hip", "gemv_n34.hip",
            "gemv_n56.hip", "gemv_n78.hip", "gemv_id.hip", "gemv_x8_n1.hip", "gemv_x8_n24.hip",
            "gemv_x8_n58.hip", "gemm.hip"]
@@ -60,11 +64,15 @@ def build(verbose=False, extra=()):
         obj = os.path.join(OBJ, s.replace(".hip", ".o"))
         jobs.append((obj, [HIPCC, *FLAGS, *SOURCE_FLAGS.get(s, []), *extra, *inc, "-c",
                            os.path.join(CSRC, s), "-o", obj]))
-    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
-        list(ex.map(lambda j: _run(j[1], verbose), jobs))
+    cobj = os.path.join(OBJ, CEILING_SOURCE.replace(".hip", ".o"))
+    cjob = (cobj, [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, CEILING_SOURCE), "-o", cobj])
+    with ThreadPoolExecutor(max_workers=len(jobs) + 1) as ex:
+        list(ex.map(lambda j: _run(j[1], verbose), jobs + [cjob]))
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in jobs],
           "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", cobj, "-o", CEILING_LIB + ".tmp"], verbose)
+    os.replace(CEILING_LIB + ".tmp", CEILING_LIB)
     return LIB
 
 
