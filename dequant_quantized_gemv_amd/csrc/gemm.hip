@@ -564,7 +564,7 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
     const int col0 = nt * kBN;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on the k group
     const int lane = tid & 63;
     const int g = lane >> 4;
     const int wm = wave & 3;   // 64-row slice of the tile
@@ -641,6 +641,52 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
 #pragma unroll
         for (int j = 0; j < kCT; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // The lane's A operands of stage `buf` (this k group's pair).
+    auto decode_stage = [&](int buf, ASet &f) __attribute__((always_inline)) {
+        const uint8_t *st = lds + buf * D::kStage;
+#pragma unroll
+        for (int i = 0; i < kRT; ++i) {
+            const uint8_t *ar = st + arow + i * 16 * (16 * D::kChunks);
+            uint32_t q[NQ];
+#pragma unroll
+            for (int t2 = 0; t2 < NQ; ++t2) q[t2] = *reinterpret_cast<const uint32_t *>(ar + qoff[t2]);
+            gm_decode<FMT>(q, lc, f[i][0], f[i][1]);
+        }
+    };
+    // The 64 products of stage `buf` (2 k halves x 8 column tiles x 4 row
+    // tiles).  The activation fragments are read two at a time, one group of
+    // eight products ahead of their use, so the matrix cores never wait for
+    // the LDS.
+    auto mma_stage = [&](int buf, const ASet &f) __attribute__((always_inline)) {
+        const uint8_t *bb = lds + buf * D::kStage + D::kAStage + kg * (kBN * kBK * 2) + bcol;
+        auto frag = [&](int q, int h) -> half8_t {
+            const int ks = q >> 2, j = 2 * (q & 3) + h;
+            return *reinterpret_cast<const half8_t *>(bb + j * 16 * 128 + (ks ? bslot1 : bslot0));
+        };
+        half8_t c0 = frag(0, 0), c1 = frag(0, 1);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int ks = q >> 2, j = 2 * (q & 3);
+            half8_t n0 = c0, n1 = c1;
+            if (q < 7) {
+                n0 = frag(q + 1, 0);
+                n1 = frag(q + 1, 1);
+            }
+#pragma unroll
+            for (int i = 0; i < kRT; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, f[i][ks]), c0,
+                                                                   acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < kRT; ++i)
+                acc[i][j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, f[i][ks]), c1,
+                                                                       acc[i][j + 1], 0, 0, 0);
+            c0 = n0;
+            c1 = n1;
+            // keep the next group's reads ahead of these products
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     if (nsup > 0) {
 #pragma unroll
         for (int t = 0; t < D::kLead; ++t) issue(t, t);
@@ -651,30 +697,10 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
             int nbuf = buf + D::kLead;
             if (nbuf >= D::kStages) nbuf -= D::kStages;
             issue(t + D::kLead, nbuf);
-            const uint8_t *st = lds + buf * D::kStage;
             if (kg == 0 || 2 * t + 1 < npairs) {
                 ASet f;
-#pragma unroll
-                for (int i = 0; i < kRT; ++i) {
-                    const uint8_t *ar = st + arow + i * 16 * (16 * D::kChunks);
-                    uint32_t q[NQ];
-#pragma unroll
-                    for (int t2 = 0; t2 < NQ; ++t2) q[t2] = *reinterpret_cast<const uint32_t *>(ar + qoff[t2]);
-                    gm_decode<FMT>(q, lc, f[i][0], f[i][1]);
-                }
-                const uint8_t *bb = st + D::kAStage + kg * (kBN * kBK * 2) + bcol;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int bslot = ks ? bslot1 : bslot0;
-#pragma unroll
-                    for (int j = 0; j < kCT; ++j) {
-                        const half8_t bf = *reinterpret_cast<const half8_t *>(bb + j * 16 * 128 + bslot);
-#pragma unroll
-                        for (int i = 0; i < kRT; ++i)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                __builtin_bit_cast(half8_t, f[i][ks]), bf, acc[i][j], 0, 0, 0);
-                    }
-                }
+                decode_stage(buf, f);
+                mma_stage(buf, f);
             }
             // stage t+1 (issued kLead-1 super-steps ago) complete for every
             // wave before anyone reads it; the kLead-1 newer stages may still
