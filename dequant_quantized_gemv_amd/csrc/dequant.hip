@@ -5,9 +5,10 @@
 // computed (fp32 value d*q + (-8*d), d*q + m, d*q; fp16 = one rounding of it)
 // and in the idea of staging the misaligned blocks through shared memory with
 // wide coalesced loads (the q8_0 kernel's shared-memory copy).  The layout
-// here is gfx950's: a 256-lane workgroup owns 256 consecutive blocks, copies
-// their bytes to LDS with 16-byte loads, and each lane then writes 16-byte
-// vectors of output, so every wave store covers 1 KiB of contiguous output.
+// here is gfx950's: a 256-lane workgroup takes chunks of 256 consecutive
+// blocks, copies their bytes to LDS with 16-byte loads, and each lane then
+// writes 16-byte vectors of output, so every wave store covers 1 KiB of
+// contiguous output.
 //
 // The matrix is a flat run of blocks (rows are back to back with no padding
 // and k % 32 == 0), so block b always produces outputs [32b, 32b + 32).
@@ -19,23 +20,12 @@ namespace qk {
 constexpr int kDqThreads = 256;
 constexpr int kDqBlocks = 256;  // quant blocks per workgroup
 
-// Copy `bytes` (even) from global memory to LDS.  ALIGNED16: src and dst are
-// 16-byte aligned, so whole 16-byte pieces move with one load each and only a
-// tail of fewer than 16 bytes falls back to 2-byte loads.
-template <bool ALIGNED16>
-__device__ __forceinline__ void stage_to_lds(uint8_t *dst, const uint8_t *__restrict__ src,
-                                             int bytes) {
-    int done = 0;
-    if (ALIGNED16) {
-        const int n16 = bytes >> 4;
-        const uint4 *s = reinterpret_cast<const uint4 *>(src);
-        uint4 *d = reinterpret_cast<uint4 *>(dst);
-        for (int i = threadIdx.x; i < n16; i += kDqThreads) d[i] = s[i];
-        done = n16 << 4;
-    }
-    const int n2 = (bytes - done) >> 1;
-    const uint16_t *s2 = reinterpret_cast<const uint16_t *>(src + done);
-    uint16_t *d2 = reinterpret_cast<uint16_t *>(dst + done);
+// Copy `bytes` (even) from global memory to LDS with 2-byte loads (input
+// that is only 2-byte aligned).
+__device__ __forceinline__ void stage_to_lds(uint8_t *dst, const uint8_t *__restrict__ src, int bytes) {
+    const int n2 = bytes >> 1;
+    const uint16_t *s2 = reinterpret_cast<const uint16_t *>(src);
+    uint16_t *d2 = reinterpret_cast<uint16_t *>(dst);
     for (int i = threadIdx.x; i < n2; i += kDqThreads) d2[i] = s2[i];
 }
 
@@ -61,14 +51,15 @@ __device__ __forceinline__ void decode4(const uint8_t *lds, int boff, int j0, fl
     }
 }
 
-template <int FMT, bool ALIGNED_IN, bool ALIGNED_OUT>
+// One chunk per workgroup, for 2-byte aligned input.
+template <int FMT, bool ALIGNED_OUT>
 __global__ __launch_bounds__(kDqThreads) void dequant_f32_kernel(
     const uint8_t *__restrict__ w, int64_t nblocks, float *__restrict__ out) {
     using F = Format<FMT>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kDqBlocks * F::kBytes];
     const int64_t blk0 = (int64_t)blockIdx.x * kDqBlocks;
     const int nb = (int)min((int64_t)kDqBlocks, nblocks - blk0);
-    stage_to_lds<ALIGNED_IN>(lds, w + blk0 * F::kBytes, nb * F::kBytes);
+    stage_to_lds(lds, w + blk0 * F::kBytes, nb * F::kBytes);
     __syncthreads();
     float *o = out + blk0 * kBlockElems;
     const int ngroups = nb * 8;  // 4-element groups
@@ -84,14 +75,14 @@ __global__ __launch_bounds__(kDqThreads) void dequant_f32_kernel(
     }
 }
 
-template <int FMT, bool ALIGNED_IN, bool ALIGNED_OUT>
+template <int FMT, bool ALIGNED_OUT>
 __global__ __launch_bounds__(kDqThreads) void dequant_f16_kernel(
     const uint8_t *__restrict__ w, int64_t nblocks, uint16_t *__restrict__ out) {
     using F = Format<FMT>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kDqBlocks * F::kBytes];
     const int64_t blk0 = (int64_t)blockIdx.x * kDqBlocks;
     const int nb = (int)min((int64_t)kDqBlocks, nblocks - blk0);
-    stage_to_lds<ALIGNED_IN>(lds, w + blk0 * F::kBytes, nb * F::kBytes);
+    stage_to_lds(lds, w + blk0 * F::kBytes, nb * F::kBytes);
     __syncthreads();
     uint16_t *o = out + blk0 * kBlockElems;
     const int ngroups = nb * 4;  // 8-element groups
@@ -118,25 +109,124 @@ __global__ __launch_bounds__(kDqThreads) void dequant_f16_kernel(
     }
 }
 
+// Aligned input (w 16-byte aligned, so every chunk of 256 blocks of 18 / 20
+// / 34 bytes starts on 16 bytes): a workgroup walks chunks c, c + gridDim.x,
+// ... and requests the next chunk's bytes into registers before it writes
+// the current chunk's outputs, so the reads of one chunk overlap the writes
+// of the one before.  Outputs are written with non-temporal 16-byte stores
+// (the output is not read again by this kernel; streaming it past the caches
+// measured 14.3 -> 12.9 us on a 4096 x 4096 Q4_0 -> fp32 dequantize).
+constexpr int kDqWgPerCu = 8;
+
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+
+template <int FMT, bool F16, bool ALIGNED_OUT>
+__global__ __launch_bounds__(kDqThreads) void dequant_loop_kernel(
+    const uint8_t *__restrict__ w, int64_t nblocks, void *__restrict__ out_) {
+    using F = Format<FMT>;
+    constexpr int kChunkBytes = kDqBlocks * F::kBytes;
+    constexpr int kU = (kChunkBytes / 16 + kDqThreads - 1) / kDqThreads;  // 16-byte pieces per thread
+    static_assert(kU <= 3, "pieces per thread");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kChunkBytes];
+    const int64_t nchunks = (nblocks + kDqBlocks - 1) / kDqBlocks;
+    const int tid = threadIdx.x;
+    int64_t c = blockIdx.x;
+    // (three named registers rather than an array: a loop-carried private
+    // array is moved to LDS by the compiler, with a wait after every load)
+    uint4 r0, r1, r2;
+    auto fetch = [&](int64_t ch) __attribute__((always_inline)) {
+        const int nb = (int)min((int64_t)kDqBlocks, nblocks - ch * kDqBlocks);
+        const int n16 = (nb * F::kBytes) >> 4;
+        const uint4 *src = reinterpret_cast<const uint4 *>(w + ch * kChunkBytes);
+        // every thread loads (a piece past the chunk's end repeats its last one)
+        r0 = src[min(tid, n16 - 1)];
+        if constexpr (kU > 1) r1 = src[min(tid + kDqThreads, n16 - 1)];
+        if constexpr (kU > 2) r2 = src[min(tid + 2 * kDqThreads, n16 - 1)];
+    };
+    fetch(c);
+    for (;;) {
+        const int nb = (int)min((int64_t)kDqBlocks, nblocks - c * kDqBlocks);
+        const int bytes = nb * F::kBytes;
+        const int n16 = bytes >> 4;
+        uint4 *l16 = reinterpret_cast<uint4 *>(lds);
+        if (tid < n16) l16[tid] = r0;
+        if constexpr (kU > 1) if (tid + kDqThreads < n16) l16[tid + kDqThreads] = r1;
+        if constexpr (kU > 2) if (tid + 2 * kDqThreads < n16) l16[tid + 2 * kDqThreads] = r2;
+        // a partial last chunk may end with fewer than 16 bytes
+        if ((bytes & 15) != 0) {
+            const uint16_t *s2 = reinterpret_cast<const uint16_t *>(w + c * kChunkBytes + (n16 << 4));
+            uint16_t *d2 = reinterpret_cast<uint16_t *>(lds + (n16 << 4));
+            for (int i = tid; i < ((bytes & 15) >> 1); i += kDqThreads) d2[i] = s2[i];
+        }
+        __syncthreads();
+        const int64_t cn = c + gridDim.x;
+        if (cn < nchunks) fetch(cn);
+        if constexpr (!F16) {
+            float *o = static_cast<float *>(out_) + c * kDqBlocks * kBlockElems;
+            for (int g = tid; g < nb * 8; g += kDqThreads) {  // 4-element groups
+                float v[4];
+                decode4<FMT>(lds, (g >> 3) * F::kBytes, (g & 7) * 4, v);
+                if (ALIGNED_OUT) {
+                    __builtin_nontemporal_store(f32x4v_t{v[0], v[1], v[2], v[3]},
+                                                reinterpret_cast<f32x4v_t *>(o + 4 * g));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[4 * g + i] = v[i];
+                }
+            }
+        } else {
+            uint16_t *o = static_cast<uint16_t *>(out_) + c * kDqBlocks * kBlockElems;
+            for (int g = tid; g < nb * 4; g += kDqThreads) {  // 8-element groups
+                float v[8];
+                decode4<FMT>(lds, (g >> 2) * F::kBytes, (g & 3) * 8, v);
+                decode4<FMT>(lds, (g >> 2) * F::kBytes, (g & 3) * 8 + 4, v + 4);
+                uint16_t h[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) h[i] = f2h(v[i]);
+                if (ALIGNED_OUT) {
+                    __builtin_nontemporal_store(
+                        u32x4v_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16),
+                                 (uint32_t)h[4] | ((uint32_t)h[5] << 16), (uint32_t)h[6] | ((uint32_t)h[7] << 16)},
+                        reinterpret_cast<u32x4v_t *>(o + 8 * g));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) o[8 * g + i] = h[i];
+                }
+            }
+        }
+        if (cn >= nchunks) break;
+        __syncthreads();  // every read of this chunk done before the next one is written
+        c = cn;
+    }
+}
+
 template <int FMT>
 static int dispatch_dequant(const uint8_t *w, int64_t nblocks, int out_dtype, void *out,
                             hipStream_t stream) {
-    const dim3 grid((unsigned)((nblocks + kDqBlocks - 1) / kDqBlocks));
     const dim3 block(kDqThreads);
     const bool ain = ((uintptr_t)w % 16) == 0;
     const bool aout = ((uintptr_t)out % 16) == 0;
-    if (out_dtype == QK_F32) {
+    const bool f32 = out_dtype == QK_F32;
+    if (ain) {
+        const int64_t nchunks = (nblocks + kDqBlocks - 1) / kDqBlocks;
+        const int64_t cap = (int64_t)device_cus() * kDqWgPerCu;
+        const dim3 grid((unsigned)(nchunks < cap ? nchunks : cap));
+        if (f32 && aout) return launch(dequant_loop_kernel<FMT, false, true>, grid, block, stream, w, nblocks, out);
+        if (f32) return launch(dequant_loop_kernel<FMT, false, false>, grid, block, stream, w, nblocks, out);
+        if (aout) return launch(dequant_loop_kernel<FMT, true, true>, grid, block, stream, w, nblocks, out);
+        return launch(dequant_loop_kernel<FMT, true, false>, grid, block, stream, w, nblocks, out);
+    }
+    // 2-byte aligned input: one chunk per workgroup, staged with 2-byte loads
+    const dim3 grid((unsigned)((nblocks + kDqBlocks - 1) / kDqBlocks));
+    if (f32) {
         float *o = static_cast<float *>(out);
-        if (ain && aout) return launch(dequant_f32_kernel<FMT, true, true>, grid, block, stream, w, nblocks, o);
-        if (ain) return launch(dequant_f32_kernel<FMT, true, false>, grid, block, stream, w, nblocks, o);
-        if (aout) return launch(dequant_f32_kernel<FMT, false, true>, grid, block, stream, w, nblocks, o);
-        return launch(dequant_f32_kernel<FMT, false, false>, grid, block, stream, w, nblocks, o);
+        if (aout) return launch(dequant_f32_kernel<FMT, true>, grid, block, stream, w, nblocks, o);
+        return launch(dequant_f32_kernel<FMT, false>, grid, block, stream, w, nblocks, o);
     }
     uint16_t *o = static_cast<uint16_t *>(out);
-    if (ain && aout) return launch(dequant_f16_kernel<FMT, true, true>, grid, block, stream, w, nblocks, o);
-    if (ain) return launch(dequant_f16_kernel<FMT, true, false>, grid, block, stream, w, nblocks, o);
-    if (aout) return launch(dequant_f16_kernel<FMT, false, true>, grid, block, stream, w, nblocks, o);
-    return launch(dequant_f16_kernel<FMT, false, false>, grid, block, stream, w, nblocks, o);
+    if (aout) return launch(dequant_f16_kernel<FMT, true>, grid, block, stream, w, nblocks, o);
+    return launch(dequant_f16_kernel<FMT, false>, grid, block, stream, w, nblocks, o);
 }
 
 int launch_dequantize(int fmt, const void *w, int64_t nblocks, int out_dtype, void *out,

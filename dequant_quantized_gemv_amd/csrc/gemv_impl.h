@@ -930,14 +930,6 @@ constexpr int kGvMaxWgPerCu = QK_GEMV_WG_PER_CU;
 #endif
 constexpr int kGvX8MaxWgPerCu = QK_GEMV_X8_WG_PER_CU;
 
-inline int device_cus() {
-    int cus = 256, dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-        cus = v;
-    return cus;
-}
-
 // One launch over `total` row groups (gpi per problem for expert launches).
 template <int FMT, int NC, int SRC, int SUB, bool FAST, bool X8>
 int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi, hipStream_t stream) {

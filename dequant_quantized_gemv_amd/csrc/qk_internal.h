@@ -34,6 +34,15 @@ inline int launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t str
     return launch_lds(kern, grid, block, 0, stream, args...);
 }
 
+// Compute units of the current device (256 on MI355X if the query fails).
+inline int device_cus() {
+    int cus = 256, dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+        cus = v;
+    return cus;
+}
+
 int launch_dequantize(int fmt, const void *w, int64_t nblocks, int out_dtype, void *out,
                       hipStream_t stream);
 
