@@ -654,8 +654,8 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
         }
     };
     // The 64 products of stage `buf` (2 k halves x 8 column tiles x 4 row
-    // tiles).  The activation fragments are read two at a time, one group of
-    // eight products ahead of their use, so the matrix cores never wait for
+    // tiles).  The activation fragments are read two at a time, two groups of
+    // eight products ahead of their use, so the matrix cores wait less for
     // the LDS.
     auto mma_stage = [&](int buf, const ASet &f) __attribute__((always_inline)) {
         const uint8_t *bb = lds + buf * D::kStage + D::kAStage + kg * (kBN * kBK * 2) + bcol;
@@ -663,15 +663,23 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
             const int ks = q >> 2, j = 2 * (q & 3) + h;
             return *reinterpret_cast<const half8_t *>(bb + j * 16 * 128 + (ks ? bslot1 : bslot0));
         };
-        half8_t c0 = frag(0, 0), c1 = frag(0, 1);
+        // groups of fragments in flight (one: 77-81 us on the Q4_0
+        // 14336 x 4096 x 512 workload; two: 74-80 us; three: no better)
+        constexpr int FA = 2;
+        half8_t fr[FA + 1][2];
+#pragma unroll
+        for (int u = 0; u < FA; ++u) {
+            fr[u][0] = frag(u, 0);
+            fr[u][1] = frag(u, 1);
+        }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int ks = q >> 2, j = 2 * (q & 3);
-            half8_t n0 = c0, n1 = c1;
-            if (q < 7) {
-                n0 = frag(q + 1, 0);
-                n1 = frag(q + 1, 1);
+            if (q + FA < 8) {
+                fr[(q + FA) % (FA + 1)][0] = frag(q + FA, 0);
+                fr[(q + FA) % (FA + 1)][1] = frag(q + FA, 1);
             }
+            const half8_t c0 = fr[q % (FA + 1)][0], c1 = fr[q % (FA + 1)][1];
 #pragma unroll
             for (int i = 0; i < kRT; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, f[i][ks]), c0,
@@ -680,9 +688,7 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
             for (int i = 0; i < kRT; ++i)
                 acc[i][j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, f[i][ks]), c1,
                                                                        acc[i][j + 1], 0, 0, 0);
-            c0 = n0;
-            c1 = n1;
-            // keep the next group's reads ahead of these products
+            // keep the later groups' reads ahead of these products
             __builtin_amdgcn_sched_barrier(0);
         }
     };
