@@ -896,11 +896,21 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
 // With 8-bit activations the Q8_0 kernels above 3 columns fit two rows per
 // wave in 8-wave workgroups (measured 15.3 -> 12.1 us at 8 columns on
 // 4096 x 4096; four rows per wave was slower for every format).
-template <int FMT, int NC, int SUB, bool FAST, bool X8 = false> struct GemvShape {
+// R2: two rows per wave (activations read from LDS once for both) for a
+// one-column launch of full-wave rows with more than 64 rows per CU, i.e. more
+// row groups of one row per wave than the launch's 8 workgroups per CU, so
+// workgroups walk several steps either way.  Measured in alternating runs on
+// one box: the grouped 7B-shaped Q4_0 layer (42 496 rows) 27.1-28.1 ->
+// 25.2-26.5 us.  With fewer rows each workgroup takes one step and halving the
+// workgroups costs more than it saves: Q4_1 11008 x 4096 8.6 -> 9.0 us, the
+// layer's 8-way tensor-parallel share (12 480 rows) 9.4 -> 11.0 us, Q8_0 4096 x
+// 4096 5.3 -> 6.2 us.
+template <int FMT, int NC, int SUB, bool FAST, bool X8 = false, bool R2 = false> struct GemvShape {
+    static_assert(!R2 || (NC == 1 && SUB == 0 && !X8), "two rows per wave: one column, full-wave rows");
     static constexpr bool kWideQ41Generic = FMT == QK_Q4_1 && NC > 4 && !FAST;
     static constexpr bool kX8Q8Wide = X8 && FMT == QK_Q8_0 && NC >= 4 && SUB == 0;
     static constexpr int kRWV =
-        kX8Q8Wide ? 2 : (NC >= 4 && FMT != QK_Q8_0 && !kWideQ41Generic ? 2 : 1);
+        (R2 || kX8Q8Wide) ? 2 : (NC >= 4 && FMT != QK_Q8_0 && !kWideQ41Generic ? 2 : 1);
     static constexpr int kWPG =
         SUB > 0 ? QK_GEMV_SHORT_WPG
                 : (kX8Q8Wide ? 8
@@ -931,10 +941,10 @@ constexpr int kGvMaxWgPerCu = QK_GEMV_WG_PER_CU;
 constexpr int kGvX8MaxWgPerCu = QK_GEMV_X8_WG_PER_CU;
 
 // One launch over `total` row groups (gpi per problem for expert launches).
-template <int FMT, int NC, int SRC, int SUB, bool FAST, bool X8>
+template <int FMT, int NC, int SRC, int SUB, bool FAST, bool X8, bool R2 = false>
 int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi, hipStream_t stream) {
-    constexpr int RWV = GemvShape<FMT, NC, SUB, FAST, X8>::kRWV;
-    constexpr int WPG = GemvShape<FMT, NC, SUB, FAST, X8>::kWPG;
+    constexpr int RWV = GemvShape<FMT, NC, SUB, FAST, X8, R2>::kRWV;
+    constexpr int WPG = GemvShape<FMT, NC, SUB, FAST, X8, R2>::kWPG;
     if (total <= 0) return QK_OK;
     if (total > INT32_MAX) return QK_ERR_INVALID_ARG;
     // Activation window: 4096 weights per column (17 KiB at one column).
@@ -955,9 +965,9 @@ int gemv_launch(const typename GemvSrc<SRC>::Args &args, int64_t total, int gpi,
     return launch_lds(kern, dim3((unsigned)nwg), dim3(64 * WPG), lds, stream, args, split);
 }
 
-template <int FMT, int NC, int SUB, bool FAST, bool X8>
+template <int FMT, int NC, int SUB, bool FAST, bool X8, bool R2 = false>
 int gemv_table_run(GemvArgs &a, hipStream_t stream) {
-    constexpr int RG = GemvShape<FMT, NC, SUB, FAST, X8>::kRowsPerGroup;
+    constexpr int RG = GemvShape<FMT, NC, SUB, FAST, X8, R2>::kRowsPerGroup;
     int64_t g = 0;
     a.gbase[0] = 0;
     for (int i = 0; i < a.count; ++i) {
@@ -965,13 +975,21 @@ int gemv_table_run(GemvArgs &a, hipStream_t stream) {
         if (g > INT32_MAX) return QK_ERR_INVALID_ARG;
         a.gbase[i + 1] = (int)g;
     }
-    if (a.count == 1) return gemv_launch<FMT, NC, kSrcOne, SUB, FAST, X8>(a.item[0], g, 0, stream);
+    if (a.count == 1) return gemv_launch<FMT, NC, kSrcOne, SUB, FAST, X8, R2>(a.item[0], g, 0, stream);
     if constexpr (X8) return QK_ERR_INVALID_ARG;  // 8-bit activations: one problem per launch
-    else return gemv_launch<FMT, NC, kSrcTable, SUB, FAST, false>(a, g, 0, stream);
+    else return gemv_launch<FMT, NC, kSrcTable, SUB, FAST, false, R2>(a, g, 0, stream);
 }
 
 template <int FMT, int NC, int SUB, bool X8>
 int gemv_table_sub(GemvArgs &a, bool fast, hipStream_t stream) {
+    if constexpr (NC == 1 && SUB == 0 && !X8) {
+        int64_t rows = 0;
+        for (int i = 0; i < a.count; ++i) rows += a.item[i].m;
+        if (rows > 64 * (int64_t)device_cus()) {
+            if (fast) return gemv_table_run<FMT, NC, SUB, true, X8, true>(a, stream);
+            return gemv_table_run<FMT, NC, SUB, false, X8, true>(a, stream);
+        }
+    }
     if (fast) return gemv_table_run<FMT, NC, SUB, true, X8>(a, stream);
     return gemv_table_run<FMT, NC, SUB, false, X8>(a, stream);
 }

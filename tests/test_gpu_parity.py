@@ -174,6 +174,21 @@ def _gpu_gemv(fmt, w, m, k, x2d, ldx=None, ldy=None, w_off=0, x_off=0, stream=No
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k,w_off", [(16403, 4096, 0), (16400, 2048, 2), (16403, 1376, 0)])
+def test_gemv_two_rows_per_wave(fmt, m, k, w_off):
+    """One-column launches of more than 64 rows per CU (16 384 on 256 CUs)
+    take two rows per wave: every row against the oracle on the aligned path
+    (ragged last row group), a 2-byte aligned matrix and an odd block count
+    (43 blocks per row), both on the generic path."""
+    _say("gemv two rows per wave", fmt, m, k, w_off)
+    w = _weights(fmt, m, k, seed=46)
+    x = synth.activations(k, 1, seed=46, tensor_id=2)
+    y = _gpu_gemv(fmt, w, m, k, x, w_off=w_off)
+    yref, s = oracle.dot(fmt, w, m, k, x, 1)
+    assert_within(y, yref, s, GEMV_TOL, f"gemv two rows {fmt} {m}x{k} w_off={w_off}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m,k,n", [(1, 32, 1), (2, 64, 2), (3, 96, 1), (13, 320, 3),
                                    (37, 2080, 5), (100, 4096, 8), (259, 11008, 2),
                                    (17, 4096, 4), (8, 256, 6), (9, 512, 7)])
@@ -517,6 +532,25 @@ def test_gemv_batched_generic_path_and_sixteen_items():
     for (w, m, k, x), y in zip(probs, ys):
         yref, s = oracle.dot("q4_0", w, m, k, x, 1)
         assert_within(y, yref, s, GEMV_TOL, f"batched generic {m}x{k}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_batched_two_rows_per_wave_generic(fmt):
+    """A grouped one-column launch past 64 rows per CU (two rows per wave)
+    whose items take the generic path (43-block rows, one item 2-byte
+    aligned): every row of every item against the oracle, and bitwise equal
+    to separate launches of the same items."""
+    shapes = [(16403, 1376, 0), (301, 4096, 2), (77, 2080, 0)]
+    _say("gemv batched two rows generic", fmt)
+    probs = []
+    for i, (m, k, _) in enumerate(shapes):
+        probs.append((_weights(fmt, m, k, seed=47, tid=i), m, k,
+                      synth.activations(k, 1, seed=47, tensor_id=10 + i)))
+    ys = _gpu_gemv_batched(fmt, probs, 1, w_offs=[o for (_, _, o) in shapes])
+    for (w, m, k, x), y, (_, _, off) in zip(probs, ys, shapes):
+        yref, s = oracle.dot(fmt, w, m, k, x, 1)
+        assert_within(y, yref, s, GEMV_TOL, f"batched two rows {fmt} {m}x{k}")
+        assert np.array_equal(y.view(np.uint32), _gpu_gemv(fmt, w, m, k, x, w_off=off).view(np.uint32))
 
 
 def test_gemv_batched_full_config3_sampled():
