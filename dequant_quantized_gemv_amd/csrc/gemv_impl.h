@@ -905,8 +905,14 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
 // workgroups costs more than it saves: Q4_1 11008 x 4096 8.6 -> 9.0 us, the
 // layer's 8-way tensor-parallel share (12 480 rows) 9.4 -> 11.0 us, Q8_0 4096 x
 // 4096 5.3 -> 6.2 us.
+//
+// R2 with 2 or 3 columns (Q4_0, and aligned Q4_1: the generic Q4_1 kernel
+// spills with two rows per wave) above 32 rows per CU: Q4_1 11008 x 4096
+// 11.4 -> 10.6 us at 2 columns, 15.6 -> 14.0 us at 3; at 4096 rows it loses
+// (5.5 -> 6.3 and 7.1 -> 7.6 us).
 template <int FMT, int NC, int SUB, bool FAST, bool X8 = false, bool R2 = false> struct GemvShape {
-    static_assert(!R2 || (NC == 1 && SUB == 0 && !X8), "two rows per wave: one column, full-wave rows");
+    static_assert(!R2 || (NC <= 3 && SUB == 0 && !X8 && (NC == 1 || (FMT != QK_Q8_0 && (FMT != QK_Q4_1 || FAST)))),
+                  "two rows per wave: up to 3 columns, full-wave rows");
     static constexpr bool kWideQ41Generic = FMT == QK_Q4_1 && NC > 4 && !FAST;
     static constexpr bool kX8Q8Wide = X8 && FMT == QK_Q8_0 && NC >= 4 && SUB == 0;
     static constexpr int kRWV =
@@ -982,12 +988,12 @@ int gemv_table_run(GemvArgs &a, hipStream_t stream) {
 
 template <int FMT, int NC, int SUB, bool X8>
 int gemv_table_sub(GemvArgs &a, bool fast, hipStream_t stream) {
-    if constexpr (NC == 1 && SUB == 0 && !X8) {
+    if constexpr (NC <= 3 && SUB == 0 && !X8 && (NC == 1 || FMT != QK_Q8_0)) {
         int64_t rows = 0;
         for (int i = 0; i < a.count; ++i) rows += a.item[i].m;
-        if (rows > 64 * (int64_t)device_cus()) {
+        if (rows > (NC == 1 ? 64 : 32) * (int64_t)device_cus()) {
             if (fast) return gemv_table_run<FMT, NC, SUB, true, X8, true>(a, stream);
-            return gemv_table_run<FMT, NC, SUB, false, X8, true>(a, stream);
+            if constexpr (NC == 1 || FMT != QK_Q4_1) return gemv_table_run<FMT, NC, SUB, false, X8, true>(a, stream);
         }
     }
     if (fast) return gemv_table_run<FMT, NC, SUB, true, X8>(a, stream);

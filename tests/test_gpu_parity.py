@@ -174,18 +174,21 @@ def _gpu_gemv(fmt, w, m, k, x2d, ldx=None, ldy=None, w_off=0, x_off=0, stream=No
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n", [1, 2, 3])
 @pytest.mark.parametrize("m,k,w_off", [(16403, 4096, 0), (16400, 2048, 2), (16403, 1376, 0)])
-def test_gemv_two_rows_per_wave(fmt, m, k, w_off):
-    """One-column launches of more than 64 rows per CU (16 384 on 256 CUs)
-    take two rows per wave: every row against the oracle on the aligned path
-    (ragged last row group), a 2-byte aligned matrix and an odd block count
-    (43 blocks per row), both on the generic path."""
-    _say("gemv two rows per wave", fmt, m, k, w_off)
+def test_gemv_two_rows_per_wave(fmt, n, m, k, w_off):
+    """Launches past the two-rows-per-wave thresholds (more than 64 rows per
+    CU at one column, 32 at two or three: 16 403 rows is past both on 256
+    CUs): every output against the oracle on the aligned path (ragged last
+    row group), a 2-byte aligned matrix and an odd block count (43 blocks per
+    row), both on the generic path (which keeps one row per wave for Q4_1
+    above one column and for Q8_0)."""
+    _say("gemv two rows per wave", fmt, n, m, k, w_off)
     w = _weights(fmt, m, k, seed=46)
-    x = synth.activations(k, 1, seed=46, tensor_id=2)
+    x = synth.activations(k, n, seed=46, tensor_id=2)
     y = _gpu_gemv(fmt, w, m, k, x, w_off=w_off)
-    yref, s = oracle.dot(fmt, w, m, k, x, 1)
-    assert_within(y, yref, s, GEMV_TOL, f"gemv two rows {fmt} {m}x{k} w_off={w_off}")
+    yref, s = oracle.dot(fmt, w, m, k, x, n)
+    assert_within(y, yref, s, GEMV_TOL, f"gemv two rows {fmt} {m}x{k} n={n} w_off={w_off}")
 
 
 @pytest.mark.parametrize("fmt", FMTS)
