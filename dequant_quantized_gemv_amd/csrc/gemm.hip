@@ -10,17 +10,19 @@
 // produces (a Q4_0 code 8 with negative d gives -0 here, +0 there: the same
 // number).
 //
-// Tile: 256 rows x 128 columns per workgroup of 4 waves; wave v owns rows
-// 64v..64v+63 and all 128 columns (4 x 8 MFMA tiles of 16 x 16, 128 fp32
-// accumulators per lane).  K advances 64 (two quant blocks, one "pair") per
-// step.  In the MFMA A operand, lane l holds row l%16 of a 16-row tile and
-// elements 8(l/16)..8(l/16)+7 of a 32-element block, so each 16 x 32 operand
-// is exactly one quant block of 16 rows.  Each lane loads only the bytes of
-// its own 8 weights (plus the scales) with dword loads, so the weights never
-// pass through LDS; the activation tile (128 columns x 64) is staged through a
-// double-buffered LDS tile read by all four waves.  Quant words are loaded
-// two steps ahead; the next step's weights are dequantized while the matrix
-// cores work on the current one.
+// Tile: 256 rows x 128 columns per workgroup of 8 waves: 4 row slices of 64
+// rows x 2 k groups.  Each wave holds a 64 x 128 fp32 accumulator tile (4 x 8
+// MFMA tiles of 16 x 16) and multiplies its k group's half of the pairs of
+// blocks; at the end the two k groups' partial sums are combined through LDS.
+// In the MFMA A operand, lane l holds row l%16 of a 16-row tile and elements
+// 8(l/16)..8(l/16)+7 of a 32-element block, so each 16 x 32 operand is
+// exactly one quant block of 16 rows, and each lane dequantizes its own 8
+// weights per block from quant bytes staged in LDS straight into operand
+// registers.  The quant bytes (row-contiguous 16-byte chunks) and the
+// activation tile pass through LDS: with k % 128 == 0 and aligned operands
+// they are copied global -> LDS by gfx950 direct loads into a 3-stage ring two
+// super-steps ahead (gemm_dma_kernel); otherwise through registers one step
+// ahead into double buffers (gemm_kernel).
 //
 // Dequantization to fp16 (Q4_0, Q8_0), packed two at a time and exact: the
 // integer code is placed in the mantissa of an fp16 (0x64XX is 1024 + XX) with
