@@ -5,7 +5,7 @@
 // computed (fp32 value d*q + (-8*d), d*q + m, d*q; fp16 = one rounding of it)
 // and in the idea of staging the misaligned blocks through shared memory with
 // wide coalesced loads (the q8_0 kernel's shared-memory copy).  The layout
-// here is gfx950's: a 256-lane workgroup takes chunks of 256 consecutive
+// here is gfx950's: a 256-lane workgroup takes chunks of 128 consecutive
 // blocks, copies their bytes to LDS with 16-byte loads, and each lane then
 // writes 16-byte vectors of output, so every wave store covers 1 KiB of
 // contiguous output.
@@ -18,7 +18,9 @@
 namespace qk {
 
 constexpr int kDqThreads = 256;
-constexpr int kDqBlocks = 256;  // quant blocks per workgroup
+// quant blocks per chunk (128 measured 2-3 % faster than 256 on a 4096 x
+// 4096 Q4_0 -> fp32 dequantize: each workgroup then takes two chunks)
+constexpr int kDqBlocks = 128;
 
 // Copy `bytes` (even) from global memory to LDS with 2-byte loads (input
 // that is only 2-byte aligned).
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(kDqThreads) void dequant_f16_kernel(
     }
 }
 
-// Aligned input (w 16-byte aligned, so every chunk of 256 blocks of 18 / 20
+// Aligned input (w 16-byte aligned, so every chunk of 128 blocks of 18 / 20
 // / 34 bytes starts on 16 bytes): a workgroup walks chunks c, c + gridDim.x,
 // ... and requests the next chunk's bytes into registers before it writes
 // the current chunk's outputs, so the reads of one chunk overlap the writes

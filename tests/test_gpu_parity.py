@@ -88,11 +88,11 @@ def test_dequantize_unaligned_paths(fmt, dtype, w_off, out_off):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("out_off", [0, 4])
 def test_dequantize_chunk_loop(fmt, dtype, out_off):
-    """More chunks of 256 blocks than the aligned-input kernel launches
-    workgroups (8 per CU): workgroups take a second chunk while the first
-    one's outputs are written, and the last chunk is ragged (195 blocks,
+    """More chunks of 128 blocks than the aligned-input kernel launches
+    workgroups (8 per CU): workgroups take further chunks while the previous
+    one's outputs are written, and the last chunk is ragged (67 blocks,
     whose Q4_0 / Q4_1 bytes end 6 / 12 bytes past a 16-byte boundary)."""
-    rows, k = 8195, 2080  # 532 675 blocks = 2080 full chunks + 195 blocks
+    rows, k = 8195, 2080  # 532 675 blocks = 4161 full chunks + 67 blocks
     _say("dequant chunk loop", fmt, dtype, out_off)
     w = _weights(fmt, rows, k, seed=13)
     got = _gpu_dequant(fmt, w, rows, k, dtype, out_off=out_off)
