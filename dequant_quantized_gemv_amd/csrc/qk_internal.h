@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <tuple>
 #include <utility>
 
@@ -34,13 +35,17 @@ inline int launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t str
     return launch_lds(kern, grid, block, 0, stream, args...);
 }
 
-// Compute units of the current device (256 on MI355X if the query fails).
+// Compute units of the current device (256 on MI355X if the query fails),
+// queried once per device and kept (launch shapes ask for it on every call).
 inline int device_cus() {
-    int cus = 256, dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-        cus = v;
-    return cus;
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices] = {};
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kMaxDevices && (v = cached[dev].load(std::memory_order_relaxed)) > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 256;
+    if (dev >= 0 && dev < kMaxDevices) cached[dev].store(v, std::memory_order_relaxed);
+    return v;
 }
 
 int launch_dequantize(int fmt, const void *w, int64_t nblocks, int out_dtype, void *out,
