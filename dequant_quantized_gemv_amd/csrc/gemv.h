@@ -28,6 +28,7 @@ constexpr int kGvMaxItems = 16;
 struct GemvArgs {
     GemvItem item[kGvMaxItems];
     int gbase[kGvMaxItems + 1];
+    int sub[kGvMaxItems];  // per-problem lane split of a one-column launch whose problems differ in it
     int count;
 };
 

@@ -460,6 +460,11 @@ __device__ __forceinline__ void pair_dot_x8(const uint32_t (&v)[RWV][Pair<FMT>::
     }
 }
 
+// Lane split of a grouped one-column launch whose problems need different
+// splits (each problem then uses the split its own launch would use, so the
+// outputs are bitwise those of separate launches).
+constexpr int kSubMixed = -1;
+
 // Where a launch's problems come from.
 enum GemvSource {
     kSrcOne = 0,     // one problem, passed in its own argument
@@ -514,30 +519,45 @@ template <int FMT, int NC, int RWV, int WPG, bool FAST, int SRC, int SUB, bool X
 __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 1 || (NC == 2 && FMT != QK_Q8_0) ? 4 : (NC == 2 ? 2 : 1)))) void gemv_kernel(const typename GemvSrc<SRC>::Args args, const GemvSplit split) {
     static_assert(SUB == 0 || RWV == 1, "several rows per wave only with one row per segment");
     static_assert(SRC != kSrcExpert || NC == 1, "expert-indexed problems have one column");
+    static_assert(SUB != kSubMixed || (SRC == kSrcTable && NC == 1 && !X8),
+                  "per-problem lane split: grouped one-column launches");
     constexpr int BS = Format<FMT>::kBytes;
     constexpr int ND = Pair<FMT>::kDwords;
-    constexpr int LPR = 64 >> SUB;              // lanes per row segment
-    constexpr int RPW = RWV << SUB;             // rows per wave
-    constexpr int RG = WPG * RPW;               // rows per group
     constexpr int NT = 64 * WPG;                // lanes per workgroup
-    constexpr int CP = LPR;                     // pairs per step
-    constexpr int CE = CP * 64;                 // weights per step
     constexpr int XW = kGvWindow;               // weights per activation window
     constexpr int XP = kGvPitch;                // LDS floats per staged column
-    static_assert(XW / CE == (1 << SUB), "steps per activation window");
-    // log2 of the steps per window, opaque to the optimiser: with the
-    // constant folded in, its schedule of the LDS reads of the eight-column
-    // Q4_1 kernel no longer fits in registers
-    int cpw_log = SUB;
-    asm volatile("" : "+s"(cpw_log));
+    static_assert(SUB == kSubMixed || XW / (64 * (64 >> SUB)) == (1 << SUB), "steps per activation window");
     extern __shared__ __attribute__((aligned(16))) float xs[];
     uint8_t *const xq = reinterpret_cast<uint8_t *>(xs);  // 8-bit activations (X8)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int seg = lane >> (6 - SUB);          // row segment of this lane
-    const int sl = lane & (LPR - 1);            // lane within the segment
+    // Lane geometry for a lane split `sub` (2^sub row segments per wave):
+    // constants when the launch has one split, per problem otherwise.
+    struct Geo {
+        int sub;  // log2 of the row segments per wave (= log2 of the steps per window)
+        int lpr;  // lanes per row segment = pairs per step
+        int rpw;  // rows per wave
+        int rg;   // rows per group
+        int seg;  // row segment of this lane
+        int sl;   // lane within the segment
+    };
+    auto geo = [&](int sub) __attribute__((always_inline)) {
+        Geo g;
+        g.sub = sub;
+        g.lpr = 64 >> sub;
+        g.rpw = RWV << sub;
+        g.rg = WPG * g.rpw;
+        g.seg = lane >> (6 - sub);
+        g.sl = lane & (g.lpr - 1);
+        return g;
+    };
+    // log2 of the steps per window of a fixed split, opaque to the optimiser:
+    // with the constant folded in, its schedule of the LDS reads of the
+    // eight-column Q4_1 kernel no longer fits in registers
+    int cpw_log = SUB == kSubMixed ? 0 : SUB;
+    asm volatile("" : "+s"(cpw_log));
     const int b = blockIdx.x;
     const int gbeg = b * split.per + min(b, split.rem);
     const int gend = gbeg + split.per + (b < split.rem ? 1 : 0);
@@ -559,7 +579,12 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         else if constexpr (SRC == kSrcTable) return &args.item[i];
         else return nullptr;  // expert problems are formed in enter()
     };
-    auto chunks = [](int nb) { return (((nb + 1) >> 1) + CP - 1) / CP; };
+    // lane split of problem i
+    auto sub_of = [&](int i) -> int {
+        if constexpr (SUB == kSubMixed) return args.sub[i];
+        else return SUB;
+    };
+    auto chunks = [](int nb, int sub) { return (((nb + 1) >> 1) + (64 >> sub) - 1) >> (6 - sub); };
 
     // Step position (uniform across the workgroup): row group g of problem
     // mi, chunk c, with the problem's descriptor held in registers.  It is
@@ -569,7 +594,12 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         int gb0, gb1;   // the problem's first row group and one past its last
         int nchunks;    // steps per row group
         int e;          // expert id (expert-indexed problems); it.w is the stack
+        int sub;        // the problem's lane split
         GemvItem it;
+    };
+    auto geo_of = [&](const Pos &q) __attribute__((always_inline)) {
+        if constexpr (SUB == kSubMixed) return geo(q.sub);
+        else return geo(SUB);
     };
     // (field by field: a whole-struct copy out of the argument segment is
     // lowered through scratch memory)
@@ -603,7 +633,8 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         }
         q.gb0 = gbase(i);
         q.gb1 = gbase(i + 1);
-        q.nchunks = chunks(q.it.nb);
+        q.sub = sub_of(i);
+        q.nchunks = chunks(q.it.nb, q.sub);
     };
     Pos P;
     P.g = gbeg;
@@ -649,11 +680,12 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
     // the prefetch stays in flight.
     auto load_step = [&](const Pos &q, uint32_t (&dst)[RWV][ND]) __attribute__((always_inline)) {
         const GemvItem &it = q.it;
+        const Geo G = geo_of(q);
         const uint8_t *w = weights(q);
-        const int row0 = (q.g - q.gb0) * RG + wave * RPW + seg * RWV;
+        const int row0 = (q.g - q.gb0) * G.rg + wave * G.rpw + G.seg * RWV;
         const int npairs = (it.nb + 1) >> 1;
         const int64_t row_bytes = (int64_t)it.nb * BS;
-        const int pp = q.c * CP + sl;
+        const int pp = q.c * G.lpr + G.sl;
         if (FAST) {
             const int ppc = min(pp, npairs - 1);
 #pragma unroll
@@ -729,7 +761,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         while (gg < gend) {
             while (gg >= gbase(ii + 1)) ++ii;
             const int nxt = min(gend, gbase(ii + 1));
-            nsteps += (nxt - gg) * chunks(item(ii)->nb);
+            nsteps += (nxt - gg) * chunks(item(ii)->nb, sub_of(ii));
             gg = nxt;
         }
     }
@@ -746,8 +778,10 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         constexpr int DEPTH = decltype(depth_tag)::value;
         constexpr bool PREFETCH = DEPTH > 0;
         const GemvItem &it = P.it;
+        const Geo G = geo_of(P);
         const int npairs = (it.nb + 1) >> 1;
-        const int wi = P.c >> cpw_log;  // activation window of this step
+        const int swl = SUB == kSubMixed ? G.sub : cpw_log;  // log2 of the steps per window
+        const int wi = P.c >> swl;  // activation window of this step
 
         // the next step, and what to prefetch: past the workgroup's last step
         // a prefetch repeats this step's loads
@@ -830,11 +864,11 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         }
 
         // compute this step
-        const int row0 = (P.g - P.gb0) * RG + wave * RPW + seg * RWV;
+        const int row0 = (P.g - P.gb0) * G.rg + wave * G.rpw + G.seg * RWV;
         const int nrows = max(0, min(RWV, it.m - row0));
-        const int pp = P.c * CP + sl;
+        const int pp = P.c * G.lpr + G.sl;
         if (nrows > 0 && pp < npairs) {
-            const int el = (P.c - (wi << cpw_log)) * CE + sl * 64;  // window element of the pair
+            const int el = (P.c - (wi << swl)) * (64 * G.lpr) + G.sl * 64;  // window element of the pair
             if constexpr (X8)
                 pair_dot_x8<FMT, NC, RWV, FAST>(cur, nrows, FAST || (2 * pp + 1 < it.nb), xq, el >> 6, acc);
             else
@@ -845,11 +879,22 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
         if (P.c == P.nchunks - 1) {
 #pragma unroll
             for (int r = 0; r < RWV; ++r) {
-                if (SUB > 0 || r < nrows) {  // (uniform across the wave when SUB == 0)
+                if (G.sub > 0 || r < nrows) {  // (uniform across the wave when the split is 0)
 #pragma unroll
                     for (int j = 0; j < NC; ++j) {
-                        const float sum = seg_sum<LPR>(acc[r][j]);
-                        if (sl == seg_store_lane(LPR) && r < nrows)
+                        float sum;
+                        if constexpr (SUB == kSubMixed) {
+                            // wave-uniform: a row group belongs to one problem
+                            switch (G.sub) {
+                            case 0: sum = seg_sum<64>(acc[r][j]); break;
+                            case 1: sum = seg_sum<32>(acc[r][j]); break;
+                            case 2: sum = seg_sum<16>(acc[r][j]); break;
+                            default: sum = seg_sum<8>(acc[r][j]); break;
+                            }
+                        } else {
+                            sum = seg_sum<(64 >> SUB)>(acc[r][j]);
+                        }
+                        if (G.sl == seg_store_lane(G.lpr) && r < nrows)
                             it.y[j * it.ldy + row0 + r] = bad(P) ? __builtin_nanf("") : sum;
                     }
                 }
@@ -921,7 +966,7 @@ template <int FMT, int NC, int SUB, bool FAST, bool X8 = false, bool R2 = false>
         SUB > 0 ? QK_GEMV_SHORT_WPG
                 : (kX8Q8Wide ? 8
                              : (NC <= 4 ? 8 : (FMT == QK_Q4_1 ? (FAST ? 12 : 8) : (FMT == QK_Q4_0 ? 8 : 4))));
-    static constexpr int kRowsPerGroup = kWPG * (kRWV << SUB);
+    static constexpr int kRowsPerGroup = SUB == kSubMixed ? kWPG : kWPG * (kRWV << SUB);  // (mixed: per problem)
 };
 
 // Rows per wave (as 2^SUB) for one-column launches whose longest row has
@@ -977,13 +1022,18 @@ int gemv_table_run(GemvArgs &a, hipStream_t stream) {
     int64_t g = 0;
     a.gbase[0] = 0;
     for (int i = 0; i < a.count; ++i) {
-        g += (a.item[i].m + RG - 1) / RG;
+        const int rg = SUB == kSubMixed ? RG << a.sub[i] : RG;
+        g += (a.item[i].m + rg - 1) / rg;
         if (g > INT32_MAX) return QK_ERR_INVALID_ARG;
         a.gbase[i + 1] = (int)g;
     }
-    if (a.count == 1) return gemv_launch<FMT, NC, kSrcOne, SUB, FAST, X8, R2>(a.item[0], g, 0, stream);
-    if constexpr (X8) return QK_ERR_INVALID_ARG;  // 8-bit activations: one problem per launch
-    else return gemv_launch<FMT, NC, kSrcTable, SUB, FAST, false, R2>(a, g, 0, stream);
+    if constexpr (SUB == kSubMixed) {
+        return gemv_launch<FMT, NC, kSrcTable, SUB, FAST, false, false>(a, g, 0, stream);  // count > 1
+    } else {
+        if (a.count == 1) return gemv_launch<FMT, NC, kSrcOne, SUB, FAST, X8, R2>(a.item[0], g, 0, stream);
+        if constexpr (X8) return QK_ERR_INVALID_ARG;  // 8-bit activations: one problem per launch
+        else return gemv_launch<FMT, NC, kSrcTable, SUB, FAST, false, R2>(a, g, 0, stream);
+    }
 }
 
 template <int FMT, int NC, int SUB, bool X8>
@@ -1004,7 +1054,20 @@ template <int FMT, int NC, bool X8>
 int gemv_table_fmt(GemvArgs &a, bool fast, hipStream_t stream) {
     if constexpr (NC == 1) {
         int npairs = 0;
-        for (int i = 0; i < a.count; ++i) npairs = max(npairs, (a.item[i].nb + 1) / 2);
+        bool mixed = false;
+        for (int i = 0; i < a.count; ++i) {
+            npairs = max(npairs, (a.item[i].nb + 1) / 2);
+            a.sub[i] = gemv_sub((a.item[i].nb + 1) / 2);
+            mixed = mixed || a.sub[i] != a.sub[0];
+        }
+        // problems whose rows want different splits (e.g. a layer's
+        // tensor-parallel share: 8-pair and 64-pair rows) keep their own
+        if constexpr (!X8) {
+            if (mixed && a.count > 1) {
+                if (fast) return gemv_table_run<FMT, NC, kSubMixed, true, false>(a, stream);
+                return gemv_table_run<FMT, NC, kSubMixed, false, false>(a, stream);
+            }
+        }
         switch (gemv_sub(npairs)) {
         case 3: return gemv_table_sub<FMT, NC, 3, X8>(a, fast, stream);
         case 2: return gemv_table_sub<FMT, NC, 2, X8>(a, fast, stream);
