@@ -439,18 +439,38 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < kCT; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // (activation fragments read one group of eight products ahead; two
+    // groups, as in the direct-load kernel, spill registers here)
     auto mma = [&](const ASet &a, int buf) __attribute__((always_inline)) {
         const uint16_t *bb = bsm + buf * kBufHalves + (lane & 15) * kPitch + 8 * g;
+        auto frag = [&](int q, int h) -> half8_t {
+            const int ks = q >> 2, j = 2 * (q & 3) + h;
+            return *reinterpret_cast<const half8_t *>(bb + j * 16 * kPitch + 32 * ks);
+        };
+        constexpr int FA = 1;
+        half8_t fr[FA + 1][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int u = 0; u < FA; ++u) {
+            fr[u][0] = frag(u, 0);
+            fr[u][1] = frag(u, 1);
+        }
 #pragma unroll
-            for (int j = 0; j < kCT; ++j) {
-                const half8_t bf = *reinterpret_cast<const half8_t *>(bb + j * 16 * kPitch + 32 * ks);
-#pragma unroll
-                for (int i = 0; i < kRT; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a[i][ks]), bf,
-                                                                       acc[i][j], 0, 0, 0);
+        for (int q = 0; q < 8; ++q) {
+            const int ks = q >> 2, j = 2 * (q & 3);
+            if (q + FA < 8) {
+                fr[(q + FA) % (FA + 1)][0] = frag(q + FA, 0);
+                fr[(q + FA) % (FA + 1)][1] = frag(q + FA, 1);
             }
+            const half8_t c0 = fr[q % (FA + 1)][0], c1 = fr[q % (FA + 1)][1];
+#pragma unroll
+            for (int i = 0; i < kRT; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a[i][ks]), c0,
+                                                                   acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < kRT; ++i)
+                acc[i][j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a[i][ks]), c1,
+                                                                       acc[i][j + 1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
