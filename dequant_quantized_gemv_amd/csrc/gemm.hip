@@ -106,6 +106,17 @@ __device__ __forceinline__ uint32_t gm_pk_mul(uint32_t a, uint32_t b) {
 __device__ __forceinline__ uint32_t gm_pack2(float a, float b) {
     return (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
 }
+// The fp32 weight d*q + m (one rounding), then its fp16 (a second rounding).
+// The fp32 value is made opaque first: otherwise the compiler fuses the fma
+// and the conversion into one mixed-precision fma that rounds the exact sum
+// straight to fp16, which differs where the fp32 rounding lands on an fp16
+// tie (d = 0x3556, m = 0x0001, q = 3: 1.0 by the definition, 1.0009765625
+// fused).
+__device__ __forceinline__ float gm_q41_weight(float d, float q, float m) {
+    float v = __builtin_fmaf(d, q, m);
+    asm volatile("" : "+v"(v));
+    return v;
+}
 __device__ __forceinline__ uint32_t gm_h2(float v) {
     const uint32_t b = f2h(v);
     return b | (b << 16);
@@ -160,10 +171,10 @@ __device__ __forceinline__ u32x4g_t gm_decode8(uint32_t qa, uint32_t qb, uint32_
         // d here is d or d/16 (exact in fp32); times the in-place code it is
         // d * q exactly, so the fma rounds d*q + m once, as the definition does
         const uint32_t ua = qa & c.mask, ub = qb & c.mask;
-        return u32x4g_t{gm_pack2(__builtin_fmaf(d, ubyte_f<0>(ua), mm), __builtin_fmaf(d, ubyte_f<1>(ua), mm)),
-                        gm_pack2(__builtin_fmaf(d, ubyte_f<2>(ua), mm), __builtin_fmaf(d, ubyte_f<3>(ua), mm)),
-                        gm_pack2(__builtin_fmaf(d, ubyte_f<0>(ub), mm), __builtin_fmaf(d, ubyte_f<1>(ub), mm)),
-                        gm_pack2(__builtin_fmaf(d, ubyte_f<2>(ub), mm), __builtin_fmaf(d, ubyte_f<3>(ub), mm))};
+        return u32x4g_t{gm_pack2(gm_q41_weight(d, ubyte_f<0>(ua), mm), gm_q41_weight(d, ubyte_f<1>(ua), mm)),
+                        gm_pack2(gm_q41_weight(d, ubyte_f<2>(ua), mm), gm_q41_weight(d, ubyte_f<3>(ua), mm)),
+                        gm_pack2(gm_q41_weight(d, ubyte_f<0>(ub), mm), gm_q41_weight(d, ubyte_f<1>(ub), mm)),
+                        gm_pack2(gm_q41_weight(d, ubyte_f<2>(ub), mm), gm_q41_weight(d, ubyte_f<3>(ub), mm))};
     }
 }
 

@@ -415,6 +415,34 @@ def test_gemm_identity_gives_fp16_weights(fmt, m, k):
     assert np.array_equal(y, W16.T), f"gemm identity {fmt} {m}x{k}"
 
 
+def test_gemm_q4_1_weights_round_through_fp32():
+    """Q4_1's fp16 weight is the RNE of the fp32 value d*q + m (itself one
+    rounding): where the exact sum lies just above an fp16 tie that the fp32
+    rounding lands on, the two-step value is the even neighbour and a single
+    rounding of the exact sum would give the other one.  Rows of such blocks
+    (d, m, q found by search over fp16 values), times X = I, must give the
+    oracle's fp16 weights bit for bit, as must qk_dequantize to fp16."""
+    cases = [(0x3556, 0x0001, 3), (0x5156, 0x0062, 3), (0x5556, 0x00C3, 3), (0x5956, 0x0124, 3),
+             (0x5956, 0x0185, 3)]
+    rows = []
+    for d, mm, q in cases:
+        blk = np.zeros(20, dtype=np.uint8)
+        blk[0:2] = np.array([d], dtype=np.uint16).view(np.uint8)
+        blk[2:4] = np.array([mm], dtype=np.uint16).view(np.uint8)
+        blk[4:] = q | (q << 4)
+        rows.append(blk)
+    w = np.concatenate(rows)
+    m, k = len(cases), 32
+    W16 = oracle.dequantize_f16("q4_1", w, m, k)
+    # the two-step value differs from a direct rounding of the exact sum here
+    for (d, mm, q), row in zip(cases, W16):
+        exact = float(np.uint16(d).view(np.float16)) * q + float(np.uint16(mm).view(np.float16))
+        assert row[0] != np.float16(exact).view(np.uint16), (d, mm, q)
+    assert np.array_equal(_gpu_dequant("q4_1", w, m, k, "f16"), W16)
+    y = _gpu_gemm("q4_1", w, m, k, np.eye(k, dtype=np.float16))
+    assert np.array_equal(y, W16.view(np.float16).astype(np.float32).T)
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m,k,n", [(257, 640, 129), (300, 2080, 17), (512, 4096, 256)])
 def test_gemm_against_fp16_weight_product(fmt, m, k, n):
