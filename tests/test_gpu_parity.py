@@ -174,6 +174,23 @@ def _gpu_gemv(fmt, w, m, k, x2d, ldx=None, ldy=None, w_off=0, x_off=0, stream=No
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_subnormal_activations(fmt):
+    """Activations in the fp32 subnormal range (N(0,1) scaled by 2^-130) and
+    products below the normal range: nothing may be flushed to zero, so the
+    outputs stay within 1e-4 * S of the oracle (a flush would give 0 against
+    a nonzero reference)."""
+    m, k, n = 130, 2080, 3
+    _say("gemv subnormal activations", fmt)
+    w = _weights(fmt, m, k, seed=48)
+    x = (synth.activations(k, n, seed=48, tensor_id=2).astype(np.float64) * 2.0 ** -130).astype(np.float32)
+    assert np.all(np.abs(x[x != 0]) < np.finfo(np.float32).tiny)
+    y = _gpu_gemv(fmt, w, m, k, x)
+    yref, s = oracle.dot(fmt, w, m, k, x, n)
+    assert np.all(s > 0)
+    assert_within(y, yref, s, GEMV_TOL, f"gemv subnormal {fmt}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n", [1, 2, 3])
 @pytest.mark.parametrize("m,k,w_off", [(16403, 4096, 0), (16400, 2048, 2), (16403, 1376, 0)])
 def test_gemv_two_rows_per_wave(fmt, n, m, k, w_off):
@@ -413,6 +430,27 @@ def test_gemm_identity_gives_fp16_weights(fmt, m, k):
     y = _gpu_gemm(fmt, w, m, k, xh)
     W16 = oracle.dequantize_f16(fmt, w, m, k).view(np.float16).astype(np.float32)
     assert np.array_equal(y, W16.T), f"gemm identity {fmt} {m}x{k}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_identity_edge_blocks(fmt):
+    """The dequantize edge blocks (subnormal, negative and zero scales, code 8
+    with a negative scale, Q8_0 -128 / 127, Q4_1 offsets of every sign)
+    through the GEMM with X = I: every output is that block's fp16 weight,
+    including fp16-subnormal weights (no flush in the packed fp16 dequant or
+    the MFMA).  The two blocks whose fp16 weights overflow to +-inf are left
+    out: with X = I their infinities meet the zero activations (inf * 0)."""
+    w_all, nb = _edge_blocks(fmt)
+    bs = synth.BLOCK_BYTES[fmt]
+    keep = [i for i in range(nb) if i not in (4, 5)]
+    w = np.concatenate([w_all[i * bs:(i + 1) * bs] for i in keep])
+    m, k = len(keep), 32
+    _say("gemm identity edge", fmt)
+    W16 = oracle.dequantize_f16(fmt, w, m, k).view(np.float16)
+    assert np.isfinite(W16).all()
+    assert (np.abs(W16[W16 != 0]) < np.float16(6.1035e-05)).any()  # fp16 subnormals occur
+    y = _gpu_gemm(fmt, w, m, k, np.eye(k, dtype=np.float16))
+    assert np.array_equal(y, W16.astype(np.float32).T)
 
 
 def test_gemm_q4_1_weights_round_through_fp32():
