@@ -174,6 +174,25 @@ def _gpu_gemv(fmt, w, m, k, x2d, ldx=None, ldy=None, w_off=0, x_off=0, stream=No
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_unit_vectors_edge_blocks(fmt):
+    """The dequantize edge blocks (all ten: subnormal, negative, zero, largest
+    and smallest scales, Q8_0 -128 / 127, Q4_1 offsets of every sign) times
+    unit vectors e_c, eight columns per call: every output is exactly the fp32
+    weight W[i, c] (one nonzero term, the rest exact zeros)."""
+    w, nb = _edge_blocks(fmt)
+    k = 32
+    W = oracle.dequantize_f32(fmt, w, nb, k)
+    assert np.isfinite(W).all()
+    _say("gemv unit vectors edge", fmt)
+    for c0 in range(0, k, 8):
+        x = np.zeros((8, k), np.float32)
+        for j in range(8):
+            x[j, c0 + j] = 1.0
+        y = _gpu_gemv(fmt, w, nb, k, x)
+        assert np.array_equal(y, W[:, c0:c0 + 8].T), f"columns {c0}..{c0 + 7}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_gemv_subnormal_activations(fmt):
     """Activations in the fp32 subnormal range (N(0,1) scaled by 2^-130) and
     products below the normal range: nothing may be flushed to zero, so the
