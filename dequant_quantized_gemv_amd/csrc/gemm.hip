@@ -287,9 +287,13 @@ constexpr size_t gm_lds_bytes() {
 }
 
 // FAST: w 4-byte aligned and an even number of blocks per row (every pair
-// starts on 4 bytes and both of its blocks exist), x 16-byte aligned and
-// ldx % 8 == 0.  YALIGNED: y 16-byte aligned and ldy % 4 == 0.
-template <int FMT, bool FAST, bool YALIGNED>
+// starts on 4 bytes and both of its blocks exist).  XFAST: x 16-byte aligned
+// and ldx % 8 == 0; otherwise each thread's 64 activation bytes are read as
+// the 17 dwords from the 4-byte boundary below them and shifted into place
+// (a 2-byte aligned column starts 2 bytes into its first dword and ends 2
+// bytes into its last, so nothing outside those dwords is read).
+// YALIGNED: y 16-byte aligned and ldy % 4 == 0.
+template <int FMT, bool FAST, bool XFAST, bool YALIGNED>
 __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
     const uint8_t *__restrict__ w, int m, int nb, const uint16_t *__restrict__ x, int64_t ldx,
     int n, float *__restrict__ y, int64_t ldy, int mtiles, int ntiles) {
@@ -410,19 +414,31 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
     auto load_b = [&](int s, XSet &xb) __attribute__((always_inline)) {
         const int pair = pbase + min(s, gsteps - 1);
         const uint16_t *p = xcol + pair * kBK;
+        if constexpr (XFAST) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if constexpr (FAST) {
-                xb[u] = *reinterpret_cast<const u32x4g_t *>(p + 8 * u);
-            } else {
-                uint32_t e[4] = {0u, 0u, 0u, 0u};
-                if (pair * kBK + 32 * bhalf + 8 * u < k) {
+            for (int u = 0; u < 4; ++u) xb[u] = *reinterpret_cast<const u32x4g_t *>(p + 8 * u);
+        } else if (pair * kBK + 32 * bhalf < k) {
+            // (k is a multiple of 32: a thread's 32 activations are all in
+            // the column or all past it)
+            const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+            const uint32_t *base = reinterpret_cast<const uint32_t *>(a & ~uintptr_t(3));
+            const uint32_t sh = (uint32_t)(a & 3);  // 0 or 2
+            uint32_t d[17];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        e[v] = (uint32_t)p[8 * u + 2 * v] | ((uint32_t)p[8 * u + 2 * v + 1] << 16);
-                }
-                xb[u] = u32x4g_t{e[0], e[1], e[2], e[3]};
+            for (int u = 0; u < 4; ++u) {
+                const u32x4g_a4 t = *reinterpret_cast<const u32x4g_a4 *>(base + 4 * u);
+                d[4 * u] = t.x; d[4 * u + 1] = t.y; d[4 * u + 2] = t.z; d[4 * u + 3] = t.w;
             }
+            d[16] = sh ? base[16] : 0u;  // only a 2-byte offset reaches into a 17th dword
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                xb[u] = u32x4g_t{__builtin_amdgcn_alignbyte(d[4 * u + 1], d[4 * u], sh),
+                                 __builtin_amdgcn_alignbyte(d[4 * u + 2], d[4 * u + 1], sh),
+                                 __builtin_amdgcn_alignbyte(d[4 * u + 3], d[4 * u + 2], sh),
+                                 __builtin_amdgcn_alignbyte(d[4 * u + 4], d[4 * u + 3], sh)};
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xb[u] = u32x4g_t{0u, 0u, 0u, 0u};
         }
     };
     auto store_b = [&](const XSet &xb, int buf) __attribute__((always_inline)) {
@@ -770,10 +786,10 @@ static int launch_gemm_dma(const uint8_t *w, int m, int nb, const uint16_t *x, i
                       w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles);
 }
 
-template <int FMT, bool FAST, bool YA>
+template <int FMT, bool FAST, bool XFAST, bool YA>
 static int launch_gemm(const uint8_t *w, int m, int nb, const uint16_t *x, int64_t ldx, int n,
                        float *y, int64_t ldy, int mtiles, int ntiles, hipStream_t stream) {
-    auto kern = gemm_kernel<FMT, FAST, YA>;
+    auto kern = gemm_kernel<FMT, FAST, XFAST, YA>;
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)gm_lds_bytes<FMT>()) != hipSuccess)
         return QK_ERR_LAUNCH;
@@ -786,17 +802,23 @@ static int dispatch_gemm(const uint8_t *w, int m, int nb, const uint16_t *x, int
                          float *y, int64_t ldy, hipStream_t stream) {
     const int mtiles = (m + kBM - 1) / kBM;
     const int ntiles = (n + kBN - 1) / kBN;
-    const bool fast = ((uintptr_t)w % 4) == 0 && (nb % 2) == 0 && ((uintptr_t)x % 16) == 0 &&
-                      (ldx % 8) == 0;
+    const bool fast = ((uintptr_t)w % 4) == 0 && (nb % 2) == 0;
+    const bool xfast = ((uintptr_t)x % 16) == 0 && (ldx % 8) == 0;
     const bool ya = ((uintptr_t)y % 16) == 0 && (ldy % 4) == 0;
     // the direct-load path moves whole super-steps (two pairs): k % 128 == 0
-    const bool dma = fast && (nb % 4) == 0;
+    const bool dma = fast && xfast && (nb % 4) == 0;
     if (dma && ya) return launch_gemm_dma<FMT, true>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
     if (dma) return launch_gemm_dma<FMT, false>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
-    if (fast && ya) return launch_gemm<FMT, true, true>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
-    if (fast) return launch_gemm<FMT, true, false>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
-    if (ya) return launch_gemm<FMT, false, true>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
-    return launch_gemm<FMT, false, false>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
+    auto run = [&](auto fw, auto fx) {
+        if (ya) return launch_gemm<FMT, decltype(fw)::value, decltype(fx)::value, true>(w, m, nb, x, ldx, n, y, ldy,
+                                                                                        mtiles, ntiles, stream);
+        return launch_gemm<FMT, decltype(fw)::value, decltype(fx)::value, false>(w, m, nb, x, ldx, n, y, ldy, mtiles,
+                                                                                 ntiles, stream);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    if (fast) return xfast ? run(T{}, T{}) : run(T{}, F{});
+    return xfast ? run(F{}, T{}) : run(F{}, F{});
 }
 
 int launch_mul_mat(int fmt, const void *w, int64_t m, int64_t k, const uint16_t *x, int64_t n,
