@@ -377,21 +377,49 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
                 qa[4 * kNC] = *reinterpret_cast<const uint32_t *>(arow[kNC] + off);
             }
         } else {
-            // 2-byte loads; a missing second block (odd block count) reads as
-            // zeros (scale 0, weights 0)
+            // A pair may start 2 bytes past a dword (2-byte aligned w, or
+            // every other row of an odd block count).  A chunk whose bytes all
+            // belong to the row is read as the dwords from the boundary below
+            // it and shifted into place (the extra dword of a 2-byte offset
+            // holds the chunk's last two bytes, so nothing outside the row's
+            // dwords is read); a chunk reaching past a missing second block
+            // (the last pair of an odd block count) takes 2-byte loads, the
+            // missing bytes reading as zeros (scale 0, weights 0).
             const bool second = 2 * pair + 1 < nb;
 #pragma unroll
             for (int u = 0; u <= kNC; ++u) {
                 const int nd = u < kNC ? 4 : kTail / 4;
                 const int pos0 = u < kNC ? 16 * ((gtid + 256 * u) % kNC) : 16 * kNC;
-                const uint16_t *hp = reinterpret_cast<const uint16_t *>(arow[u] + off);
+                const uint8_t *a = arow[u] + off;
+                if (second || pos0 + 4 * nd <= F::kBytes) {
+                    const uintptr_t ai = reinterpret_cast<uintptr_t>(a);
+                    const uint32_t *base = reinterpret_cast<const uint32_t *>(ai & ~uintptr_t(3));
+                    const uint32_t sh = (uint32_t)(ai & 3);  // 0 or 2
+                    uint32_t d[5];
+                    if (nd == 4) {
+                        const u32x4g_a4 t = *reinterpret_cast<const u32x4g_a4 *>(base);
+                        d[0] = t.x; d[1] = t.y; d[2] = t.z; d[3] = t.w;
+                    } else if (nd == 2) {
+                        const u32x2g_a4 t = *reinterpret_cast<const u32x2g_a4 *>(base);
+                        d[0] = t.x; d[1] = t.y; d[2] = 0u; d[3] = 0u;
+                    } else {
+                        d[0] = base[0]; d[1] = 0u; d[2] = 0u; d[3] = 0u;
+                    }
+                    d[4] = 0u;
+                    if (sh) d[nd] = base[nd];
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    if (d < nd) {
-                        const int o = pos0 + 4 * d;
-                        const uint32_t lo = (o < F::kBytes || second) ? (uint32_t)hp[2 * d] : 0u;
-                        const uint32_t hi = (o + 2 < F::kBytes || second) ? (uint32_t)hp[2 * d + 1] : 0u;
-                        qa[4 * u + d] = lo | (hi << 16);
+                    for (int e = 0; e < 4; ++e)
+                        if (e < nd) qa[4 * u + e] = __builtin_amdgcn_alignbyte(d[e + 1], d[e], sh);
+                } else {
+                    const uint16_t *hp = reinterpret_cast<const uint16_t *>(a);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (e < nd) {
+                            const int o = pos0 + 4 * e;
+                            const uint32_t lo = o < F::kBytes ? (uint32_t)hp[2 * e] : 0u;
+                            const uint32_t hi = o + 2 < F::kBytes ? (uint32_t)hp[2 * e + 1] : 0u;
+                            qa[4 * u + e] = lo | (hi << 16);
+                        }
                     }
                 }
             }
