@@ -59,7 +59,7 @@ int qk_dequantize(int fmt, const void *w, int64_t rows, int64_t k, int out_dtype
     if (rows < 0 || k < 0 || k % 32 != 0) return QK_ERR_INVALID_ARG;
     if (rows == 0 || k == 0) return QK_OK;
     if (k > kMaxDim || rows > INT64_MAX / (k / 32)) return QK_ERR_INVALID_ARG;
-    // 2-byte aligned input: one workgroup per chunk of 128 blocks, one grid dimension
+    // chunks of 128 blocks are numbered in 32 bits on the device side
     if ((rows * (k / 32) + 127) / 128 > (int64_t)INT32_MAX) return QK_ERR_INVALID_ARG;
     if (w == nullptr || out == nullptr) return QK_ERR_INVALID_ARG;
     const size_t es = out_dtype == QK_F32 ? 4 : 2;

@@ -12,6 +12,8 @@
 //
 // The matrix is a flat run of blocks (rows are back to back with no padding
 // and k % 32 == 0), so block b always produces outputs [32b, 32b + 32).
+#include <type_traits>
+
 #include "qk_common.h"
 #include "qk_internal.h"
 
@@ -21,15 +23,6 @@ constexpr int kDqThreads = 256;
 // quant blocks per chunk (128 measured 2-3 % faster than 256 on a 4096 x
 // 4096 Q4_0 -> fp32 dequantize: each workgroup then takes two chunks)
 constexpr int kDqBlocks = 128;
-
-// Copy `bytes` (even) from global memory to LDS with 2-byte loads (input
-// that is only 2-byte aligned).
-__device__ __forceinline__ void stage_to_lds(uint8_t *dst, const uint8_t *__restrict__ src, int bytes) {
-    const int n2 = bytes >> 1;
-    const uint16_t *s2 = reinterpret_cast<const uint16_t *>(src);
-    uint16_t *d2 = reinterpret_cast<uint16_t *>(dst);
-    for (int i = threadIdx.x; i < n2; i += kDqThreads) d2[i] = s2[i];
-}
 
 // Four consecutive elements j0..j0+3 (j0 % 4 == 0) of the block at LDS offset
 // boff, as fp32 in the definition's operation order.
@@ -53,77 +46,24 @@ __device__ __forceinline__ void decode4(const uint8_t *lds, int boff, int j0, fl
     }
 }
 
-// One chunk per workgroup, for 2-byte aligned input.
-template <int FMT, bool ALIGNED_OUT>
-__global__ __launch_bounds__(kDqThreads) void dequant_f32_kernel(
-    const uint8_t *__restrict__ w, int64_t nblocks, float *__restrict__ out) {
-    using F = Format<FMT>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kDqBlocks * F::kBytes];
-    const int64_t blk0 = (int64_t)blockIdx.x * kDqBlocks;
-    const int nb = (int)min((int64_t)kDqBlocks, nblocks - blk0);
-    stage_to_lds(lds, w + blk0 * F::kBytes, nb * F::kBytes);
-    __syncthreads();
-    float *o = out + blk0 * kBlockElems;
-    const int ngroups = nb * 8;  // 4-element groups
-    for (int g = threadIdx.x; g < ngroups; g += kDqThreads) {
-        float v[4];
-        decode4<FMT>(lds, (g >> 3) * F::kBytes, (g & 7) * 4, v);
-        if (ALIGNED_OUT) {
-            *reinterpret_cast<float4 *>(o + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[4 * g + i] = v[i];
-        }
-    }
-}
-
-template <int FMT, bool ALIGNED_OUT>
-__global__ __launch_bounds__(kDqThreads) void dequant_f16_kernel(
-    const uint8_t *__restrict__ w, int64_t nblocks, uint16_t *__restrict__ out) {
-    using F = Format<FMT>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kDqBlocks * F::kBytes];
-    const int64_t blk0 = (int64_t)blockIdx.x * kDqBlocks;
-    const int nb = (int)min((int64_t)kDqBlocks, nblocks - blk0);
-    stage_to_lds(lds, w + blk0 * F::kBytes, nb * F::kBytes);
-    __syncthreads();
-    uint16_t *o = out + blk0 * kBlockElems;
-    const int ngroups = nb * 4;  // 8-element groups
-    for (int g = threadIdx.x; g < ngroups; g += kDqThreads) {
-        const int boff = (g >> 2) * F::kBytes;
-        const int j0 = (g & 3) * 8;
-        float v[8];
-        decode4<FMT>(lds, boff, j0, v);
-        decode4<FMT>(lds, boff, j0 + 4, v + 4);
-        uint16_t h[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = f2h(v[i]);
-        if (ALIGNED_OUT) {
-            uint4 p;
-            p.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-            p.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-            p.z = (uint32_t)h[4] | ((uint32_t)h[5] << 16);
-            p.w = (uint32_t)h[6] | ((uint32_t)h[7] << 16);
-            *reinterpret_cast<uint4 *>(o + 8 * g) = p;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[8 * g + i] = h[i];
-        }
-    }
-}
-
-// Aligned input (w 16-byte aligned, so every chunk of 128 blocks of 18 / 20
-// / 34 bytes starts on 16 bytes): a workgroup walks chunks c, c + gridDim.x,
-// ... and requests the next chunk's bytes into registers before it writes
-// the current chunk's outputs, so the reads of one chunk overlap the writes
-// of the one before.  Outputs are written with non-temporal 16-byte stores
-// (the output is not read again by this kernel; streaming it past the caches
-// measured 14.3 -> 12.9 us on a 4096 x 4096 Q4_0 -> fp32 dequantize).
+// A workgroup walks chunks of 128 blocks c, c + gridDim.x, ... and requests
+// the next chunk's bytes into registers before it writes the current chunk's
+// outputs, so the reads of one chunk overlap the writes of the one before.
+// Chunks are 2304 / 2560 / 4352 bytes, multiples of 16, so every 16-byte
+// piece of every chunk has the alignment of w.  A16: w 16-byte aligned, one
+// 16-byte load per piece.  Otherwise (w 2- or 4-byte aligned) a piece is read
+// as the four dwords from the 4-byte boundary at or below it, plus for a
+// 2-byte offset the dword holding its last two bytes, and shifted into place
+// when it is written to LDS (every dword read holds bytes of the piece).
+// Outputs are written with non-temporal 16-byte stores (the output is not
+// read again by this kernel; streaming it past the caches measured 14.3 ->
+// 12.9 us on a 4096 x 4096 Q4_0 -> fp32 dequantize).
 constexpr int kDqWgPerCu = 8;
 
 typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 
-template <int FMT, bool F16, bool ALIGNED_OUT>
+template <int FMT, bool F16, bool ALIGNED_OUT, bool A16>
 __global__ __launch_bounds__(kDqThreads) void dequant_loop_kernel(
     const uint8_t *__restrict__ w, int64_t nblocks, void *__restrict__ out_) {
     using F = Format<FMT>;
@@ -134,17 +74,34 @@ __global__ __launch_bounds__(kDqThreads) void dequant_loop_kernel(
     const int64_t nchunks = (nblocks + kDqBlocks - 1) / kDqBlocks;
     const int tid = threadIdx.x;
     int64_t c = blockIdx.x;
-    // (three named registers rather than an array: a loop-carried private
-    // array is moved to LDS by the compiler, with a wait after every load)
-    uint4 r0, r1, r2;
+    // (named registers rather than arrays: a loop-carried private array is
+    // moved to LDS by the compiler, with a wait after every load)
+    typedef uint32_t u32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
+    const uint32_t sh = A16 ? 0u : (uint32_t)(reinterpret_cast<uintptr_t>(w) & 3);  // 0 or 2
+    const uint8_t *const wb = w - sh;  // 4-byte aligned
+    u32x4a4_t r0, r1, r2;
+    uint32_t e0 = 0u, e1 = 0u, e2 = 0u;  // last dword of a 2-byte offset piece
+    auto piece = [&](const uint8_t *cb, int i, u32x4a4_t &r, uint32_t &e) __attribute__((always_inline)) {
+        if constexpr (A16) {
+            r = *reinterpret_cast<const u32x4a4_t *>(reinterpret_cast<const uint4 *>(cb) + i);
+        } else {
+            r = *reinterpret_cast<const u32x4a4_t *>(cb + 16 * i);
+            if (sh) e = *reinterpret_cast<const uint32_t *>(cb + 16 * i + 16);
+        }
+    };
     auto fetch = [&](int64_t ch) __attribute__((always_inline)) {
         const int nb = (int)min((int64_t)kDqBlocks, nblocks - ch * kDqBlocks);
         const int n16 = (nb * F::kBytes) >> 4;
-        const uint4 *src = reinterpret_cast<const uint4 *>(w + ch * kChunkBytes);
+        const uint8_t *cb = wb + ch * kChunkBytes;
         // every thread loads (a piece past the chunk's end repeats its last one)
-        r0 = src[min(tid, n16 - 1)];
-        if constexpr (kU > 1) r1 = src[min(tid + kDqThreads, n16 - 1)];
-        if constexpr (kU > 2) r2 = src[min(tid + 2 * kDqThreads, n16 - 1)];
+        piece(cb, min(tid, n16 - 1), r0, e0);
+        if constexpr (kU > 1) piece(cb, min(tid + kDqThreads, n16 - 1), r1, e1);
+        if constexpr (kU > 2) piece(cb, min(tid + 2 * kDqThreads, n16 - 1), r2, e2);
+    };
+    auto placed = [&](const u32x4a4_t &r, uint32_t e) -> uint4 {
+        if constexpr (A16) return make_uint4(r.x, r.y, r.z, r.w);
+        else return make_uint4(__builtin_amdgcn_alignbyte(r.y, r.x, sh), __builtin_amdgcn_alignbyte(r.z, r.y, sh),
+                               __builtin_amdgcn_alignbyte(r.w, r.z, sh), __builtin_amdgcn_alignbyte(e, r.w, sh));
     };
     fetch(c);
     for (;;) {
@@ -152,9 +109,9 @@ __global__ __launch_bounds__(kDqThreads) void dequant_loop_kernel(
         const int bytes = nb * F::kBytes;
         const int n16 = bytes >> 4;
         uint4 *l16 = reinterpret_cast<uint4 *>(lds);
-        if (tid < n16) l16[tid] = r0;
-        if constexpr (kU > 1) if (tid + kDqThreads < n16) l16[tid + kDqThreads] = r1;
-        if constexpr (kU > 2) if (tid + 2 * kDqThreads < n16) l16[tid + 2 * kDqThreads] = r2;
+        if (tid < n16) l16[tid] = placed(r0, e0);
+        if constexpr (kU > 1) if (tid + kDqThreads < n16) l16[tid + kDqThreads] = placed(r1, e1);
+        if constexpr (kU > 2) if (tid + 2 * kDqThreads < n16) l16[tid + 2 * kDqThreads] = placed(r2, e2);
         // a partial last chunk may end with fewer than 16 bytes
         if ((bytes & 15) != 0) {
             const uint16_t *s2 = reinterpret_cast<const uint16_t *>(w + c * kChunkBytes + (n16 << 4));
@@ -207,28 +164,24 @@ template <int FMT>
 static int dispatch_dequant(const uint8_t *w, int64_t nblocks, int out_dtype, void *out,
                             hipStream_t stream) {
     const dim3 block(kDqThreads);
-    const bool ain = ((uintptr_t)w % 16) == 0;
+    const bool a16 = ((uintptr_t)w % 16) == 0;
     const bool aout = ((uintptr_t)out % 16) == 0;
     const bool f32 = out_dtype == QK_F32;
-    if (ain) {
-        const int64_t nchunks = (nblocks + kDqBlocks - 1) / kDqBlocks;
-        const int64_t cap = (int64_t)device_cus() * kDqWgPerCu;
-        const dim3 grid((unsigned)(nchunks < cap ? nchunks : cap));
-        if (f32 && aout) return launch(dequant_loop_kernel<FMT, false, true>, grid, block, stream, w, nblocks, out);
-        if (f32) return launch(dequant_loop_kernel<FMT, false, false>, grid, block, stream, w, nblocks, out);
-        if (aout) return launch(dequant_loop_kernel<FMT, true, true>, grid, block, stream, w, nblocks, out);
-        return launch(dequant_loop_kernel<FMT, true, false>, grid, block, stream, w, nblocks, out);
-    }
-    // 2-byte aligned input: one chunk per workgroup, staged with 2-byte loads
-    const dim3 grid((unsigned)((nblocks + kDqBlocks - 1) / kDqBlocks));
+    const int64_t nchunks = (nblocks + kDqBlocks - 1) / kDqBlocks;
+    const int64_t cap = (int64_t)device_cus() * kDqWgPerCu;
+    const dim3 grid((unsigned)(nchunks < cap ? nchunks : cap));
+    auto run = [&](auto f16, auto ao, auto in16) {
+        return launch(dequant_loop_kernel<FMT, decltype(f16)::value, decltype(ao)::value, decltype(in16)::value>,
+                      grid, block, stream, w, nblocks, out);
+    };
+    using T = std::true_type;
+    using Fl = std::false_type;
     if (f32) {
-        float *o = static_cast<float *>(out);
-        if (aout) return launch(dequant_f32_kernel<FMT, true>, grid, block, stream, w, nblocks, o);
-        return launch(dequant_f32_kernel<FMT, false>, grid, block, stream, w, nblocks, o);
+        if (a16) return aout ? run(Fl{}, T{}, T{}) : run(Fl{}, Fl{}, T{});
+        return aout ? run(Fl{}, T{}, Fl{}) : run(Fl{}, Fl{}, Fl{});
     }
-    uint16_t *o = static_cast<uint16_t *>(out);
-    if (aout) return launch(dequant_f16_kernel<FMT, true>, grid, block, stream, w, nblocks, o);
-    return launch(dequant_f16_kernel<FMT, false>, grid, block, stream, w, nblocks, o);
+    if (a16) return aout ? run(T{}, T{}, T{}) : run(T{}, Fl{}, T{});
+    return aout ? run(T{}, T{}, Fl{}) : run(T{}, Fl{}, Fl{});
 }
 
 int launch_dequantize(int fmt, const void *w, int64_t nblocks, int out_dtype, void *out,
