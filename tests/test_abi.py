@@ -128,6 +128,18 @@ def test_binding_raises_on_error_status():
     assert "misaligned" in str(err) and err.status == qk.QK_ERR_ALIGNMENT
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every call raises: there is no fallback."""
+    monkeypatch.setattr(qk, "LIB_PATH", str(tmp_path / "libqk.so"))
+    monkeypatch.setattr(qk, "_lib", None)
+    with pytest.raises(ImportError, match="not built"):
+        qk.load()
+    with pytest.raises(ImportError):
+        qk.qk_mul_mat_vec(E.QK_Q4_0, W, 8, 64, X, 1, 64, Y, 8, 0)
+    with pytest.raises(ImportError):
+        qk.block_bytes("q4_0")
+
+
 def _items(*tups):
     return qk.make_items(list(tups))
 

@@ -45,30 +45,65 @@ def _replays_match(t, run, outs, replays=4):
             assert t.equal(o.view(t.int32), w.view(t.int32)), f"replay {r} differs"
 
 
-def test_graph_gemv_batched_expert_x8_gemm_dequant():
+D_RANGE = {"q4_0": synth.D_Q4, "q4_1": synth.D_Q4, "q8_0": synth.D_Q8}
+
+# (m, k): a 128-multiple k (direct-to-LDS GEMM, whole activation windows), a
+# ragged k of 67 blocks (register-staged GEMM, partial window, odd pair
+# count), and a tall matrix (two rows per wave in the 1-column GEMV).
+SHAPES = [(300, 2048), (257, 32 * 67), (16403, 1024)]
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+@pytest.mark.parametrize("m,k", SHAPES, ids=[f"{m}x{k}" for m, k in SHAPES])
+def test_graph_gemv_batched_expert_x8_gemm_dequant(fmt, m, k):
     t = torch()
     dev = "cuda"
-    _say("graph replays")
-    m, k = 300, 2048
-    w = t.from_numpy(synth.quant_matrix("q4_0", m, k, seed=3, tensor_id=1, d_range=synth.D_Q4)).to(dev)
+    _say("graph replays", fmt, m, k)
+    w = t.from_numpy(synth.quant_matrix(fmt, m, k, seed=3, tensor_id=1, d_range=D_RANGE[fmt])).to(dev)
     x = t.from_numpy(synth.activations(k, 3, seed=3, tensor_id=2)).to(dev)
+    x1 = x[:1].contiguous()
     xh = x.half().contiguous()
     y1 = t.empty((3, m), device=dev)
+    y1n = t.empty((1, m), device=dev)
     y2 = t.empty((3, m), device=dev)
     y3 = t.empty((3, m), device=dev)
     yd = t.empty((m, k), device=dev)
+    ydh = t.empty((m, k), dtype=t.float16, device=dev)
     ne, nu = 6, 2
-    ws = t.from_numpy(synth.quant_matrix("q4_0", ne * m, k, seed=4, tensor_id=1, d_range=synth.D_Q4)).to(dev)
+    me = min(m, 300)
+    ws = t.from_numpy(synth.quant_matrix(fmt, ne * me, k, seed=4, tensor_id=1, d_range=D_RANGE[fmt])).to(dev)
     ids = t.tensor([[5, 1], [0, 5]], dtype=t.int32, device=dev)
-    ye = t.empty((2, nu, m), device=dev)
-    yb = [t.empty((3, m), device=dev) for _ in range(2)]
+    ye = t.empty((2, nu, me), device=dev)
+    yb = [t.empty((3, m), device=dev), t.empty((3, me), device=dev)]
 
     def run():
-        qk.mul_mat_vec("q4_0", w, m, k, x, y=y1)
-        qk.mul_mat_vec_x8("q4_0", w, m, k, x, y=y2)
-        qk.mul_mat("q4_0", w, m, k, xh, y=y3)
-        qk.dequantize("q4_0", w, m, k, "f32", out=yd)
-        qk.mul_mat_vec_id("q4_0", ws, ne, m, k, ids, x[:2], y=ye)
-        qk.mul_mat_vec_batched("q4_0", [(w, m, k, x), (ws, m, k, x)], ys=yb)
+        qk.mul_mat_vec(fmt, w, m, k, x, y=y1)
+        qk.mul_mat_vec(fmt, w, m, k, x1, y=y1n)
+        qk.mul_mat_vec_x8(fmt, w, m, k, x, y=y2)
+        qk.mul_mat(fmt, w, m, k, xh, y=y3)
+        qk.dequantize(fmt, w, m, k, "f32", out=yd)
+        qk.dequantize(fmt, w, m, k, "f16", out=ydh)
+        qk.mul_mat_vec_id(fmt, ws, ne, me, k, ids, x[:2], y=ye)
+        qk.mul_mat_vec_batched(fmt, [(w, m, k, x), (ws, me, k, x)], ys=yb)
 
-    _replays_match(t, run, [y1, y2, y3, yd, ye] + yb)
+    _replays_match(t, run, [y1, y1n, y2, y3, yd, ydh, ye] + yb)
+
+
+def test_graph_empty_sum_fill():
+    """k == 0 writes the empty sum with a fill kernel, not a memory fill, so a
+    captured launch sets the outputs to 0 again on every replay."""
+    t = torch()
+    _say("graph replays k == 0")
+    dummy = t.zeros(64, dtype=t.uint8, device="cuda")
+    y = t.empty((2, 5), device="cuda")
+    yg = t.empty((40, 7), device="cuda")
+
+    def run():
+        s = t.cuda.current_stream().cuda_stream
+        assert qk.qk_mul_mat_vec("q4_1", dummy.data_ptr(), 5, 0, dummy.data_ptr(), 2, 0, y.data_ptr(), 5,
+                                 s) == qk.QK_OK
+        assert qk.qk_mul_mat("q8_0", dummy.data_ptr(), 7, 0, dummy.data_ptr(), 40, 0, yg.data_ptr(), 7,
+                             s) == qk.QK_OK
+
+    _replays_match(t, run, [y, yg])
+    assert t.count_nonzero(y).item() == 0 and t.count_nonzero(yg).item() == 0
