@@ -243,26 +243,43 @@ __device__ __forceinline__ void gm_finish(floatx4_t (&acc)[kRT][kCT], uint8_t *l
     }
 
     // acc[i][j][e] is row 64*wm + 16i + 4*(lane/16) + e, column 16j + lane%16
-    // of the tile; this group stores j = 4KG..4KG+3.
+    // of the tile; this group stores j = 4KG..4KG+3.  Row tiles i and i+1 of
+    // a column tile go out as two stores that each cover 32 rows (one 128-byte
+    // line) of 8 columns: within each row of 16 lanes, lanes 0-7 hand their
+    // rows 16-31 to lanes 8-15 and take those lanes' rows 0-15 (DPP rotation
+    // by 8).  Stores of 16 rows of 16 columns would write every line in two
+    // halves, which costs about half as many bytes again in HBM writes.
+    const int c8 = lane & 7;
+    const bool up = (lane & 8) != 0;
+    auto put = [&](const floatx4_t &v, int col, int row) {
+        if (col >= n) return;
+        float *p = y + (int64_t)col * ldy + row;
+        if (YALIGNED && row + 3 < m) {
+            // non-temporal: every tile writes its outputs at the end, all at once
+            __builtin_nontemporal_store(v, reinterpret_cast<floatx4_t *>(p));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (row + e < m) p[e] = v[e];
+        }
+    };
 #pragma unroll
     for (int jl = 0; jl < 4; ++jl) {
         constexpr int jm = 4 * KG;
-        const int col = col0 + (jm + jl) * 16 + (lane & 15);
-        if (col >= n) continue;
-        float *ycol = y + (int64_t)col * ldy;
+        const int colt = col0 + (jm + jl) * 16;
 #pragma unroll
-        for (int i = 0; i < kRT; ++i) {
-            const int row = row0 + wm * 64 + i * 16 + 4 * g;
-            const floatx4_t v = acc[i][jm + jl];
-            if (YALIGNED && row + 3 < m) {
-                // non-temporal: every tile writes its outputs at the end,
-                // all at once (measured 1-5 % faster than plain stores)
-                __builtin_nontemporal_store(v, reinterpret_cast<floatx4_t *>(ycol + row));
-            } else {
+        for (int ip = 0; ip < kRT / 2; ++ip) {
+            const floatx4_t a = acc[2 * ip][jm + jl], b = acc[2 * ip + 1][jm + jl];
+            floatx4_t r;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (row + e < m) ycol[row + e] = v[e];
+            for (int e = 0; e < 4; ++e) {
+                const float s = up ? a[e] : b[e];
+                r[e] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x128, 0xF,
+                                                                          0xF, false));  // row_ror:8
             }
+            const int row = row0 + wm * 64 + ip * 32 + (up ? 16 : 0) + 4 * g;
+            put(up ? r : a, colt + c8, row);
+            put(up ? b : r, colt + 8 + c8, row);
         }
     }
 }
