@@ -63,7 +63,8 @@ constexpr int kCT = 8;           // 16-column MFMA tiles per wave
 // Quant dwords one lane loads per 16-row tile and step.  Byte offsets from the
 // start of the pair (g = lane/16, h = g % 2 picks the half of a block's quant
 // bytes):
-//   Q4_0 (36-byte pair): 8h, 8h+4, 8h+8 | 20+8h, 24+8h | (h ? 0 : 16)
+//   Q4_0 (36-byte pair): 8h, 8h+4, 8h+8 | 20+8h, 24+8h | (h ? 0 : 16), the last
+//     one from the partner lane's registers, not from LDS (gm_partner_scale)
 //   Q4_1 (40-byte pair): 0 | 4+8h, 8+8h | 20 | 24+8h, 28+8h
 //   Q8_0 (68-byte pair): 8g, 8g+4, 8g+8 | 36+8g, 40+8g | 0 | 32
 template <int FMT> struct GmQ;
@@ -199,6 +200,26 @@ __device__ __forceinline__ void gm_decode(const uint32_t (&q)[GmQ<FMT>::kN], con
         const float d1 = h2f(q[3] & 0xFFFFu) * c.dscale, m1 = h2f(q[3] >> 16);
         a0 = gm_decode8<FMT>(q[1], q[2], 0u, d0, m0, c);
         a1 = gm_decode8<FMT>(q[4], q[5], 0u, d1, m1, c);
+    }
+}
+
+// Quant dwords a lane reads from LDS per 16-row tile and step.  For Q4_0 the
+// last one (the dword holding the scale of the block whose quant bytes the
+// lane does not otherwise read) is taken from the lane 16 away instead: the
+// same row, other half of the quant bytes, which has block 0's scale in its
+// slot 0 (h = 0) or block 1's in its slot 2 (h = 1).  Read from LDS, the two
+// halves' scale dwords fall on the same banks for rows 8 apart.
+template <int FMT> constexpr int gm_lds_slots() { return FMT == QK_Q4_0 ? 5 : GmQ<FMT>::kN; }
+
+template <int FMT>
+__device__ __forceinline__ void gm_partner_scale(uint32_t (&q)[GmQ<FMT>::kN], int g) {
+    if constexpr (FMT == QK_Q4_0) {
+        const bool odd = (g & 1) != 0;
+        const uint32_t s = odd ? q[2] : q[0];
+        // rows of 16 lanes: the odd rows of the first operand trade places
+        // with the even rows of the second
+        const auto r = __builtin_amdgcn_permlane16_swap(s, s, false, false);
+        q[5] = odd ? r[0] : r[1];
     }
 }
 
@@ -500,7 +521,9 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
         for (int i = 0; i < kRT; ++i) {
             uint32_t q[NQ];
 #pragma unroll
-            for (int t = 0; t < NQ; ++t) q[t] = *reinterpret_cast<const uint32_t *>(st + i * 16 * kAP + gm_offset<FMT>(t, g));
+            for (int t = 0; t < gm_lds_slots<FMT>(); ++t)
+                q[t] = *reinterpret_cast<const uint32_t *>(st + i * 16 * kAP + gm_offset<FMT>(t, g));
+            gm_partner_scale<FMT>(q, g);
             gm_decode<FMT>(q, lc, a[i][0], a[i][1]);
         }
     };
@@ -745,7 +768,8 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
             const uint8_t *ar = st + arow + i * 16 * (16 * D::kChunks);
             uint32_t q[NQ];
 #pragma unroll
-            for (int t2 = 0; t2 < NQ; ++t2) q[t2] = *reinterpret_cast<const uint32_t *>(ar + qoff[t2]);
+            for (int t2 = 0; t2 < gm_lds_slots<FMT>(); ++t2) q[t2] = *reinterpret_cast<const uint32_t *>(ar + qoff[t2]);
+            gm_partner_scale<FMT>(q, g);
             gm_decode<FMT>(q, lc, f[i][0], f[i][1]);
         }
     };
