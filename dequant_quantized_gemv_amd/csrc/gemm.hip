@@ -623,6 +623,11 @@ template <int FMT> struct GmDma {
     static constexpr int kRow = 4 * Format<FMT>::kBytes;            // quant bytes per row and super-step
     static constexpr int kChunks = (kRow + 15) / 16;
     static constexpr int kPad = 16 * kChunks - kRow;
+    // Rows 8-15 of every 16-row tile are stored 4 bytes later in their LDS
+    // row (their chunks are loaded from 4 bytes earlier), so that the dwords
+    // the lanes of rows r and r + 8 read in one instruction fall on
+    // different banks.  Needs 4 spare bytes in the row (Q4_0, Q8_0).
+    static constexpr bool kShift = kPad >= 4;
     static constexpr int kAStage = kBM * 16 * kChunks;              // bytes
     static constexpr int kBStage = 2 * kBN * kBK * 2;               // bytes (two tiles)
     static constexpr int kStage = kAStage + kBStage;
@@ -701,8 +706,15 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
     for (int u = 0; u < D::kAPerThread; ++u) {
         const int e = min(kGmThreads * u + tid, kBM * D::kChunks - 1);
         const int r = e / D::kChunks, c = e % D::kChunks;
-        const int off = c < D::kChunks - 1 ? 16 * c : D::kRow - 16;
-        asrc[u] = w + (int64_t)min(row0 + r, m - 1) * row_bytes + off;
+        const int sh = (D::kShift && (r & 8)) ? 4 : 0;
+        const int R = min(row0 + r, m - 1);
+        // the last chunk keeps its place at the end of the super-step's bytes;
+        // a shifted first chunk reaches 4 bytes into the previous super-step or
+        // row, which exists unless the row is a clamped copy of row 0 (m == 1,
+        // never stored): that one starts at 0
+        int off = c < D::kChunks - 1 ? 16 * c - sh : D::kRow - 16;
+        if (R == 0 && off < 0) off = 0;
+        asrc[u] = w + (int64_t)R * row_bytes + off;
     }
     // Activation chunk u: linear chunk e = 512u + tid, tile e / 1024 (the
     // k group), column (e / 8) % 128, stored slot e % 8 holding logical
@@ -739,9 +751,11 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
         }
     };
 
-    // LDS byte offset of quant byte o (of the super-step's row bytes)
+    // LDS byte offset of quant byte o (of the super-step's row bytes) in this
+    // lane's row: the last chunk holds the row's last 16 bytes
+    const int lsh = (D::kShift && (lane & 8)) ? 4 : 0;
     auto aoff_lds = [&](int o) __attribute__((always_inline)) {
-        return o < 16 * (D::kChunks - 1) ? o : o + D::kPad;
+        return o < 16 * (D::kChunks - 1) - lsh ? o + lsh : o + D::kPad;
     };
     int qoff[NQ];
 #pragma unroll
