@@ -20,9 +20,10 @@
 // weights per block from quant bytes staged in LDS straight into operand
 // registers.  The quant bytes (row-contiguous 16-byte chunks) and the
 // activation tile pass through LDS: with k % 128 == 0 and aligned operands
-// they are copied global -> LDS by gfx950 direct loads into a 3-stage ring two
-// super-steps ahead (gemm_dma_kernel); otherwise through registers one step
-// ahead into double buffers (gemm_kernel).
+// they are copied global -> LDS by gfx950 direct loads into a ring of 3
+// stages (Q4_0) or 2 (Q4_1, Q8_0) that many super-steps minus one ahead
+// (gemm_dma_kernel); otherwise through registers one step ahead into double
+// buffers (gemm_kernel).
 //
 // Dequantization to fp16 (Q4_0, Q8_0), packed two at a time and exact: the
 // integer code is placed in the mantissa of an fp16 (0x64XX is 1024 + XX) with
