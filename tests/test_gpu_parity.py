@@ -452,6 +452,25 @@ def test_gemm_identity_gives_fp16_weights(fmt, m, k):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", [1, 7, 8, 9, 15, 16, 17, 33, 263])
+@pytest.mark.parametrize("k", [128, 256])
+def test_gemm_identity_direct_load_rows(fmt, m, k):
+    """The direct-to-LDS GEMM path (k % 128 == 0, aligned operands) with
+    X = I: every output is exactly one fp16 weight.  Rows 8-15 of each
+    16-row tile sit 4 bytes later in LDS than rows 0-7 (their chunks load from
+    4 bytes earlier); these row counts put real rows on both sides of that
+    split, in partial tiles, and with m = 1 every other row of the tile is a
+    clamped copy of row 0 whose shifted first chunk must not start before the
+    weights."""
+    _say("gemm identity direct-load rows", fmt, m, k)
+    w = _weights(fmt, m, k, seed=45)
+    xh = np.eye(k, dtype=np.float16)
+    y = _gpu_gemm(fmt, w, m, k, xh)
+    W16 = oracle.dequantize_f16(fmt, w, m, k).view(np.float16).astype(np.float32)
+    assert np.array_equal(y, W16.T), f"gemm identity direct-load {fmt} {m}x{k}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_gemm_identity_edge_blocks(fmt):
     """The dequantize edge blocks (subnormal, negative and zero scales, code 8
     with a negative scale, Q8_0 -128 / 127, Q4_1 offsets of every sign)
