@@ -481,7 +481,32 @@ def run_configs(torch, qk, synth, oracle, timer, steps, warmup, clib):
         "parity": "ok" if ok else "FAILED", "us_per_launch": round(sec * 1e6, 2),
         "TFLOPs": round(tf, 1), "pct_of_mfma_f16_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 1),
         "mfma_loop_TFLOPs": round(loop_tf, 1), "pct_of_mfma_loop": round(100 * tf / loop_tf, 1)}
-    del wc, gw, gk
+    del gw, gk
+
+    # the same weights at smaller batches (the first nb activation columns):
+    # up to 128 columns there is one column tile, so 56 workgroups for 256 CUs
+    batches = {}
+    for nb in (16, 64, 128):
+        yb = torch.empty((nb, m), dtype=torch.float32, device="cuda")
+
+        def gmb(i, nb=nb, yb=yb):
+            lib.qk_mul_mat(qk.QK_Q4_0, wc[i % R].data_ptr(), m, k, xd.data_ptr(), nb, k, yb.data_ptr(), m,
+                           torch.cuda.current_stream().cuda_stream)
+
+        gmb(0)
+        torch.cuda.synchronize()
+        jb = rng.integers(0, nb, 128)
+        ib = rng.integers(0, m, 128)
+        yr, s = oracle.dot_entries("q4_0", w, m, k, xh.view(np.uint16).ravel(), k, ib, jb, x_is_f16=True)
+        okb = bool(np.all(np.abs(yb.cpu().numpy()[jb, ib].astype(np.float64) - yr) <= 1e-2 * s))
+        gw, gk = timer.capture(gmb, max(warmup // 10, 2)), timer.capture(gmb, st)
+        timer.time_graph(gw)
+        secb = timer.time_graph(gk) / st
+        batches[str(nb)] = {"parity": "ok" if okb else "FAILED", "us_per_launch": round(secb * 1e6, 2),
+                            "TFLOPs": round(2.0 * m * nb * k / secb / 1e12, 1)}
+        del gw, gk, yb
+    res["gemm_q4_0_14336x4096_n512"]["smaller_batches"] = batches
+    del wc
 
     log("decode layer, one GPU's share of 8-way tensor parallelism")
     torch.cuda.synchronize()
