@@ -60,6 +60,7 @@ constexpr int kBK = 64;          // elements of K per step (one pair of blocks)
 constexpr int kPitch = kBK + 8;  // halves per LDS column (144 bytes: spreads columns over banks)
 constexpr int kRT = 4;           // 16-row MFMA tiles per wave
 constexpr int kCT = 8;           // 16-column MFMA tiles per wave
+constexpr int kGmSmallBatch = 32;  // up to this many columns: the 64 x 32 direct-load tile
 
 // Quant dwords one lane loads per 16-row tile and step.  Byte offsets from the
 // start of the pair (g = lane/16, h = g % 2 picks the half of a block's quant
@@ -306,6 +307,38 @@ __device__ __forceinline__ void gm_finish(floatx4_t (&acc)[kRT][kCT], uint8_t *l
     }
 }
 
+// Combine the eight k groups of a 64 x 32 tile (the small-batch shape) and
+// store it: every wave writes its 8 partial 16 x 16 tiles to LDS (8 waves x 8
+// tiles x 64 lanes x 16 bytes), then wave w adds tile w of all eight groups,
+// in group order, and stores it.
+template <bool YALIGNED>
+__device__ __forceinline__ void gm_finish8(floatx4_t (&acc)[kRT][2], uint8_t *lds, int wave, int lane, int row0,
+                                           int col0, int m, int n, float *__restrict__ y, int64_t ldy) {
+    floatx4_t *red = reinterpret_cast<floatx4_t *>(lds);
+#pragma unroll
+    for (int i = 0; i < kRT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) red[(wave * 8 + i * 2 + j) * 64 + lane] = acc[i][j];
+    __syncthreads();
+    floatx4_t v = red[wave * 64 + lane];
+#pragma unroll
+    for (int grp = 1; grp < 8; ++grp) v += red[(grp * 8 + wave) * 64 + lane];
+    // tile `wave` is row tile wave / 2, column tile wave % 2; the lane holds
+    // rows 4 (lane / 16) .. + 3 of column lane % 16
+    const int col = col0 + (wave & 1) * 16 + (lane & 15);
+    const int row = row0 + (wave >> 1) * 16 + 4 * (lane >> 4);
+    if (col < n) {
+        float *p = y + (int64_t)col * ldy + row;
+        if (YALIGNED && row + 3 < m) {
+            __builtin_nontemporal_store(v, reinterpret_cast<floatx4_t *>(p));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (row + e < m) p[e] = v[e];
+        }
+    }
+}
+
 // LDS bytes per weight row and step in the quant stage (the pair, padded so
 // that rows start on 16 bytes; the pitch in dwords is 4 mod 8 or 8 mod 16,
 // which spreads 16 consecutive rows over distinct banks).
@@ -481,12 +514,17 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
     auto load_b = [&](int s, XSet &xb) __attribute__((always_inline)) {
         const int pair = pbase + min(s, gsteps - 1);
         const uint16_t *p = xcol + pair * kBK;
-        if constexpr (XFAST) {
+        // k is a multiple of 32: a thread's 32 activations are all in the
+        // column or all past it (the missing second block of an odd block
+        // count), and those past it are zeros, never loaded: for the last
+        // column they would lie past the end of x
+        if (pair * kBK + 32 * bhalf >= k) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xb[u] = u32x4g_t{0u, 0u, 0u, 0u};
+        } else if constexpr (XFAST) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) xb[u] = *reinterpret_cast<const u32x4g_t *>(p + 8 * u);
-        } else if (pair * kBK + 32 * bhalf < k) {
-            // (k is a multiple of 32: a thread's 32 activations are all in
-            // the column or all past it)
+        } else {
             const uintptr_t a = reinterpret_cast<uintptr_t>(p);
             const uint32_t *base = reinterpret_cast<const uint32_t *>(a & ~uintptr_t(3));
             const uint32_t sh = (uint32_t)(a & 3);  // 0 or 2
@@ -503,9 +541,6 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
                                  __builtin_amdgcn_alignbyte(d[4 * u + 2], d[4 * u + 1], sh),
                                  __builtin_amdgcn_alignbyte(d[4 * u + 3], d[4 * u + 2], sh),
                                  __builtin_amdgcn_alignbyte(d[4 * u + 4], d[4 * u + 3], sh)};
-        } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) xb[u] = u32x4g_t{0u, 0u, 0u, 0u};
         }
     };
     auto store_b = [&](const XSet &xb, int buf) __attribute__((always_inline)) {
@@ -620,38 +655,55 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
 // lane, and 16 consecutive columns of a fragment read then fall on distinct
 // banks).
 // ---------------------------------------------------------------------------
-template <int FMT> struct GmDma {
-    static constexpr int kRow = 4 * Format<FMT>::kBytes;            // quant bytes per row and super-step
+// Tile shapes of the direct-load kernel: KG k groups of waves and 8 / KG row
+// slices of 64 rows.  KG = 2: 256 x 128 tiles (a super-step is two pairs);
+// KG = 8: 64 x 32 tiles for batches of up to 32 columns, where 256-row tiles
+// leave most CUs idle (14336 rows: 56 tiles, against 224 of 64 rows); a
+// super-step is then eight pairs, one per wave.
+template <int KG> struct GmTile {
+    static_assert(KG == 2 || KG == 8, "tile shape");
+    static constexpr int kSlices = 8 / KG;
+    static constexpr int kRows = 64 * kSlices;
+    static constexpr int kCols = KG == 2 ? 128 : 32;
+    static constexpr int kColTiles = kCols / 16;
+};
+
+template <int FMT, int KG = 2> struct GmDma {
+    using T = GmTile<KG>;
+    static constexpr int kRow = 2 * KG * Format<FMT>::kBytes;       // quant bytes per row and super-step
     // Q4_1's 80 row bytes fill five chunks exactly; a sixth gives the spare
     // bytes for the row shift below, at the price of a 2-stage ring (measured
     // 2-6 % faster than 3 stages without the shift)
-    static constexpr int kChunks = FMT == QK_Q4_1 ? 6 : (kRow + 15) / 16;
+    static constexpr int kChunks = (FMT == QK_Q4_1 && KG == 2) ? 6 : (kRow + 15) / 16;
     static constexpr int kPad = 16 * kChunks - kRow;
     // Rows 8-15 of every 16-row tile are stored 4 bytes later in their LDS
     // row (their chunks are loaded from 4 bytes earlier), so that the dwords
     // the lanes of rows r and r + 8 read in one instruction fall on
     // different banks.  Needs 4 spare bytes in the row.
     static constexpr bool kShift = kPad >= 4;
-    static constexpr int kAStage = kBM * 16 * kChunks;              // bytes
-    static constexpr int kBStage = 2 * kBN * kBK * 2;               // bytes (two tiles)
+    static constexpr int kAStage = T::kRows * 16 * kChunks;         // bytes
+    static constexpr int kBStage = KG * T::kCols * kBK * 2;         // bytes (one tile per k group)
     static constexpr int kStage = kAStage + kBStage;
     static constexpr int kStages = 3 * kStage <= 160 * 1024 ? 3 : 2;
     static constexpr int kLead = kStages - 1;                       // super-steps loaded ahead
-    static constexpr int kAPerThread = (kBM * kChunks + kGmThreads - 1) / kGmThreads;
+    static constexpr int kAPerThread = (T::kRows * kChunks + kGmThreads - 1) / kGmThreads;
     static constexpr int kBPerThread = kBStage / 16 / kGmThreads;  // 4
     // Direct loads a wave issues per stage.  Wave v issues quant chunk u when
     // 512u + 64v < kBM * kChunks, so the last waves may issue one fewer; the
     // count used in the waits is the smallest one (wave 7's): leaving that
     // many newer loads outstanding completes the older stage for every wave
     // (a wave with more newer loads merely waits for one of them as well).
-    static constexpr int kAMin = (kBM * kChunks - 64 * 7 + kGmThreads - 1) / kGmThreads;
+    static constexpr int kAMin = (T::kRows * kChunks - 64 * 7 + kGmThreads - 1) / kGmThreads;
+    static_assert((T::kRows * kChunks) % 64 == 0, "whole waves of quant chunks");
     static constexpr int kLoadsPerStage = kAMin + kBPerThread;
 };
 
-template <int FMT>
+template <int FMT, int KG>
 constexpr size_t gm_dma_lds_bytes() {
-    return (size_t)GmDma<FMT>::kStages * GmDma<FMT>::kStage > 8 * 8 * 64 * 16
-               ? (size_t)GmDma<FMT>::kStages * GmDma<FMT>::kStage
+    // the partial-sum exchange after the k loop takes 8 waves x 8 tiles x 64
+    // lanes x 16 bytes for either shape
+    return (size_t)GmDma<FMT, KG>::kStages * GmDma<FMT, KG>::kStage > 8 * 8 * 64 * 16
+               ? (size_t)GmDma<FMT, KG>::kStages * GmDma<FMT, KG>::kStage
                : 8 * 8 * 64 * 16;
 }
 
@@ -670,12 +722,14 @@ __device__ __forceinline__ void gm_wait_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int FMT, bool YALIGNED>
+template <int FMT, bool YALIGNED, int KG>
 __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
     const uint8_t *__restrict__ w, int m, int nb, const uint16_t *__restrict__ x, int64_t ldx,
     int n, float *__restrict__ y, int64_t ldy, int mtiles, int ntiles) {
     using F = Format<FMT>;
-    using D = GmDma<FMT>;
+    using D = GmDma<FMT, KG>;
+    using T = GmTile<KG>;
+    constexpr int CT = T::kColTiles;
     constexpr int NQ = GmQ<FMT>::kN;
     constexpr int kPairBytes = 2 * F::kBytes;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -688,17 +742,17 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
     const int L = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
     const int mt = L / ntiles;
     const int nt = L - mt * ntiles;
-    const int row0 = mt * kBM;
-    const int col0 = nt * kBN;
+    const int row0 = mt * T::kRows;
+    const int col0 = nt * T::kCols;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches on the k group
     const int lane = tid & 63;
     const int g = lane >> 4;
-    const int wm = wave & 3;   // 64-row slice of the tile
-    const int kg = wave >> 2;  // k group: first or second pair of each super-step
-    const int npairs = nb / 2;                 // nb % 4 == 0 here: whole super-steps
-    const int nsup = (npairs + 1) / 2;         // super-steps
+    const int wm = wave % T::kSlices;  // 64-row slice of the tile
+    const int kg = wave / T::kSlices;  // k group: pair kg of each super-step
+    const int npairs = nb / 2;         // whole super-steps here (nb % (2 KG) == 0)
+    const int nsup = (npairs + KG - 1) / KG;
     const int64_t row_bytes = (int64_t)nb * F::kBytes;
     const GmLaneConst lc = gm_lane_const<FMT>(g);
 
@@ -708,7 +762,7 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
     const uint8_t *asrc[D::kAPerThread];
 #pragma unroll
     for (int u = 0; u < D::kAPerThread; ++u) {
-        const int e = min(kGmThreads * u + tid, kBM * D::kChunks - 1);
+        const int e = min(kGmThreads * u + tid, T::kRows * D::kChunks - 1);
         const int r = e / D::kChunks, c = e % D::kChunks;
         const int sh = (D::kShift && (r & 8)) ? 4 : 0;
         const int R = min(row0 + r, m - 1);
@@ -720,15 +774,15 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
         if (R == 0 && off < 0) off = 0;
         asrc[u] = w + (int64_t)R * row_bytes + off;
     }
-    // Activation chunk u: linear chunk e = 512u + tid, tile e / 1024 (the
-    // k group), column (e / 8) % 128, stored slot e % 8 holding logical
+    // Activation chunk u: linear chunk e = 512u + tid, tile e / (8 kCols) (the
+    // k group), column (e / 8) % kCols, stored slot e % 8 holding logical
     // 16-byte chunk (e % 8) ^ ((column / 2) % 8).
     const uint16_t *bsrc[D::kBPerThread];
     int bgrp[D::kBPerThread];
 #pragma unroll
     for (int u = 0; u < D::kBPerThread; ++u) {
         const int e = kGmThreads * u + tid;
-        const int grp = e >> 10, col = (e >> 3) & (kBN - 1), p = e & 7;
+        const int grp = e / (8 * T::kCols), col = (e >> 3) & (T::kCols - 1), p = e & 7;
         const int q = p ^ ((col >> 1) & 7);
         bgrp[u] = grp;
         bsrc[u] = x + (int64_t)min(col0 + col, n - 1) * ldx + 8 * q;
@@ -739,18 +793,16 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
     auto issue = [&](int t, int buf) __attribute__((always_inline)) {
         t = min(t, nsup - 1);
         uint8_t *st = lds + buf * D::kStage;
-        const int64_t aoff = (int64_t)(2 * t) * kPairBytes;
-        // quant bytes of the second pair of a super-step past the last pair
-        // are never used (that step's k group 1 skips its multiply)
+        const int64_t aoff = (int64_t)(KG * t) * kPairBytes;
 #pragma unroll
         for (int u = 0; u < D::kAPerThread; ++u) {
-            if (kGmThreads * u + wave * 64 < kBM * D::kChunks)  // wave-uniform
+            if (kGmThreads * u + wave * 64 < T::kRows * D::kChunks)  // wave-uniform
                 gm_dma16(asrc[u] + aoff, st + 16 * (kGmThreads * u + wave * 64));
         }
         uint8_t *bst = st + D::kAStage;
 #pragma unroll
         for (int u = 0; u < D::kBPerThread; ++u) {
-            const int pair = min(2 * t + bgrp[u], npairs - 1);
+            const int pair = min(KG * t + bgrp[u], npairs - 1);
             gm_dma16(bsrc[u] + pair * kBK, bst + 16 * (kGmThreads * u + wave * 64));
         }
     };
@@ -772,11 +824,11 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
     const int bslot1 = 16 * ((1 * 4 + g) ^ ((lane & 15) >> 1));
 
     typedef u32x4g_t ASet[kRT][2];
-    floatx4_t acc[kRT][kCT];
+    floatx4_t acc[kRT][CT];
 #pragma unroll
     for (int i = 0; i < kRT; ++i)
 #pragma unroll
-        for (int j = 0; j < kCT; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < CT; ++j) acc[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     // The lane's A operands of stage `buf` (this k group's pair).
     auto decode_stage = [&](int buf, ASet &f) __attribute__((always_inline)) {
@@ -791,29 +843,31 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
             gm_decode<FMT>(q, lc, f[i][0], f[i][1]);
         }
     };
-    // The 64 products of stage `buf` (2 k halves x 8 column tiles x 4 row
-    // tiles).  The activation fragments are read two at a time, two groups of
-    // eight products ahead of their use, so the matrix cores wait less for
-    // the LDS.
+    // The products of stage `buf` (2 k halves x CT column tiles x 4 row
+    // tiles), in groups of two column tiles.  The activation fragments are
+    // read two at a time, two groups ahead of their use, so the matrix cores
+    // wait less for the LDS.
+    constexpr int GH = CT / 2;  // groups per k half
     auto mma_stage = [&](int buf, const ASet &f) __attribute__((always_inline)) {
-        const uint8_t *bb = lds + buf * D::kStage + D::kAStage + kg * (kBN * kBK * 2) + bcol;
+        const uint8_t *bb = lds + buf * D::kStage + D::kAStage + kg * (T::kCols * kBK * 2) + bcol;
         auto frag = [&](int q, int h) -> half8_t {
-            const int ks = q >> 2, j = 2 * (q & 3) + h;
+            const int ks = q / GH, j = 2 * (q % GH) + h;
             return *reinterpret_cast<const half8_t *>(bb + j * 16 * 128 + (ks ? bslot1 : bslot0));
         };
         // groups of fragments in flight (one: 77-81 us on the Q4_0
         // 14336 x 4096 x 512 workload; two: 74-80 us; three: no better)
         constexpr int FA = 2;
+        constexpr int NG = 2 * GH;  // groups per stage
         half8_t fr[FA + 1][2];
 #pragma unroll
-        for (int u = 0; u < FA; ++u) {
+        for (int u = 0; u < FA && u < NG; ++u) {
             fr[u][0] = frag(u, 0);
             fr[u][1] = frag(u, 1);
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int ks = q >> 2, j = 2 * (q & 3);
-            if (q + FA < 8) {
+        for (int q = 0; q < NG; ++q) {
+            const int ks = q / GH, j = 2 * (q % GH);
+            if (q + FA < NG) {
                 fr[(q + FA) % (FA + 1)][0] = frag(q + FA, 0);
                 fr[(q + FA) % (FA + 1)][1] = frag(q + FA, 1);
             }
@@ -841,7 +895,7 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
             int nbuf = buf + D::kLead;
             if (nbuf >= D::kStages) nbuf -= D::kStages;
             issue(t + D::kLead, nbuf);
-            if (kg == 0 || 2 * t + 1 < npairs) {
+            if (KG * t + kg < npairs) {  // wave-uniform
                 ASet f;
                 decode_stage(buf, f);
                 mma_stage(buf, f);
@@ -856,21 +910,27 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
         gm_wait_barrier<0>();
     }
 
-    if (kg == 0)
+    if constexpr (KG == 8) {
+        gm_finish8<YALIGNED>(acc, lds, wave, lane, row0, col0, m, n, y, ldy);
+    } else if (kg == 0) {
         gm_finish<0, YALIGNED>(acc, lds, wave, lane, row0, col0, m, n, y, ldy);
-    else
+    } else {
         gm_finish<1, YALIGNED>(acc, lds, wave, lane, row0, col0, m, n, y, ldy);
+    }
 }
 
-template <int FMT, bool YA>
+template <int FMT, bool YA, int KG>
 static int launch_gemm_dma(const uint8_t *w, int m, int nb, const uint16_t *x, int64_t ldx, int n,
-                           float *y, int64_t ldy, int mtiles, int ntiles, hipStream_t stream) {
-    auto kern = gemm_dma_kernel<FMT, YA>;
+                           float *y, int64_t ldy, hipStream_t stream) {
+    using T = GmTile<KG>;
+    const int mtiles = (m + T::kRows - 1) / T::kRows;
+    const int ntiles = (n + T::kCols - 1) / T::kCols;
+    auto kern = gemm_dma_kernel<FMT, YA, KG>;
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)gm_dma_lds_bytes<FMT>()) != hipSuccess)
+                            (int)gm_dma_lds_bytes<FMT, KG>()) != hipSuccess)
         return QK_ERR_LAUNCH;
-    return launch_lds(kern, dim3((unsigned)(mtiles * ntiles)), dim3(kGmThreads), gm_dma_lds_bytes<FMT>(), stream,
-                      w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles);
+    return launch_lds(kern, dim3((unsigned)(mtiles * ntiles)), dim3(kGmThreads), gm_dma_lds_bytes<FMT, KG>(),
+                      stream, w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles);
 }
 
 template <int FMT, bool FAST, bool XFAST, bool YA>
@@ -892,10 +952,15 @@ static int dispatch_gemm(const uint8_t *w, int m, int nb, const uint16_t *x, int
     const bool fast = ((uintptr_t)w % 4) == 0 && (nb % 2) == 0;
     const bool xfast = ((uintptr_t)x % 16) == 0 && (ldx % 8) == 0;
     const bool ya = ((uintptr_t)y % 16) == 0 && (ldy % 4) == 0;
-    // the direct-load path moves whole super-steps (two pairs): k % 128 == 0
+    // the direct-load path moves whole super-steps (two pairs, or eight for
+    // the small-batch tile): k % 128 == 0, or k % 512 == 0
     const bool dma = fast && xfast && (nb % 4) == 0;
-    if (dma && ya) return launch_gemm_dma<FMT, true>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
-    if (dma) return launch_gemm_dma<FMT, false>(w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, stream);
+    if (dma && n <= kGmSmallBatch && (nb % 16) == 0)
+        return ya ? launch_gemm_dma<FMT, true, 8>(w, m, nb, x, ldx, n, y, ldy, stream)
+                  : launch_gemm_dma<FMT, false, 8>(w, m, nb, x, ldx, n, y, ldy, stream);
+    if (dma)
+        return ya ? launch_gemm_dma<FMT, true, 2>(w, m, nb, x, ldx, n, y, ldy, stream)
+                  : launch_gemm_dma<FMT, false, 2>(w, m, nb, x, ldx, n, y, ldy, stream);
     auto run = [&](auto fw, auto fx) {
         if (ya) return launch_gemm<FMT, decltype(fw)::value, decltype(fx)::value, true>(w, m, nb, x, ldx, n, y, ldy,
                                                                                         mtiles, ntiles, stream);

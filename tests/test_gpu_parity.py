@@ -471,6 +471,31 @@ def test_gemm_identity_direct_load_rows(fmt, m, k):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k,n", [(1, 512, 1), (63, 512, 5), (64, 1024, 17), (65, 512, 32),
+                                   (300, 1024, 32), (1000, 512, 9)])
+def test_gemm_small_batch_tile(fmt, m, k, n):
+    """Up to 32 columns with k % 512 == 0 the GEMM takes the 64 x 32 tile
+    whose eight waves each multiply one pair of every eight (eight partial
+    sums added through LDS): random activations within 1e-2 * S, and
+    one-hot activations (column j picks k index 16j + j % 16, so every
+    k group and both halves of a pair are hit) give exactly the fp16
+    weights."""
+    _say("gemm small batch", fmt, m, k, n)
+    w = _weights(fmt, m, k, seed=46)
+    xh = synth.activations(k, n, seed=46, tensor_id=2, dtype=np.float16)
+    y = _gpu_gemm(fmt, w, m, k, xh)
+    yref, s = oracle.dot(fmt, w, m, k, xh.view(np.uint16), n, x_is_f16=True)
+    assert_within(y, yref, s, GEMM_TOL, f"gemm small batch {fmt} {m}x{k} n={n}")
+    cols = [(16 * j + j % 16) % k for j in range(32)]
+    xo = np.zeros((32, k), np.float16)
+    for j, c in enumerate(cols):
+        xo[j, c] = 1.0
+    yo = _gpu_gemm(fmt, w, m, k, xo)
+    W16 = oracle.dequantize_f16(fmt, w, m, k).view(np.float16).astype(np.float32)
+    assert np.array_equal(yo, W16[:, cols].T), f"gemm small batch one-hot {fmt} {m}x{k}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_gemm_identity_edge_blocks(fmt):
     """The dequantize edge blocks (subnormal, negative and zero scales, code 8
     with a negative scale, Q8_0 -128 / 127, Q4_1 offsets of every sign)
