@@ -60,7 +60,13 @@ constexpr int kBK = 64;          // elements of K per step (one pair of blocks)
 constexpr int kPitch = kBK + 8;  // halves per LDS column (144 bytes: spreads columns over banks)
 constexpr int kRT = 4;           // 16-row MFMA tiles per wave
 constexpr int kCT = 8;           // 16-column MFMA tiles per wave
-constexpr int kGmSmallBatch = 32;  // up to this many columns: the 64 x 32 direct-load tile
+// The 64 x 32 direct-load tile takes batches of up to kGmSmallBatch columns,
+// and up to kGmSmallBatchMax where 256 x 128 tiles would not cover the CUs
+// (each further 32 columns decode the weights once more).  Q4_0 14336 x 4096:
+// n = 16 / 33 / 64 / 96 / 128 in 15.5 / 28.5 / 30.7 / 44.3 / 58.5 us against
+// 65-70 us with the large tile; at n = 256 the large tile takes 70 us.
+constexpr int kGmSmallBatch = 32;
+constexpr int kGmSmallBatchMax = 128;
 
 // Quant dwords one lane loads per 16-row tile and step.  Byte offsets from the
 // start of the pair (g = lane/16, h = g % 2 picks the half of a block's quant
@@ -955,7 +961,9 @@ static int dispatch_gemm(const uint8_t *w, int m, int nb, const uint16_t *x, int
     // the direct-load path moves whole super-steps (two pairs, or eight for
     // the small-batch tile): k % 128 == 0, or k % 512 == 0
     const bool dma = fast && xfast && (nb % 4) == 0;
-    if (dma && n <= kGmSmallBatch && (nb % 16) == 0)
+    const bool small = dma && (nb % 16) == 0 &&
+                       (n <= kGmSmallBatch || (n <= kGmSmallBatchMax && mtiles * ntiles < device_cus()));
+    if (small)
         return ya ? launch_gemm_dma<FMT, true, 8>(w, m, nb, x, ldx, n, y, ldy, stream)
                   : launch_gemm_dma<FMT, false, 8>(w, m, nb, x, ldx, n, y, ldy, stream);
     if (dma)
