@@ -73,12 +73,23 @@ def _draw_gemm(rng):
                 x_off=int(rng.choice([0, 0, 1, 8])))
 
 
+def _draw_gemm_small(rng):
+    # k a multiple of 512 and at most 128 columns: the 64 x 32 small-batch tile
+    # (with aligned, 8-element-multiple strides; other strides take the
+    # register-staged path)
+    m, nb, n = int(rng.integers(1, 701)), 16 * int(rng.integers(1, 5)), int(rng.integers(1, 129))
+    k = 32 * nb
+    return dict(fmt=_fmt(rng), m=m, k=k, n=n, ldx=k + int(rng.choice([0, 0, 8, 3])),
+                ldy=m + int(rng.choice([0, 0, 4, 1])), w_off=0, x_off=int(rng.choice([0, 0, 0, 8])))
+
+
 DEQUANT = _cases(0xD0, 24, _draw_dequant)
 GEMV = _cases(0xD1, 40, _draw_gemv)
 GEMV_X8 = _cases(0xD2, 20, _draw_gemv)
 BATCHED = _cases(0xD3, 12, _draw_batched)
 EXPERT = _cases(0xD4, 12, _draw_expert)
 GEMM = _cases(0xD5, 16, _draw_gemm)
+GEMM_SMALL = _cases(0xD6, 12, _draw_gemm_small)
 
 
 @pytest.mark.parametrize("c", DEQUANT, ids=[f"dq{i}" for i in range(len(DEQUANT))])
@@ -150,3 +161,14 @@ def test_sweep_gemm(c):
                   w_off=c["w_off"])
     yref, s = oracle.dot(c["fmt"], w, c["m"], c["k"], xh.view(np.uint16), c["n"], x_is_f16=True)
     assert_within(y, yref, s, GEMM_TOL, f"sweep gemm {c}")
+
+
+@pytest.mark.parametrize("c", GEMM_SMALL, ids=[f"gemm_small{i}" for i in range(len(GEMM_SMALL))])
+def test_sweep_gemm_small_batch(c):
+    _say("sweep gemm small batch", c)
+    w = _weights(c["fmt"], c["m"], c["k"], seed=66)
+    xh = synth.activations(c["k"], c["n"], seed=66, tensor_id=2, dtype=np.float16)
+    y = _gpu_gemm(c["fmt"], w, c["m"], c["k"], xh, ldx=c["ldx"], ldy=c["ldy"], x_off=c["x_off"],
+                  w_off=c["w_off"])
+    yref, s = oracle.dot(c["fmt"], w, c["m"], c["k"], xh.view(np.uint16), c["n"], x_is_f16=True)
+    assert_within(y, yref, s, GEMM_TOL, f"sweep gemm small batch {c}")
