@@ -237,7 +237,7 @@ __device__ __forceinline__ void gm_partner_scale(uint32_t (&q)[GmQ<FMT>::kN], in
 // partner through LDS (8 waves x 8 tiles x 64 lanes x 16 bytes).  Column
 // indices are compile-time constants so that the accumulators stay in
 // registers, hence one instance per group.
-template <int KG, bool YALIGNED>
+template <int KG, bool YALIGNED, bool ACC = false>
 __device__ __forceinline__ void gm_finish(floatx4_t (&acc)[kRT][kCT], uint8_t *lds, int wave, int lane,
                                           int row0, int col0, int m, int n, float *__restrict__ y,
                                           int64_t ldy) {
@@ -280,16 +280,19 @@ __device__ __forceinline__ void gm_finish(floatx4_t (&acc)[kRT][kCT], uint8_t *l
     // halves, which costs about half as many bytes again in HBM writes.
     const int c8 = lane & 7;
     const bool up = (lane & 8) != 0;
+    // ACC: add to the outputs already in y (the second launch of a split K)
     auto put = [&](const floatx4_t &v, int col, int row) {
         if (col >= n) return;
         float *p = y + (int64_t)col * ldy + row;
         if (YALIGNED && row + 3 < m) {
+            floatx4_t o = v;
+            if constexpr (ACC) o += *reinterpret_cast<const floatx4_t *>(p);
             // non-temporal: every tile writes its outputs at the end, all at once
-            __builtin_nontemporal_store(v, reinterpret_cast<floatx4_t *>(p));
+            __builtin_nontemporal_store(o, reinterpret_cast<floatx4_t *>(p));
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (row + e < m) p[e] = v[e];
+                if (row + e < m) p[e] = ACC ? p[e] + v[e] : v[e];
         }
     };
 #pragma unroll
@@ -728,10 +731,14 @@ __device__ __forceinline__ void gm_wait_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int FMT, bool YALIGNED, int KG>
+// nb blocks of each row are multiplied; rows are row_nb blocks apart (row_nb >
+// nb when a second launch takes the rest of K, with ACC adding its products to
+// y).
+template <int FMT, bool YALIGNED, int KG, bool ACC>
 __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
     const uint8_t *__restrict__ w, int m, int nb, const uint16_t *__restrict__ x, int64_t ldx,
-    int n, float *__restrict__ y, int64_t ldy, int mtiles, int ntiles) {
+    int n, float *__restrict__ y, int64_t ldy, int mtiles, int ntiles, int row_nb) {
+    static_assert(!ACC || KG == 2, "only the 256 x 128 tile accumulates");
     using F = Format<FMT>;
     using D = GmDma<FMT, KG>;
     using T = GmTile<KG>;
@@ -759,7 +766,7 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
     const int kg = wave / T::kSlices;  // k group: pair kg of each super-step
     const int npairs = nb / 2;         // whole super-steps here (nb % (2 KG) == 0)
     const int nsup = (npairs + KG - 1) / KG;
-    const int64_t row_bytes = (int64_t)nb * F::kBytes;
+    const int64_t row_bytes = (int64_t)row_nb * F::kBytes;
     const GmLaneConst lc = gm_lane_const<FMT>(g);
 
     // Direct-load roles.  Quant chunk u of this thread: linear chunk
@@ -919,24 +926,24 @@ __global__ __launch_bounds__(kGmThreads) void gemm_dma_kernel(
     if constexpr (KG == 8) {
         gm_finish8<YALIGNED>(acc, lds, wave, lane, row0, col0, m, n, y, ldy);
     } else if (kg == 0) {
-        gm_finish<0, YALIGNED>(acc, lds, wave, lane, row0, col0, m, n, y, ldy);
+        gm_finish<0, YALIGNED, ACC>(acc, lds, wave, lane, row0, col0, m, n, y, ldy);
     } else {
-        gm_finish<1, YALIGNED>(acc, lds, wave, lane, row0, col0, m, n, y, ldy);
+        gm_finish<1, YALIGNED, ACC>(acc, lds, wave, lane, row0, col0, m, n, y, ldy);
     }
 }
 
-template <int FMT, bool YA, int KG>
+template <int FMT, bool YA, int KG, bool ACC = false>
 static int launch_gemm_dma(const uint8_t *w, int m, int nb, const uint16_t *x, int64_t ldx, int n,
-                           float *y, int64_t ldy, hipStream_t stream) {
+                           float *y, int64_t ldy, hipStream_t stream, int row_nb) {
     using T = GmTile<KG>;
     const int mtiles = (m + T::kRows - 1) / T::kRows;
     const int ntiles = (n + T::kCols - 1) / T::kCols;
-    auto kern = gemm_dma_kernel<FMT, YA, KG>;
+    auto kern = gemm_dma_kernel<FMT, YA, KG, ACC>;
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)gm_dma_lds_bytes<FMT, KG>()) != hipSuccess)
         return QK_ERR_LAUNCH;
     return launch_lds(kern, dim3((unsigned)(mtiles * ntiles)), dim3(kGmThreads), gm_dma_lds_bytes<FMT, KG>(),
-                      stream, w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles);
+                      stream, w, m, nb, x, ldx, n, y, ldy, mtiles, ntiles, row_nb);
 }
 
 template <int FMT, bool FAST, bool XFAST, bool YA>
@@ -961,14 +968,23 @@ static int dispatch_gemm(const uint8_t *w, int m, int nb, const uint16_t *x, int
     // the direct-load path moves whole super-steps (two pairs, or eight for
     // the small-batch tile): k % 128 == 0, or k % 512 == 0
     const bool dma = fast && xfast && (nb % 4) == 0;
-    const bool small = dma && (nb % 16) == 0 &&
+    const bool small = dma && nb >= 16 &&
                        (n <= kGmSmallBatch || (n <= kGmSmallBatchMax && mtiles * ntiles < device_cus()));
-    if (small)
-        return ya ? launch_gemm_dma<FMT, true, 8>(w, m, nb, x, ldx, n, y, ldy, stream)
-                  : launch_gemm_dma<FMT, false, 8>(w, m, nb, x, ldx, n, y, ldy, stream);
+    if (small) {
+        // the small-batch tile takes whole eight-pair super-steps; the 4, 8 or
+        // 12 blocks left over go to a second launch that adds its products
+        const int nb16 = nb - nb % 16;
+        int st = ya ? launch_gemm_dma<FMT, true, 8>(w, m, nb16, x, ldx, n, y, ldy, stream, nb)
+                    : launch_gemm_dma<FMT, false, 8>(w, m, nb16, x, ldx, n, y, ldy, stream, nb);
+        if (st != QK_OK || nb16 == nb) return st;
+        const uint8_t *wr = w + (size_t)nb16 * Format<FMT>::kBytes;
+        const uint16_t *xr = x + (size_t)nb16 * kBlockElems;
+        return ya ? launch_gemm_dma<FMT, true, 2, true>(wr, m, nb - nb16, xr, ldx, n, y, ldy, stream, nb)
+                  : launch_gemm_dma<FMT, false, 2, true>(wr, m, nb - nb16, xr, ldx, n, y, ldy, stream, nb);
+    }
     if (dma)
-        return ya ? launch_gemm_dma<FMT, true, 2>(w, m, nb, x, ldx, n, y, ldy, stream)
-                  : launch_gemm_dma<FMT, false, 2>(w, m, nb, x, ldx, n, y, ldy, stream);
+        return ya ? launch_gemm_dma<FMT, true, 2>(w, m, nb, x, ldx, n, y, ldy, stream, nb)
+                  : launch_gemm_dma<FMT, false, 2>(w, m, nb, x, ldx, n, y, ldy, stream, nb);
     auto run = [&](auto fw, auto fx) {
         if (ya) return launch_gemm<FMT, decltype(fw)::value, decltype(fx)::value, true>(w, m, nb, x, ldx, n, y, ldy,
                                                                                         mtiles, ntiles, stream);

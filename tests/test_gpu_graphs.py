@@ -49,8 +49,9 @@ D_RANGE = {"q4_0": synth.D_Q4, "q4_1": synth.D_Q4, "q8_0": synth.D_Q8}
 
 # (m, k): a 128-multiple k (direct-to-LDS GEMM, whole activation windows), a
 # ragged k of 67 blocks (register-staged GEMM, partial window, odd pair
-# count), and a tall matrix (two rows per wave in the 1-column GEMV).
-SHAPES = [(300, 2048), (257, 32 * 67), (16403, 1024)]
+# count), a tall matrix (two rows per wave in the 1-column GEMV), and 20
+# blocks (the small-batch GEMM tile on 16, a second launch adding the other 4).
+SHAPES = [(300, 2048), (257, 32 * 67), (16403, 1024), (300, 640)]
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])

@@ -473,10 +473,12 @@ def test_gemm_identity_direct_load_rows(fmt, m, k):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m,k,n", [(1, 512, 1), (63, 512, 5), (64, 1024, 17), (65, 512, 32),
                                    (300, 1024, 32), (1000, 512, 9), (300, 512, 33), (257, 1024, 100),
-                                   (70, 512, 128)])
+                                   (70, 512, 128), (130, 640, 8), (300, 896, 40), (65, 11008, 16)])
 def test_gemm_small_batch_tile(fmt, m, k, n):
-    """Up to 32 columns with k % 512 == 0 (up to 128 where the 256 x 128
-    tiles would not cover the CUs) the GEMM takes the 64 x 32 tile
+    """Up to 32 columns with k % 128 == 0 and at least 16 blocks (up to 128
+    where the 256 x 128 tiles would not cover the CUs) the GEMM takes the
+    64 x 32 tile for the first multiple of 16 blocks and adds the 4, 8 or 12
+    blocks left over (k = 640, 896, 11008 here) in a second launch; the tile
     whose eight waves each multiply one pair of every eight (eight partial
     sums added through LDS): random activations within 1e-2 * S, and
     one-hot activations (column j picks k index 16j + j % 16, so every

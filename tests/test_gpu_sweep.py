@@ -74,10 +74,11 @@ def _draw_gemm(rng):
 
 
 def _draw_gemm_small(rng):
-    # k a multiple of 512 and at most 128 columns: the 64 x 32 small-batch tile
+    # k a multiple of 128 and at most 128 columns: the 64 x 32 small-batch tile
     # (with aligned, 8-element-multiple strides; other strides take the
     # register-staged path)
-    m, nb, n = int(rng.integers(1, 701)), 16 * int(rng.integers(1, 5)), int(rng.integers(1, 129))
+    m, n = int(rng.integers(1, 701)), int(rng.integers(1, 129))
+    nb = 16 * int(rng.integers(1, 5)) + 4 * int(rng.integers(0, 4))  # leftover blocks: second launch
     k = 32 * nb
     return dict(fmt=_fmt(rng), m=m, k=k, n=n, ldx=k + int(rng.choice([0, 0, 8, 3])),
                 ldy=m + int(rng.choice([0, 0, 4, 1])), w_off=0, x_off=int(rng.choice([0, 0, 0, 8])))
