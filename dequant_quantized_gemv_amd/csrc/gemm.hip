@@ -683,9 +683,9 @@ template <int FMT, int KG = 2> struct GmDma {
     // Rows that fill their chunks exactly get one more chunk, which gives the
     // spare bytes for the row shift below: Q4_1 at KG = 2 (80 bytes, at the
     // price of a 2-stage ring: measured 2-6 % faster than 3 stages without the
-    // shift), and Q4_0 / Q8_0 at KG = 8 (288 / 544 bytes; the ring keeps its
-    // depth).  Q4_1 at KG = 8 would lose its third stage and keeps 20 chunks.
-    static constexpr int kChunks = (kRow + 15) / 16 + (((kRow % 16) == 0 && (KG == 2) == (FMT == QK_Q4_1)) ? 1 : 0);
+    // shift), and every format at KG = 8 (288 / 320 / 544 bytes; the ring keeps
+    // its depth: Q4_1's three stages take 162 816 of the 163 840 bytes).
+    static constexpr int kChunks = (kRow + 15) / 16 + (((kRow % 16) == 0 && (KG == 8 || FMT == QK_Q4_1)) ? 1 : 0);
     static constexpr int kPad = 16 * kChunks - kRow;
     // Rows 8-15 of every 16-row tile are stored 4 bytes later in their LDS
     // row (their chunks are loaded from 4 bytes earlier), so that the dwords
