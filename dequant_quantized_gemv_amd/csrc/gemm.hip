@@ -37,6 +37,14 @@
 // Tiles are assigned so that the workgroups of one XCD (the hardware sends
 // workgroup i to XCD i % 8) cover consecutive tiles, column tile fastest, so
 // the workgroups sharing a weight row tile share that XCD's L2.
+//
+// Small batches: with 256 x 128 tiles a tall matrix has too few tiles to cover
+// the CUs (14336 rows: 56), so up to 32 columns (128 where the large tiles
+// would number fewer than the CUs) the direct-load kernel runs 64 x 32 tiles
+// whose eight waves each take one pair of every eight; their partial sums are
+// added through LDS in a fixed order.  Block counts that are not a multiple of
+// 16 leave 4-12 blocks to a second launch of the large tile that adds its
+// products to y.
 #include <type_traits>
 
 #include "qk_common.h"
