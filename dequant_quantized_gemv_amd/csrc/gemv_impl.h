@@ -371,12 +371,19 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // scale d = 2^e, e the smallest integer >= -126 with 127 * 2^e >= max|x|, and
 // q = x / d rounded half to even (exact decisions: the division by a power of
 // two rounds nothing).  Writes the 32 codes to `codes` (16-byte aligned LDS)
-// and (d, sum of the codes) to `scale`.  An all-zero block has d = 0.
+// and (d, sum of the codes) to `scale`.  An all-zero block has d = 0; a block
+// holding an infinite or NaN value has d = NaN (its codes are then
+// meaningless), so every product that uses it is NaN.
 __device__ __forceinline__ void x8_block(const f32x4_t (&v)[8], uint8_t *codes, uint8_t *scale) {
     float amax = 0.0f;
+    bool finite = true;  // (|x| <= FLT_MAX is false for infinities and NaN)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
         amax = fmaxf(fmaxf(fmaxf(amax, fabsf(v[i].x)), fmaxf(fabsf(v[i].y), fabsf(v[i].z))), fabsf(v[i].w));
+        finite = finite && fabsf(v[i].x) <= 3.40282347e38f && fabsf(v[i].y) <= 3.40282347e38f &&
+                 fabsf(v[i].z) <= 3.40282347e38f && fabsf(v[i].w) <= 3.40282347e38f;
+    }
+    if (!finite) amax = 0.0f;  // keeps the scale computation below in range
     int ex;
     const float mant = frexpf(amax, &ex);  // amax = mant * 2^ex, mant in [0.5, 1)
     // 127 * 2^(ex-7) >= amax  <=>  mant <= 127/128
@@ -398,7 +405,7 @@ __device__ __forceinline__ void x8_block(const f32x4_t (&v)[8], uint8_t *codes, 
     }
     *reinterpret_cast<u32x4_t *>(codes) = u32x4_t{wd[0], wd[1], wd[2], wd[3]};
     *reinterpret_cast<u32x4_t *>(codes + 16) = u32x4_t{wd[4], wd[5], wd[6], wd[7]};
-    const float d = amax == 0.0f ? 0.0f : ldexpf(1.0f, e);
+    const float d = !finite ? __builtin_nanf("") : (amax == 0.0f ? 0.0f : ldexpf(1.0f, e));
     *reinterpret_cast<u32x2_t *>(scale) = u32x2_t{__builtin_bit_cast(uint32_t, d), (uint32_t)qsum};
 }
 

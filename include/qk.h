@@ -130,7 +130,9 @@ int qk_mul_mat_vec(int fmt, const void *w, int64_t m, int64_t k,
  * column is first quantized (inside the kernel, no scratch memory) to codes
  * q = round-half-even(x / d) with a power-of-two scale d = 2^e, e the
  * smallest integer >= -126 with 127 * 2^e >= max|x| over the block (d = 0 for
- * an all-zero block), and the products use x^ = d * q:
+ * an all-zero block; d = NaN for a block holding an infinite or NaN value,
+ * so every output that uses such a block is NaN), and the products use
+ * x^ = d * q:
  *
  *   y[j*ldy + i] = sum_c W[i, c] * x^[j][c]      for i < m, j < n   (overwrite)
  *

@@ -286,10 +286,19 @@ void orc_dot_id(int fmt, const uint8_t *w, int64_t n_experts, int64_t expert_str
  * and q = 0.  The product then uses the dequantized activation x^ = d * q.
  * ------------------------------------------------------------------- */
 
-/* Quantize one block of 32 fp32 values: codes q[32], returns d. */
+/* Quantize one block of 32 fp32 values: codes q[32], returns d.  A block
+ * holding an infinite or NaN value has no finite scale: its scale is NaN and
+ * its codes 0, so every product that uses the block is NaN (as the plain
+ * product with such an activation is infinite or NaN). */
 float orc_quantize_x8_block(const float *x, int8_t *q)
 {
     double amax = 0.0;
+    for (int t = 0; t < 32; ++t) {
+        if (!isfinite(x[t])) {
+            for (int u = 0; u < 32; ++u) q[u] = 0;
+            return NAN;
+        }
+    }
     for (int t = 0; t < 32; ++t) {
         const double a = fabs((double)x[t]);
         if (a > amax) amax = a;

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 from dequant_quantized_gemv_amd import qk, synth
-from tests.gpu_helpers import Guarded, assert_within, to_dev_bytes, x_dev, torch
+from tests.gpu_helpers import Guarded, assert_within, oracle_rows, to_dev_bytes, x_dev, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -123,19 +123,33 @@ def test_x8_empty_rows():
     assert np.all(out.host(np.float32) == 0.0) and out.guards_intact()
 
 
-@pytest.mark.parametrize("n", [1, 4, 8])
-def test_x8_full_q4_1_11008x4096_sampled(n):
-    """The Q4_1 11008 x 4096 workload with 8-bit activations: 256 sampled
-    rows checked against the oracle (row slices of the full matrix)."""
+@pytest.mark.parametrize("fmt", FMTS)
+def test_x8_nonfinite_activations_give_nan(fmt):
+    """A block holding an infinity or a NaN has a NaN scale: every output of
+    its column is NaN; the other columns stay within tolerance."""
+    m, k = 70, 32 * 6
+    w = synth.quant_matrix(fmt, m, k, seed=97, tensor_id=1, d_range=D_RANGE[fmt])
+    x = synth.activations(k, 4, seed=97, tensor_id=2)
+    x[0, 70] = np.inf
+    x[1, 5] = -np.inf
+    x[2, 190] = np.nan
+    _say("x8 non-finite", fmt)
+    y = _gemv_x8(fmt, w, m, k, x)
+    yref, s = oracle.dot_x8(fmt, w, m, k, x, 4)
+    assert np.isnan(yref[:3]).all() and np.isnan(y[:3]).all()
+    assert_within(y[3:], yref[3:], s[3:], TOL, f"x8 finite column {fmt}")
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_x8_full_q4_1_11008x4096(n):
+    """The Q4_1 11008 x 4096 workload with 8-bit activations: every output
+    against the oracle."""
     cfg = synth.WORKLOADS["gemv_q4_1_11008x4096"]
     seed = synth.workload_seed(cfg["id"])
     m, k = cfg["m"], cfg["k"]
     w = synth.quant_matrix("q4_1", m, k, seed=seed, tensor_id=0, d_range=cfg["d"], m_range=cfg["mr"])
-    x = synth.activations(k, 8, seed=seed, tensor_id=100)[:n]
+    x = np.ascontiguousarray(synth.activations(k, 8, seed=seed, tensor_id=100)[:n])
     _say("x8 full q4_1", n)
-    y = _gemv_x8("q4_1", w, m, k, np.ascontiguousarray(x))
-    rows = np.sort(np.random.default_rng(n).choice(m, 256, replace=False))
-    rb = (k // 32) * 20
-    wsub = np.concatenate([w[r * rb:(r + 1) * rb] for r in rows])
-    yref, s = oracle.dot_x8("q4_1", wsub, len(rows), k, x, n)
-    assert_within(y[:, rows], yref, s, TOL, f"x8 full q4_1 n={n}")
+    y = _gemv_x8("q4_1", w, m, k, x)
+    yref, s = oracle_rows(oracle.dot_x8, "q4_1", w, m, k, x, n)
+    assert_within(y, yref, s, TOL, f"x8 full q4_1 n={n}")

@@ -515,3 +515,23 @@ def test_x8_rounding_mistakes_are_caught():
     x2 = np.array([np.float32(v) for v in b2["x"]], dtype=np.float64)
     plain = np.rint(x2 / (np.abs(x2).max() / 127))
     assert list(plain.astype(int)) != b2["q"]
+
+
+def test_x8_nonfinite_block_gives_nan():
+    """A block holding an infinity or a NaN has scale NaN and codes 0, so every
+    product that uses it is NaN; the other columns are untouched."""
+    k = 64
+    x = np.zeros((3, k), dtype=np.float32)
+    x[:, :] = (np.arange(k) % 5 - 2).astype(np.float32)
+    x[0, 40] = np.inf
+    x[1, 3] = np.nan
+    q, d = oracle.quantize_x8(x, k, 3)
+    assert np.isnan(d[0, 1]) and np.isnan(d[1, 0])
+    assert np.all(q[0, 32:] == 0) and np.all(q[1, :32] == 0)
+    assert d[0, 0] == 2.0 ** -5 and d[2, 0] == 2.0 ** -5 and d[1, 1] == 2.0 ** -5
+    w = synth.quant_matrix("q4_1", 4, k, seed=9, tensor_id=1, d_range=(1e-3, 2e-2))
+    y, s = oracle.dot_x8("q4_1", w, 4, k, x, 3)
+    assert np.isnan(y[0]).all() and np.isnan(y[1]).all()
+    assert np.isfinite(y[2]).all()
+    yp, _ = oracle.dot("q4_1", w, 4, k, x[2], 1)
+    assert np.array_equal(y[2], yp[0])  # lossless codes: the same exact sums
