@@ -1,5 +1,9 @@
-"""Helpers for the GPU parity tests: device buffers with guard bands, and the
-tolerance check against the fp64 oracle."""
+"""Helpers for the GPU parity tests: device buffers with guard bands, the
+tolerance check against the fp64 oracle, and the oracle run over row ranges
+in host threads (full-size workloads checked on every output in seconds)."""
+from concurrent.futures import ThreadPoolExecutor
+import os
+
 import numpy as np
 
 CANARY_BYTE = 0xA5
@@ -59,11 +63,13 @@ def x_dev(x2d, ld, dtype, offset_elems=0):
 
 
 def assert_within(y, yref, s, rel, what=""):
-    """|y - yref| <= rel * S elementwise; where S == 0 the result must be 0."""
+    """|y - yref| <= rel * S elementwise; where S == 0 the result must be 0.
+    Anything not shown to be within the bound fails: a NaN or infinite output
+    (whose comparison is never true) included."""
     y = np.asarray(y, dtype=np.float64)
     err = np.abs(y - yref)
     lim = rel * s
-    bad = err > lim
+    bad = ~(err <= lim)
     zero = s == 0
     bad |= zero & (y != 0)
     if np.any(bad):
@@ -72,3 +78,39 @@ def assert_within(y, yref, s, rel, what=""):
             f"{what}: {int(bad.sum())} of {bad.size} outside {rel}*S; first {idx.tolist()}: "
             f"y={y[bad][:5]} ref={yref[bad][:5]} S={s[bad][:5]}")
     return float(np.max(err / np.where(s > 0, s, 1)))
+
+
+def host_threads():
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except (AttributeError, OSError):
+        return max(1, os.cpu_count() or 1)
+
+
+def oracle_rows(fn, fmt, w, m, k, *args, **kw):
+    """fn(fmt, w_rows, rows, k, *args, **kw) -> (y (n, rows), s (n, rows)),
+    called on row ranges of W in host threads (the oracle's C entry points
+    release the GIL) and concatenated: the oracle's own result, row for row."""
+    rb = (k // 32) * {"q4_0": 18, "q4_1": 20, "q8_0": 34}[fmt]
+    threads = host_threads()
+    step = max(1, -(-m // (threads * 4)))
+    chunks = [(r, min(m, r + step)) for r in range(0, m, step)]
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda c: fn(fmt, w[c[0] * rb:c[1] * rb], c[1] - c[0], k, *args, **kw), chunks))
+    return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1)
+
+
+def gemm_reference(oracle, fmt, w, m, k, xh):
+    """Every output of a GEMM against fp16 activations xh (n, k): the fp64
+    product of the oracle's fp32 weights with the exactly decoded
+    activations, and S = |W| |X| (a matmul as a step; the product itself is
+    pinned against the oracle's dot products on the CPU)."""
+    rb = (k // 32) * {"q4_0": 18, "q4_1": 20, "q8_0": 34}[fmt]
+    threads = host_threads()
+    step = max(1, -(-m // (threads * 4)))
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda r: oracle.dequantize_f32(fmt, w[r * rb:min(m, r + step) * rb],
+                                                             min(m, r + step) - r, k), range(0, m, step)))
+    wf = np.concatenate(parts, axis=0).astype(np.float64)
+    xf = np.asarray(xh, dtype=np.float16).astype(np.float64)
+    return xf @ wf.T, np.abs(xf) @ np.abs(wf).T

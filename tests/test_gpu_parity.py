@@ -16,7 +16,8 @@ import pytest
 
 import oracle
 from dequant_quantized_gemv_amd import qk, synth
-from tests.gpu_helpers import Guarded, assert_within, to_dev_bytes, x_dev, torch
+from tests.gpu_helpers import (Guarded, assert_within, gemm_reference, oracle_rows, to_dev_bytes,
+                               x_dev, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -328,18 +329,6 @@ def test_gemv_side_stream():
     assert_within(y, yref, sc, GEMV_TOL, "side stream")
 
 
-def _sampled_check(fmt, w, m, k, x2d, y, rng, count, rel, x_is_f16=False, what=""):
-    n = x2d.shape[0]
-    ii = rng.integers(0, m, size=count)
-    jj = rng.integers(0, n, size=count)
-    # always include the first and last rows and columns
-    ii[:4] = [0, m - 1, 0, m - 1]
-    jj[:4] = [0, 0, n - 1, n - 1]
-    xf = x2d.view(np.uint16) if x_is_f16 else x2d
-    yr, sr = oracle.dot_entries(fmt, w, m, k, xf.ravel(), k, ii, jj, x_is_f16=x_is_f16)
-    return assert_within(y[jj, ii], yr, sr, rel, what)
-
-
 def test_gemv_full_config1():
     """Q8_0 4096 x 4096, batch 1: every output against the oracle."""
     cfg = synth.WORKLOADS["gemv_q8_0_4096x4096_n1"]
@@ -352,22 +341,36 @@ def test_gemv_full_config1():
     assert_within(y, yref, s, GEMV_TOL, "config1")
 
 
+_CONFIG2 = {}
+
+
+def _config2():
+    """Q4_1 11008 x 4096, its 8-column activation draw and the oracle's
+    products for all 8 columns (columns 1..n serve every n)."""
+    if not _CONFIG2:
+        cfg = synth.WORKLOADS["gemv_q4_1_11008x4096"]
+        seed = synth.workload_seed(cfg["id"])
+        w = synth.quant_matrix("q4_1", cfg["m"], cfg["k"], seed=seed, tensor_id=0, d_range=cfg["d"],
+                               m_range=cfg["mr"])
+        x = np.ascontiguousarray(synth.activations(cfg["k"], 8, seed=seed, tensor_id=100))
+        yref, s = oracle_rows(oracle.dot, "q4_1", w, cfg["m"], cfg["k"], x, 8)
+        _CONFIG2.update(w=w, x=x, yref=yref, s=s, m=cfg["m"], k=cfg["k"])
+    return _CONFIG2
+
+
 @pytest.mark.parametrize("n", [1, 2, 4, 8])
-def test_gemv_full_config2_sampled(n):
-    """Q4_1 11008 x 4096 with n columns (first n of one 8-column draw)."""
-    cfg = synth.WORKLOADS["gemv_q4_1_11008x4096"]
-    seed = synth.workload_seed(cfg["id"])
+def test_gemv_full_config2(n):
+    """Q4_1 11008 x 4096 with n columns (first n of one 8-column draw): every
+    output against the oracle."""
+    c = _config2()
     _say("gemv config2", n)
-    w = synth.quant_matrix("q4_1", cfg["m"], cfg["k"], seed=seed, tensor_id=0, d_range=cfg["d"],
-                           m_range=cfg["mr"])
-    x = synth.activations(cfg["k"], 8, seed=seed, tensor_id=100)[:n]
-    y = _gpu_gemv("q4_1", w, cfg["m"], cfg["k"], x)
-    _sampled_check("q4_1", w, cfg["m"], cfg["k"], x, y, np.random.default_rng(n), 768,
-                   GEMV_TOL, what=f"config2 n={n}")
+    y = _gpu_gemv("q4_1", c["w"], c["m"], c["k"], c["x"][:n])
+    assert_within(y, c["yref"][:n], c["s"][:n], GEMV_TOL, f"config2 n={n}")
 
 
-def test_gemv_full_config3_sampled():
-    """The 7B-shaped layer: q, k, v, o, gate, up, down (Q4_0, batch 1)."""
+def test_gemv_full_config3():
+    """The 7B-shaped layer: q, k, v, o, gate, up, down (Q4_0, batch 1), each
+    as its own launch, every output against the oracle."""
     cfg = synth.WORKLOADS["gemv_q4_0_decode_layer"]
     seed = synth.workload_seed(cfg["id"])
     for tid, (name, m, k) in enumerate(cfg["layer"]):
@@ -375,8 +378,8 @@ def test_gemv_full_config3_sampled():
         w = synth.quant_matrix("q4_0", m, k, seed=seed, tensor_id=tid, d_range=cfg["d"])
         x = synth.activations(k, 1, seed=seed, tensor_id=100 + tid)
         y = _gpu_gemv("q4_0", w, m, k, x)
-        _sampled_check("q4_0", w, m, k, x, y, np.random.default_rng(tid), 384, GEMV_TOL,
-                       what=f"config3 {name}")
+        yref, s = oracle_rows(oracle.dot, "q4_0", w, m, k, x, 1)
+        assert_within(y, yref, s, GEMV_TOL, f"config3 {name}")
 
 
 # ---------------------------------------------------------------------------
@@ -567,16 +570,17 @@ def test_gemm_against_fp16_weight_product(fmt, m, k, n):
     assert np.all(err <= bound), f"max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}"
 
 
-def test_gemm_full_config4_sampled():
-    """Q4_0 14336 x 4096 times fp16 4096 x 512: sampled outputs against the oracle."""
+def test_gemm_full_config4():
+    """Q4_0 14336 x 4096 times fp16 4096 x 512: all 7.3 M outputs against the
+    fp64 product of the oracle's weights with the activations."""
     cfg = synth.WORKLOADS["gemm_q4_0_14336x4096_n512"]
     seed = synth.workload_seed(cfg["id"])
     _say("gemm config4")
     w = synth.quant_matrix("q4_0", cfg["m"], cfg["k"], seed=seed, tensor_id=0, d_range=cfg["d"])
     xh = synth.activations(cfg["k"], cfg["n"], seed=seed, tensor_id=100, dtype=np.float16)
     y = _gpu_gemm("q4_0", w, cfg["m"], cfg["k"], xh)
-    _sampled_check("q4_0", w, cfg["m"], cfg["k"], xh, y, np.random.default_rng(4), 1024,
-                   GEMM_TOL, x_is_f16=True, what="config4")
+    yref, s = gemm_reference(oracle, "q4_0", w, cfg["m"], cfg["k"], xh)
+    assert_within(y, yref, s, GEMM_TOL, "config4")
 
 
 # ---------------------------------------------------------------------------
@@ -689,8 +693,28 @@ def test_gemv_batched_two_rows_per_wave_generic(fmt):
         assert np.array_equal(y.view(np.uint32), _gpu_gemv(fmt, w, m, k, x, w_off=off).view(np.uint32))
 
 
-def test_gemv_batched_full_config3_sampled():
-    """The whole 7B-shaped decode layer in one launch (Q4_0, batch 1)."""
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_batched_two_rows_per_wave_aligned(fmt):
+    """A grouped one-column launch past 64 rows per CU on the aligned path
+    (two rows per wave, problems from the table, 4-byte aligned weights with
+    an even block count): every output of every item against the oracle, and
+    bitwise equal to separate launches."""
+    shapes = [(16403, 4096), (301, 2048), (77, 8192)]
+    _say("gemv batched two rows aligned", fmt)
+    probs = []
+    for i, (m, k) in enumerate(shapes):
+        probs.append((_weights(fmt, m, k, seed=53, tid=i), m, k,
+                      synth.activations(k, 1, seed=53, tensor_id=10 + i)))
+    ys = _gpu_gemv_batched(fmt, probs, 1)
+    for (w, m, k, x), y in zip(probs, ys):
+        yref, s = oracle_rows(oracle.dot, fmt, w, m, k, x, 1)
+        assert_within(y, yref, s, GEMV_TOL, f"batched two rows aligned {fmt} {m}x{k}")
+        assert np.array_equal(y.view(np.uint32), _gpu_gemv(fmt, w, m, k, x).view(np.uint32))
+
+
+def test_gemv_batched_full_config3():
+    """The whole 7B-shaped decode layer in one launch (Q4_0, batch 1): every
+    output of every matrix against the oracle."""
     cfg = synth.WORKLOADS["gemv_q4_0_decode_layer"]
     seed = synth.workload_seed(cfg["id"])
     _say("gemv batched config3")
@@ -700,5 +724,5 @@ def test_gemv_batched_full_config3_sampled():
         probs.append((w, m, k, synth.activations(k, 1, seed=seed, tensor_id=100 + tid)))
     ys = _gpu_gemv_batched("q4_0", probs, 1)
     for tid, ((w, m, k, x), y) in enumerate(zip(probs, ys)):
-        _sampled_check("q4_0", w, m, k, x, y, np.random.default_rng(50 + tid), 256, GEMV_TOL,
-                       what=f"batched config3 item {tid}")
+        yref, s = oracle_rows(oracle.dot, "q4_0", w, m, k, x, 1)
+        assert_within(y, yref, s, GEMV_TOL, f"batched config3 item {tid}")
