@@ -149,30 +149,91 @@ def qk_mul_mat(fmt, w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream=0):
 
 # ---------------------------------------------------------------------------
 # torch-tensor conveniences (allocation by torch, compute by libqk)
+#
+# The C ABI sees only pointers, so these wrappers check every tensor on the
+# host before anything is launched: dtype, shape, a contiguous innermost
+# dimension, enough weight bytes, one CUDA device for all operands.  A
+# mismatch raises TypeError or ValueError and enqueues nothing.
 # ---------------------------------------------------------------------------
+
+_BLOCK_BYTES = {QK_Q4_0: 18, QK_Q4_1: 20, QK_Q8_0: 34}
+
+
+def _weight_check(fmt, w, rows, k):
+    import torch
+    code = _fmt(fmt)
+    if code not in _BLOCK_BYTES:
+        raise ValueError(f"unknown format {fmt!r}")
+    if rows < 0 or k < 0 or k % 32 != 0:
+        raise ValueError(f"bad shape rows={rows}, k={k} (k must be a non-negative multiple of 32)")
+    if not isinstance(w, torch.Tensor) or w.dtype != torch.uint8:
+        raise TypeError("w must be a uint8 tensor of block bytes")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    need = rows * (k // 32) * _BLOCK_BYTES[code]
+    if w.numel() < need:
+        raise ValueError(f"w holds {w.numel()} bytes, a {rows} x {k} matrix needs {need}")
+
+
+def _cols_check(t, name, dtype, n, length):
+    """t is (n, >= length) of dtype with contiguous rows (ggml columns)."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype:
+        raise TypeError(f"{name} must be a {dtype} tensor")
+    if t.dim() != 2 or t.shape[0] != n or t.shape[1] < length:
+        raise ValueError(f"{name} must have shape ({n}, >= {length}), got {tuple(t.shape)}")
+    if n > 0 and length > 0 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous columns (stride(1) == 1)")
+
+
+def _same_device(*ts):
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a CUDA device")
+    for t in ts[1:]:
+        if t.device != dev:
+            raise ValueError(f"tensors on different devices: {dev} and {t.device}")
+
 
 def dequantize(fmt, w, rows, k, out_dtype="f32", out=None, stream=None):
     """Dequantize a rows x k matrix held as block bytes in a uint8 CUDA tensor."""
     import torch
+    if out_dtype not in ("f32", "f16"):
+        raise ValueError(f"out_dtype must be 'f32' or 'f16', got {out_dtype!r}")
     dt = {"f32": (QK_F32, torch.float32), "f16": (QK_F16, torch.float16)}[out_dtype]
+    _weight_check(fmt, w, rows, k)
     if out is None:
         out = torch.empty((rows, k), dtype=dt[1], device=w.device)
+    if not isinstance(out, torch.Tensor) or out.dtype != dt[1]:
+        raise TypeError(f"out must be a {dt[1]} tensor for out_dtype {out_dtype!r}")
+    if tuple(out.shape) != (rows, k) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous ({rows}, {k}) tensor")
+    _same_device(w, out)
     st = qk_dequantize(fmt, w.data_ptr(), rows, k, dt[0], out.data_ptr(), _stream(stream))
     _check(st, "qk_dequantize")
     return out
 
 
-def mul_mat_vec(fmt, w, m, k, x, y=None, stream=None):
-    """y (n, m) = x (n, k) @ W^T for 1..8 fp32 columns; rows of x and y are the
-    ggml columns (contiguous, ldx = x.stride(0), ldy = y.stride(0))."""
+def _gemv_args(fmt, w, m, k, x, y):
     import torch
     if x.dim() == 1:
         x = x.view(1, -1)
     n = x.shape[0]
-    if x.dtype != torch.float32 or x.stride(1) != 1:
-        raise TypeError("x must be float32 with contiguous columns")
+    if not 1 <= n <= 8:
+        raise ValueError(f"1..8 activation columns, got {n}")
+    _weight_check(fmt, w, m, k)
+    _cols_check(x, "x", torch.float32, n, k)
     if y is None:
         y = torch.empty((n, m), dtype=torch.float32, device=x.device)
+    _cols_check(y, "y", torch.float32, n, m)
+    _same_device(w, x, y)
+    return x, y, n
+
+
+def mul_mat_vec(fmt, w, m, k, x, y=None, stream=None):
+    """y (n, m) = x (n, k) @ W^T for 1..8 fp32 columns; rows of x and y are the
+    ggml columns (contiguous, ldx = x.stride(0), ldy = y.stride(0))."""
+    x, y, n = _gemv_args(fmt, w, m, k, x, y)
     st = qk_mul_mat_vec(fmt, w.data_ptr(), m, k, x.data_ptr(), n, x.stride(0),
                         y.data_ptr(), y.stride(0), _stream(stream))
     _check(st, "qk_mul_mat_vec")
@@ -182,14 +243,7 @@ def mul_mat_vec(fmt, w, m, k, x, y=None, stream=None):
 def mul_mat_vec_x8(fmt, w, m, k, x, y=None, stream=None):
     """As mul_mat_vec, with the activations quantized to 8 bits per 32-element
     block inside the kernel and integer dot products (qk_mul_mat_vec_x8)."""
-    import torch
-    if x.dim() == 1:
-        x = x.view(1, -1)
-    n = x.shape[0]
-    if x.dtype != torch.float32 or x.stride(1) != 1:
-        raise TypeError("x must be float32 with contiguous columns")
-    if y is None:
-        y = torch.empty((n, m), dtype=torch.float32, device=x.device)
+    x, y, n = _gemv_args(fmt, w, m, k, x, y)
     st = qk_mul_mat_vec_x8(fmt, w.data_ptr(), m, k, x.data_ptr(), n, x.stride(0),
                            y.data_ptr(), y.stride(0), _stream(stream))
     _check(st, "qk_mul_mat_vec_x8")
@@ -202,14 +256,20 @@ def mul_mat_vec_batched(fmt, problems, ys=None, stream=None):
     import torch
     if not problems:
         return []
+    if len(problems) > QK_MAX_BATCH:
+        raise ValueError(f"at most {QK_MAX_BATCH} problems per launch")
     n = problems[0][3].shape[0] if problems[0][3].dim() == 2 else 1
     if ys is None:
         ys = [torch.empty((n, m), dtype=torch.float32, device=x.device) for (_, m, _, x) in problems]
+    if len(ys) != len(problems):
+        raise ValueError("one output per problem")
     tup = []
     for (w, m, k, x), y in zip(problems, ys):
         x2 = x.view(1, -1) if x.dim() == 1 else x
-        if x2.dtype != torch.float32 or x2.stride(1) != 1 or x2.shape[0] != n:
-            raise TypeError("every x must be float32 (n, k) with contiguous columns and the same n")
+        if x2.shape[0] != n:
+            raise ValueError("every x must have the same number of columns")
+        x2, y, _ = _gemv_args(fmt, w, m, k, x2, y)
+        _same_device(problems[0][0], w)
         tup.append((w.data_ptr(), m, k, x2.data_ptr(), x2.stride(0), y.data_ptr(), y.stride(0)))
     arr = make_items(tup)
     st = qk_mul_mat_vec_batched(fmt, arr, len(tup), n, _stream(stream))
@@ -224,21 +284,33 @@ def mul_mat_vec_id(fmt, w, n_experts, m, k, ids, x, y=None, expert_stride=None, 
     (default: packed); ids: int32 CUDA tensor (n_tokens, n_used).  Returns y
     shaped (n_tokens, n_used, m) fp32."""
     import torch
-    if ids.dtype != torch.int32 or ids.dim() != 2 or ids.stride(1) != 1:
+    if not isinstance(ids, torch.Tensor) or ids.dtype != torch.int32 or ids.dim() != 2 or ids.stride(1) != 1:
         raise TypeError("ids must be int32 (n_tokens, n_used) with contiguous rows")
     n_tokens, n_used = ids.shape
-    if x.dtype != torch.float32 or x.stride(-1) != 1:
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or x.stride(-1) != 1:
         raise TypeError("x must be float32 with contiguous vectors")
-    if x.dim() == 2:
+    if x.dim() == 2 and x.shape[0] == n_tokens and x.shape[1] >= k:
         x_slot, x_tok = 0, x.stride(0)
-    elif x.dim() == 3:
+    elif x.dim() == 3 and tuple(x.shape[:2]) == (n_tokens, n_used) and x.shape[2] >= k:
         x_slot, x_tok = x.stride(1), x.stride(0)
     else:
-        raise TypeError("x must be (n_tokens, k) or (n_tokens, n_used, k)")
+        raise ValueError(f"x must be ({n_tokens}, >= {k}) or ({n_tokens}, {n_used}, >= {k}), "
+                         f"got {tuple(x.shape)}")
+    one = m * (k // 32) * _BLOCK_BYTES.get(_fmt(fmt), 0)
     if expert_stride is None:
-        expert_stride = m * row_bytes(fmt, k)
+        expert_stride = one
+    if n_experts < 1 or expert_stride < one:
+        raise ValueError("n_experts >= 1 and expert_stride >= one expert matrix")
+    _weight_check(fmt, w, m, k)
+    if w.numel() < (n_experts - 1) * expert_stride + one:
+        raise ValueError(f"w holds {w.numel()} bytes, the stack needs {(n_experts - 1) * expert_stride + one}")
     if y is None:
         y = torch.empty((n_tokens, n_used, m), dtype=torch.float32, device=x.device)
+    if not isinstance(y, torch.Tensor) or y.dtype != torch.float32:
+        raise TypeError("y must be a float32 tensor")
+    if tuple(y.shape) != (n_tokens, n_used, m) or (m > 0 and y.stride(2) != 1):
+        raise ValueError(f"y must have shape ({n_tokens}, {n_used}, {m}) with contiguous rows")
+    _same_device(w, ids, x, y)
     st = qk_mul_mat_vec_id(fmt, w.data_ptr(), n_experts, expert_stride, m, k, ids.data_ptr(),
                            ids.stride(0), n_used, n_tokens, x.data_ptr(), x_slot, x_tok,
                            y.data_ptr(), y.stride(1), y.stride(0), _stream(stream))
@@ -249,11 +321,15 @@ def mul_mat_vec_id(fmt, w, n_experts, m, k, ids, x, y=None, expert_stride=None, 
 def mul_mat(fmt, w, m, k, x, y=None, stream=None):
     """y (n, m) = x (n, k, fp16) @ f16(W)^T on the matrix cores."""
     import torch
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise TypeError("x must be a 2-D float16 tensor (n, k)")
     n = x.shape[0]
-    if x.dtype != torch.float16 or x.stride(1) != 1:
-        raise TypeError("x must be float16 with contiguous columns")
+    _weight_check(fmt, w, m, k)
+    _cols_check(x, "x", torch.float16, n, k)
     if y is None:
         y = torch.empty((n, m), dtype=torch.float32, device=x.device)
+    _cols_check(y, "y", torch.float32, n, m)
+    _same_device(w, x, y)
     st = qk_mul_mat(fmt, w.data_ptr(), m, k, x.data_ptr(), n, x.stride(0),
                     y.data_ptr(), y.stride(0), _stream(stream))
     _check(st, "qk_mul_mat")

@@ -206,3 +206,68 @@ def _id_args(**kw):
 ])
 def test_mul_mat_vec_id_validation(kw, want):
     assert qk.qk_mul_mat_vec_id(*_id_args(**kw), 0) == want
+
+
+# ---------------------------------------------------------------------------
+# the torch wrappers check every tensor on the host before any launch
+# ---------------------------------------------------------------------------
+
+@pytest.fixture
+def no_launch(monkeypatch):
+    """Any call that reaches the library fails the test."""
+    def boom():
+        raise AssertionError("the wrapper reached the library")
+    monkeypatch.setattr(qk, "load", boom)
+
+
+def _t():
+    import torch
+    return torch
+
+
+def test_wrappers_reject_bad_tensors(no_launch):
+    t = _t()
+    m, k = 8, 64
+    w = t.zeros(m * (k // 32) * 18, dtype=t.uint8)
+    x = t.zeros((2, k), dtype=t.float32)
+    cases = [
+        (lambda: qk.mul_mat_vec("q4_0", w, m, k, x, y=t.zeros((2, m), dtype=t.float16)), TypeError),
+        (lambda: qk.mul_mat_vec("q4_0", w, m, k, x, y=t.zeros((2, m - 1))), ValueError),
+        (lambda: qk.mul_mat_vec("q4_0", w, m, k, x, y=t.zeros((1, m))), ValueError),
+        (lambda: qk.mul_mat_vec("q4_0", w, m, k, t.zeros((2, k - 32))), ValueError),
+        (lambda: qk.mul_mat_vec("q4_0", w, m, k, t.zeros((2, k), dtype=t.float64)), TypeError),
+        (lambda: qk.mul_mat_vec("q4_0", w, m, k, t.zeros((k, 2)).t()), ValueError),
+        (lambda: qk.mul_mat_vec("q4_0", w[:-1], m, k, x), ValueError),
+        (lambda: qk.mul_mat_vec("q4_0", w.float(), m, k, x), TypeError),
+        (lambda: qk.mul_mat_vec("q4_0", w, m, k, t.zeros((9, k))), ValueError),
+        (lambda: qk.mul_mat_vec("q4_0", w, m, 48, x), ValueError),
+        (lambda: qk.mul_mat_vec("q9_9", w, m, k, x), ValueError),
+        (lambda: qk.mul_mat_vec_x8("q4_0", w, m, k, x, y=t.zeros((2, m), dtype=t.float16)), TypeError),
+        (lambda: qk.dequantize("q4_0", w, m, k, "f32", out=t.zeros((m, k), dtype=t.float16)), TypeError),
+        (lambda: qk.dequantize("q4_0", w, m, k, "f16", out=t.zeros((m, k - 1), dtype=t.float16)), ValueError),
+        (lambda: qk.dequantize("q4_0", w, m, k, "bf16"), ValueError),
+        (lambda: qk.mul_mat("q4_0", w, m, k, x), TypeError),
+        (lambda: qk.mul_mat("q4_0", w, m, k, x.half(), y=t.zeros((2, m), dtype=t.float16)), TypeError),
+        (lambda: qk.mul_mat("q4_0", w, m, k, t.zeros((2, k - 32), dtype=t.float16)), ValueError),
+        (lambda: qk.mul_mat_vec_batched("q4_0", [(w, m, k, x)], ys=[t.zeros((2, m - 1))]), ValueError),
+        (lambda: qk.mul_mat_vec_id("q4_0", w, 1, m, k, t.zeros((1, 2), dtype=t.int64), x[:1]), TypeError),
+        (lambda: qk.mul_mat_vec_id("q4_0", w, 2, m, k, t.zeros((1, 2), dtype=t.int32), x[:1]), ValueError),
+        (lambda: qk.mul_mat_vec_id("q4_0", w, 1, m, k, t.zeros((1, 2), dtype=t.int32), x[:1],
+                                   y=t.zeros((1, 2, m - 1))), ValueError),
+    ]
+    for i, (fn, exc) in enumerate(cases):
+        with pytest.raises(exc):
+            fn()
+
+
+def test_wrappers_reject_host_tensors(no_launch):
+    """Well-formed tensors that are not on a CUDA device never reach a kernel."""
+    t = _t()
+    m, k = 8, 64
+    w = t.zeros(m * (k // 32) * 34, dtype=t.uint8)
+    with pytest.raises(ValueError, match="CUDA"):
+        qk.mul_mat_vec("q8_0", w, m, k, t.zeros((1, k)))
+    with pytest.raises(ValueError, match="CUDA"):
+        qk.dequantize("q8_0", w, m, k)
+    with pytest.raises(ValueError, match="CUDA"):
+        qk.mul_mat("q8_0", w, m, k, t.zeros((3, k), dtype=t.float16))
