@@ -1,29 +1,42 @@
-"""Benchmark of the quantized GEMV hot path on one MI355X.
+"""Benchmark of the quantized dequantize / GEMV / GEMM hot path on one MI355X.
 
-Default workload: Q8_0 GEMV, W 4096 x 4096 times one fp32 activation column
-(x ~ N(0,1)), y = W x in fp32.  A step is one qk_mul_mat_vec call: block
-decode, fused dequantize + dot products, wave/workgroup reduction, dispatch.
+Headline: Q8_0 GEMV, W 4096 x 4096 times one fp32 activation column
+(x ~ N(0,1)), y = W x in fp32.  A step is one qk_mul_mat_vec call (block
+decode, fused dequantize + dot products, wave reduction, dispatch).  The same
+line carries every workload (dequantize, the Q4_1 GEMV at 1/2/4/8 columns, the
+7B-shaped Q4_0 decode layer, the Q4_0 GEMM) and the next rows (8-bit
+activations, expert-indexed decode, one GPU's tensor-parallel share, small
+GEMM batches) under "configs" and "extras".
 
 Measurement
   * Inputs live in HBM before the timed region.  Every working set here fits
-    in the 256 MB Infinity Cache, so the benchmark rotates through R copies of
-    the weights (R * |W| >= 1 GiB): launch i reads copy i % R, which is never
+    in the 256 MB Infinity Cache, so each workload rotates through R copies of
+    its weights (R * |W| >= 1 GiB): step i reads copy i % R, never
     cache-resident.
-  * Launches are captured into a HIP graph (torch.cuda.CUDAGraph) so host
-    launch overhead is out of the way; the timed region is one replay of K
-    launches, bracketed by synchronization, timed with HIP events recorded on
-    the stream the kernels run on.
-  * Before timing, the output is checked against the CPU oracle (every row).
-  * metric value = weight bytes per launch * K / elapsed  (effective weight GB/s)
-  * roofline.achieved = algorithmic bytes per launch (W + x + y) / average
-    launch time; peak = 8 TB/s HBM.
-  * cpu_baseline: the oracle (plain C, fp64, one thread) on the same matrix.
-  * practical_ceiling: a plain streaming-read kernel (libqk_ceiling.so) over
-    the same weight bytes, same rotation and launch pattern; --configs adds
-    it per GEMV workload and an MFMA-only loop for the GEMM.
+  * Steps are issued by a native launch loop (libqk_bench.so: no interpreter
+    between launches, so the GPU never waits for the host) on one stream.  W
+    warm-up steps, a device synchronization, then K timed steps between two
+    HIP events recorded on that stream, and a synchronization.  Before each
+    workload's warm-up the GPU's clocks are brought out of their idle state by
+    streaming reads of an unrelated buffer (host-side work such as the oracle
+    checks leaves the GPU idle for seconds).
+  * Per-launch distribution: 20 warm-up launches, then 200 launches with an
+    event after every 10 (an event between single launches adds its own cost
+    to each); median, p10 and p90 of the per-launch time of the 20 groups.
+  * Parity first: before a workload is timed its output is checked against
+    the CPU oracle on every element (bit-exact for dequantize, within 1e-4*S
+    for the GEMVs, 1e-2*S for the GEMM); after timing, the output of the last
+    timed launch must equal the checked one bit for bit.
+  * Rooflines: HBM 8 TB/s; fp16 dense MFMA 2.5 PFLOP/s; fp32 vector ALU
+    78.6 TFLOP/s (256 CUs x 64 lanes x 2 flops per FMA x 2.4 GHz: the build
+    keeps packed fp32 instructions off).  The Q4_1 GEMV is reported against
+    max(HBM time, ALU time); the GEMM against the MFMA peak.
+  * cpu_baseline: the oracle (plain C, fp64) timed on this host: one thread on
+    a bounded row sample (scaled), and T threads (T = CPUs in the affinity
+    mask) over the whole workload, which is also the parity reference.
 
-Options: --workload NAME runs another single-GEMV workload as the headline;
---configs also measures every workload and adds them under "configs".
+Options: --quick skips the extras; --headline-only times the headline alone
+(for profiler runs); --no-cpu skips the single-thread baseline legs.
 """
 import argparse
 import ctypes
@@ -31,8 +44,10 @@ import hashlib
 import json
 import math
 import os
+import platform
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -42,61 +57,210 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+VALU_F32_PEAK_TFLOPS = 78.6
 COLD_BYTES = 1 << 30
+SETTLE_MS = 30.0
+DIST_WARMUP, DIST_LAUNCHES, DIST_GROUP = 20, 200, 10
 PROFILES = os.path.join(ROOT, "profiles")
 GEMV_SOURCES = ["gemv.hip", "gemv.h", "gemv_impl.h", "gemv_n1.hip", "qk_common.h",
                 "qk_internal.h"]
+METRIC = "effective weight GB/s (% of HBM peak) for Q4_0/Q8_0 GEMV; batched TFLOP/s"
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def load_ceiling():
-    """The practical-ceiling kernels (libqk_ceiling.so, built with libqk)."""
-    path = os.path.join(ROOT, "dequant_quantized_gemv_amd", "libqk_ceiling.so")
-    if not os.path.exists(path):
-        raise SystemExit(f"{path} is not built; run __graft_entry__.build()")
-    lib = ctypes.CDLL(path)
-    lib.qkc_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
-    lib.qkc_stream_read.restype = ctypes.c_int
-    lib.qkc_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    lib.qkc_mfma_loop.restype = ctypes.c_int
-    return lib
+# ---------------------------------------------------------------------------
+# native launch loop and ceilings (libqk_bench.so)
+# ---------------------------------------------------------------------------
+
+_CALL_FIELDS = [("op", "i"), ("fmt", "i"), ("w", "p"), ("m", "i"), ("k", "i"), ("x", "p"),
+                ("n", "i"), ("ldx", "i"), ("y", "p"), ("ldy", "i"), ("out_dtype", "i"),
+                ("items", "p"), ("count", "i"), ("n_experts", "i"), ("expert_stride", "i"),
+                ("ids", "p"), ("ld_ids", "i"), ("n_used", "i"), ("n_tokens", "i"),
+                ("x_slot", "i"), ("x_tok", "i"), ("y_slot", "i"), ("y_tok", "i")]
 
 
-def stream_read_time(torch, timer, clib, ptrs, nbytes, steps, warmup):
-    """Seconds per streaming read of nbytes, launch i reading ptrs[i % len]
-    (the same cold rotation as the kernel it is compared with)."""
-    sink = torch.zeros(4, device="cuda")
-    R = len(ptrs)
-
-    def rd(i):
-        if clib.qkc_stream_read(ptrs[i % R], nbytes, sink.data_ptr(),
-                                torch.cuda.current_stream().cuda_stream) != 0:
-            raise RuntimeError("qkc_stream_read failed")
-
-    gw, gk = timer.capture(rd, max(warmup, 1)), timer.capture(lambda i: rd(i + warmup), steps)
-    timer.time_graph(gw)
-    sec = timer.time_graph(gk) / steps
-    del gw, gk
-    return sec
+class QkbCall(ctypes.Structure):
+    """struct qkb_call of bench_support.hip: one qk C ABI call."""
+    _fields_ = [(n, ctypes.c_int64 if t == "i" else ctypes.c_void_p) for n, t in _CALL_FIELDS]
 
 
-def mfma_loop_tflops(torch, timer, clib):
-    """fp16 MFMA rate of a register-only loop over every CU (TFLOP/s)."""
-    sink = torch.zeros(4, device="cuda")
-    wgs = torch.cuda.get_device_properties(0).multi_processor_count
-    iters = 4000
+OPS = {"dequantize": 0, "mul_mat_vec": 1, "mul_mat_vec_x8": 2, "mul_mat_vec_batched": 3,
+       "mul_mat_vec_id": 4, "mul_mat": 5, "stream_read": 6}
 
-    def run(i):
-        if clib.qkc_mfma_loop(wgs, iters, sink.data_ptr(), torch.cuda.current_stream().cuda_stream) != 0:
-            raise RuntimeError("qkc_mfma_loop failed")
 
-    gw, gk = timer.capture(run, 2), timer.capture(run, 5)
-    timer.time_graph(gw)
-    sec = timer.time_graph(gk) / 5
-    return wgs * 8 * iters * 32 * (2.0 * 16 * 16 * 32) / sec / 1e12
+class Runner:
+    """Steps of qk calls issued and timed by the native loop on one stream."""
+
+    def __init__(self, torch):
+        self.t = torch
+        path = os.path.join(ROOT, "dequant_quantized_gemv_amd", "libqk_bench.so")
+        if not os.path.exists(path):
+            raise SystemExit(f"{path} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        lib.qkb_time_steps.argtypes = [ctypes.POINTER(QkbCall), ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                       ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]
+        lib.qkb_time_steps.restype = ctypes.c_int
+        lib.qkb_settle.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_double, vp]
+        lib.qkb_settle.restype = ctypes.c_int
+        lib.qkc_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+        lib.qkc_mfma_loop.restype = ctypes.c_int
+        self.lib = lib
+        self.stream = torch.cuda.Stream()
+        self.sink = torch.zeros(64, device="cuda")
+        self.settle_buf = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+
+    @staticmethod
+    def call(op, **kw):
+        c = QkbCall()
+        c.op = OPS[op]
+        for name, v in kw.items():
+            setattr(c, name, v)
+        return c
+
+    def stream_read(self, ptr, nbytes):
+        return self.call("stream_read", w=ptr, k=nbytes, y=self.sink.data_ptr())
+
+    def settle(self, ms=SETTLE_MS):
+        if ms > 0 and self.lib.qkb_settle(self.settle_buf.data_ptr(), self.settle_buf.numel(),
+                                          self.sink.data_ptr(), ms, self.stream.cuda_stream) != 0:
+            raise RuntimeError("qkb_settle failed")
+
+    def time_steps(self, variants, warmup, steps, group=0):
+        """variants: list (rotation) of lists of QkbCall (one step each).
+        Returns (seconds for the timed steps, and with group > 0 the seconds
+        per step of each group of `group` consecutive steps, else None)."""
+        per = len(variants[0])
+        arr = (QkbCall * (per * len(variants)))()
+        for v, calls in enumerate(variants):
+            assert len(calls) == per
+            for j, c in enumerate(calls):
+                arr[v * per + j] = c
+        total = ctypes.c_float()
+        ng = steps // group if group > 0 else 0
+        dist = (ctypes.c_float * ng)() if group > 0 else None
+        st = self.lib.qkb_time_steps(arr, per, len(variants), warmup, steps, max(group, 1),
+                                     self.stream.cuda_stream, ctypes.byref(total), dist)
+        if st != 0:
+            raise RuntimeError(f"qkb_time_steps failed with status {st}")
+        return total.value / 1e3, (np.array(dist[:], dtype=np.float64) / 1e3 / group if group > 0 else None)
+
+    def measure(self, variants, steps, warmup):
+        """Settle, W warm-up + K timed steps back to back, then the per-step
+        distribution: 20 warm-up steps and 200 timed ones, in groups of 10."""
+        self.settle()
+        sec, _ = self.time_steps(variants, warmup, steps)
+        _, d = self.time_steps(variants, DIST_WARMUP, DIST_LAUNCHES, group=DIST_GROUP)
+        return dict(us=sec / steps * 1e6, median_us=float(np.median(d)) * 1e6,
+                    p10_us=float(np.percentile(d, 10)) * 1e6, p90_us=float(np.percentile(d, 90)) * 1e6)
+
+    def mfma_loop_tflops(self):
+        """fp16 MFMA rate of a register-only loop over every CU (TFLOP/s)."""
+        wgs = self.t.cuda.get_device_properties(0).multi_processor_count
+        iters = 4000
+        self.settle()
+        best = math.inf
+        for _ in range(3):
+            e0 = self.t.cuda.Event(enable_timing=True)
+            e1 = self.t.cuda.Event(enable_timing=True)
+            with self.t.cuda.stream(self.stream):
+                e0.record(self.stream)
+                if self.lib.qkc_mfma_loop(wgs, iters, self.sink.data_ptr(), self.stream.cuda_stream) != 0:
+                    raise RuntimeError("qkc_mfma_loop failed")
+                e1.record(self.stream)
+            self.t.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / 1e3)
+        return wgs * 8 * iters * 32 * (2.0 * 16 * 16 * 32) / best / 1e12
+
+
+def rnd(v, nd=3):
+    return None if v is None else round(float(v), nd)
+
+
+def timing_fields(t):
+    return {"us_per_step": rnd(t["us"]), "median_us": rnd(t["median_us"]), "p10_us": rnd(t["p10_us"]),
+            "p90_us": rnd(t["p90_us"])}
+
+
+def copies_for(nbytes, minimum=2):
+    return max(minimum, math.ceil(COLD_BYTES / max(nbytes, 1)))
+
+
+def rotation(torch, t, nbytes):
+    """[t, copies...]: R tensors, R * nbytes >= 1 GiB."""
+    R = copies_for(nbytes)
+    return [t] + [t.clone() for _ in range(R - 1)]
+
+
+# ---------------------------------------------------------------------------
+# oracle helpers (parity reference and CPU baseline)
+# ---------------------------------------------------------------------------
+
+def host_threads():
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except (AttributeError, OSError):
+        return max(1, os.cpu_count() or 1)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+BLOCK_BYTES = {"q4_0": 18, "q4_1": 20, "q8_0": 34}
+
+
+def row_bytes(fmt, k):
+    return (k // 32) * BLOCK_BYTES[fmt]
+
+
+def oracle_rows(fn, fmt, w, m, k, threads, *args):
+    """fn(fmt, w_rows, rows, k, *args) -> (y (n, rows), s (n, rows)) over row
+    ranges in `threads` host threads (the oracle's C calls release the GIL);
+    returns the concatenated (y, s) and the wall time."""
+    rb = row_bytes(fmt, k)
+    step = max(1, -(-m // (threads * 4)))
+    chunks = [(r, min(m, r + step)) for r in range(0, m, step)]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda c: fn(fmt, w[c[0] * rb:c[1] * rb], c[1] - c[0], k, *args), chunks))
+    el = time.perf_counter() - t0
+    return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1), el
+
+
+def single_thread_rows(fn, fmt, w, m, k, budget_s, *args):
+    """One thread on the first r rows, r grown until the call takes about
+    budget_s; returns (rows, seconds)."""
+    rb = row_bytes(fmt, k)
+    r = min(m, 16)
+    while True:
+        t0 = time.perf_counter()
+        fn(fmt, w[:r * rb], r, k, *args)
+        el = time.perf_counter() - t0
+        if el >= budget_s or r == m:
+            return r, el
+        r = min(m, max(r * 2, int(r * budget_s / max(el, 1e-6))))
+
+
+def within(y, yr, s, rel):
+    """Every element: |y - yr| <= rel * S (NaN or inf anywhere fails); returns
+    (ok, max |y - yr| / S)."""
+    y = np.asarray(y, dtype=np.float64)
+    err = np.abs(y - yr)
+    ok = bool(np.all(err <= rel * s)) and bool(np.all(np.isfinite(y)))
+    worst = float(np.max(err / np.where(s > 0, s, 1))) if err.size else 0.0
+    return ok, worst
 
 
 def kernel_source_hash(names):
@@ -141,549 +305,402 @@ def copy_calibration(torch, mib):
     log(f"copy calibration: {mib} MiB read + {mib} MiB written per copy, 5 copies")
 
 
-class Timer:
-    """Graph-captured launches timed with HIP events on the launch stream."""
-
-    def __init__(self, torch):
-        self.t = torch
-
-    def capture(self, fn, count):
-        t = self.t
-        g = t.cuda.CUDAGraph()
-        s = t.cuda.Stream()
-        s.wait_stream(t.cuda.current_stream())
-        with t.cuda.stream(s):
-            with t.cuda.graph(g, stream=s):
-                for i in range(count):
-                    fn(i)
-        t.cuda.current_stream().wait_stream(s)
-        t.cuda.synchronize()
-        return g
-
-    def time_graph(self, g):
-        t = self.t
-        t.cuda.synchronize()
-        st = t.cuda.current_stream()
-        e0 = t.cuda.Event(enable_timing=True)
-        e1 = t.cuda.Event(enable_timing=True)
-        e0.record(st)
-        g.replay()
-        e1.record(st)
-        t.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3  # seconds
-
-
-def copies_for(nbytes, minimum=2):
-    return max(minimum, math.ceil(COLD_BYTES / max(nbytes, 1)))
-
-
 # ---------------------------------------------------------------------------
 # workloads
 # ---------------------------------------------------------------------------
 
-def setup_gemv(torch, qk, synth, oracle, fmt, m, k, n, seed, wtid, xtid, d, mr=None,
-               check="full", rng_seed=0):
-    """Device copies of one GEMV problem plus the parity check of one launch."""
-    w = synth.quant_matrix(fmt, m, k, seed=seed, tensor_id=wtid, d_range=d,
-                           **({"m_range": mr} if mr else {}))
-    x = synth.activations(k, 8 if n > 1 else 1, seed=seed, tensor_id=xtid)[:n]
+class Ctx:
+    def __init__(self, torch, qk, synth, oracle, run, args):
+        self.torch, self.qk, self.synth, self.oracle, self.run = torch, qk, synth, oracle, run
+        self.steps, self.warmup = args.steps, args.warmup
+        self.threads = host_threads()
+        self.single = not args.no_cpu
+        self.budget = args.cpu_budget
+
+
+def gemv_roofline(fmt, m, k, n, sec):
+    """Roofline of a fp32-activation GEMV launch: HBM for the algorithmic
+    bytes, and the fp32 vector ALU for the 2*m*k*n flops; the bound is the
+    larger time."""
+    wb = m * row_bytes(fmt, k)
+    algo = wb + 4 * n * (k + m)
+    t_hbm = algo / (HBM_PEAK_GBPS * 1e9)
+    t_alu = 2.0 * m * k * n / (VALU_F32_PEAK_TFLOPS * 1e12)
+    if t_alu > t_hbm:
+        return {"bound": "alu", "achieved": rnd(2.0 * m * k * n / sec / 1e12, 2),
+                "peak": VALU_F32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": rnd(t_alu / sec, 4),
+                "hbm_frac": rnd(t_hbm / sec, 4)}
+    return {"bound": "hbm", "achieved": rnd(algo / sec / 1e9, 2), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": rnd(t_hbm / sec, 4)}
+
+
+def run_gemv(c, fmt, m, k, ns, seed, d, mr=None, entry="mul_mat_vec", xtid=100, ceiling=False):
+    """Single-GEMV workloads (one per column count in ns, all columns from one
+    8-column draw): parity on every output, then timing."""
+    torch, qk, synth, oracle = c.torch, c.qk, c.synth, c.oracle
+    w = synth.quant_matrix(fmt, m, k, seed=seed, tensor_id=0, d_range=d, **({"m_range": mr} if mr else {}))
+    nmax = max(ns)
+    x_all = synth.activations(k, 8 if nmax > 1 else 1, seed=seed, tensor_id=xtid)[:nmax]
+    x_all = np.ascontiguousarray(x_all)
+    ref_fn = oracle.dot if entry == "mul_mat_vec" else oracle.dot_x8
+    yr, sr, t_mt = oracle_rows(ref_fn, fmt, w, m, k, c.threads, x_all, nmax)
     wd = torch.from_numpy(w).cuda()
-    xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
-    y = torch.empty((n, m), dtype=torch.float32, device="cuda")
-    qk.mul_mat_vec(fmt, wd, m, k, xd, y=y)
-    torch.cuda.synchronize()
-    yh = y.cpu().numpy().astype(np.float64)
-    if check == "none":
-        return dict(w=w, x=x, wd=wd, xd=xd, y=y, ok=True, worst=0.0)
-    if check == "full":
-        yr, s = oracle.dot(fmt, w, m, k, x, n)
-        ok = bool(np.all(np.abs(yh - yr) <= 1e-4 * s))
-        worst = float(np.max(np.abs(yh - yr) / np.where(s > 0, s, 1)))
-    else:
-        rng = np.random.default_rng(rng_seed)
-        ii = rng.integers(0, m, size=256)
-        jj = rng.integers(0, n, size=256)
-        yr, s = oracle.dot_entries(fmt, w, m, k, x.ravel(), k, ii, jj)
-        got = yh[jj, ii]
-        ok = bool(np.all(np.abs(got - yr) <= 1e-4 * s))
-        worst = float(np.max(np.abs(got - yr) / np.where(s > 0, s, 1)))
-    return dict(w=w, x=x, wd=wd, xd=xd, y=y, ok=ok, worst=worst)
+    copies = rotation(torch, wd, w.size)
+    xd = torch.from_numpy(x_all).cuda()
+    out = {}
+    wb = w.size
+    for n in ns:
+        y = torch.empty((n, m), dtype=torch.float32, device="cuda")
+        variants = [[c.run.call(entry, fmt=qk.FORMATS[fmt], w=cp.data_ptr(), m=m, k=k, x=xd.data_ptr(), n=n,
+                                ldx=k, y=y.data_ptr(), ldy=m)] for cp in copies]
+        c.run.time_steps(variants[:1], 0, 1)
+        got = y.cpu().numpy()
+        ok, worst = within(got, yr[:n], sr[:n], 1e-4)
+        if not ok:
+            raise SystemExit(f"{fmt} {m}x{k} n={n} {entry}: parity FAILED before timing (max err/S {worst:.3g})")
+        t = c.run.measure(variants, c.steps, c.warmup)
+        same = bool(np.array_equal(y.cpu().numpy().view(np.uint32), got.view(np.uint32)))
+        if not same:
+            raise SystemExit(f"{fmt} {m}x{k} n={n}: timed output differs from the checked one")
+        sec = t["us"] / 1e6
+        rec = {"parity": f"every output within 1e-4*S{'_x8' if entry != 'mul_mat_vec' else ''}",
+               "max_err_over_S": float(f"{worst:.3g}"), **timing_fields(t),
+               "weight_GBps": rnd(wb / sec / 1e9, 1), "pct_of_hbm_peak": rnd(100 * wb / sec / 1e9 / HBM_PEAK_GBPS, 2),
+               "roofline": gemv_roofline(fmt, m, k, n, sec)}
+        if ceiling:
+            cs, _ = c.run.time_steps([[c.run.stream_read(cp.data_ptr(), wb)] for cp in copies], c.warmup, c.steps)
+            rec["stream_read_us"] = rnd(cs / c.steps * 1e6)
+            rec["pct_of_stream_read"] = rnd(100 * (cs / c.steps) / sec, 1)
+        out[n] = rec
+        del y
+    cpu = {"threads": c.threads, "threads_GBps": rnd(wb * nmax / max(nmax, 1) / t_mt / 1e9, 4),
+           "threads_sample": f"whole {m}x{k} matrix x {nmax} column(s) ({t_mt:.2f} s)"}
+    if c.single:
+        r, el = single_thread_rows(ref_fn, fmt, w, m, k, c.budget, x_all, nmax)
+        cpu["single_thread_GBps"] = rnd(r * row_bytes(fmt, k) / el / 1e9, 4)
+        cpu["single_thread_sample"] = f"first {r} of {m} rows x {nmax} column(s), {el:.2f} s, scaled to the matrix"
+    del copies, wd, xd
+    torch.cuda.empty_cache()
+    return out, cpu, dict(w=w, x=x_all)
 
 
-def gemv_bytes(fmt, m, k, n):
-    bs = {"q4_0": 18, "q4_1": 20, "q8_0": 34}[fmt]
-    wb = m * (k // 32) * bs
-    return wb, wb + 4 * n * (k + m)
-
-
-def bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup, entry="qk_mul_mat_vec",
-               clib=None):
-    wb, algo = gemv_bytes(fmt, m, k, n)
-    R = copies_for(wb)
-    copies = [prob["wd"]] + [prob["wd"].clone() for _ in range(R - 1)]
-    xd, y = prob["xd"], prob["y"]
-    lib = qk.load()
-    code = qk.FORMATS[fmt]
-    ptrs = [c.data_ptr() for c in copies]
-    xp, yp = xd.data_ptr(), y.data_ptr()
-
-    call = getattr(lib, entry)
-
-    def launch(i):
-        st = call(code, ptrs[i % R], m, k, xp, n, k, yp, m, torch.cuda.current_stream().cuda_stream)
-        if st != 0:
-            raise RuntimeError(f"{entry}: {qk.status_string(st)}")
-
-    gw = timer.capture(launch, max(warmup, 1))
-    gk = timer.capture(lambda i: launch(i + warmup), steps)
-    timer.time_graph(gw)
-    sec = timer.time_graph(gk)
-    del gw, gk
-    out = dict(seconds=sec, per_launch_s=sec / steps, weight_bytes=wb, algo_bytes=algo, copies=R)
-    if clib is not None:
-        # the same bytes streamed by a plain read kernel, same rotation
-        out["stream_read_s"] = stream_read_time(torch, timer, clib, ptrs, wb, steps, warmup)
-    del copies
-    return out
-
-
-def cpu_baseline_gemv(oracle, prob, fmt, m, k, n, budget_s=10.0):
-    wb, _ = gemv_bytes(fmt, m, k, n)
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        oracle.dot(fmt, prob["w"], m, k, prob["x"], n)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or passes >= 200:
-            break
-    return dict(value=round(wb * passes / el / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample=f"full {m}x{k} {fmt} matrix x {n} column(s), {passes} passes, "
-                       f"{el:.1f} s, one thread")
-
-
-def run_headline(torch, qk, synth, oracle, timer, name, steps, warmup, with_cpu, clib):
-    cfg = synth.WORKLOADS[name]
+def run_headline(c):
+    synth = c.synth
+    cfg = synth.WORKLOADS["gemv_q8_0_4096x4096_n1"]
     seed = synth.workload_seed(cfg["id"])
-    fmt = cfg["fmt"]
-    if "layer" in cfg or name.startswith("dequant") or name.startswith("gemm"):
-        raise SystemExit(f"--workload {name}: the headline is a single GEMV; use --configs")
-    n = cfg["n"] if isinstance(cfg["n"], int) else cfg["n"][0]
     m, k = cfg["m"], cfg["k"]
-    prob = setup_gemv(torch, qk, synth, oracle, fmt, m, k, n, seed, 0, 100, cfg["d"],
-                      cfg.get("mr"))
-    if not prob["ok"]:
-        raise SystemExit(f"parity check failed before timing (max err/S {prob['worst']:.3g})")
-    log(f"parity ok: max |y-ref|/S = {prob['worst']:.3g}")
-    r = bench_gemv(torch, qk, timer, prob, fmt, m, k, n, steps, warmup, clib=clib)
-    gbps = r["weight_bytes"] * steps / r["seconds"] / 1e9
-    achieved = r["algo_bytes"] / r["per_launch_s"] / 1e9
-    traffic = stored_traffic(f"gemv_{fmt}_{m}x{k}_n{n}", GEMV_SOURCES)
-    out = {
-        "metric": "effective weight GB/s (% of HBM peak) for Q4_0/Q8_0 GEMV; batched TFLOP/s",
-        "value": round(gbps, 2),
+    res, cpu, _ = run_gemv(c, "q8_0", m, k, (1,), seed, cfg["d"], ceiling=True)
+    r = res[1]
+    sec = r["us_per_step"] / 1e6
+    wb = m * row_bytes("q8_0", k)
+    algo = wb + 4 * (k + m)
+    log(f"headline: {r['us_per_step']} us per step (median {r['median_us']})")
+    line = {
+        "metric": METRIC,
+        "value": rnd(wb / sec / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": round(r["seconds"] * 1e3 / steps, 6),
+        "steps": c.steps,
+        "warmup": c.warmup,
+        "ms_per_step": rnd(sec * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": name, "format": fmt, "m": m, "k": k, "n": n,
-                   "cold_weight_copies": r["copies"], "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic},
-        # a plain streaming read of the same weight bytes (same cold rotation,
-        # same launch pattern): the practical ceiling on this chip
-        "practical_ceiling": {"stream_read_us": round(r["stream_read_s"] * 1e6, 3),
-                              "stream_read_GBps": round(r["weight_bytes"] / r["stream_read_s"] / 1e9, 1),
-                              "frac_of_stream_read": round(r["stream_read_s"] / r["per_launch_s"], 4)},
+        "config": {"workload": "gemv_q8_0_4096x4096_n1", "format": "q8_0", "m": m, "k": k, "n": 1,
+                   "cold_weight_copies": copies_for(wb), "pct_of_hbm_peak": r["pct_of_hbm_peak"]},
+        "timing": {"method": "native launch loop on one stream; HIP events around the K timed steps",
+                   "clock_settle_ms": SETTLE_MS,
+                   "per_launch_us": {"median": r["median_us"], "p10": r["p10_us"], "p90": r["p90_us"],
+                                     "launches": DIST_LAUNCHES, "warmup": DIST_WARMUP,
+                                     "over": f"groups of {DIST_GROUP} launches"}},
+        "roofline": {"bound": "hbm", "achieved": rnd(algo / sec / 1e9, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": rnd(algo / sec / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": stored_traffic("gemv_q8_0_4096x4096_n1", GEMV_SOURCES)},
+        "practical_ceiling": {"stream_read_us": r["stream_read_us"],
+                              "stream_read_GBps": rnd(wb / (r["stream_read_us"] / 1e6) / 1e9, 1),
+                              "frac_of_stream_read": rnd(r["pct_of_stream_read"] / 100, 4)},
+        "parity": r["parity"] + f" (max err/S {r['max_err_over_S']})",
     }
-    if with_cpu:
-        log("timing the CPU oracle baseline")
-        out["cpu_baseline"] = cpu_baseline_gemv(oracle, prob, fmt, m, k, n)
-    return out
+    cb = {"value": cpu["threads_GBps"], "unit": "GB/s", "cores": cpu["threads"], "kind": "oracle",
+          "sample": f"{cpu['threads_sample']} in {cpu['threads']} threads", "cpu_model": cpu_model()}
+    if "single_thread_GBps" in cpu:
+        cb["single_thread_value"] = cpu["single_thread_GBps"]
+        cb["single_thread_sample"] = cpu["single_thread_sample"]
+    line["cpu_baseline"] = cb
+    return line, r, cpu
 
 
-def run_configs(torch, qk, synth, oracle, timer, steps, warmup, clib):
-    """Every workload, each parity-checked before it is timed."""
-    res = {}
-    # C0: dequantize Q4_0 4096x4096 -> fp32
+def run_dequant(c):
+    torch, qk, synth, oracle = c.torch, c.qk, c.synth, c.oracle
     cfg = synth.WORKLOADS["dequant_q4_0_4096x4096_f32"]
     seed = synth.workload_seed(cfg["id"])
     m, k = cfg["m"], cfg["k"]
     w = synth.quant_matrix("q4_0", m, k, seed=seed, tensor_id=0, d_range=cfg["d"])
+    rb = row_bytes("q4_0", k)
+    step = -(-m // (c.threads * 4))
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(c.threads) as ex:
+        parts = list(ex.map(lambda r: oracle.dequantize_f32("q4_0", w[r * rb:min(m, r + step) * rb],
+                                                             min(m, r + step) - r, k), range(0, m, step)))
+    t_mt = time.perf_counter() - t0
+    ref = np.concatenate(parts, axis=0)
     wd = torch.from_numpy(w).cuda()
-    out = qk.dequantize("q4_0", wd, m, k, "f32")
-    ok = np.array_equal(out.cpu().numpy().view(np.uint32),
-                        oracle.dequantize_f32("q4_0", w, m, k).view(np.uint32))
-    inb, outb = w.size, m * k * 4
-    R = copies_for(inb + outb)
-    ins = [wd] + [wd.clone() for _ in range(R - 1)]
-    outs = [out] + [torch.empty_like(out) for _ in range(R - 1)]
-    lib = qk.load()
-
-    def dq(i):
-        lib.qk_dequantize(qk.QK_Q4_0, ins[i % R].data_ptr(), m, k, qk.QK_F32,
-                          outs[i % R].data_ptr(), torch.cuda.current_stream().cuda_stream)
-
-    st = max(steps // 4, 20)
-    gw, gk = timer.capture(dq, warmup), timer.capture(lambda i: dq(i + warmup), st)
-    timer.time_graph(gw)
-    sec = timer.time_graph(gk) / st
-    res["dequant_q4_0_4096x4096_f32"] = {
-        "parity": "bit-exact" if ok else "FAILED", "us_per_launch": round(sec * 1e6, 3),
-        "total_GBps": round((inb + outb) / sec / 1e9, 1),
-        "weight_GBps": round(inb / sec / 1e9, 1),
-        "pct_of_hbm_peak": round(100 * (inb + outb) / sec / 1e9 / HBM_PEAK_GBPS, 1)}
-    del ins, outs, gw, gk
-
-    # C1 and C2: single GEMVs
-    for name, ns in (("gemv_q8_0_4096x4096_n1", (1,)), ("gemv_q4_1_11008x4096", (1, 2, 4, 8))):
-        cfg = synth.WORKLOADS[name]
-        seed = synth.workload_seed(cfg["id"])
-        for n in ns:
-            prob = setup_gemv(torch, qk, synth, oracle, cfg["fmt"], cfg["m"], cfg["k"], n, seed, 0,
-                              100, cfg["d"], cfg.get("mr"), check="sampled", rng_seed=n)
-            r = bench_gemv(torch, qk, timer, prob, cfg["fmt"], cfg["m"], cfg["k"], n, steps, warmup,
-                           clib=clib)
-            gbps = r["weight_bytes"] / r["per_launch_s"] / 1e9
-            res[f"{name}" + ("" if len(ns) == 1 else f"_n{n}")] = {
-                "parity": "ok" if prob["ok"] else "FAILED", "max_err_over_S": prob["worst"],
-                "us_per_launch": round(r["per_launch_s"] * 1e6, 3),
-                "weight_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
-                "stream_read_us": round(r["stream_read_s"] * 1e6, 3),
-                "pct_of_stream_read": round(100 * r["stream_read_s"] / r["per_launch_s"], 1)}
-            del prob
-
-    # C2 again with 8-bit activations (qk_mul_mat_vec_x8), checked against the
-    # oracle's product with the same quantized activations
-    cfg = synth.WORKLOADS["gemv_q4_1_11008x4096"]
-    seed = synth.workload_seed(cfg["id"])
-    for n in (1, 2, 4, 8):
-        prob = setup_gemv(torch, qk, synth, oracle, "q4_1", cfg["m"], cfg["k"], n, seed, 0, 100,
-                          cfg["d"], cfg.get("mr"), check="none")
-        y8 = qk.mul_mat_vec_x8("q4_1", prob["wd"], cfg["m"], cfg["k"], prob["xd"])
-        torch.cuda.synchronize()
-        rows = np.sort(np.random.default_rng(n).choice(cfg["m"], 128, replace=False))
-        rb = (cfg["k"] // 32) * 20
-        wsub = np.concatenate([prob["w"][r * rb:(r + 1) * rb] for r in rows])
-        yr, sr = oracle.dot_x8("q4_1", wsub, len(rows), cfg["k"], prob["x"], n)
-        got = y8.cpu().numpy()[:, rows].astype(np.float64)
-        ok8 = bool(np.all(np.abs(got - yr) <= 1e-4 * sr))
-        r = bench_gemv(torch, qk, timer, prob, "q4_1", cfg["m"], cfg["k"], n, steps, warmup,
-                       entry="qk_mul_mat_vec_x8")
-        gbps = r["weight_bytes"] / r["per_launch_s"] / 1e9
-        res[f"gemv_q4_1_11008x4096_x8_n{n}"] = {
-            "parity": "ok" if ok8 else "FAILED", "us_per_launch": round(r["per_launch_s"] * 1e6, 3),
-            "weight_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
-        del prob
-
-    # C3: the decode layer, 7 GEMVs per step (from a clean allocator: weight
-    # copies carved out of the previous workloads' freed blocks measured
-    # slower than fresh allocations)
-    torch.cuda.synchronize()
+    ins = rotation(torch, wd, w.size + m * k * 4)
+    outs = [torch.empty((m, k), dtype=torch.float32, device="cuda") for _ in ins]
+    variants = [[c.run.call("dequantize", fmt=qk.QK_Q4_0, w=i.data_ptr(), m=m, k=k, out_dtype=qk.QK_F32,
+                            y=o.data_ptr())] for i, o in zip(ins, outs)]
+    c.run.time_steps(variants[:1], 0, 1)
+    if not np.array_equal(outs[0].cpu().numpy().view(np.uint32), ref.view(np.uint32)):
+        raise SystemExit("dequantize: parity FAILED before timing")
+    t = c.run.measure(variants, c.steps, c.warmup)
+    if not all(torch.equal(o.view(torch.int32), outs[0].view(torch.int32)) for o in outs):
+        raise SystemExit("dequantize: timed outputs differ from the checked one")
+    sec = t["us"] / 1e6
+    total = w.size + m * k * 4
+    rec = {"parity": "bit-exact on every output", **timing_fields(t),
+           "total_GBps": rnd(total / sec / 1e9, 1), "weight_GBps": rnd(w.size / sec / 1e9, 1),
+           "pct_of_hbm_peak": rnd(100 * total / sec / 1e9 / HBM_PEAK_GBPS, 2),
+           "roofline": {"bound": "hbm", "achieved": rnd(total / sec / 1e9, 2), "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": rnd(total / sec / 1e9 / HBM_PEAK_GBPS, 4)},
+           "cpu": {"threads": c.threads, "threads_total_GBps": rnd(total / t_mt / 1e9, 4)}}
+    if c.single:
+        r = max(1, m // 8)
+        t0 = time.perf_counter()
+        oracle.dequantize_f32("q4_0", w[:r * rb], r, k)
+        el = time.perf_counter() - t0
+        rec["cpu"]["single_thread_total_GBps"] = rnd(r * (rb + 4 * k) / el / 1e9, 4)
+        rec["cpu"]["single_thread_sample"] = f"first {r} of {m} rows, {el:.2f} s"
+    del ins, outs, wd
     torch.cuda.empty_cache()
-    cfg = synth.WORKLOADS["gemv_q4_0_decode_layer"]
+    return rec
+
+
+def run_layer(c, name, with_cpu=True):
+    """The 7 GEMVs of one decode layer: one grouped launch per step, and seven
+    separate launches per step; plus each matrix's own launches (the sum of
+    their median durations)."""
+    torch, qk, synth, oracle = c.torch, c.qk, c.synth, c.oracle
+    cfg = synth.WORKLOADS[name]
     seed = synth.workload_seed(cfg["id"])
-    probs, wtot = [], 0
+    probs, wtot, t_mt = [], 0, 0.0
     for tid, (nm, m, k) in enumerate(cfg["layer"]):
-        p = setup_gemv(torch, qk, synth, oracle, "q4_0", m, k, 1, seed, tid, 100 + tid, cfg["d"],
-                       check="sampled", rng_seed=tid)
-        p.update(m=m, k=k)
-        probs.append(p)
-        wtot += gemv_bytes("q4_0", m, k, 1)[0]
+        w = synth.quant_matrix("q4_0", m, k, seed=seed, tensor_id=tid, d_range=cfg["d"])
+        x = np.ascontiguousarray(synth.activations(k, 1, seed=seed, tensor_id=100 + tid))
+        yr, sr, el = oracle_rows(oracle.dot, "q4_0", w, m, k, c.threads, x, 1)
+        t_mt += el
+        probs.append(dict(nm=nm, m=m, k=k, w=w, x=x, yr=yr, sr=sr, wd=torch.from_numpy(w).cuda(),
+                          xd=torch.from_numpy(x).cuda(), y=torch.empty((1, m), dtype=torch.float32, device="cuda")))
+        wtot += w.size
     R = copies_for(wtot)
-    layer_copies = [[p["wd"]] + [p["wd"].clone() for _ in range(R - 1)] for p in probs]
+    for p in probs:
+        p["copies"] = [p["wd"]] + [p["wd"].clone() for _ in range(R - 1)]
+    item_sets = [qk.make_items([(p["copies"][r].data_ptr(), p["m"], p["k"], p["xd"].data_ptr(), p["k"],
+                                 p["y"].data_ptr(), p["m"]) for p in probs]) for r in range(R)]
+    grouped = [[c.run.call("mul_mat_vec_batched", fmt=qk.QK_Q4_0, items=ctypes.addressof(s), count=len(probs),
+                           n=1)] for s in item_sets]
+    separate = [[c.run.call("mul_mat_vec", fmt=qk.QK_Q4_0, w=p["copies"][r].data_ptr(), m=p["m"], k=p["k"],
+                            x=p["xd"].data_ptr(), n=1, ldx=p["k"], y=p["y"].data_ptr(), ldy=p["m"])
+                 for p in probs] for r in range(R)]
+    worst = 0.0
 
-    def layer(i):
-        s = torch.cuda.current_stream().cuda_stream
-        for p, cps in zip(probs, layer_copies):
-            lib.qk_mul_mat_vec(qk.QK_Q4_0, cps[i % R].data_ptr(), p["m"], p["k"], p["xd"].data_ptr(),
-                               1, p["k"], p["y"].data_ptr(), p["m"], s)
+    def check(what):
+        nonlocal worst
+        outs = []
+        for p in probs:
+            got = p["y"].cpu().numpy()
+            ok, wr = within(got, p["yr"], p["sr"], 1e-4)
+            if not ok:
+                raise SystemExit(f"{name} {what} {p['nm']}: parity FAILED (max err/S {wr:.3g})")
+            worst = max(worst, wr)
+            outs.append(got)
+        return outs
 
-    st = max(steps // 7, 20)
-    gw, gk = timer.capture(layer, warmup), timer.capture(lambda i: layer(i + warmup), st)
-    timer.time_graph(gw)
-    sec = timer.time_graph(gk) / st
-    del gw, gk
-
-    # the same layer as one grouped launch (qk_mul_mat_vec_batched)
-    item_sets = [qk.make_items([(cps[r].data_ptr(), p["m"], p["k"], p["xd"].data_ptr(), p["k"],
-                                 p["y"].data_ptr(), p["m"]) for p, cps in zip(probs, layer_copies)])
-                 for r in range(R)]
-
-    def grouped(i):
-        lib.qk_mul_mat_vec_batched(qk.QK_Q4_0, item_sets[i % R], len(probs), 1,
-                                   torch.cuda.current_stream().cuda_stream)
-
-    grouped(0)
-    torch.cuda.synchronize()
-    gok = True
-    for tid, p in enumerate(probs):
-        rng = np.random.default_rng(200 + tid)
-        ii = rng.integers(0, p["m"], 128)
-        yr, sr = oracle.dot_entries("q4_0", p["w"], p["m"], p["k"], p["x"].ravel(), p["k"], ii,
-                                    np.zeros_like(ii))
-        got = p["y"].cpu().numpy()[0, ii].astype(np.float64)
-        gok = gok and bool(np.all(np.abs(got - yr) <= 1e-4 * sr))
-    gw, gk = timer.capture(grouped, warmup), timer.capture(lambda i: grouped(i + warmup), st)
-    timer.time_graph(gw)
-    secg = timer.time_graph(gk) / st
-    # a streaming read of the layer's weight bytes as one buffer per copy
-    flat = [torch.empty(wtot, dtype=torch.uint8, device="cuda") for _ in range(R)]
-    sr = stream_read_time(torch, timer, clib, [f.data_ptr() for f in flat], wtot, st, warmup)
-    del flat
-    res["gemv_q4_0_decode_layer"] = {
-        "parity": "ok" if all(p["ok"] for p in probs) and gok else "FAILED",
-        "separate_launches": {"us_per_layer": round(sec * 1e6, 3), "weight_GBps": round(wtot / sec / 1e9, 1),
-                              "pct_of_hbm_peak": round(100 * wtot / sec / 1e9 / HBM_PEAK_GBPS, 1)},
-        "grouped_launch": {"us_per_layer": round(secg * 1e6, 3), "weight_GBps": round(wtot / secg / 1e9, 1),
-                           "pct_of_hbm_peak": round(100 * wtot / secg / 1e9 / HBM_PEAK_GBPS, 1),
-                           "stream_read_us": round(sr * 1e6, 3),
-                           "pct_of_stream_read": round(100 * sr / secg, 1)}}
-    del probs, layer_copies, gw, gk, item_sets
-
-    # C4: GEMM
-    torch.cuda.synchronize()
+    out = {"weight_bytes": wtot, "cold_layer_copies": R}
+    for label, variants in (("grouped_launch", grouped), ("separate_launches", separate)):
+        for p in probs:
+            p["y"].fill_(float("nan"))
+        c.run.time_steps(variants[:1], 0, 1)
+        checked = check(label)
+        t = c.run.measure(variants, c.steps, c.warmup)
+        after = [p["y"].cpu().numpy() for p in probs]
+        if not all(np.array_equal(a.view(np.uint32), b.view(np.uint32)) for a, b in zip(after, checked)):
+            raise SystemExit(f"{name} {label}: timed outputs differ from the checked ones")
+        sec = t["us"] / 1e6
+        out[label] = {**timing_fields(t), "weight_GBps": rnd(wtot / sec / 1e9, 1),
+                      "pct_of_hbm_peak": rnd(100 * wtot / sec / 1e9 / HBM_PEAK_GBPS, 2)}
+    # each matrix alone: the median of its own launches
+    med = {}
+    for i, p in enumerate(probs):
+        _, d = c.run.time_steps([[separate[r][i]] for r in range(R)], DIST_WARMUP, DIST_LAUNCHES,
+                                group=DIST_GROUP)
+        med[p["nm"]] = float(np.median(d)) * 1e6
+    smed = sum(med.values()) / 1e6
+    # (each matrix's launches back to back: a launch's time here includes the
+    # gap to the next launch, which the grouped launch pays once)
+    out["sum_of_kernel_medians"] = {"us": rnd(smed * 1e6), "per_matrix_median_us": {k: rnd(v) for k, v in med.items()},
+                                    "weight_GBps": rnd(wtot / smed / 1e9, 1),
+                                    "pct_of_hbm_peak": rnd(100 * wtot / smed / 1e9 / HBM_PEAK_GBPS, 2)}
+    out["parity"] = "every output within 1e-4*S (grouped and separate launches)"
+    out["max_err_over_S"] = float(f"{worst:.3g}")
+    sec = out["grouped_launch"]["us_per_step"] / 1e6
+    algo = wtot + sum(4 * (p["k"] + p["m"]) for p in probs)
+    out["roofline"] = {"bound": "hbm", "achieved": rnd(algo / sec / 1e9, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": rnd(algo / sec / 1e9 / HBM_PEAK_GBPS, 4), "launch": "grouped"}
+    if with_cpu:
+        out["cpu"] = {"threads": c.threads, "threads_GBps": rnd(wtot / t_mt / 1e9, 4)}
+        if c.single:
+            p = max(probs, key=lambda q: q["w"].size)
+            r, el = single_thread_rows(oracle.dot, "q4_0", p["w"], p["m"], p["k"], c.budget, p["x"], 1)
+            out["cpu"]["single_thread_GBps"] = rnd(r * row_bytes("q4_0", p["k"]) / el / 1e9, 4)
+            out["cpu"]["single_thread_sample"] = f"first {r} rows of {p['nm']}, {el:.2f} s"
+    del probs, item_sets, grouped, separate
     torch.cuda.empty_cache()
+    return out
+
+
+def gemm_reference(oracle, fmt, w, m, k, xh, threads):
+    """fp64 product of the oracle's dequantized fp32 weights with the fp16
+    activations (decoded exactly), and S = |W| |X|; (n, m) arrays."""
+    rb = row_bytes(fmt, k)
+    step = -(-m // (threads * 4))
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda r: oracle.dequantize_f32(fmt, w[r * rb:min(m, r + step) * rb],
+                                                             min(m, r + step) - r, k), range(0, m, step)))
+    wf = np.concatenate(parts, axis=0).astype(np.float64)
+    xf = xh.astype(np.float64)  # (n, k): fp16 -> fp64 is exact
+    y = xf @ wf.T
+    s = np.abs(xf) @ np.abs(wf).T
+    return y, s
+
+
+def run_gemm(c):
+    torch, qk, synth, oracle = c.torch, c.qk, c.synth, c.oracle
     cfg = synth.WORKLOADS["gemm_q4_0_14336x4096_n512"]
     seed = synth.workload_seed(cfg["id"])
     m, k, n = cfg["m"], cfg["k"], cfg["n"]
     w = synth.quant_matrix("q4_0", m, k, seed=seed, tensor_id=0, d_range=cfg["d"])
     xh = synth.activations(k, n, seed=seed, tensor_id=100, dtype=np.float16)
+    t0 = time.perf_counter()
+    yr, sr = gemm_reference(oracle, "q4_0", w, m, k, xh, c.threads)
+    t_ref = time.perf_counter() - t0
     wd = torch.from_numpy(w).cuda()
     xd = torch.from_numpy(xh).cuda()
-    y = qk.mul_mat("q4_0", wd, m, k, xd)
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(4)
-    ii, jj = rng.integers(0, m, 256), rng.integers(0, n, 256)
-    yr, s = oracle.dot_entries("q4_0", w, m, k, xh.view(np.uint16).ravel(), k, ii, jj, x_is_f16=True)
-    got = y.cpu().numpy()[jj, ii].astype(np.float64)
-    ok = bool(np.all(np.abs(got - yr) <= 1e-2 * s))
-    R = copies_for(w.size, minimum=4)
-    wc = [wd] + [wd.clone() for _ in range(R - 1)]
-
-    def gm(i):
-        lib.qk_mul_mat(qk.QK_Q4_0, wc[i % R].data_ptr(), m, k, xd.data_ptr(), n, k, y.data_ptr(), m,
-                       torch.cuda.current_stream().cuda_stream)
-
-    st = max(steps // 20, 20)
-    gw, gk = timer.capture(gm, max(warmup // 10, 2)), timer.capture(gm, st)
-    timer.time_graph(gw)
-    sec = timer.time_graph(gk) / st
-    tf = 2.0 * m * n * k / sec / 1e12
-    loop_tf = mfma_loop_tflops(torch, timer, clib)
-    res["gemm_q4_0_14336x4096_n512"] = {
-        "parity": "ok" if ok else "FAILED", "us_per_launch": round(sec * 1e6, 2),
-        "TFLOPs": round(tf, 1), "pct_of_mfma_f16_peak": round(100 * tf / MFMA_F16_PEAK_TFLOPS, 1),
-        "mfma_loop_TFLOPs": round(loop_tf, 1), "pct_of_mfma_loop": round(100 * tf / loop_tf, 1)}
-    del gw, gk
-
-    # the same weights at smaller batches (the first nb activation columns):
-    # up to 128 columns there is one column tile, so 56 workgroups for 256 CUs
-    batches = {}
-    for nb in (16, 64, 128):
-        yb = torch.empty((nb, m), dtype=torch.float32, device="cuda")
-
-        def gmb(i, nb=nb, yb=yb):
-            lib.qk_mul_mat(qk.QK_Q4_0, wc[i % R].data_ptr(), m, k, xd.data_ptr(), nb, k, yb.data_ptr(), m,
-                           torch.cuda.current_stream().cuda_stream)
-
-        gmb(0)
-        torch.cuda.synchronize()
-        jb = rng.integers(0, nb, 128)
-        ib = rng.integers(0, m, 128)
-        yr, s = oracle.dot_entries("q4_0", w, m, k, xh.view(np.uint16).ravel(), k, ib, jb, x_is_f16=True)
-        okb = bool(np.all(np.abs(yb.cpu().numpy()[jb, ib].astype(np.float64) - yr) <= 1e-2 * s))
-        gw, gk = timer.capture(gmb, max(warmup // 10, 2)), timer.capture(gmb, st)
-        timer.time_graph(gw)
-        secb = timer.time_graph(gk) / st
-        batches[str(nb)] = {"parity": "ok" if okb else "FAILED", "us_per_launch": round(secb * 1e6, 2),
-                            "TFLOPs": round(2.0 * m * nb * k / secb / 1e12, 1)}
-        del gw, gk, yb
-    res["gemm_q4_0_14336x4096_n512"]["smaller_batches"] = batches
-    del wc
-
-    log("decode layer, one GPU's share of 8-way tensor parallelism")
-    torch.cuda.synchronize()
+    wc = rotation(torch, wd, w.size)
+    out, keep = {}, {}
+    for nb in (n, 16, 64, 128):
+        y = torch.empty((nb, m), dtype=torch.float32, device="cuda")
+        variants = [[c.run.call("mul_mat", fmt=qk.QK_Q4_0, w=cp.data_ptr(), m=m, k=k, x=xd.data_ptr(), n=nb, ldx=k,
+                                y=y.data_ptr(), ldy=m)] for cp in wc]
+        c.run.time_steps(variants[:1], 0, 1)
+        got = y.cpu().numpy()
+        ok, worst = within(got, yr[:nb], sr[:nb], 1e-2)
+        if not ok:
+            raise SystemExit(f"GEMM n={nb}: parity FAILED before timing (max err/S {worst:.3g})")
+        t = c.run.measure(variants, c.steps, c.warmup)
+        if not np.array_equal(y.cpu().numpy().view(np.uint32), got.view(np.uint32)):
+            raise SystemExit(f"GEMM n={nb}: timed output differs from the checked one")
+        sec = t["us"] / 1e6
+        tf = 2.0 * m * nb * k / sec / 1e12
+        rec = {"parity": "every output within 1e-2*S", "max_err_over_S": float(f"{worst:.3g}"),
+               **timing_fields(t), "TFLOPs": rnd(tf, 1), "pct_of_mfma_f16_peak": rnd(100 * tf / MFMA_F16_PEAK_TFLOPS, 2),
+               "roofline": {"bound": "mfma", "achieved": rnd(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": rnd(tf / MFMA_F16_PEAK_TFLOPS, 4)}}
+        if nb == n:
+            out = rec
+        else:
+            keep[str(nb)] = rec
+        del y
+    loop = c.run.mfma_loop_tflops()
+    out["mfma_loop_TFLOPs"] = rnd(loop, 1)
+    out["pct_of_mfma_loop"] = rnd(100 * out["TFLOPs"] / loop, 1)
+    out["cpu"] = {"threads": c.threads, "reference": f"fp64 BLAS product of the oracle's weights ({t_ref:.2f} s)"}
+    # the oracle's own products: 16 of the 512 columns, scaled by 32
+    x16 = np.ascontiguousarray(xh[:16].view(np.uint16))
+    _, _, t_mt = oracle_rows(lambda f, ww, mm, kk, xx, nn: oracle.dot(f, ww, mm, kk, xx, nn, x_is_f16=True),
+                             "q4_0", w, m, k, c.threads, x16, 16)
+    out["cpu"]["threads_TFLOPs"] = rnd(2.0 * m * 16 * k / t_mt / 1e12, 6)
+    out["cpu"]["threads_sample"] = f"16 of {n} columns, whole matrix ({t_mt:.2f} s), scaled by {n // 16}"
+    if c.single:
+        r, el = single_thread_rows(lambda f, ww, mm, kk, xx, nn: oracle.dot(f, ww, mm, kk, xx, nn, x_is_f16=True),
+                                   "q4_0", w, m, k, c.budget, x16, 16)
+        out["cpu"]["single_thread_TFLOPs"] = rnd(2.0 * r * 16 * k / el / 1e12, 6)
+        out["cpu"]["single_thread_sample"] = f"first {r} rows x 16 of {n} columns, {el:.2f} s, scaled"
+    out["smaller_batches"] = keep
+    del wc, wd, xd
     torch.cuda.empty_cache()
-    res["gemv_q4_0_decode_layer_tp8_share"] = run_share_layer(torch, qk, synth, oracle, timer, steps,
-                                                              warmup)
-
-    log("expert-indexed decode")
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    res["gemv_q4_0_moe_experts"] = run_moe(torch, qk, synth, oracle, timer, steps, warmup)
-    return res
-
-
-def run_share_layer(torch, qk, synth, oracle, timer, steps, warmup):
-    """One GPU's share of the decode layer under 8-way tensor parallelism (row
-    shards of q, k, v, gate, up; K shards of o and down): the GEMVs of one
-    token as one grouped launch and as separate launches.  The all-reduce of
-    the K-shard partial sums is not part of it (one GPU)."""
-    cfg = synth.WORKLOADS["gemv_q4_0_decode_layer_tp8_share"]
-    seed = synth.workload_seed(cfg["id"])
-    lib = qk.load()
-    probs, wtot = [], 0
-    for tid, (nm, m, k) in enumerate(cfg["layer"]):
-        p = setup_gemv(torch, qk, synth, oracle, "q4_0", m, k, 1, seed, tid, 100 + tid, cfg["d"])
-        p.update(m=m, k=k)
-        probs.append(p)
-        wtot += gemv_bytes("q4_0", m, k, 1)[0]
-    R = copies_for(wtot)
-    copies = [[p["wd"]] + [p["wd"].clone() for _ in range(R - 1)] for p in probs]
-    sets = [qk.make_items([(cps[r].data_ptr(), p["m"], p["k"], p["xd"].data_ptr(), p["k"],
-                            p["y"].data_ptr(), p["m"]) for p, cps in zip(probs, copies)])
-            for r in range(R)]
-
-    def grouped(i):
-        lib.qk_mul_mat_vec_batched(qk.QK_Q4_0, sets[i % R], len(probs), 1,
-                                   torch.cuda.current_stream().cuda_stream)
-
-    def separate(i):
-        s = torch.cuda.current_stream().cuda_stream
-        for p, cps in zip(probs, copies):
-            lib.qk_mul_mat_vec(qk.QK_Q4_0, cps[i % R].data_ptr(), p["m"], p["k"], p["xd"].data_ptr(),
-                               1, p["k"], p["y"].data_ptr(), p["m"], s)
-
-    grouped(0)
-    torch.cuda.synchronize()
-    ok = all(p["ok"] for p in probs)
-    for p in probs:
-        yr, sr = oracle.dot("q4_0", p["w"], p["m"], p["k"], p["x"], 1)
-        got = p["y"].cpu().numpy().astype(np.float64)
-        ok = ok and bool(np.all(np.abs(got - yr) <= 1e-4 * sr))
-    out = {"parity": "ok" if ok else "FAILED", "weight_bytes": wtot}
-    st = max(steps // 4, 20)
-    for name, fn in (("grouped_launch", grouped), ("separate_launches", separate)):
-        gw, gk = timer.capture(fn, warmup), timer.capture(lambda i: fn(i + warmup), st)
-        timer.time_graph(gw)
-        sec = timer.time_graph(gk) / st
-        del gw, gk
-        out[name] = {"us_per_layer": round(sec * 1e6, 3), "weight_GBps": round(wtot / sec / 1e9, 1),
-                     "pct_of_hbm_peak": round(100 * wtot / sec / 1e9 / HBM_PEAK_GBPS, 1)}
     return out
 
 
-def run_moe(torch, qk, synth, oracle, timer, steps, warmup):
+def run_moe(c):
     """Expert-indexed decode: per token, the gate, up and down projections of
     8 of 128 Q4_0 experts (768 x 2048, 768 x 2048, 2048 x 768), three
-    qk_mul_mat_vec_id calls; and the same with gate and up merged per expert
-    (two calls).  Expert choices change every step and the stacks rotate over
-    copies, so the experts a step reads are never cache-resident."""
+    qk_mul_mat_vec_id calls per step.  Expert choices change every step and
+    the stacks rotate over copies."""
+    torch, qk, synth, oracle = c.torch, c.qk, c.synth, c.oracle
     cfg = synth.WORKLOADS["gemv_q4_0_moe_experts"]
     seed = synth.workload_seed(cfg["id"])
     ne, nu, nt = cfg["n_experts"], cfg["n_used"], cfg["n_tokens"]
-    lib = qk.load()
-    stacks, ok = [], True
-    for tid, (nm, m, k) in enumerate(cfg["layer"]):
-        w = synth.quant_matrix("q4_0", ne * m, k, seed=seed, tensor_id=tid, d_range=cfg["d"])
-        shared = nm != "down"
-        # gate and up read the same hidden state; down one vector per slot
-        xtid = 100 if shared else 100 + tid
-        x = synth.activations(k, nt * (1 if shared else nu), seed=seed, tensor_id=xtid)
-        stacks.append(dict(nm=nm, m=m, k=k, w=w, wd=torch.from_numpy(w).cuda(), x=x,
-                           xd=torch.from_numpy(np.ascontiguousarray(x)).cuda(), shared=shared,
-                           y=torch.empty((nt, nu, m), dtype=torch.float32, device="cuda"),
-                           one=m * (k // 32) * 18))
     n_sets = 64
     ids = np.stack([synth.expert_ids(nt, nu, ne, seed=seed, tensor_id=50 + i) for i in range(n_sets)])
     ids_d = torch.from_numpy(ids).cuda()
-    sel_bytes = sum(nt * nu * p["one"] for p in stacks)
+    stacks = []
+    for tid, (nm, m, k) in enumerate(cfg["layer"]):
+        w = synth.quant_matrix("q4_0", ne * m, k, seed=seed, tensor_id=tid, d_range=cfg["d"])
+        shared = nm != "down"
+        x = synth.activations(k, nt * (1 if shared else nu), seed=seed, tensor_id=100 if shared else 100 + tid)
+        stacks.append(dict(nm=nm, m=m, k=k, w=w, wd=torch.from_numpy(w).cuda(), x=x,
+                           xd=torch.from_numpy(np.ascontiguousarray(x)).cuda(), shared=shared,
+                           y=torch.empty((nt, nu, m), dtype=torch.float32, device="cuda"),
+                           one=m * row_bytes("q4_0", k)))
     R = copies_for(sum(p["w"].size for p in stacks))
     for p in stacks:
         p["copies"] = [p["wd"]] + [p["wd"].clone() for _ in range(R - 1)]
-
-    def call(p, wptr, idp):
-        x_slot = 0 if p["shared"] else p["k"]
-        x_tok = p["k"] if p["shared"] else nu * p["k"]
-        return lib.qk_mul_mat_vec_id(qk.QK_Q4_0, wptr, ne, p["one"], p["m"],
-                                     p["k"], idp, nu, nu, nt, p["xd"].data_ptr(), x_slot, x_tok,
-                                     p["y"].data_ptr(), p["m"], nu * p["m"],
-                                     torch.cuda.current_stream().cuda_stream)
-
-    def layer(i):
-        idp = ids_d[i % n_sets].data_ptr()
+    variants = []
+    for r in range(max(R, n_sets)):
+        step = []
         for p in stacks:
-            st = call(p, p["copies"][i % R].data_ptr(), idp)
-            if st != 0:
-                raise RuntimeError(f"qk_mul_mat_vec_id: {qk.status_string(st)}")
-
-    layer(0)
-    torch.cuda.synchronize()
-    worst = 0.0
+            step.append(c.run.call("mul_mat_vec_id", fmt=qk.QK_Q4_0, w=p["copies"][r % R].data_ptr(), n_experts=ne,
+                                   expert_stride=p["one"], m=p["m"], k=p["k"], ids=ids_d[r % n_sets].data_ptr(),
+                                   ld_ids=nu, n_used=nu, n_tokens=nt, x=p["xd"].data_ptr(),
+                                   x_slot=0 if p["shared"] else p["k"], x_tok=p["k"] if p["shared"] else nu * p["k"],
+                                   y=p["y"].data_ptr(), y_slot=p["m"], y_tok=nu * p["m"]))
+        variants.append(step)
+    c.run.time_steps(variants[:1], 0, 1)
+    worst, checked = 0.0, []
     for p in stacks:
         xs = p["x"].reshape(nt, p["k"]) if p["shared"] else p["x"].reshape(nt, nu, p["k"])
         yr, sr = oracle.dot_id("q4_0", p["w"], ne, p["one"], p["m"], p["k"], ids[0], nu, nt, xs,
                                0 if p["shared"] else p["k"], p["k"] if p["shared"] else nu * p["k"])
-        got = p["y"].cpu().numpy().astype(np.float64)
-        ok = ok and bool(np.all(np.abs(got - yr) <= 1e-4 * sr))
-        worst = max(worst, float(np.max(np.abs(got - yr) / np.where(sr > 0, sr, 1))))
-    st = max(steps // 3, 20)
-    gw, gk = timer.capture(layer, warmup), timer.capture(lambda i: layer(i + warmup), st)
-    timer.time_graph(gw)
-    sec = timer.time_graph(gk) / st
-    del gw, gk
-    out = {"parity": "ok" if ok else "FAILED", "max_err_over_S": worst,
-           "us_per_token": round(sec * 1e6, 3), "launches_per_token": len(stacks),
-           "selected_weight_bytes": sel_bytes,
-           "weight_GBps": round(sel_bytes / sec / 1e9, 1),
-           "pct_of_hbm_peak": round(100 * sel_bytes / sec / 1e9 / HBM_PEAK_GBPS, 1)}
-
-    # the same weights with gate and up merged per expert (one 1536 x 2048
-    # matrix an expert: gate rows, then up rows), so one call covers both
-    gate, up, down = stacks
-    mg = gate["m"] + up["m"]
-    layer(0)
-    torch.cuda.synchronize()
-    ref_gate, ref_up = gate["y"].clone(), up["y"].clone()
-    gate["copies"] = up["copies"] = None
-    gate["wd"] = up["wd"] = None
+        got = p["y"].cpu().numpy()
+        ok, wr = within(got, yr, sr, 1e-4)
+        if not ok:
+            raise SystemExit(f"expert decode {p['nm']}: parity FAILED (max err/S {wr:.3g})")
+        worst = max(worst, wr)
+        checked.append(got)
+    t = c.run.measure(variants, c.steps, c.warmup)
+    sel = sum(nt * nu * p["one"] for p in stacks)
+    sec = t["us"] / 1e6
+    out = {"parity": "every output within 1e-4*S", "max_err_over_S": float(f"{worst:.3g}"), **timing_fields(t),
+           "launches_per_step": len(stacks), "selected_weight_bytes": sel,
+           "weight_GBps": rnd(sel / sec / 1e9, 1), "pct_of_hbm_peak": rnd(100 * sel / sec / 1e9 / HBM_PEAK_GBPS, 2)}
+    del stacks, variants
     torch.cuda.empty_cache()
-    merged = np.concatenate([gate["w"].reshape(ne, -1), up["w"].reshape(ne, -1)], axis=1).ravel()
-    md = torch.from_numpy(merged).cuda()
-    mcopies = [md] + [md.clone() for _ in range(R - 1)]
-    ym = torch.empty((nt, nu, mg), dtype=torch.float32, device="cuda")
-    one_m = mg * (gate["k"] // 32) * 18
-
-    def merged_layer(i):
-        s = torch.cuda.current_stream().cuda_stream
-        idp = ids_d[i % n_sets].data_ptr()
-        st1 = lib.qk_mul_mat_vec_id(qk.QK_Q4_0, mcopies[i % R].data_ptr(), ne, one_m, mg, gate["k"],
-                                    idp, nu, nu, nt, gate["xd"].data_ptr(), 0, gate["k"],
-                                    ym.data_ptr(), mg, nu * mg, s)
-        st2 = call(down, down["copies"][i % R].data_ptr(), idp)
-        if st1 != 0 or st2 != 0:
-            raise RuntimeError("qk_mul_mat_vec_id failed")
-
-    merged_layer(0)
-    torch.cuda.synchronize()
-    # the merged call's rows are the separate calls' outputs, bit for bit
-    same = bool(torch.equal(ym[:, :, :gate["m"]], ref_gate) and torch.equal(ym[:, :, gate["m"]:], ref_up))
-    gw, gk = timer.capture(merged_layer, warmup), timer.capture(lambda i: merged_layer(i + warmup), st)
-    timer.time_graph(gw)
-    secm = timer.time_graph(gk) / st
-    del gw, gk, mcopies
-    out["merged_gate_up"] = {"parity": "bitwise equal to separate calls" if same else "FAILED",
-                             "us_per_token": round(secm * 1e6, 3), "launches_per_token": 2,
-                             "weight_GBps": round(sel_bytes / secm / 1e9, 1),
-                             "pct_of_hbm_peak": round(100 * sel_bytes / secm / 1e9 / HBM_PEAK_GBPS, 1)}
     return out
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="gemv_q8_0_4096x4096_n1")
-    ap.add_argument("--configs", action="store_true", help="also measure every workload")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="skip the extras (next rows)")
+    ap.add_argument("--headline-only", action="store_true", help="time the headline GEMV only")
+    ap.add_argument("--configs", action="store_true", help="(accepted for compatibility: always on)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the single-thread oracle legs")
+    ap.add_argument("--cpu-budget", type=float, default=1.5, metavar="S",
+                    help="seconds of single-thread oracle work per workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -691,6 +708,8 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        raise SystemExit("--steps must be >= 1 and --warmup >= 0")
 
     import torch
     import oracle
@@ -699,17 +718,44 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     qk.load()  # fails loudly if libqk.so is not built
-    clib = load_ceiling()
     torch.cuda.set_device(0)
-    timer = Timer(torch)
-    out = run_headline(torch, qk, synth, oracle, timer, args.workload, args.steps, args.warmup,
-                       not args.no_cpu, clib)
+    c = Ctx(torch, qk, synth, oracle, Runner(torch), args)
+    t_start = time.perf_counter()
+    line, _, _ = run_headline(c)
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
-    if args.configs:
-        log("measuring every workload")
-        out["configs"] = run_configs(torch, qk, synth, oracle, timer, args.steps, args.warmup, clib)
-    print(json.dumps(out), flush=True)
+    if not args.headline_only:
+        cfgs = {}
+        log("C0 dequantize")
+        cfgs["C0_dequant_q4_0_4096x4096_f32"] = run_dequant(c)
+        cfgs["C1_gemv_q8_0_4096x4096_n1"] = {"see": "headline (value, ms_per_step, roofline, timing)"}
+        log("C2 Q4_1 GEMV n = 1, 2, 4, 8")
+        cw = synth.WORKLOADS["gemv_q4_1_11008x4096"]
+        res, cpu, keep2 = run_gemv(c, "q4_1", cw["m"], cw["k"], (1, 2, 4, 8), synth.workload_seed(cw["id"]), cw["d"],
+                                   cw["mr"], ceiling=True)
+        for n, rec in res.items():
+            cfgs[f"C2_gemv_q4_1_11008x4096_n{n}"] = rec
+        cfgs["C2_gemv_q4_1_11008x4096_n8"]["cpu"] = cpu
+        log("C3 decode layer")
+        cfgs["C3_gemv_q4_0_decode_layer"] = run_layer(c, "gemv_q4_0_decode_layer")
+        log("C4 GEMM")
+        cfgs["C4_gemm_q4_0_14336x4096_n512"] = run_gemm(c)
+        line["configs"] = cfgs
+        if not args.quick:
+            ext = {}
+            log("extras: 8-bit activations")
+            res, _, _ = run_gemv(c, "q4_1", cw["m"], cw["k"], (1, 2, 4, 8), synth.workload_seed(cw["id"]), cw["d"],
+                                 cw["mr"], entry="mul_mat_vec_x8")
+            for n, rec in res.items():
+                ext[f"gemv_x8_q4_1_11008x4096_n{n}"] = rec
+            log("extras: tensor-parallel share")
+            share = run_layer(c, "gemv_q4_0_decode_layer_tp8_share", with_cpu=False)
+            ext["gemv_q4_0_decode_layer_tp8_share"] = share
+            log("extras: expert-indexed decode")
+            ext["gemv_q4_0_moe_experts"] = run_moe(c)
+            line["extras"] = ext
+    line["bench_wall_s"] = rnd(time.perf_counter() - t_start, 1)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

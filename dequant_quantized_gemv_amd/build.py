@@ -13,10 +13,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqk.so")
-# The benchmark's practical-ceiling kernels (streaming read, MFMA loop): a
-# library of their own, not part of the qk C ABI.
-CEILING_SOURCE = "ceiling.hip"
-CEILING_LIB = os.path.join(PKG, "libqk_ceiling.so")
+# The benchmark's helpers (practical-ceiling kernels, the native launch loop
+# that times steps of qk calls): a library of their own, linked against
+# libqk.so and not part of the qk C ABI.
+BENCH_SOURCE = "bench_support.hip"
+BENCH_LIB = os.path.join(PKG, "libqk_bench.so")
 SOURCES = ["api.hip", "dequant.hip", "gemv.hip", "gemv_n1.hip", "gemv_n2.hip", "gemv_n34.hip",
            "gemv_n56.hip", "gemv_n78.hip", "gemv_id.hip", "gemv_x8_n1.hip", "gemv_x8_n24.hip",
            "gemv_x8_n58.hip", "gemm.hip"]
@@ -64,15 +65,16 @@ def build(verbose=False, extra=()):
         obj = os.path.join(OBJ, s.replace(".hip", ".o"))
         jobs.append((obj, [HIPCC, *FLAGS, *SOURCE_FLAGS.get(s, []), *extra, *inc, "-c",
                            os.path.join(CSRC, s), "-o", obj]))
-    cobj = os.path.join(OBJ, CEILING_SOURCE.replace(".hip", ".o"))
-    cjob = (cobj, [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, CEILING_SOURCE), "-o", cobj])
+    cobj = os.path.join(OBJ, BENCH_SOURCE.replace(".hip", ".o"))
+    cjob = (cobj, [HIPCC, *FLAGS, *extra, *inc, "-c", os.path.join(CSRC, BENCH_SOURCE), "-o", cobj])
     with ThreadPoolExecutor(max_workers=len(jobs) + 1) as ex:
         list(ex.map(lambda j: _run(j[1], verbose), jobs + [cjob]))
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in jobs],
           "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", cobj, "-o", CEILING_LIB + ".tmp"], verbose)
-    os.replace(CEILING_LIB + ".tmp", CEILING_LIB)
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", cobj, "-L", PKG, "-l:libqk.so",
+          "-Wl,-rpath,$ORIGIN", "-o", BENCH_LIB + ".tmp"], verbose)
+    os.replace(BENCH_LIB + ".tmp", BENCH_LIB)
     return LIB
 
 

@@ -1,11 +1,23 @@
-// ceiling.hip - practical ceilings for the benchmark, built as its own small
-// library (libqk_ceiling.so; not part of the qk C ABI): a streaming read of a
-// buffer and a register-only MFMA loop.  The benchmark times them on its
-// launch stream next to the kernels it measures, so each workload can be
-// reported against what this chip delivers for the same bytes or flops.
+// bench_support.hip - measurement helpers for the benchmark, built as a small
+// library of their own (libqk_bench.so; not part of the qk C ABI):
+//
+//  * practical ceilings: a streaming read of a buffer and a register-only
+//    MFMA loop, timed next to the kernels they bound;
+//  * a native launch loop: a "step" is a short list of qk C ABI calls, and
+//    warm-up steps followed by timed steps are issued from C++ with HIP
+//    events recorded on the launch stream, so no interpreter sits between
+//    launches and the GPU never waits for the host;
+//  * a clock-settling phase (streaming reads of an unrelated buffer for a
+//    given wall time) that brings the GPU out of its idle power state after
+//    host-side work, before a workload's warm-up.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <chrono>
+#include <vector>
+
+#include "qk.h"
 
 namespace {
 
@@ -56,6 +68,19 @@ __global__ __launch_bounds__(512) void mfma_loop_kernel(int iters, float *sink) 
     if (s == 1.2345f) sink[0] = s;
 }
 
+int stream_read(const void *p, size_t bytes, float *sink, hipStream_t stream) {
+    if (((uintptr_t)p & 15) != 0) return 1;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    const unsigned grid = (unsigned)cus * 8;
+    size_t n16 = bytes / 16;
+    void *args[] = {&p, &n16, &sink};
+    return hipLaunchKernel(reinterpret_cast<const void *>(stream_read_kernel), dim3(grid),
+                           dim3(kReadThreads), args, 0, stream) == hipSuccess ? 0 : 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -63,18 +88,7 @@ extern "C" {
 // Streams the first bytes - bytes % 16 bytes of p (16-byte aligned) on
 // `stream`.  Returns 0, or 1 if the launch failed or p is misaligned.
 int qkc_stream_read(const void *p, size_t bytes, float *sink, void *stream) {
-    if (((uintptr_t)p & 15) != 0) return 1;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    const unsigned grid = (unsigned)cus * 8;
-    void *args[] = {&p, &bytes, &sink};
-    size_t n16 = bytes / 16;
-    args[1] = &n16;
-    return hipLaunchKernel(reinterpret_cast<const void *>(stream_read_kernel), dim3(grid),
-                           dim3(kReadThreads), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess
-               ? 0 : 1;
+    return stream_read(p, bytes, sink, static_cast<hipStream_t>(stream));
 }
 
 // Runs `workgroups` x 8 waves of the MFMA loop for `iters` iterations;
@@ -83,6 +97,142 @@ int qkc_mfma_loop(int workgroups, int iters, float *sink, void *stream) {
     void *args[] = {&iters, &sink};
     return hipLaunchKernel(reinterpret_cast<const void *>(mfma_loop_kernel), dim3((unsigned)workgroups),
                            dim3(512), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : 1;
+}
+
+// One call of the qk C ABI with its arguments.  Every field is 8 bytes wide
+// so the layout is the same for any caller; fields an operation does not use
+// are ignored.
+enum qkb_op {
+    QKB_DEQUANTIZE = 0,           // fmt, w, m (rows), k, out_dtype, y (out)
+    QKB_MUL_MAT_VEC = 1,          // fmt, w, m, k, x, n, ldx, y, ldy
+    QKB_MUL_MAT_VEC_X8 = 2,       // as QKB_MUL_MAT_VEC
+    QKB_MUL_MAT_VEC_BATCHED = 3,  // fmt, items, count, n
+    QKB_MUL_MAT_VEC_ID = 4,       // fmt, w, n_experts, expert_stride, m, k, ids, ld_ids, n_used,
+                                  // n_tokens, x, x_slot, x_tok, y, y_slot, y_tok
+    QKB_MUL_MAT = 5,              // fmt, w, m, k, x (fp16), n, ldx, y, ldy
+    QKB_STREAM_READ = 6,          // w (16-byte aligned), k (bytes), y (sink)
+};
+
+typedef struct qkb_call {
+    int64_t op;
+    int64_t fmt;
+    const void *w;
+    int64_t m;
+    int64_t k;
+    const void *x;
+    int64_t n;
+    int64_t ldx;
+    void *y;
+    int64_t ldy;
+    int64_t out_dtype;
+    const qk_mat_vec_item *items;
+    int64_t count;
+    int64_t n_experts;
+    int64_t expert_stride;
+    const int32_t *ids;
+    int64_t ld_ids;
+    int64_t n_used;
+    int64_t n_tokens;
+    int64_t x_slot;
+    int64_t x_tok;
+    int64_t y_slot;
+    int64_t y_tok;
+} qkb_call;
+
+static int issue(const qkb_call &c, hipStream_t s) {
+    switch (c.op) {
+    case QKB_DEQUANTIZE:
+        return qk_dequantize((int)c.fmt, c.w, c.m, c.k, (int)c.out_dtype, c.y, s);
+    case QKB_MUL_MAT_VEC:
+        return qk_mul_mat_vec((int)c.fmt, c.w, c.m, c.k, static_cast<const float *>(c.x), c.n, c.ldx,
+                              static_cast<float *>(c.y), c.ldy, s);
+    case QKB_MUL_MAT_VEC_X8:
+        return qk_mul_mat_vec_x8((int)c.fmt, c.w, c.m, c.k, static_cast<const float *>(c.x), c.n, c.ldx,
+                                 static_cast<float *>(c.y), c.ldy, s);
+    case QKB_MUL_MAT_VEC_BATCHED:
+        return qk_mul_mat_vec_batched((int)c.fmt, c.items, (int)c.count, c.n, s);
+    case QKB_MUL_MAT_VEC_ID:
+        return qk_mul_mat_vec_id((int)c.fmt, c.w, c.n_experts, c.expert_stride, c.m, c.k, c.ids, c.ld_ids,
+                                 c.n_used, c.n_tokens, static_cast<const float *>(c.x), c.x_slot, c.x_tok,
+                                 static_cast<float *>(c.y), c.y_slot, c.y_tok, s);
+    case QKB_MUL_MAT:
+        return qk_mul_mat((int)c.fmt, c.w, c.m, c.k, c.x, c.n, c.ldx, static_cast<float *>(c.y), c.ldy, s);
+    case QKB_STREAM_READ:
+        return stream_read(c.w, (size_t)c.k, static_cast<float *>(c.y), s) == 0 ? 0 : QK_ERR_LAUNCH;
+    default:
+        return QK_ERR_INVALID_ARG;
+    }
+}
+
+// Issues step i: calls[(i % variants) * per_step .. + per_step).
+static int issue_step(const qkb_call *calls, int per_step, int variants, int64_t i, hipStream_t s) {
+    const qkb_call *c = calls + (size_t)(i % variants) * per_step;
+    for (int j = 0; j < per_step; ++j) {
+        const int st = issue(c[j], s);
+        if (st != 0) return st;
+    }
+    return 0;
+}
+
+// Runs `warmup` untimed steps (steps 0 .. warmup-1 of the rotation), waits for
+// the device, then times `steps` further steps between two HIP events on
+// `stream` and waits again.  *total_ms gets the elapsed time of the timed
+// steps.  If group_ms is not NULL, an event is also recorded after every
+// `group` timed steps (steps % group == 0) and group_ms[g] gets the time of
+// group g: an event between single launches adds its own cost to each, so
+// a distribution is taken over groups of launches.
+// Returns 0, a qk status of the first failing call, or 100 + a HIP error.
+int qkb_time_steps(const qkb_call *calls, int per_step, int variants, int warmup, int steps,
+                   int group, void *stream, float *total_ms, float *group_ms) {
+    if (calls == nullptr || per_step <= 0 || variants <= 0 || warmup < 0 || steps <= 0 ||
+        group <= 0 || total_ms == nullptr || (group_ms != nullptr && steps % group != 0))
+        return QK_ERR_INVALID_ARG;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int ngroups = group_ms != nullptr ? steps / group : 1;
+    std::vector<hipEvent_t> ev((size_t)ngroups + 1, nullptr);
+    int rc = 0;
+    hipError_t e = hipSuccess;
+    for (size_t i = 0; i < ev.size() && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+    for (int64_t i = 0; e == hipSuccess && rc == 0 && i < warmup; ++i)
+        rc = issue_step(calls, per_step, variants, i, s);
+    if (e == hipSuccess && rc == 0) e = hipDeviceSynchronize();
+    if (e == hipSuccess && rc == 0) e = hipEventRecord(ev[0], s);
+    for (int64_t t = 0; e == hipSuccess && rc == 0 && t < steps; ++t) {
+        rc = issue_step(calls, per_step, variants, warmup + t, s);
+        if (rc == 0 && group_ms != nullptr && (t + 1) % group == 0)
+            e = hipEventRecord(ev[(size_t)((t + 1) / group)], s);
+    }
+    if (e == hipSuccess && rc == 0 && group_ms == nullptr) e = hipEventRecord(ev[1], s);
+    const hipError_t es = hipDeviceSynchronize();
+    if (e == hipSuccess) e = es;
+    if (e == hipSuccess && rc == 0) {
+        e = hipEventElapsedTime(total_ms, ev[0], ev[(size_t)ngroups]);
+        for (int g = 0; e == hipSuccess && group_ms != nullptr && g < ngroups; ++g)
+            e = hipEventElapsedTime(&group_ms[g], ev[(size_t)g], ev[(size_t)g + 1]);
+    }
+    for (hipEvent_t x : ev)
+        if (x != nullptr) (void)hipEventDestroy(x);
+    if (rc != 0) return rc;
+    return e == hipSuccess ? 0 : 100 + (int)e;
+}
+
+// Streaming reads of `bytes` of buf (16-byte aligned) issued back to back for
+// `ms` milliseconds of wall time, then waits for them: brings the GPU's clocks
+// out of their idle state before a workload's warm-up.  Returns 0 or 1.
+int qkb_settle(const void *buf, size_t bytes, float *sink, double ms, void *stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const auto t0 = std::chrono::steady_clock::now();
+    int launched = 0;
+    for (;;) {
+        // a few launches between clock reads; at most 64 in flight at once
+        for (int i = 0; i < 4; ++i)
+            if (stream_read(buf, bytes, sink, s) != 0) return 1;
+        launched += 4;
+        if (launched % 64 == 0 && hipStreamSynchronize(s) != hipSuccess) return 1;
+        const double el = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+        if (el >= ms) break;
+    }
+    return hipStreamSynchronize(s) == hipSuccess ? 0 : 1;
 }
 
 }  // extern "C"
