@@ -1057,8 +1057,19 @@ int gemv_table_sub(GemvArgs &a, bool fast, hipStream_t stream) {
     return gemv_table_run<FMT, NC, SUB, false, X8>(a, stream);
 }
 
+// The GEMV for 4..8 columns on the matrix cores (gemv_mfma.h): one problem,
+// 4-byte aligned weights with an even block count, k <= kGvWindow.  (At 2 or
+// 3 columns the vector-ALU kernel below measured faster: Q4_1 11008 x 4096
+// at 2 columns 11.0 us against 14.8 us.)
+template <int FMT, int NC>
+int gemv_mfma_launch(const GemvItem &it, hipStream_t stream);
+
 template <int FMT, int NC, bool X8>
 int gemv_table_fmt(GemvArgs &a, bool fast, hipStream_t stream) {
+    if constexpr (NC >= 4 && !X8) {
+        if (a.count == 1 && fast && a.item[0].nb * kBlockElems <= kGvWindow)
+            return gemv_mfma_launch<FMT, NC>(a.item[0], stream);
+    }
     if constexpr (NC == 1) {
         int npairs = 0;
         bool mixed = false;

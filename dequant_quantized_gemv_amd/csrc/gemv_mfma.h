@@ -1,0 +1,286 @@
+// gemv_mfma.h - the fused quantized GEMV for 4..8 fp32 columns with the
+// products on the matrix cores (v_mfma_f32_4x4x1_16b_f32).
+//
+// What is computed is the GEMV of gemv_impl.h (dequantize_mul_mat_vec under
+// the ggml_cuda_op_mul_mat row-range x column-count driver of the
+// "llama_cpp 0.12.1 -> 0.12.2" ggml-cuda.cu diff): y[j][i] = sum_c W[i,c]
+// x[j][c], each term the exact fp32 weight (the dequantize definition: d*q
+// + (-8*d), d*q + m, d*q) times the fp32 activation.  With several columns
+// the per-weight work of the vector ALU is dominated by the n multiply-adds;
+// here they run on the matrix cores instead, and the vector ALU only rebuilds
+// each fp32 weight once for all columns.
+//
+// The fp32 4x4x1 MFMA does 16 independent 4x4 outer-product updates,
+// D_g += A_g (4 values) x B_g (4 values), g = lane / 4; on gfx950 each
+// update is a fused multiply-add per element (one rounding, fp32 denormals
+// kept), so every term is rounded exactly as an FMA on the vector ALU rounds
+// it.  The 16 updates are used as 16 k-streams of one row-quad: lane (g, c)
+// (c = lane % 4) supplies the weight of row c of the quad and the activation
+// of column c at the same k, and block g accumulates the 4 x 4 partial sums
+// of its stream.  A row-quad's pairs are split over KQ waves (1, 2 or 4, as
+// k needs): lane group g of wave kq takes pair g + 16 kq of each of the four
+// rows (a pair is two blocks, 64 weights: 36 / 40 / 68 bytes, dword aligned,
+// loaded straight into registers).  A stream is two or four fp32 FMA chains
+// of at most 32 terms (elements t % 2 or t % 4); the chains and the 16
+// streams are added in trees (2 + 4 levels), and the KQ waves' sums in
+// sequence, so |y - exact| <= (32 + 6 + 3) * 2^-24 * S to first order.
+//
+// Activations: the row's whole activation window (k <= 4096 weights, up to
+// 8 columns) is staged once per workgroup in LDS, column c at c * kMfPitch
+// floats and element e at e + 4 * (e / 64): the 16 reads of a quarter-wave
+// (4 lane groups x 4 columns, 16 bytes each) then fall in distinct banks.
+// Workgroups are one per CU when the window is large (8 columns: 140 KB) and
+// walk a contiguous range of row-quads in rounds, so the window is staged once
+// per workgroup.  In a round each row-quad is split over KQ waves (pairs
+// g + 16 kq), whose partial sums meet in LDS and are added in a fixed order
+// by the first of them: deterministic, with no atomics.
+#pragma once
+
+#include "gemv_impl.h"
+
+namespace qk {
+
+typedef float f32x4m_t __attribute__((ext_vector_type(4)));
+
+// LDS floats per staged column: 4096 weights + 4 floats of padding per 64,
+// and 16 more so consecutive columns start 16 banks apart.
+constexpr int kMfPitch = kGvWindow + kGvWindow / 16 + 16;
+// Largest k (weights per row) the matrix-core GEMV takes: one staged window.
+constexpr int kMfMaxK = kGvWindow;
+
+// The fp32 weights of quant word i of block b of a pair, the dequantize
+// definition's value (exact for Q4_0 and Q8_0, one rounding of d*q + m for
+// Q4_1): Q4 words give elements 4i..4i+3 (low nibbles) in w[0..3] and
+// 16+4i..16+4i+3 (high nibbles) in w[4..7]; Q8_0 words give elements
+// 4i..4i+3 in w[0..3].
+template <int FMT>
+__device__ __forceinline__ void word_weights(const uint32_t (&v)[Pair<FMT>::kDwords], int b, int i,
+                                             float d, float mm, float (&w)[8]) {
+    if constexpr (FMT == QK_Q8_0) {
+        const uint32_t qw = b == 0 ? shift2(v[i], v[i + 1]) : v[9 + i];
+        w[0] = d * (float)(int8_t)(qw);
+        w[1] = d * (float)(int8_t)(qw >> 8);
+        w[2] = d * (float)(int8_t)(qw >> 16);
+        w[3] = d * (float)(int8_t)(qw >> 24);
+    } else {
+        const uint32_t qw = pair_qs<FMT>(v, b, i);
+        uint32_t lo = qw & 0x0F0F0F0Fu;
+        uint32_t hi = (qw >> 4) & 0x0F0F0F0Fu;
+        // opaque, so each nibble converts with one byte-select convert
+        // (v_cvt_f32_ubyte1..3) instead of a field extract and a convert
+        asm volatile("" : "+v"(lo), "+v"(hi));
+        w[0] = wval(d, ubyte_f<0>(lo), mm);
+        w[1] = wval(d, ubyte_f<1>(lo), mm);
+        w[2] = wval(d, ubyte_f<2>(lo), mm);
+        w[3] = wval(d, ubyte_f<3>(lo), mm);
+        w[4] = wval(d, ubyte_f<0>(hi), mm);
+        w[5] = wval(d, ubyte_f<1>(hi), mm);
+        w[6] = wval(d, ubyte_f<2>(hi), mm);
+        w[7] = wval(d, ubyte_f<3>(hi), mm);
+    }
+}
+
+template <int FMT, int NC, int WPG, int KQ>
+__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) void gemv_mfma_kernel(
+    const GemvItem it, const int qper, const int qrem) {
+    static_assert(NC >= 1 && NC <= 8, "1..8 columns");
+    static_assert((KQ == 1 || KQ == 2 || KQ == 4) && WPG % KQ == 0, "K split");
+    constexpr int CG = (NC + 3) / 4;  // column groups of 4 (one MFMA each per k)
+    constexpr int ND = Pair<FMT>::kDwords;
+    constexpr int BS = Format<FMT>::kBytes;
+    constexpr int NT = 64 * WPG;
+    constexpr int RPR = WPG / KQ;  // row-quads per round
+    extern __shared__ __attribute__((aligned(16))) float xs[];
+    // per wave, its partial sums of one round: [cg][column c][row r]
+    float *const part = xs + NC * kMfPitch;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int kq = wave % KQ;    // which pair of the row this wave's lanes take
+    const int slot = wave / KQ;  // which row-quad of the round
+    const int g = lane >> 2;     // k-stream (lane group)
+    const int c = lane & 3;      // row of the quad (A) and column of the group (B)
+    const int b = blockIdx.x;
+    const int q0 = b * qper + min(b, qrem);
+    const int q1 = q0 + qper + (b < qrem ? 1 : 0);
+    const int npairs = it.nb >> 1;  // an even block count on this path
+    const int kk = it.nb * 32;
+    const int64_t row_bytes = (int64_t)it.nb * BS;
+    const int p = g + 16 * kq;       // the lane's pair of every row it reads
+    const bool valid = p < npairs;   // a pair past the row: weights 0
+
+    // the lane's pair of row-quad q (a row past m, or a pair past the row,
+    // reads a clamped valid address; its weights are zeroed below)
+    auto load = [&](int q, uint32_t (&dst)[ND]) __attribute__((always_inline)) {
+        const int row = min(4 * q + c, it.m - 1);
+        load_pair_fast<FMT>(it.w + (int64_t)row * row_bytes + (int64_t)min(p, npairs - 1) * (2 * BS), dst);
+    };
+
+    // The activations go to LDS: NC columns of KQ * 1024 elements, zero past
+    // k (every lane then reads finite values).  Their loads are issued first,
+    // unconditionally (a clamped address, the value zeroed after), then the
+    // first row-quad's weight loads: loads complete in order, so the LDS
+    // stores wait only for the activations and the weights' HBM latency
+    // overlaps the staging.
+    constexpr int PER_COL = KQ * 256;  // float4s per column
+    constexpr int TOT = NC * PER_COL;
+    constexpr int IT = (TOT + NT - 1) / NT;
+    f32x4m_t tmp[IT];
+#pragma unroll
+    for (int u = 0; u < IT; ++u) {
+        const int idx = min(tid + u * NT, TOT - 1);
+        const int j = idx / PER_COL;
+        const int e = (idx % PER_COL) << 2;
+        tmp[u] = *reinterpret_cast<const f32x4_a4 *>(it.x + j * it.ldx + min(e, kk - 4));
+    }
+    // the wave's pairs of its first D rounds (unconditional, clamped, so the
+    // waits that follow are counted exactly); each round then requests the
+    // round D ahead into the registers it has just used.  (Deeper prefetch
+    // measured slower: most workgroups have only one to three rounds, and
+    // the clamped extra loads of the first rounds are then wasted.)
+    constexpr int D = 2;
+    uint32_t v[D][ND];
+#pragma unroll
+    for (int r = 0; r < D; ++r) load(min(q0 + slot + r * RPR, q1 - 1), v[r]);
+#pragma unroll
+    for (int u = 0; u < IT; ++u) {
+        const int idx = tid + u * NT;
+        const int j = idx / PER_COL;
+        const int e = (idx % PER_COL) << 2;
+        const f32x4m_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (TOT % NT == 0 || idx < TOT)
+            *reinterpret_cast<f32x4m_t *>(xs + j * kMfPitch + e + (e >> 6) * 4) = e < kk ? tmp[u] : z;
+    }
+    __syncthreads();
+
+    // the B operand of column group cg: column cg*4 + c (a lane whose column
+    // is past NC reads column NC-1; its sums are never stored)
+    int colo[CG];
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) colo[cg] = min(cg * 4 + c, NC - 1) * kMfPitch;
+
+    // One round: RPR row-quads, each split over KQ waves (one pair per lane).
+    auto round = [&](const int qb, uint32_t (&cur)[ND]) __attribute__((always_inline)) {
+        const int q = qb + slot;
+        // CH independent accumulation chains per column group (element
+        // t % CH), added at the end: four for one group, two for two
+        constexpr int CH = CG == 1 ? 4 : 2;
+        f32x4m_t acc[CG][CH];
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg)
+#pragma unroll
+            for (int u = 0; u < CH; ++u) acc[cg][u] = f32x4m_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if (q < q1) {
+#pragma unroll
+            for (int bk = 0; bk < 2; ++bk) {
+                float d = h2f(pair_d<FMT>(cur, bk));
+                float mm = 0.0f;
+                if constexpr (FMT == QK_Q4_1) mm = h2f(pair_m_q41(cur, bk));
+                else if constexpr (FMT == QK_Q4_0) mm = -8.0f * d;
+                d = valid ? d : 0.0f;
+                mm = valid ? mm : 0.0f;
+                constexpr int NW = FMT == QK_Q8_0 ? 8 : 4;  // quant words per block
+#pragma unroll
+                for (int wi = 0; wi < NW; ++wi) {
+                    float wt[8];
+                    word_weights<FMT>(cur, bk, wi, d, mm, wt);
+#pragma unroll
+                    for (int h = 0; h < (FMT == QK_Q8_0 ? 1 : 2); ++h) {
+                        // elements 4wi..4wi+3 (h = 0) or 16+4wi.. (h = 1) of the block
+                        const int e = 64 * p + 32 * bk + 16 * h + 4 * wi;
+                        const int eo = e + (e >> 6) * 4;
+                        f32x4m_t xb[CG];
+#pragma unroll
+                        for (int cg = 0; cg < CG; ++cg)
+                            xb[cg] = *reinterpret_cast<const f32x4m_t *>(xs + colo[cg] + eo);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+#pragma unroll
+                            for (int cg = 0; cg < CG; ++cg)
+                                acc[cg][u % CH] = __builtin_amdgcn_mfma_f32_4x4x1f32(wt[4 * h + u], xb[cg][u],
+                                                                                     acc[cg][u % CH], 0, 0, 0);
+                    }
+                    // keep the next word's LDS reads from being hoisted above
+                    // this one (bounds the live activations)
+                    asm volatile("" ::: "memory");
+                }
+            }
+        }
+        // the pair of the wave's round D ahead into the registers just used
+        if (q + D * RPR < q1) load(q + D * RPR, cur);
+        // the 16 streams of each (row, column) are lanes c, c + 4, ..., c + 60:
+        // a DPP tree within each 16-lane row, then across rows; lanes 0..3
+        // write the wave's sums of rows 0..3 of column c
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float sm = acc[cg][0][r] + acc[cg][1][r];
+                if constexpr (CH == 4) sm += acc[cg][2][r] + acc[cg][3][r];
+                sm += dpp<0x124>(sm);  // row_ror:4
+                sm += dpp<0x128>(sm);  // row_ror:8
+                sm += __shfl_xor(sm, 16);
+                sm += __shfl_xor(sm, 32);
+                if (g == 0) part[((wave * CG + cg) * 4 + c) * 4 + r] = sm;
+            }
+        }
+        __syncthreads();
+        // the KQ waves of a row-quad in order: the first one adds and stores
+        if (kq == 0 && q < q1 && lane < 16 * CG) {
+            const int r = lane & 3;
+            const int cc = (lane >> 2) & 3;
+            const int cg = lane >> 4;
+            const int col = cg * 4 + cc;
+            float sm = part[((wave * CG + cg) * 4 + cc) * 4 + r];
+#pragma unroll
+            for (int k2 = 1; k2 < KQ; ++k2) sm += part[(((wave + k2) * CG + cg) * 4 + cc) * 4 + r];
+            const int ro = 4 * q + r;
+            if (col < NC && ro < it.m) it.y[col * it.ldy + ro] = sm;
+        }
+        __syncthreads();  // the partial slots are reused by the next round
+    };
+    for (int qb = q0; qb < q1; qb += D * RPR) {
+#pragma unroll
+        for (int r = 0; r < D; ++r)
+            if (qb + r * RPR < q1) round(qb + r * RPR, v[r]);  // (uniform across the workgroup)
+    }
+}
+
+// Waves per workgroup by column count: the staged window takes NC * 17.5 KB
+// of LDS, so 8 columns fit one workgroup per CU (16 waves), 4 columns two (8
+// waves each), 2 or 3 columns four (4 waves each): 16 waves per CU in all.
+template <int NC> struct MfShape {
+    static constexpr int kWPG = NC > 4 ? 16 : (NC > 2 ? 8 : 4);
+};
+
+template <int FMT, int NC, int KQ>
+int gemv_mfma_run(const GemvItem &it, hipStream_t stream) {
+    constexpr int WPG = MfShape<NC>::kWPG;
+    const size_t lds = ((size_t)NC * kMfPitch + (size_t)WPG * ((NC + 3) / 4) * 16) * sizeof(float);
+    const int per_cu = max(1, (int)((160 * 1024) / lds));
+    const int64_t quads = ((int64_t)it.m + 3) / 4;
+    if (quads > INT32_MAX) return QK_ERR_INVALID_ARG;
+    const int64_t cap = (int64_t)device_cus() * per_cu;
+    const int nwg = (int)(quads < cap ? quads : cap);
+    auto kern = gemv_mfma_kernel<FMT, NC, WPG, KQ>;
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return QK_ERR_LAUNCH;
+    return launch_lds(kern, dim3((unsigned)nwg), dim3(64 * WPG), lds, stream, it, (int)(quads / nwg),
+                      (int)(quads % nwg));
+}
+
+// y = W x for NC = 4..8 columns on the matrix cores: one problem, weights
+// 4-byte aligned with an even block count, k <= kMfMaxK.  Each row-quad is
+// split over KQ waves, one pair of blocks per lane.
+template <int FMT, int NC>
+int gemv_mfma_launch(const GemvItem &it, hipStream_t stream) {
+    const int npairs = it.nb >> 1;
+    if (npairs <= 16) return gemv_mfma_run<FMT, NC, 1>(it, stream);
+    if (npairs <= 32) return gemv_mfma_run<FMT, NC, 2>(it, stream);
+    return gemv_mfma_run<FMT, NC, 4>(it, stream);
+}
+
+}  // namespace qk

@@ -1,6 +1,6 @@
 // gemv_n56.hip - instances of the fused quantized GEMV for 5 and 6 column(s)
 // (kernels in gemv_impl.h; one file per column count so they build in parallel).
-#include "gemv_impl.h"
+#include "gemv_mfma.h"
 
 namespace qk {
 

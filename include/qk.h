@@ -109,7 +109,11 @@ int qk_dequantize(int fmt, const void *w, int64_t rows, int64_t k,
  *
  * Each product uses the exact fp32 weight value, so the result is within a
  * few fp32 roundings per term of the exact sum: |y - exact| is a small
- * multiple of 2^-24 * sum_c |W[i,c] x[j*ldx+c]|.
+ * multiple of 2^-24 * sum_c |W[i,c] x[j*ldx+c]|.  With 4..8 columns, weights
+ * 4-byte aligned with an even block count and k <= 4096, the multiply-adds
+ * run on the matrix cores (fp32 MFMA, each a fused multiply-add with one
+ * rounding, like the vector ALU's), in a different order than the vector-ALU
+ * kernel the other cases use.
  * Source: dequantize_mul_mat_vec (the "dmmv" tuning block) and the
  * ggml_cuda_op_mul_mat row-range x column-count driver in the same diff,
  * which use it when the right operand is a vector.
@@ -169,9 +173,12 @@ typedef struct qk_mat_vec_item {
 /*
  * qk_mul_mat_vec_batched - several independent GEMVs of one format and one
  * column count n in a single launch (for example the q/k/v/o, gate/up and down
- * projections of one decode step, or a set of expert matrices).  Each item is
- * computed exactly as qk_mul_mat_vec would compute it; one launch amortizes
- * the fixed launch cost over all items' weights.
+ * projections of one decode step, or a set of expert matrices); one launch
+ * amortizes the fixed launch cost over all items' weights.  Each item is
+ * computed exactly as qk_mul_mat_vec would compute it, bit for bit, except
+ * where a single call of 4..8 columns would take the matrix-core kernel: a
+ * grouped launch computes every item on the vector ALU, and the two agree
+ * within the error bound.  (A one-item call is a single call.)
  * Source: as qk_mul_mat_vec (dequantize_mul_mat_vec under ggml_cuda_op_mul_mat,
  * "llama_cpp 0.12.1 -> 0.12.2" ggml-cuda.cu diff), applied per item.
  *

@@ -329,6 +329,24 @@ def test_gemv_side_stream():
     assert_within(y, yref, sc, GEMV_TOL, "side stream")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k,n", [(1, 64, 4), (3, 512, 5), (5, 1088, 8), (63, 2112, 4), (1001, 4096, 6),
+                                   (257, 1024, 7), (20000, 4096, 4), (4099, 2048, 8)])
+def test_gemv_matrix_core_path(fmt, m, k, n):
+    """The 4..8-column GEMV on the matrix cores (aligned weights, even block
+    count, k <= 4096): a row-quad split over 1, 2 or 4 waves (16, 32 or 64
+    pairs per row, ragged pair counts), ragged last row-quads, several rounds
+    per workgroup; every output against the oracle, and a second launch
+    bitwise equal to the first (the partial sums meet in a fixed order)."""
+    _say("gemv matrix cores", fmt, m, k, n)
+    w = _weights(fmt, m, k, seed=58)
+    x = synth.activations(k, n, seed=58, tensor_id=3)
+    y = _gpu_gemv(fmt, w, m, k, x)
+    yref, s = oracle_rows(oracle.dot, fmt, w, m, k, x, n)
+    assert_within(y, yref, s, GEMV_TOL, f"gemv matrix cores {fmt} {m}x{k} n={n}")
+    assert np.array_equal(y.view(np.uint32), _gpu_gemv(fmt, w, m, k, x).view(np.uint32))
+
+
 def test_gemv_full_config1():
     """Q8_0 4096 x 4096, batch 1: every output against the oracle."""
     cfg = synth.WORKLOADS["gemv_q8_0_4096x4096_n1"]
