@@ -26,6 +26,8 @@ Block byte layouts (little-endian binary16 fields, blocks of 32 weights):
   Q4_0: d[2] qs[16]          (18 bytes)
   Q4_1: d[2] m[2] qs[16]     (20 bytes)
   Q8_0: d[2] qs[32] (int8)   (34 bytes)
+  Q5_0: d[2] qh[4] qs[16]    (22 bytes; qh little-endian, bit t = bit 4 of code t)
+  Q5_1: d[2] m[2] qh[4] qs[16] (24 bytes)
 A matrix is ``rows`` rows of k/32 blocks each, rows back to back.
 """
 import numpy as np
@@ -34,10 +36,12 @@ GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
-BLOCK_BYTES = {"q4_0": 18, "q4_1": 20, "q8_0": 34}
-QS_OFFSET = {"q4_0": 2, "q4_1": 4, "q8_0": 2}
+BLOCK_BYTES = {"q4_0": 18, "q4_1": 20, "q8_0": 34, "q5_0": 22, "q5_1": 24}
+QS_OFFSET = {"q4_0": 2, "q4_1": 4, "q8_0": 2, "q5_0": 6, "q5_1": 8}
+QH_OFFSET = {"q5_0": 2, "q5_1": 4}
+HAS_M = ("q4_1", "q5_1")
 
-FIELD_D, FIELD_M, FIELD_QS, FIELD_X, FIELD_X2, FIELD_IDS = 0, 1, 2, 3, 4, 5
+FIELD_D, FIELD_M, FIELD_QS, FIELD_X, FIELD_X2, FIELD_IDS, FIELD_QH = 0, 1, 2, 3, 4, 5, 6
 
 
 def _mix(z):
@@ -89,7 +93,9 @@ def pack_blocks(fmt, d_bits, codes, m_bits=None):
 
     d_bits, m_bits: binary16 bit patterns, shape (nblocks,).
     codes: shape (nblocks, 32); 0..15 for Q4_x (element t < 16 goes to the low
-    nibble of qs[t], t >= 16 to the high nibble of qs[t-16]); -128..127 for Q8_0.
+    nibble of qs[t], t >= 16 to the high nibble of qs[t-16]); 0..31 for Q5_x
+    (the low four bits as Q4_x, bit 4 of element t in bit t of qh);
+    -128..127 for Q8_0.
     Returns a flat uint8 array of nblocks * block_bytes.
     """
     d_bits = np.asarray(d_bits, dtype=np.uint16).ravel()
@@ -100,9 +106,9 @@ def pack_blocks(fmt, d_bits, codes, m_bits=None):
     bs = BLOCK_BYTES[fmt]
     out = np.zeros((nb, bs), dtype=np.uint8)
     out[:, 0:2] = d_bits.astype("<u2").view(np.uint8).reshape(nb, 2)
-    if fmt == "q4_1":
+    if fmt in HAS_M:
         if m_bits is None:
-            raise ValueError("q4_1 needs m")
+            raise ValueError(f"{fmt} needs m")
         m_bits = np.asarray(m_bits, dtype=np.uint16).ravel()
         out[:, 2:4] = m_bits.astype("<u2").view(np.uint8).reshape(nb, 2)
     off = QS_OFFSET[fmt]
@@ -111,6 +117,15 @@ def pack_blocks(fmt, d_bits, codes, m_bits=None):
         if c.min(initial=0) < 0 or c.max(initial=0) > 15:
             raise ValueError("Q4 codes must be 0..15")
         out[:, off:off + 16] = (c[:, :16] | (c[:, 16:] << 4)).astype(np.uint8)
+    elif fmt in ("q5_0", "q5_1"):
+        c = codes.astype(np.int64)
+        if c.min(initial=0) < 0 or c.max(initial=0) > 31:
+            raise ValueError("Q5 codes must be 0..31")
+        lo = c & 15
+        out[:, off:off + 16] = (lo[:, :16] | (lo[:, 16:] << 4)).astype(np.uint8)
+        qh = ((c >> 4) << np.arange(32, dtype=np.int64)).sum(axis=1).astype(np.uint32)
+        hoff = QH_OFFSET[fmt]
+        out[:, hoff:hoff + 4] = qh.astype("<u4").view(np.uint8).reshape(nb, 4)
     else:
         c = codes.astype(np.int64)
         if c.min(initial=0) < -128 or c.max(initial=0) > 127:
@@ -128,12 +143,17 @@ def quant_matrix(fmt, rows, k, seed, tensor_id, d_range, m_range=(-0.1, 0.0)):
     out = np.empty((nb, bs), dtype=np.uint8)
     d = uniform_half_bits(stream_key(seed, tensor_id, FIELD_D), nb, *d_range)
     out[:, 0:2] = d.astype("<u2").view(np.uint8).reshape(nb, 2)
-    if fmt == "q4_1":
+    if fmt in HAS_M:
         m = uniform_half_bits(stream_key(seed, tensor_id, FIELD_M), nb, *m_range)
         out[:, 2:4] = m.astype("<u2").view(np.uint8).reshape(nb, 2)
+    if fmt in QH_OFFSET:
+        # one 32-bit draw (the low half of a 64-bit one) gives a block's qh
+        z = splitmix64(stream_key(seed, tensor_id, FIELD_QH), nb) & np.uint64(0xFFFFFFFF)
+        hoff = QH_OFFSET[fmt]
+        out[:, hoff:hoff + 4] = z.astype("<u4").view(np.uint8).reshape(nb, 4)
     off = QS_OFFSET[fmt]
     key = stream_key(seed, tensor_id, FIELD_QS)
-    if fmt in ("q4_0", "q4_1"):
+    if fmt in ("q4_0", "q4_1", "q5_0", "q5_1"):
         # two 64-bit draws give the 16 quant bytes of a block
         z = splitmix64(key, 2 * nb)
         out[:, off:off + 16] = z.view(np.uint8).reshape(nb, 16)

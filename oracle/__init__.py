@@ -22,7 +22,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-FORMATS = {"q4_0": 0, "q4_1": 1, "q8_0": 2}
+FORMATS = {"q4_0": 0, "q4_1": 1, "q8_0": 2, "q5_0": 3, "q5_1": 4}
 
 _lib = None
 

@@ -1,6 +1,6 @@
 /*
  * qk_oracle.c - plain, slow CPU oracle for ggml block-quantized dequantize,
- * GEMV and GEMM (formats Q4_0, Q4_1, Q8_0).
+ * GEMV and GEMM (formats Q4_0, Q4_1, Q8_0, Q5_0, Q5_1).
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference the GPU
  * library is checked against.  Only the test suite, the package smoke check
@@ -23,6 +23,13 @@
  *      followed by 32 signed bytes (64 blocks fill 2176 bytes, so 34 bytes a
  *      block); value q*d.
  *    - the dequantize_row_*_cuda launchers: 32 weights per block (nb32 = k/32).
+ *  - Q5_0 and Q5_1 are named only by the to_fp16 / to_fp32 dispatch of the
+ *    same diff (dequantize_block_cuda with dequantize_q5_0 / dequantize_q5_1,
+ *    blocks of QK5_0 / QK5_1 weights); their byte layout and arithmetic are
+ *    not printed on the pages.  Reading taken (ggml's published block
+ *    format): Q5_0 = d (fp16), qh (4 bytes, little-endian: bit t is bit 4 of
+ *    code t), qs (16 bytes, low four bits as Q4_0); value (q - 16) * d.
+ *    Q5_1 = d, m (fp16), qh, qs; value d*q + m.
  *  - The dot-product definition y[i,j] = sum_c W[i,c] * X[c,j] is the plain
  *    matrix-vector / matrix-matrix product that dequantize_mul_mat_vec and the
  *    mul_mat path compute (same diff page, ggml_cuda_op_mul_mat and the
@@ -36,6 +43,8 @@
 #define ORC_Q4_0 0
 #define ORC_Q4_1 1
 #define ORC_Q8_0 2
+#define ORC_Q5_0 3
+#define ORC_Q5_1 4
 
 /* ---------------------------------------------------------------------
  * IEEE-754 binary16 codec, written from the format definition:
@@ -109,6 +118,8 @@ int orc_block_bytes(int fmt)
     case ORC_Q4_0: return 2 + 16;        /* d, qs[16] */
     case ORC_Q4_1: return 2 + 2 + 16;    /* d, m, qs[16] */
     case ORC_Q8_0: return 2 + 32;        /* d, qs[32] (int8) */
+    case ORC_Q5_0: return 2 + 4 + 16;    /* d, qh, qs[16] */
+    case ORC_Q5_1: return 2 + 2 + 4 + 16; /* d, m, qh, qs[16] */
     default: return 0;
     }
 }
@@ -129,6 +140,15 @@ int orc_code(int fmt, const uint8_t *blk, int t)
     }
     case ORC_Q8_0:
         return (int)(int8_t)blk[2 + t];
+    case ORC_Q5_0:
+    case ORC_Q5_1: {
+        const uint8_t *qhp = blk + (fmt == ORC_Q5_0 ? 2 : 4);
+        const uint8_t *qs = qhp + 4;
+        const uint32_t qh = (uint32_t)qhp[0] | ((uint32_t)qhp[1] << 8) |
+                            ((uint32_t)qhp[2] << 16) | ((uint32_t)qhp[3] << 24);
+        const int low = (t < 16) ? (qs[t] & 0x0F) : (qs[t - 16] >> 4);
+        return low | (int)(((qh >> t) & 1u) << 4);
+    }
     default:
         return 0;
     }
@@ -153,6 +173,15 @@ float orc_value(int fmt, const uint8_t *blk, int t)
     }
     case ORC_Q8_0:
         return d * c;
+    case ORC_Q5_0: {
+        const float cc = c - 16.0f;   /* exact: a small integer */
+        return cc * d;
+    }
+    case ORC_Q5_1: {
+        const float m = orc_half_to_float(orc_le16(blk + 2));
+        const float p = d * c;
+        return p + m;
+    }
     default:
         return NAN;
     }
@@ -331,9 +360,10 @@ void orc_quantize_x8(const float *x, int64_t k, int64_t n, int64_t ldx, int8_t *
 
 /* y[j*m + i] = sum_c W[i,c] * x^[j][c] in fp64 (x^ = d * q as above), and
  * the tolerance scale s[j*m + i]: the sum over blocks of |d_x * d * I| for
- * Q4_0 / Q8_0 and |d_x * d * I| + |d_x * m * Q| for Q4_1, where I is the
- * block's integer dot product of codes (Q4_0 codes taken as q - 8) and Q the
- * sum of the activation codes: the magnitudes of the terms a kernel rounds. */
+ * Q4_0 / Q8_0 / Q5_0 and |d_x * d * I| + |d_x * m * Q| for Q4_1 / Q5_1, where
+ * I is the block's integer dot product of codes (Q4_0 codes taken as q - 8,
+ * Q5_0 codes as q - 16) and Q the sum of the activation codes: the
+ * magnitudes of the terms a kernel rounds. */
 void orc_dot_x8(int fmt, const uint8_t *w, int64_t m, int64_t k, const float *x, int64_t n,
                 int64_t ldx, double *y, double *s)
 {
@@ -351,13 +381,14 @@ void orc_dot_x8(int fmt, const uint8_t *w, int64_t m, int64_t k, const float *x,
                 for (int t = 0; t < 32; ++t) {
                     int c = orc_code(fmt, blk, t);
                     if (fmt == ORC_Q4_0) c -= 8;
+                    if (fmt == ORC_Q5_0) c -= 16;
                     isum += (double)c * (double)q[t];
                     qsum += (double)q[t];
                     /* the plain product with the dequantized activation */
                     acc += (double)orc_value(fmt, blk, t) * ((double)dx * (double)q[t]);
                 }
                 mag += fabs((double)dx * dw * isum);
-                if (fmt == ORC_Q4_1)
+                if (fmt == ORC_Q4_1 || fmt == ORC_Q5_1)
                     mag += fabs((double)dx * (double)orc_half_to_float(orc_le16(blk + 2)) * qsum);
             }
             y[j * m + i] = acc;

@@ -85,6 +85,8 @@ def test_hand_worked_block(blk):
     assert np.array_equal(got, want)
     for t in blk["positive_zero_at"]:
         assert got[t].view(np.uint32) == 0, f"element {t} must be +0.0"
+    for t in blk.get("negative_zero_at", []):
+        assert got[t].view(np.uint32) == 0x80000000, f"element {t} must be -0.0"
     # per-element entry point agrees with the matrix one
     assert all(oracle.value(fmt, raw, t) == want[t] for t in range(32))
     # fp16 output: every value here is exactly representable
@@ -112,10 +114,10 @@ def test_hand_worked_dot(case):
 # layout, exact values, round trip
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0", "q5_0", "q5_1"])
 def test_nibble_and_byte_index_layout(fmt):
     # one marked code per block, at every position in turn; d = 1 (0x3C00), m = 0
-    base = 8 if fmt == "q4_0" else 0
+    base = {"q4_0": 8, "q5_0": 16}.get(fmt, 0)
     codes = np.full((32, 32), base, dtype=np.int64)
     for t in range(32):
         codes[t, t] = base + 5
@@ -127,12 +129,27 @@ def test_nibble_and_byte_index_layout(fmt):
     blk = w.reshape(32, -1)
     off = synth.QS_OFFSET[fmt]
     for t in range(32):
+        lo, lm = base & 15, (base + 5) & 15
         if fmt == "q8_0":
             assert blk[t, off + t] == 5
         elif t < 16:
-            assert blk[t, off + t] == (base + 5) | (base << 4)
+            assert blk[t, off + t] == lm | (lo << 4)
         else:
-            assert blk[t, off + t - 16] == base | ((base + 5) << 4)
+            assert blk[t, off + t - 16] == lo | (lm << 4)
+        if fmt in synth.QH_OFFSET:
+            # bit 4 of code u in bit u of the little-endian qh word
+            h = synth.QH_OFFSET[fmt]
+            qh = int.from_bytes(bytes(blk[t, h:h + 4]), "little")
+            want = sum((((base + 5) if u == t else base) >> 4 & 1) << u for u in range(32))
+            assert qh == want
+    # a code with bit 4 set and low bits 0 (16), next to 15: the high bit matters
+    if fmt in ("q5_0", "q5_1"):
+        codes = np.zeros((1, 32), dtype=np.int64)
+        codes[0, 3], codes[0, 20] = 16, 15
+        w = synth.pack_blocks(fmt, [0x3C00], codes, m_bits=[0])
+        got = oracle.dequantize_f32(fmt, w, 1, 32).ravel()
+        off16 = 16 if fmt == "q5_0" else 0
+        assert got[3] == 16 - off16 and got[20] == 15 - off16 and got[0] == -off16
 
 
 def _d_values():
@@ -142,11 +159,13 @@ def _d_values():
     return np.array(bits, dtype=np.uint16)
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q5_0"])
 def test_every_code_exact_against_rationals(fmt):
     dbits = _d_values()
     if fmt == "q4_0":
         code_set = np.arange(16)
+    elif fmt == "q5_0":
+        code_set = np.arange(32)
     else:
         code_set = np.arange(-128, 128)
     nb = dbits.size * ((code_set.size + 31) // 32)
@@ -159,18 +178,23 @@ def test_every_code_exact_against_rationals(fmt):
         d = Fraction(float(dv[b]))
         for t in range(32):
             c = int(codes[b, t])
-            exact = d * (c - 8) if fmt == "q4_0" else d * c
+            exact = d * (c - {"q4_0": 8, "q5_0": 16}.get(fmt, 0))
             assert Fraction(float(got[b, t])) == exact
+            if fmt == "q5_0" and exact == 0:
+                # (q - 16) * d: a zero product's sign is the XOR of its
+                # factors' signs, q - 16 being +0 for q = 16
+                assert np.signbit(got[b, t]) == ((c < 16) != bool(np.signbit(dv[b])))
 
 
-def test_q4_1_exact_where_representable():
+@pytest.mark.parametrize("fmt", ["q4_1", "q5_1"])
+def test_q4_1_exact_where_representable(fmt):
     # d*c is always exact in fp32; d*c + m is exact whenever the rational sum
     # fits in 24 bits -- pick such d, m
     dbits = np.array([0x3C00, 0x3400, 0x2000, 0x0400, 0x0001, 0xB800], dtype=np.uint16)
     mbits = np.array([0xBC00, 0x0000, 0x2E66, 0xAE66, 0x0001, 0x3555], dtype=np.uint16)
-    codes = np.tile(np.arange(16), (dbits.size, 2))
-    w = synth.pack_blocks("q4_1", dbits, codes, m_bits=mbits)
-    got = oracle.dequantize_f32("q4_1", w, dbits.size, 32)
+    codes = np.tile(np.arange(16 if fmt == "q4_1" else 32), (dbits.size, 2 if fmt == "q4_1" else 1))
+    w = synth.pack_blocks(fmt, dbits, codes, m_bits=mbits)
+    got = oracle.dequantize_f32(fmt, w, dbits.size, 32)
     d = dbits.view(np.float16).astype(np.float64)
     m = mbits.view(np.float16).astype(np.float64)
     for b in range(dbits.size):
@@ -195,7 +219,7 @@ def test_q4_1_single_rounding_generic():
         assert got[t] == np.float32(1000.0 * int(codes[0, t]) + mv)
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0", "q5_0", "q5_1"])
 def test_round_trip_exactly_representable(fmt):
     rng = np.random.default_rng(7)
     nb = 64
@@ -205,14 +229,16 @@ def test_round_trip_exactly_representable(fmt):
     if fmt == "q8_0":
         codes = rng.integers(-128, 128, size=(nb, 32))
     else:
-        codes = rng.integers(0, 16, size=(nb, 32))
+        codes = rng.integers(0, 32 if fmt.startswith("q5") else 16, size=(nb, 32))
     w = synth.pack_blocks(fmt, dbits, codes, m_bits=mbits)
     vals = oracle.dequantize_f32(fmt, w, nb, 32).astype(np.float64)
     d = dbits.view(np.float16).astype(np.float64)[:, None]
     m = mbits.view(np.float16).astype(np.float64)[:, None]
     if fmt == "q4_0":
         rec = vals / d + 8
-    elif fmt == "q4_1":
+    elif fmt == "q5_0":
+        rec = vals / d + 16
+    elif fmt in ("q4_1", "q5_1"):
         rec = (vals - m) / d
     else:
         rec = vals / d
@@ -223,7 +249,7 @@ def test_round_trip_exactly_representable(fmt):
 
 def test_f16_output_is_one_rne_of_f32():
     # random blocks plus overflow cases: fp16 max d with extreme codes -> +-inf
-    for fmt in ("q4_0", "q4_1", "q8_0"):
+    for fmt in ("q4_0", "q4_1", "q8_0", "q5_0", "q5_1"):
         w = synth.quant_matrix(fmt, 8, 256, seed=99, tensor_id=1, d_range=(1e-3, 2e-2))
         f32 = oracle.dequantize_f32(fmt, w, 8, 256)
         f16 = oracle.dequantize_f16(fmt, w, 8, 256)
@@ -246,7 +272,7 @@ def test_f16_output_is_one_rne_of_f32():
 # products
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0", "q5_0", "q5_1"])
 def test_dot_matches_numpy_fp64_matmul(fmt):
     m, k, n = 13, 320, 3
     w = synth.quant_matrix(fmt, m, k, seed=5, tensor_id=2, d_range=(1e-3, 2e-2))
@@ -258,7 +284,7 @@ def test_dot_matches_numpy_fp64_matmul(fmt):
     np.testing.assert_allclose(s, np.abs(X) @ np.abs(W).T, rtol=1e-13)
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0", "q5_0", "q5_1"])
 def test_dot_unit_vectors_give_columns(fmt):
     m, k = 5, 96
     w = synth.quant_matrix(fmt, m, k, seed=6, tensor_id=2, d_range=(1e-3, 2e-2))
@@ -334,6 +360,39 @@ def test_mistakes_are_caught_by_pins():
     mul_form = dz * (np.float32(zb[2] & 15) - np.float32(8))
     assert np.signbit(mul_form)          # the other order gives -0.0 ...
     assert not np.signbit(oracle.dequantize_f32("q4_0", zb, 1, 32)[0, 0])  # ... the oracle +0.0
+
+
+def test_q5_mistakes_are_caught_by_pins():
+    """Planted Q5 layout mistakes (on the CPU, in a copy of the decode steps)
+    are rejected by the hand-worked blocks: qh read big-endian, qh bits in
+    reversed order, the high bit dropped, and the d*q + (-16*d) order (sign of
+    zero)."""
+    g = {b["name"]: b for b in _golden()["blocks"]}
+
+    def decode(raw, qh_of, use_high=True):
+        d = np.float32(raw[:2].view("<u2").view(np.float16)[0])
+        qh = qh_of(raw[2:6])
+        qs = raw[6:22]
+        low = np.concatenate([qs & 15, qs >> 4]).astype(np.int64)
+        hb = np.array([(qh >> t) & 1 for t in range(32)], dtype=np.int64) if use_high else 0
+        return (low | (hb << 4)).astype(np.float32) - np.float32(16), d
+
+    le = lambda b: int.from_bytes(bytes(b), "little")
+    be = lambda b: int.from_bytes(bytes(b), "big")
+    rev = lambda b: int(format(le(b), "032b")[::-1], 2)
+    blk = _hex_bytes(g["q5_0_bit_order"]["bytes_hex"])
+    want = np.array([float(v) for v in g["q5_0_bit_order"]["values"]], dtype=np.float32)
+    c, d = decode(blk, le)
+    assert np.array_equal(c * d, want)                  # the layout as read
+    for qh_of, hi in ((be, True), (rev, True), (le, False)):
+        c, d = decode(blk, qh_of, hi)
+        assert not np.array_equal(c * d, want)
+    zb = _hex_bytes(g["q5_0_sign_of_zero"]["bytes_hex"])
+    c, dz = decode(zb, le)
+    assert np.signbit((c * dz)[0])                       # (q - 16) * d: -0.0 ...
+    alt = (c + np.float32(16)) * dz + np.float32(-16) * dz
+    assert not np.signbit(alt[0])                        # ... the other order +0.0
+    assert np.signbit(oracle.dequantize_f32("q5_0", zb, 1, 32)[0, 0])
 
 
 # ---------------------------------------------------------------------------
@@ -483,7 +542,7 @@ def test_x8_hand_worked_dots():
             assert list(s[0]) == [float(Fraction(v)) for v in case["s"]]
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0", "q5_0", "q5_1"])
 def test_x8_dot_is_the_product_with_quantized_activations(fmt):
     """dot_x8 equals the plain product with x^ = d * q (a different route
     through the oracle: the fp64 product of dequantized weights and
