@@ -1,4 +1,5 @@
-// dequant.hip - standalone dequantize of ggml Q4_0 / Q4_1 / Q8_0 to fp32 / fp16.
+// dequant.hip - standalone dequantize of ggml Q4_0 / Q4_1 / Q8_0 / Q5_0 / Q5_1
+// to fp32 / fp16.
 //
 // Follows the dequantize_block_q4_0 / _q4_1 and dequantize_block_q8_0_f16
 // kernels of the "llama_cpp 0.12.1 -> 0.12.2" ggml-cuda.cu diff in what is
@@ -38,18 +39,28 @@ __device__ __forceinline__ void decode4(const uint8_t *lds, int boff, int j0, fl
         uint32_t q = lds_u32_a2(lds, boff + F::kQsOffset + (j0 & 15));
         if (j0 >= 16) q >>= 4;
         q &= 0x0F0F0F0Fu;
-        const float off = (FMT == QK_Q4_0) ? -8.0f * d : h2f(lds_u16(lds, boff + 2));
-        v[0] = d * ubyte_f<0>(q) + off;
-        v[1] = d * ubyte_f<1>(q) + off;
-        v[2] = d * ubyte_f<2>(q) + off;
-        v[3] = d * ubyte_f<3>(q) + off;
+        if constexpr (FMT == QK_Q5_0 || FMT == QK_Q5_1)
+            q |= q5_high4((lds_u32_a2(lds, boff + Format<FMT>::kQhOffset) >> j0) & 0xFu);
+        if constexpr (FMT == QK_Q5_0) {
+            // (q - 16) * d: the difference is exact, the product rounds once
+            v[0] = (ubyte_f<0>(q) - 16.0f) * d;
+            v[1] = (ubyte_f<1>(q) - 16.0f) * d;
+            v[2] = (ubyte_f<2>(q) - 16.0f) * d;
+            v[3] = (ubyte_f<3>(q) - 16.0f) * d;
+        } else {
+            const float off = (FMT == QK_Q4_0) ? -8.0f * d : h2f(lds_u16(lds, boff + 2));
+            v[0] = d * ubyte_f<0>(q) + off;
+            v[1] = d * ubyte_f<1>(q) + off;
+            v[2] = d * ubyte_f<2>(q) + off;
+            v[3] = d * ubyte_f<3>(q) + off;
+        }
     }
 }
 
 // A workgroup walks chunks of 128 blocks c, c + gridDim.x, ... and requests
 // the next chunk's bytes into registers before it writes the current chunk's
 // outputs, so the reads of one chunk overlap the writes of the one before.
-// Chunks are 2304 / 2560 / 4352 bytes, multiples of 16, so every 16-byte
+// Chunks are 2304 / 2560 / 4352 / 2816 / 3072 bytes, multiples of 16, so every 16-byte
 // piece of every chunk has the alignment of w.  A16: w 16-byte aligned, one
 // 16-byte load per piece.  Otherwise (w 2- or 4-byte aligned) a piece is read
 // as the four dwords from the 4-byte boundary at or below it, plus for a
@@ -142,7 +153,13 @@ __global__ __launch_bounds__(kDqThreads) void dequant_loop_kernel(
                 decode4<FMT>(lds, (g >> 2) * F::kBytes, (g & 3) * 8 + 4, v + 4);
                 uint16_t h[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) h[i] = f2h(v[i]);
+                for (int i = 0; i < 8; ++i) {
+                    // opaque: the compiler otherwise folds a product and its
+                    // conversion into v_fma_mix*_f16 with a +0 addend, which
+                    // turns a -0 product (Q5_0 with q = 16, d < 0) into +0
+                    asm volatile("" : "+v"(v[i]));
+                    h[i] = f2h(v[i]);
+                }
                 if (ALIGNED_OUT) {
                     __builtin_nontemporal_store(
                         u32x4v_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16),
@@ -191,6 +208,8 @@ int launch_dequantize(int fmt, const void *w, int64_t nblocks, int out_dtype, vo
     case QK_Q4_0: return dispatch_dequant<QK_Q4_0>(wb, nblocks, out_dtype, out, stream);
     case QK_Q4_1: return dispatch_dequant<QK_Q4_1>(wb, nblocks, out_dtype, out, stream);
     case QK_Q8_0: return dispatch_dequant<QK_Q8_0>(wb, nblocks, out_dtype, out, stream);
+    case QK_Q5_0: return dispatch_dequant<QK_Q5_0>(wb, nblocks, out_dtype, out, stream);
+    case QK_Q5_1: return dispatch_dequant<QK_Q5_1>(wb, nblocks, out_dtype, out, stream);
     default: return QK_ERR_UNSUPPORTED;
     }
 }

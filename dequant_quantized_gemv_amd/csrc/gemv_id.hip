@@ -9,6 +9,8 @@ int gemv_expert(int fmt, const GemvExpert &e, bool fast, hipStream_t stream) {
     case QK_Q4_0: return gemv_expert_fmt<QK_Q4_0>(e, fast, stream);
     case QK_Q4_1: return gemv_expert_fmt<QK_Q4_1>(e, fast, stream);
     case QK_Q8_0: return gemv_expert_fmt<QK_Q8_0>(e, fast, stream);
+    case QK_Q5_0: return gemv_expert_fmt<QK_Q5_0>(e, fast, stream);
+    case QK_Q5_1: return gemv_expert_fmt<QK_Q5_1>(e, fast, stream);
     default: return QK_ERR_INVALID_ARG;
     }
 }

@@ -9,8 +9,9 @@
 // on the page; this one is designed for gfx950.
 //
 // Work split.  A workgroup of WPG waves owns a group of consecutive rows.  K
-// is walked in chunks of pairs of blocks: a pair of Q4_0 / Q4_1 / Q8_0 blocks
-// is 36 / 40 / 68 bytes, a whole number of dwords, so with an even block count
+// is walked in chunks of pairs of blocks: a pair of Q4_0 / Q4_1 / Q8_0 /
+// Q5_0 / Q5_1 blocks is 36 / 40 / 68 / 44 / 48 bytes, a whole number of
+// dwords, so with an even block count
 // per row every pair starts on 4 bytes and comes straight into registers with
 // dword-aligned 16-byte loads (plain loads: streaming hints measured slower on
 // this chip).  For rows of more than 32 pairs a wave owns RWV rows and lane p
@@ -38,6 +39,8 @@
 //    convert and is multiplied by x in one FMA; the block's sum is scaled by d.
 //  * Q4_1: the exact fp32 weight d*q + m is rebuilt per element (one FMA,
 //    exact because d*q is exact) and multiplied into the accumulator.
+//  * Q5_0 / Q5_1: as Q4_0 / Q4_1 with 5-bit codes, bit 4 of each taken from
+//    the block's qh word (q - 16 is exact in fp16 as well).
 // Reduction: a 64-lane DPP butterfly per (row, column); lane 0 writes y.
 #pragma once
 
@@ -59,6 +62,13 @@ template <int FMT> struct Pair;
 template <> struct Pair<QK_Q4_0> { static constexpr int kDwords = 9; };
 template <> struct Pair<QK_Q4_1> { static constexpr int kDwords = 10; };
 template <> struct Pair<QK_Q8_0> { static constexpr int kDwords = 17; };
+template <> struct Pair<QK_Q5_0> { static constexpr int kDwords = 11; };
+template <> struct Pair<QK_Q5_1> { static constexpr int kDwords = 12; };
+
+// Formats whose weight is d*q + m (rebuilt exactly in fp32 per element).
+template <int FMT> constexpr bool kHasM = FMT == QK_Q4_1 || FMT == QK_Q5_1;
+// Formats whose block sum is scaled by d once (codes exact as small numbers).
+template <int FMT> constexpr bool kNibbleOffset = FMT == QK_Q4_0 || FMT == QK_Q5_0;
 
 // acc + (fp16 in the low / high half of h) * x, fused, one rounding.
 __device__ __forceinline__ float fma_mix_lo(uint32_t h, float x, float acc) {
@@ -161,23 +171,53 @@ __device__ __forceinline__ void load_pair_shift(const uint8_t *__restrict__ p,
     for (int i = 0; i < N - 1; ++i) v[i] = __builtin_amdgcn_alignbyte(d[i + 1], d[i], sh);
 }
 
-// fp16 bits of d (and m) of block b of the pair.
+// fp16 bits of d (and m) of block b of the pair.  Block 1 starts at byte 18
+// (Q4_0), 20 (Q4_1), 34 (Q8_0), 22 (Q5_0) or 24 (Q5_1).
 template <int FMT>
 __device__ __forceinline__ uint32_t pair_d(const uint32_t (&v)[Pair<FMT>::kDwords], int b) {
     if constexpr (FMT == QK_Q4_0) return b == 0 ? (v[0] & 0xFFFFu) : (v[4] >> 16);
     if constexpr (FMT == QK_Q4_1) return b == 0 ? (v[0] & 0xFFFFu) : (v[5] & 0xFFFFu);
+    if constexpr (FMT == QK_Q5_0) return b == 0 ? (v[0] & 0xFFFFu) : (v[5] >> 16);
+    if constexpr (FMT == QK_Q5_1) return b == 0 ? (v[0] & 0xFFFFu) : (v[6] & 0xFFFFu);
     return b == 0 ? (v[0] & 0xFFFFu) : (v[8] >> 16);
 }
-__device__ __forceinline__ uint32_t pair_m_q41(const uint32_t (&v)[10], int b) {
-    return b == 0 ? (v[0] >> 16) : (v[5] >> 16);
+template <int FMT>
+__device__ __forceinline__ uint32_t pair_m(const uint32_t (&v)[Pair<FMT>::kDwords], int b) {
+    static_assert(kHasM<FMT>, "d*q + m formats");
+    if constexpr (FMT == QK_Q4_1) return b == 0 ? (v[0] >> 16) : (v[5] >> 16);
+    return b == 0 ? (v[0] >> 16) : (v[6] >> 16);
 }
 
-// Quant word i of block b (Q4: i < 4, bytes 4i..4i+3; Q8: i < 8).
+// Quant word i of block b (Q4 / Q5: i < 4, bytes 4i..4i+3 of qs; Q8: i < 8).
 template <int FMT>
 __device__ __forceinline__ uint32_t pair_qs(const uint32_t (&v)[Pair<FMT>::kDwords], int b, int i) {
     if constexpr (FMT == QK_Q4_0) return b == 0 ? shift2(v[i], v[i + 1]) : v[5 + i];
     if constexpr (FMT == QK_Q4_1) return b == 0 ? v[1 + i] : v[6 + i];
+    if constexpr (FMT == QK_Q5_0) return b == 0 ? shift2(v[1 + i], v[2 + i]) : v[7 + i];
+    if constexpr (FMT == QK_Q5_1) return b == 0 ? v[2 + i] : v[8 + i];
     return b == 0 ? shift2(v[i], v[i + 1]) : v[9 + i];
+}
+
+// Q5: the qh word of block b (bit t = bit 4 of code t).
+template <int FMT>
+__device__ __forceinline__ uint32_t pair_qh(const uint32_t (&v)[Pair<FMT>::kDwords], int b) {
+    if constexpr (FMT == QK_Q5_0) return b == 0 ? shift2(v[0], v[1]) : v[6];
+    else return b == 0 ? v[1] : v[7];
+}
+
+// The codes of quant word i of block b as bytes: lo = elements 4i..4i+3,
+// hi = elements 16+4i..16+4i+3 (Q4: 0..15; Q5: 0..31 with bit 4 from qh).
+template <int FMT>
+__device__ __forceinline__ void pair_codes(const uint32_t (&v)[Pair<FMT>::kDwords], int b, int i,
+                                           uint32_t &lo, uint32_t &hi) {
+    const uint32_t qw = pair_qs<FMT>(v, b, i);
+    lo = qw & 0x0F0F0F0Fu;
+    hi = (qw >> 4) & 0x0F0F0F0Fu;
+    if constexpr (FMT == QK_Q5_0 || FMT == QK_Q5_1) {
+        const uint32_t qh = pair_qh<FMT>(v, b);
+        lo |= q5_high4((qh >> (4 * i)) & 0xFu);
+        hi |= q5_high4((qh >> (16 + 4 * i)) & 0xFu);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -228,6 +268,26 @@ __device__ __forceinline__ float group_q8_0_split(uint32_t lo, uint32_t hi, cons
     return s;
 }
 
+// Q5_0 group: sum over the 8 elements of (q - 16) * x, added to s; lo / hi
+// hold the 5-bit codes of elements 4i..4i+3 and 16+4i..16+4i+3 as bytes
+// (1024 + q - 1040 = q - 16, exact in fp16).
+__device__ __forceinline__ float group_q5_0(uint32_t lo, uint32_t hi, const float4 &xa, const float4 &xb,
+                                            float s) {
+    const uint32_t l01 = pk_add_f16(bytes_to_f16_lo(lo), -1040.0f);
+    const uint32_t l23 = pk_add_f16(bytes_to_f16_hi(lo), -1040.0f);
+    const uint32_t h01 = pk_add_f16(bytes_to_f16_lo(hi), -1040.0f);
+    const uint32_t h23 = pk_add_f16(bytes_to_f16_hi(hi), -1040.0f);
+    s = fma_mix_lo(l01, xa.x, s);
+    s = fma_mix_hi(l01, xa.y, s);
+    s = fma_mix_lo(l23, xa.z, s);
+    s = fma_mix_hi(l23, xa.w, s);
+    s = fma_mix_lo(h01, xb.x, s);
+    s = fma_mix_hi(h01, xb.y, s);
+    s = fma_mix_lo(h23, xb.z, s);
+    s = fma_mix_hi(h23, xb.w, s);
+    return s;
+}
+
 // Q4_1 group: exact weights d*q + m times x, added to acc.
 __device__ __forceinline__ float group_q4_1(uint32_t qw, float d, float mm, const float4 &xa,
                                             const float4 &xb, float a) {
@@ -268,7 +328,7 @@ __device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDw
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         if (!FAST && b == 1 && !second) break;
-        if constexpr (FMT == QK_Q4_1) {
+        if constexpr (kHasM<FMT>) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float4 xa[NC], xb[NC];
@@ -281,10 +341,9 @@ __device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDw
                 for (int r = 0; r < RWV; ++r) {
                     if (FAST || r < nrows) {  // fast path: rows clamped, stores guarded
                         const float d = h2f(pair_d<FMT>(v[r], b));
-                        const float mm = h2f(pair_m_q41(v[r], b));
-                        const uint32_t qw = pair_qs<FMT>(v[r], b, i);
-                        const uint32_t lo = qw & 0x0F0F0F0Fu;
-                        const uint32_t hi = (qw >> 4) & 0x0F0F0F0Fu;
+                        const float mm = h2f(pair_m<FMT>(v[r], b));
+                        uint32_t lo, hi;
+                        pair_codes<FMT>(v[r], b, i, lo, hi);
                         const float w0 = wval(d, ubyte_f<0>(lo), mm), w1 = wval(d, ubyte_f<1>(lo), mm);
                         const float w2 = wval(d, ubyte_f<2>(lo), mm), w3 = wval(d, ubyte_f<3>(lo), mm);
                         const float w4 = wval(d, ubyte_f<0>(hi), mm), w5 = wval(d, ubyte_f<1>(hi), mm);
@@ -321,15 +380,19 @@ __device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDw
 #pragma unroll
                 for (int j = 0; j < NC; ++j) {
                     xa[j] = x_lds(xs, xp, j, el + 32 * b + 4 * i);
-                    if (FMT == QK_Q4_0) xb[j] = x_lds(xs, xp, j, el + 32 * b + 16 + 4 * i);
+                    if (kNibbleOffset<FMT>) xb[j] = x_lds(xs, xp, j, el + 32 * b + 16 + 4 * i);
                 }
 #pragma unroll
                 for (int r = 0; r < RWV; ++r) {
                     if (FAST || r < nrows) {  // fast path: rows clamped, stores guarded
+                        uint32_t lo = 0, hi = 0;
+                        if constexpr (FMT == QK_Q5_0) pair_codes<FMT>(v[r], b, i, lo, hi);
 #pragma unroll
                         for (int j = 0; j < NC; ++j) {
                             if constexpr (FMT == QK_Q4_0) {
                                 s[r][j] = group_q4_0(pair_qs<FMT>(v[r], b, i), xa[j], xb[j], s[r][j]);
+                            } else if constexpr (FMT == QK_Q5_0) {
+                                s[r][j] = group_q5_0(lo, hi, xa[j], xb[j], s[r][j]);
                             } else if (b == 0) {
                                 s[r][j] = group_q8_0_split(v[r][i], v[r][i + 1], xa[j], s[r][j]);
                             } else {
@@ -412,8 +475,8 @@ __device__ __forceinline__ void x8_block(const f32x4_t (&v)[8], uint8_t *codes, 
 // Integer-dot products of one wave's RWV rows with this lane's pair (pair pw
 // of the window) against 8-bit activations, added to acc: per block and
 // column, eight 4-way int8 dot products (exact), then one scaled add,
-// d_w * d_x * I (Q4_0: codes taken as q - 8 through the code sum), and for
-// Q4_1 also m_w * d_x * (sum of the activation codes).
+// d_w * d_x * I (Q4_0 / Q5_0: codes taken as q - 8 / q - 16 through the code
+// sum), and for Q4_1 / Q5_1 also m_w * d_x * (sum of the activation codes).
 template <int FMT, int NC, int RWV, bool FAST>
 __device__ __forceinline__ void pair_dot_x8(const uint32_t (&v)[RWV][Pair<FMT>::kDwords], int nrows,
                                             bool second, const uint8_t *xq, int pw,
@@ -427,16 +490,15 @@ __device__ __forceinline__ void pair_dot_x8(const uint32_t (&v)[RWV][Pair<FMT>::
 #pragma unroll
         for (int r = 0; r < RWV; ++r) {
             dw[r] = h2f(pair_d<FMT>(v[r], b));
-            if constexpr (FMT == QK_Q4_1) mw[r] = h2f(pair_m_q41(v[r], b));
+            if constexpr (kHasM<FMT>) mw[r] = h2f(pair_m<FMT>(v[r], b));
             else mw[r] = 0.0f;
 #pragma unroll
             for (int i = 0; i < NW; ++i) {
-                const uint32_t qw = pair_qs<FMT>(v[r], b, i);
                 if constexpr (FMT == QK_Q8_0) {
-                    wq[r][i] = qw;
+                    wq[r][i] = pair_qs<FMT>(v[r], b, i);
                 } else {
-                    wq[r][i] = qw & 0x0F0F0F0Fu;             // elements 4i..4i+3
-                    wq[r][4 + i] = (qw >> 4) & 0x0F0F0F0Fu;  // elements 16+4i..16+4i+3
+                    // elements 4i..4i+3 and 16+4i..16+4i+3
+                    pair_codes<FMT>(v[r], b, i, wq[r][i], wq[r][4 + i]);
                 }
             }
         }
@@ -458,8 +520,9 @@ __device__ __forceinline__ void pair_dot_x8(const uint32_t (&v)[RWV][Pair<FMT>::
                     for (int i = 0; i < 8; ++i)
                         isum = __builtin_amdgcn_sdot4((int)wq[r][i], (int)xc[i], isum, false);
                     if constexpr (FMT == QK_Q4_0) isum -= 8 * qs;
+                    if constexpr (FMT == QK_Q5_0) isum -= 16 * qs;
                     acc[r][j] += (float)isum * (dw[r] * dx);
-                    if constexpr (FMT == QK_Q4_1) acc[r][j] += (float)qs * (mw[r] * dx);
+                    if constexpr (kHasM<FMT>) acc[r][j] += (float)qs * (mw[r] * dx);
                 }
             }
             if constexpr (NC >= 3) asm volatile("" ::: "memory");
@@ -963,16 +1026,16 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
 // 11.4 -> 10.6 us at 2 columns, 15.6 -> 14.0 us at 3; at 4096 rows it loses
 // (5.5 -> 6.3 and 7.1 -> 7.6 us).
 template <int FMT, int NC, int SUB, bool FAST, bool X8 = false, bool R2 = false> struct GemvShape {
-    static_assert(!R2 || (NC <= 3 && SUB == 0 && !X8 && (NC == 1 || (FMT != QK_Q8_0 && (FMT != QK_Q4_1 || FAST)))),
+    static_assert(!R2 || (NC <= 3 && SUB == 0 && !X8 && (NC == 1 || (FMT != QK_Q8_0 && (!kHasM<FMT> || FAST)))),
                   "two rows per wave: up to 3 columns, full-wave rows");
-    static constexpr bool kWideQ41Generic = FMT == QK_Q4_1 && NC > 4 && !FAST;
+    static constexpr bool kWideQ41Generic = kHasM<FMT> && NC > 4 && !FAST;
     static constexpr bool kX8Q8Wide = X8 && FMT == QK_Q8_0 && NC >= 4 && SUB == 0;
     static constexpr int kRWV =
         (R2 || kX8Q8Wide) ? 2 : (NC >= 4 && FMT != QK_Q8_0 && !kWideQ41Generic ? 2 : 1);
     static constexpr int kWPG =
         SUB > 0 ? QK_GEMV_SHORT_WPG
                 : (kX8Q8Wide ? 8
-                             : (NC <= 4 ? 8 : (FMT == QK_Q4_1 ? (FAST ? 12 : 8) : (FMT == QK_Q4_0 ? 8 : 4))));
+                             : (NC <= 4 ? 8 : (kHasM<FMT> ? (FAST ? 12 : 8) : (FMT == QK_Q8_0 ? 4 : 8))));
     static constexpr int kRowsPerGroup = SUB == kSubMixed ? kWPG : kWPG * (kRWV << SUB);  // (mixed: per problem)
 };
 
@@ -1050,7 +1113,7 @@ int gemv_table_sub(GemvArgs &a, bool fast, hipStream_t stream) {
         for (int i = 0; i < a.count; ++i) rows += a.item[i].m;
         if (rows > (NC == 1 ? 64 : 32) * (int64_t)device_cus()) {
             if (fast) return gemv_table_run<FMT, NC, SUB, true, X8, true>(a, stream);
-            if constexpr (NC == 1 || FMT != QK_Q4_1) return gemv_table_run<FMT, NC, SUB, false, X8, true>(a, stream);
+            if constexpr (NC == 1 || !kHasM<FMT>) return gemv_table_run<FMT, NC, SUB, false, X8, true>(a, stream);
         }
     }
     if (fast) return gemv_table_run<FMT, NC, SUB, true, X8>(a, stream);
@@ -1102,6 +1165,8 @@ int gemv_table(int fmt, GemvArgs &a, bool fast, hipStream_t stream) {
     case QK_Q4_0: return gemv_table_fmt<QK_Q4_0, NC, false>(a, fast, stream);
     case QK_Q4_1: return gemv_table_fmt<QK_Q4_1, NC, false>(a, fast, stream);
     case QK_Q8_0: return gemv_table_fmt<QK_Q8_0, NC, false>(a, fast, stream);
+    case QK_Q5_0: return gemv_table_fmt<QK_Q5_0, NC, false>(a, fast, stream);
+    case QK_Q5_1: return gemv_table_fmt<QK_Q5_1, NC, false>(a, fast, stream);
     default: return QK_ERR_INVALID_ARG;
     }
 }
@@ -1112,6 +1177,8 @@ int gemv_table_x8(int fmt, GemvArgs &a, bool fast, hipStream_t stream) {
     case QK_Q4_0: return gemv_table_fmt<QK_Q4_0, NC, true>(a, fast, stream);
     case QK_Q4_1: return gemv_table_fmt<QK_Q4_1, NC, true>(a, fast, stream);
     case QK_Q8_0: return gemv_table_fmt<QK_Q8_0, NC, true>(a, fast, stream);
+    case QK_Q5_0: return gemv_table_fmt<QK_Q5_0, NC, true>(a, fast, stream);
+    case QK_Q5_1: return gemv_table_fmt<QK_Q5_1, NC, true>(a, fast, stream);
     default: return QK_ERR_INVALID_ARG;
     }
 }

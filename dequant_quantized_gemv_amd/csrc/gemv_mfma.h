@@ -49,10 +49,10 @@ constexpr int kMfPitch = kGvWindow + kGvWindow / 16 + 16;
 constexpr int kMfMaxK = kGvWindow;
 
 // The fp32 weights of quant word i of block b of a pair, the dequantize
-// definition's value (exact for Q4_0 and Q8_0, one rounding of d*q + m for
-// Q4_1): Q4 words give elements 4i..4i+3 (low nibbles) in w[0..3] and
-// 16+4i..16+4i+3 (high nibbles) in w[4..7]; Q8_0 words give elements
-// 4i..4i+3 in w[0..3].
+// definition's value (exact for Q4_0, Q5_0 and Q8_0, one rounding of
+// d*q + m for Q4_1 and Q5_1): Q4 / Q5 words give elements 4i..4i+3 (low
+// nibbles, plus bit 4 from qh for Q5) in w[0..3] and 16+4i..16+4i+3 (high
+// nibbles) in w[4..7]; Q8_0 words give elements 4i..4i+3 in w[0..3].
 template <int FMT>
 __device__ __forceinline__ void word_weights(const uint32_t (&v)[Pair<FMT>::kDwords], int b, int i,
                                              float d, float mm, float (&w)[8]) {
@@ -63,9 +63,8 @@ __device__ __forceinline__ void word_weights(const uint32_t (&v)[Pair<FMT>::kDwo
         w[2] = d * (float)(int8_t)(qw >> 16);
         w[3] = d * (float)(int8_t)(qw >> 24);
     } else {
-        const uint32_t qw = pair_qs<FMT>(v, b, i);
-        uint32_t lo = qw & 0x0F0F0F0Fu;
-        uint32_t hi = (qw >> 4) & 0x0F0F0F0Fu;
+        uint32_t lo, hi;
+        pair_codes<FMT>(v, b, i, lo, hi);
         // opaque, so each nibble converts with one byte-select convert
         // (v_cvt_f32_ubyte1..3) instead of a field extract and a convert
         asm volatile("" : "+v"(lo), "+v"(hi));
@@ -176,8 +175,11 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
             for (int bk = 0; bk < 2; ++bk) {
                 float d = h2f(pair_d<FMT>(cur, bk));
                 float mm = 0.0f;
-                if constexpr (FMT == QK_Q4_1) mm = h2f(pair_m_q41(cur, bk));
+                // (d*q + mm: exact for the offset formats, -8d and -16d
+                // being exact and (q - 8) d, (q - 16) d representable)
+                if constexpr (kHasM<FMT>) mm = h2f(pair_m<FMT>(cur, bk));
                 else if constexpr (FMT == QK_Q4_0) mm = -8.0f * d;
+                else if constexpr (FMT == QK_Q5_0) mm = -16.0f * d;
                 d = valid ? d : 0.0f;
                 mm = valid ? mm : 0.0f;
                 constexpr int NW = FMT == QK_Q8_0 ? 8 : 4;  // quant words per block

@@ -6,6 +6,10 @@
 //         element j+16 (high nibble); value d*q + (-8*d).
 //   Q4_1: d, m (fp16) then 16 quant bytes as above; value d*q + m.
 //   Q8_0: d (fp16) then 32 int8; value d*q.
+//   Q5_0: d, qh (4 bytes, bit t = bit 4 of code t), 16 quant bytes as Q4_0;
+//         value (q - 16) * d.  Q5_1: d, m, qh, 16 quant bytes; value d*q + m.
+//         (Named only in the diff's to_fp16 / to_fp32 dispatch; ggml's block
+//         format.)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,12 +25,27 @@ template <int FMT> struct Format;
 template <> struct Format<QK_Q4_0> { static constexpr int kBytes = 18, kQsOffset = 2, kQsBytes = 16; };
 template <> struct Format<QK_Q4_1> { static constexpr int kBytes = 20, kQsOffset = 4, kQsBytes = 16; };
 template <> struct Format<QK_Q8_0> { static constexpr int kBytes = 34, kQsOffset = 2, kQsBytes = 32; };
+template <> struct Format<QK_Q5_0> {
+    static constexpr int kBytes = 22, kQhOffset = 2, kQsOffset = 6, kQsBytes = 16;
+};
+template <> struct Format<QK_Q5_1> {
+    static constexpr int kBytes = 24, kQhOffset = 4, kQsOffset = 8, kQsBytes = 16;
+};
+
+// Bit 4 of four consecutive Q5 codes: bits b (0..3) of `four` -> bit 4 of
+// byte b (the multiply places bit b at bit 8b, with no carries between the
+// shifted copies, which sit 7 bits apart).
+__device__ __forceinline__ uint32_t q5_high4(uint32_t four) {
+    return ((four * 0x00204081u) & 0x01010101u) << 4;
+}
 
 inline int block_bytes_host(int fmt) {
     switch (fmt) {
     case QK_Q4_0: return Format<QK_Q4_0>::kBytes;
     case QK_Q4_1: return Format<QK_Q4_1>::kBytes;
     case QK_Q8_0: return Format<QK_Q8_0>::kBytes;
+    case QK_Q5_0: return Format<QK_Q5_0>::kBytes;
+    case QK_Q5_1: return Format<QK_Q5_1>::kBytes;
     default: return 0;
     }
 }

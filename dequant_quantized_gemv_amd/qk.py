@@ -13,11 +13,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqk.so")
 
 # enum qk_format / qk_dtype / qk_status (include/qk.h)
-QK_Q4_0, QK_Q4_1, QK_Q8_0 = 1, 2, 3
+QK_Q4_0, QK_Q4_1, QK_Q8_0, QK_Q5_0, QK_Q5_1 = 1, 2, 3, 4, 5
 QK_F32, QK_F16 = 0, 1
 QK_OK, QK_ERR_INVALID_ARG, QK_ERR_UNSUPPORTED, QK_ERR_ALIGNMENT, QK_ERR_LAUNCH = 0, 1, 2, 3, 4
 
-FORMATS = {"q4_0": QK_Q4_0, "q4_1": QK_Q4_1, "q8_0": QK_Q8_0}
+FORMATS = {"q4_0": QK_Q4_0, "q4_1": QK_Q4_1, "q8_0": QK_Q8_0, "q5_0": QK_Q5_0, "q5_1": QK_Q5_1}
 SYMBOLS = ("qk_block_bytes", "qk_row_bytes", "qk_status_string", "qk_version",
            "qk_dequantize", "qk_mul_mat_vec", "qk_mul_mat_vec_x8", "qk_mul_mat_vec_batched",
            "qk_mul_mat_vec_id", "qk_mul_mat")
@@ -156,7 +156,7 @@ def qk_mul_mat(fmt, w_ptr, m, k, x_ptr, n, ldx, y_ptr, ldy, stream=0):
 # mismatch raises TypeError or ValueError and enqueues nothing.
 # ---------------------------------------------------------------------------
 
-_BLOCK_BYTES = {QK_Q4_0: 18, QK_Q4_1: 20, QK_Q8_0: 34}
+_BLOCK_BYTES = {QK_Q4_0: 18, QK_Q4_1: 20, QK_Q8_0: 34, QK_Q5_0: 22, QK_Q5_1: 24}
 
 
 def _weight_check(fmt, w, rows, k):

@@ -8,11 +8,19 @@
  *   QK_Q4_0  d[2] qs[16]       18 bytes  w = d*q + (-8*d),  q = nibble 0..15
  *   QK_Q4_1  d[2] m[2] qs[16]  20 bytes  w = d*q + m
  *   QK_Q8_0  d[2] qs[32]       34 bytes  w = d*q,           q = int8
+ *   QK_Q5_0  d[2] qh[4] qs[16] 22 bytes  w = (q - 16) * d,  q = 0..31
+ *   QK_Q5_1  d[2] m[2] qh[4] qs[16]  24 bytes  w = d*q + m, q = 0..31
  * For Q4_x, quant byte j holds element j in its low nibble and element j+16 in
  * its high nibble.  Source: "llama_cpp 0.12.1 -> 0.12.2" diff of ggml-cuda.cu
  * (diffend, page 4), hunks adding dequantize_block_q4_0, dequantize_block_q4_1
  * and dequantize_block_q8_0_f16; the row launchers dequantize_row_q4_*_cuda
  * give the 32-weight block (nb32 = k/32).
+ * Q5_x: the same diff names these formats only in ggml_get_to_fp16_cuda /
+ * ggml_get_to_fp32_cuda (dequantize_block_cuda with dequantize_q5_0 / _q5_1);
+ * their layout is not printed there and follows ggml's block format: the low
+ * four bits of each code as in Q4_x, bit 4 of code t in bit t of qh (a
+ * little-endian 32-bit word).  Q5_0's (q - 16) * d makes q = 16 with d < 0
+ * a -0.0 (Q4_0's form gives +0.0).
  *
  * Matrix layout follows ggml (ne0 is the contiguous dimension):
  *   W  m rows of k weights (row-major blocks as above);
@@ -46,7 +54,9 @@ extern "C" {
 enum qk_format {
     QK_Q4_0 = 1,
     QK_Q4_1 = 2,
-    QK_Q8_0 = 3
+    QK_Q8_0 = 3,
+    QK_Q5_0 = 4,
+    QK_Q5_1 = 5
 };
 
 /* Output element types of qk_dequantize. */
@@ -66,7 +76,7 @@ enum qk_status {
     QK_ERR_LAUNCH = 4         /* the HIP runtime refused the kernel launch */
 };
 
-/* Bytes per 32-weight block: 18, 20 or 34; 0 for an unknown format. */
+/* Bytes per 32-weight block: 18, 20, 34, 22 or 24; 0 for an unknown format. */
 size_t qk_block_bytes(int fmt);
 
 /* Bytes of one row of k weights (k a multiple of 32); 0 on a bad argument. */
@@ -84,14 +94,15 @@ int qk_version(void);
  *   out[r*k + c] = W[r, c]   for r < rows, c < k.
  *
  * fp32: the value is computed in fp32 in the order shown in the format table
- * (multiply, then add; no fused multiply-add), which is exact for Q4_0 and
- * Q8_0 and one round-to-nearest-even for Q4_1.  Q4_0 with q = 8 gives +0.0.
+ * (multiply, then add; no fused multiply-add), which is exact for Q4_0, Q8_0
+ * and Q5_0 and one round-to-nearest-even for Q4_1 and Q5_1.  Q4_0 with q = 8
+ * gives +0.0; Q5_0 with q = 16 gives a zero with the sign of d.
  * fp16: one round-to-nearest-even of that fp32 value (overflow to +-inf,
  * subnormals kept).
  * Source: dequantize_block_q4_0 / _q4_1 / _q8_0_f16 hunks and the
  * ggml_get_to_fp16_cuda / ggml_get_to_fp32_cuda dispatch in the same diff.
  *
- *   fmt        QK_Q4_0, QK_Q4_1 or QK_Q8_0
+ *   fmt        QK_Q4_0, QK_Q4_1, QK_Q8_0, QK_Q5_0 or QK_Q5_1
  *   w          rows*k/32 blocks; 2-byte aligned
  *   rows, k    rows >= 0, k >= 0, k % 32 == 0
  *   out_dtype  QK_F32 or QK_F16
@@ -242,6 +253,8 @@ int qk_mul_mat_vec_id(int fmt, const void *w, int64_t n_experts, int64_t expert_
  *   y[j*ldy + i] = sum_c f16(W[i, c]) * x[j*ldx + c]   for i < m, j < n
  *
  * f16(W) is the qk_dequantize fp16 value (one RNE of the fp32 weight).
+ * Formats QK_Q4_0, QK_Q4_1 and QK_Q8_0 (QK_Q5_0 / QK_Q5_1:
+ * QK_ERR_UNSUPPORTED, nothing enqueued).
  * Source: the dequantize-to-fp16 then GEMM path (ggml_get_to_fp16_cuda feeding
  * the BLAS mul_mat) and ggml_cuda_mul_mat's choice of a batched kernel when
  * the right operand has more than one column, in the same diff.

@@ -6,6 +6,16 @@ import os
 
 import numpy as np
 
+from dequant_quantized_gemv_amd import synth
+
+# formats of the dequantize and GEMV entry points; the GEMM takes the first three
+FMTS = ["q4_0", "q4_1", "q8_0", "q5_0", "q5_1"]
+GEMM_FMTS = ["q4_0", "q4_1", "q8_0"]
+# fp16 scale ranges of the synthetic weights per format
+D_RANGE = {"q4_0": synth.D_Q4, "q4_1": synth.D_Q4, "q8_0": synth.D_Q8, "q5_0": synth.D_Q8,
+           "q5_1": synth.D_Q8}
+BLOCK_BYTES = {"q4_0": 18, "q4_1": 20, "q8_0": 34, "q5_0": 22, "q5_1": 24}
+
 CANARY_BYTE = 0xA5
 GUARD = 4096  # bytes of guard band before and after every output
 
@@ -91,7 +101,7 @@ def oracle_rows(fn, fmt, w, m, k, *args, **kw):
     """fn(fmt, w_rows, rows, k, *args, **kw) -> (y (n, rows), s (n, rows)),
     called on row ranges of W in host threads (the oracle's C entry points
     release the GIL) and concatenated: the oracle's own result, row for row."""
-    rb = (k // 32) * {"q4_0": 18, "q4_1": 20, "q8_0": 34}[fmt]
+    rb = (k // 32) * BLOCK_BYTES[fmt]
     threads = host_threads()
     step = max(1, -(-m // (threads * 4)))
     chunks = [(r, min(m, r + step)) for r in range(0, m, step)]
@@ -105,7 +115,7 @@ def gemm_reference(oracle, fmt, w, m, k, xh):
     product of the oracle's fp32 weights with the exactly decoded
     activations, and S = |W| |X| (a matmul as a step; the product itself is
     pinned against the oracle's dot products on the CPU)."""
-    rb = (k // 32) * {"q4_0": 18, "q4_1": 20, "q8_0": 34}[fmt]
+    rb = (k // 32) * BLOCK_BYTES[fmt]
     threads = host_threads()
     step = max(1, -(-m // (threads * 4)))
     with ThreadPoolExecutor(threads) as ex:

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_binding_constants_match_header():
     enums = _declared_enums()
-    for name in ("QK_Q4_0", "QK_Q4_1", "QK_Q8_0", "QK_F32", "QK_F16", "QK_OK",
+    for name in ("QK_Q4_0", "QK_Q4_1", "QK_Q8_0", "QK_Q5_0", "QK_Q5_1", "QK_F32", "QK_F16", "QK_OK",
                  "QK_ERR_INVALID_ARG", "QK_ERR_UNSUPPORTED", "QK_ERR_ALIGNMENT",
                  "QK_ERR_LAUNCH"):
         assert getattr(qk, name) == enums[name], name
@@ -49,6 +49,9 @@ def test_sizes_and_strings(lib):
     assert qk.block_bytes("q4_0") == 18
     assert qk.block_bytes("q4_1") == 20
     assert qk.block_bytes("q8_0") == 34
+    assert qk.block_bytes("q5_0") == 22
+    assert qk.block_bytes("q5_1") == 24
+    assert qk.row_bytes("q5_1", 4096) == 128 * 24
     assert lib.qk_block_bytes(0) == 0 and lib.qk_block_bytes(99) == 0
     assert qk.row_bytes("q4_0", 4096) == 2304
     assert qk.row_bytes("q8_0", 11008) == 344 * 34
@@ -107,7 +110,9 @@ def test_mul_mat_vec_validation(args, want):
 
 
 @pytest.mark.parametrize("args,want", [
-    ((4, W, 8, 64, X, 16, 64, Y, 8), E.QK_ERR_UNSUPPORTED),
+    ((99, W, 8, 64, X, 16, 64, Y, 8), E.QK_ERR_UNSUPPORTED),
+    ((E.QK_Q5_0, W, 8, 64, X, 16, 64, Y, 8), E.QK_ERR_UNSUPPORTED),  # no Q5 GEMM
+    ((E.QK_Q5_1, W, 8, 64, X, 16, 64, Y, 8), E.QK_ERR_UNSUPPORTED),
     ((E.QK_Q4_0, W, 8, 40, X, 16, 64, Y, 8), E.QK_ERR_INVALID_ARG),
     ((E.QK_Q4_0, W, 8, 64, X, -3, 64, Y, 8), E.QK_ERR_INVALID_ARG),
     ((E.QK_Q4_0, W, 8, 64, X, 16, 32, Y, 8), E.QK_ERR_INVALID_ARG),

@@ -17,12 +17,10 @@ import pytest
 
 import oracle
 from dequant_quantized_gemv_amd import qk, synth
-from tests.gpu_helpers import Guarded, assert_within, to_dev_bytes, x_dev, torch
+from tests.gpu_helpers import D_RANGE, FMTS, Guarded, assert_within, to_dev_bytes, x_dev, torch
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["q4_0", "q4_1", "q8_0"]
-D_RANGE = {"q4_0": synth.D_Q4, "q4_1": synth.D_Q4, "q8_0": synth.D_Q8}
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_blocks.json")
 TOL = 1e-4
 CANARY32 = 0xA5A5A5A5

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from dequant_quantized_gemv_amd import qk, synth
-from tests.gpu_helpers import torch
+from tests.gpu_helpers import D_RANGE, FMTS, GEMM_FMTS, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,6 @@ def _replays_match(t, run, outs, replays=4):
             assert t.equal(o.view(t.int32), w.view(t.int32)), f"replay {r} differs"
 
 
-D_RANGE = {"q4_0": synth.D_Q4, "q4_1": synth.D_Q4, "q8_0": synth.D_Q8}
 
 # (m, k): a 128-multiple k (direct-to-LDS GEMM, whole activation windows), a
 # ragged k of 67 blocks (register-staged GEMM, partial window, odd pair
@@ -54,7 +53,7 @@ D_RANGE = {"q4_0": synth.D_Q4, "q4_1": synth.D_Q4, "q8_0": synth.D_Q8}
 SHAPES = [(300, 2048), (257, 32 * 67), (16403, 1024), (300, 640)]
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m,k", SHAPES, ids=[f"{m}x{k}" for m, k in SHAPES])
 def test_graph_gemv_batched_expert_x8_gemm_dequant(fmt, m, k):
     t = torch()
@@ -81,13 +80,15 @@ def test_graph_gemv_batched_expert_x8_gemm_dequant(fmt, m, k):
         qk.mul_mat_vec(fmt, w, m, k, x, y=y1)
         qk.mul_mat_vec(fmt, w, m, k, x1, y=y1n)
         qk.mul_mat_vec_x8(fmt, w, m, k, x, y=y2)
-        qk.mul_mat(fmt, w, m, k, xh, y=y3)
+        if fmt in GEMM_FMTS:
+            qk.mul_mat(fmt, w, m, k, xh, y=y3)
         qk.dequantize(fmt, w, m, k, "f32", out=yd)
         qk.dequantize(fmt, w, m, k, "f16", out=ydh)
         qk.mul_mat_vec_id(fmt, ws, ne, me, k, ids, x[:2], y=ye)
         qk.mul_mat_vec_batched(fmt, [(w, m, k, x), (ws, me, k, x)], ys=yb)
 
-    _replays_match(t, run, [y1, y1n, y2, y3, yd, ydh, ye] + yb)
+    outs = [y1, y1n, y2, yd, ydh, ye] + yb + ([y3] if fmt in GEMM_FMTS else [])
+    _replays_match(t, run, outs)
 
 
 def test_graph_empty_sum_fill():

@@ -16,13 +16,11 @@ import pytest
 
 import oracle
 from dequant_quantized_gemv_amd import qk, synth
-from tests.gpu_helpers import (Guarded, assert_within, gemm_reference, oracle_rows, to_dev_bytes,
-                               x_dev, torch)
+from tests.gpu_helpers import (D_RANGE, FMTS, GEMM_FMTS, Guarded, assert_within, gemm_reference,
+                               oracle_rows, to_dev_bytes, x_dev, torch)
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["q4_0", "q4_1", "q8_0"]
-D_RANGE = {"q4_0": synth.D_Q4, "q4_1": synth.D_Q4, "q8_0": synth.D_Q8}
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_blocks.json")
 GEMV_TOL = 1e-4
 GEMM_TOL = 1e-2
@@ -101,13 +99,15 @@ def test_dequantize_chunk_loop(fmt, dtype, out_off):
 
 
 def _edge_blocks(fmt):
-    """Subnormal and negative d, q = 8 with d < 0 (sign of zero), Q8 -128/127,
-    fp16 overflow to +-inf, +-0 d."""
+    """Subnormal and negative d, q = 8 (Q4_0) / 16 (Q5_0) with d < 0 (sign
+    of zero), Q8 -128/127, Q5 codes 0 and 31, fp16 overflow to +-inf, +-0 d."""
     dbits = np.array([0x0001, 0x03FF, 0x8001, 0xB800, 0x7BFF, 0xFBFF, 0x0000, 0x8000,
                       0x3C00, 0x2E66], dtype=np.uint16)
     nb = dbits.size
     if fmt == "q8_0":
         codes = np.tile(np.array([-128, 127, 0, -1, 1, 64, -64, 100] * 4), (nb, 1))
+    elif fmt in ("q5_0", "q5_1"):
+        codes = np.tile(np.array([16, 0, 31, 15, 17, 1, 30, 16] * 4), (nb, 1))
     else:
         codes = np.tile(np.array([8, 0, 15, 7, 9, 1, 14, 8] * 4), (nb, 1))
     mbits = np.array([0x8001, 0x0001, 0xB800, 0x3800, 0x7BFF, 0x0000, 0x8000, 0xBC00,
@@ -138,6 +138,8 @@ def test_dequantize_hand_worked_blocks():
         assert np.array_equal(got, want)
         for t in blk["positive_zero_at"]:
             assert got[t].view(np.uint32) == 0
+        for t in blk.get("negative_zero_at", []):
+            assert got[t].view(np.uint32) == 0x80000000
 
 
 def test_dequantize_full_config0():
@@ -386,6 +388,27 @@ def test_gemv_full_config2(n):
     assert_within(y, c["yref"][:n], c["s"][:n], GEMV_TOL, f"config2 n={n}")
 
 
+_Q5_FULL = {}
+
+
+@pytest.mark.parametrize("fmt", ["q5_0", "q5_1"])
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_gemv_q5_full_size(fmt, n):
+    """Q5_0 / Q5_1 11008 x 4096 (the Q4_1 workload's shape) with n columns,
+    the first n of one 8-column draw: every output against the oracle, on
+    the one-column, two-column and matrix-core kernels."""
+    if fmt not in _Q5_FULL:
+        m, k = 11008, 4096
+        w = synth.quant_matrix(fmt, m, k, seed=57, tensor_id=0, d_range=D_RANGE[fmt])
+        x = np.ascontiguousarray(synth.activations(k, 8, seed=57, tensor_id=100))
+        yref, s = oracle_rows(oracle.dot, fmt, w, m, k, x, 8)
+        _Q5_FULL[fmt] = (w, x, yref, s, m, k)
+    w, x, yref, s, m, k = _Q5_FULL[fmt]
+    _say("gemv q5 full", fmt, n)
+    y = _gpu_gemv(fmt, w, m, k, x[:n])
+    assert_within(y, yref[:n], s[:n], GEMV_TOL, f"q5 full {fmt} n={n}")
+
+
 def test_gemv_full_config3():
     """The 7B-shaped layer: q, k, v, o, gate, up, down (Q4_0, batch 1), each
     as its own launch, every output against the oracle."""
@@ -419,7 +442,7 @@ def _gpu_gemm(fmt, w, m, k, xh, ldx=None, ldy=None, x_off=0, w_off=0):
     return np.stack([y[j * ldy: j * ldy + m] for j in range(n)])
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
 @pytest.mark.parametrize("m,k,n", [(1, 32, 1), (130, 96, 3), (128, 128, 128), (257, 640, 129),
                                    (64, 4096, 200), (300, 2080, 17)])
 def test_gemm_within_tolerance(fmt, m, k, n):
@@ -431,7 +454,7 @@ def test_gemm_within_tolerance(fmt, m, k, n):
     assert_within(y, yref, s, GEMM_TOL, f"gemm {fmt} {m}x{k} n={n}")
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
 def test_gemm_strides_and_unaligned(fmt):
     m, k, n = 200, 1024, 70
     _say("gemm strided", fmt)
@@ -441,6 +464,21 @@ def test_gemm_strides_and_unaligned(fmt):
         y = _gpu_gemm(fmt, w, m, k, xh, ldx=ldx, ldy=ldy, x_off=x_off, w_off=w_off)
         yref, s = oracle.dot(fmt, w, m, k, xh.view(np.uint16), n, x_is_f16=True)
         assert_within(y, yref, s, GEMM_TOL, f"gemm strided {fmt} {ldx} {ldy} {x_off}")
+
+
+@pytest.mark.parametrize("fmt", ["q5_0", "q5_1"])
+def test_gemm_q5_is_unsupported(fmt):
+    """The GEMM has no Q5 tile layout: QK_ERR_UNSUPPORTED, output untouched."""
+    m, k, n = 64, 256, 16
+    w = _weights(fmt, m, k, seed=45)
+    hw, wp = to_dev_bytes(w)
+    hx, xp = x_dev(synth.activations(k, n, seed=45, tensor_id=2, dtype=np.float16).view(np.uint16), k,
+                   np.uint16)
+    out = Guarded(n * m * 4)
+    st = qk.qk_mul_mat(fmt, wp, m, k, xp, n, k, out.ptr, m, _stream())
+    assert st == qk.QK_ERR_UNSUPPORTED
+    assert np.all(out.host(np.uint32) == 0xA5A5A5A5) and out.guards_intact()
+    del hw, hx
 
 
 def test_gemm_matches_exact_fp16_weight_products():
@@ -458,7 +496,7 @@ def test_gemm_matches_exact_fp16_weight_products():
         assert np.array_equal(y[j], W16[:, c])
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
 @pytest.mark.parametrize("m,k", [(300, 256), (77, 160), (129, 32)])
 def test_gemm_identity_gives_fp16_weights(fmt, m, k):
     """With X = I (n = k one-hot columns) every output is one fp16 weight:
@@ -472,7 +510,7 @@ def test_gemm_identity_gives_fp16_weights(fmt, m, k):
     assert np.array_equal(y, W16.T), f"gemm identity {fmt} {m}x{k}"
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
 @pytest.mark.parametrize("m", [1, 7, 8, 9, 15, 16, 17, 33, 263])
 @pytest.mark.parametrize("k", [128, 256])
 def test_gemm_identity_direct_load_rows(fmt, m, k):
@@ -491,7 +529,7 @@ def test_gemm_identity_direct_load_rows(fmt, m, k):
     assert np.array_equal(y, W16.T), f"gemm identity direct-load {fmt} {m}x{k}"
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
 @pytest.mark.parametrize("m,k,n", [(1, 512, 1), (63, 512, 5), (64, 1024, 17), (65, 512, 32),
                                    (300, 1024, 32), (1000, 512, 9), (300, 512, 33), (257, 1024, 100),
                                    (70, 512, 128), (130, 640, 8), (300, 896, 40), (65, 11008, 16)])
@@ -520,7 +558,7 @@ def test_gemm_small_batch_tile(fmt, m, k, n):
     assert np.array_equal(yo, W16[:, cols].T), f"gemm small batch one-hot {fmt} {m}x{k}"
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
 def test_gemm_identity_edge_blocks(fmt):
     """The dequantize edge blocks (subnormal, negative and zero scales, code 8
     with a negative scale, Q8_0 -128 / 127, Q4_1 offsets of every sign)
@@ -569,7 +607,7 @@ def test_gemm_q4_1_weights_round_through_fp32():
     assert np.array_equal(y, W16.view(np.float16).astype(np.float32).T)
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
 @pytest.mark.parametrize("m,k,n", [(257, 640, 129), (300, 2080, 17), (512, 4096, 256)])
 def test_gemm_against_fp16_weight_product(fmt, m, k, n):
     """Against the exact product of the oracle's fp16 weights and the fp16

@@ -17,7 +17,7 @@ import oracle
 from dequant_quantized_gemv_amd import synth
 from tests.gpu_helpers import assert_within
 from tests.test_gpu_experts import _gpu_id, _oracle_id, _stack
-from tests.test_gpu_parity import (FMTS, GEMM_TOL, GEMV_TOL, _gpu_dequant, _gpu_gemm, _gpu_gemv,
+from tests.test_gpu_parity import (GEMM_TOL, GEMV_TOL, _gpu_dequant, _gpu_gemm, _gpu_gemv,
                                    _gpu_gemv_batched, _oracle_bits, _say, _weights)
 from tests.test_gpu_x8 import _gemv_x8
 
@@ -30,7 +30,13 @@ def _cases(seed, count, draw):
 
 
 def _fmt(rng):
-    return FMTS[int(rng.integers(0, 3))]
+    return ("q4_0", "q4_1", "q8_0")[int(rng.integers(0, 3))]
+
+
+def _as_q5(cases, seed):
+    """The same draws with the format replaced by Q5_0 or Q5_1 (own stream)."""
+    rng = np.random.default_rng(seed)
+    return [dict(c, fmt=("q5_0", "q5_1")[int(rng.integers(0, 2))]) for c in cases]
 
 
 def _draw_dequant(rng):
@@ -89,6 +95,11 @@ GEMV = _cases(0xD1, 40, _draw_gemv)
 GEMV_X8 = _cases(0xD2, 20, _draw_gemv)
 BATCHED = _cases(0xD3, 12, _draw_batched)
 EXPERT = _cases(0xD4, 12, _draw_expert)
+DEQUANT += _as_q5(_cases(0xE0, 10, _draw_dequant), 0xE0)
+GEMV += _as_q5(_cases(0xE1, 20, _draw_gemv), 0xE1)
+GEMV_X8 += _as_q5(_cases(0xE2, 10, _draw_gemv), 0xE2)
+BATCHED += _as_q5(_cases(0xE3, 6, _draw_batched), 0xE3)
+EXPERT += _as_q5(_cases(0xE4, 6, _draw_expert), 0xE4)
 GEMM = _cases(0xD5, 16, _draw_gemm)
 GEMM_SMALL = _cases(0xD6, 12, _draw_gemm_small)
 

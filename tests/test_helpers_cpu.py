@@ -30,7 +30,7 @@ def test_assert_within_zero_scale_needs_exact_zero():
         assert_within(np.array([0.0, 1e-30]), ref, s, 1e-4, "tiny")
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0", "q5_0", "q5_1"])
 def test_oracle_rows_equals_oracle_dot(fmt):
     m, k, n = 173, 256, 3
     w = synth.quant_matrix(fmt, m, k, seed=31, tensor_id=1, d_range=(1e-3, 2e-2))
@@ -43,7 +43,7 @@ def test_oracle_rows_equals_oracle_dot(fmt):
     assert np.array_equal(q, q2) and np.array_equal(qs, qs2)
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_1", "q8_0", "q5_0", "q5_1"])
 def test_gemm_reference_matches_oracle_dot_f16(fmt):
     m, k, n = 41, 320, 5
     w = synth.quant_matrix(fmt, m, k, seed=33, tensor_id=1, d_range=(1e-3, 2e-2))
