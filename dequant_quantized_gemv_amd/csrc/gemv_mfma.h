@@ -48,11 +48,26 @@ constexpr int kMfPitch = kGvWindow + kGvWindow / 16 + 16;
 // Largest k (weights per row) the matrix-core GEMV takes: one staged window.
 constexpr int kMfMaxK = kGvWindow;
 
-// The fp32 weights of quant word i of block b of a pair, the dequantize
-// definition's value (exact for Q4_0, Q5_0 and Q8_0, one rounding of
-// d*q + m for Q4_1 and Q5_1): Q4 / Q5 words give elements 4i..4i+3 (low
-// nibbles, plus bit 4 from qh for Q5) in w[0..3] and 16+4i..16+4i+3 (high
-// nibbles) in w[4..7]; Q8_0 words give elements 4i..4i+3 in w[0..3].
+// The value of lane l ^ 16 or l ^ 32, from gfx950's row-swap instructions:
+// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with
+// the even rows of its second (v_permlane32_swap: the upper half of the
+// first with the lower half of the second), so with x in both, the first
+// holds the partner's value in odd rows (upper half), the second in even
+// rows (lower half).  Written as inline asm so that the compiler sees both
+// registers change; the two wait states before it cover a vector write of
+// either operand just ahead (the hazard the compiler itself pads for these
+// instructions).  Vector-ALU operations, no LDS access.
+__device__ __forceinline__ float lane_xor16(float x, bool odd_row) {
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return __builtin_bit_cast(float, odd_row ? a : b);
+}
+__device__ __forceinline__ float lane_xor32(float x, bool upper_half) {
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return __builtin_bit_cast(float, upper_half ? a : b);
+}
+
 template <int FMT>
 __device__ __forceinline__ void word_weights(const uint32_t (&v)[Pair<FMT>::kDwords], int b, int i,
                                              float d, float mm, float (&w)[8]) {
@@ -90,7 +105,8 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
     constexpr int NT = 64 * WPG;
     constexpr int RPR = WPG / KQ;  // row-quads per round
     extern __shared__ __attribute__((aligned(16))) float xs[];
-    // per wave, its partial sums of one round: [cg][column c][row r]
+    // per wave, its partial sums of one round: [cg][column c][row r], in two
+    // sets used by alternate rounds
     float *const part = xs + NC * kMfPitch;
 
     const int tid = threadIdx.x;
@@ -153,14 +169,20 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     __syncthreads();
 
+    // partial sum of (wave w, column group cg, column c, row r) in a slot set
+    auto part_at = [](float *set, int w, int cg, int cc, int r) -> float & {
+        return set[((w * CG + cg) * 4 + cc) * 4 + r];
+    };
+
     // the B operand of column group cg: column cg*4 + c (a lane whose column
     // is past NC reads column NC-1; its sums are never stored)
     int colo[CG];
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) colo[cg] = min(cg * 4 + c, NC - 1) * kMfPitch;
 
-    // One round: RPR row-quads, each split over KQ waves (one pair per lane).
-    auto round = [&](const int qb, uint32_t (&cur)[ND]) __attribute__((always_inline)) {
+    // One round: RPR row-quads, each split over KQ waves (one pair per lane);
+    // its partial sums go to set `ps` of the partial slots.
+    auto round = [&](const int qb, uint32_t (&cur)[ND], const int ps) __attribute__((always_inline)) {
         const int q = qb + slot;
         // CH independent accumulation chains per column group (element
         // t % CH), added at the end: four for one group, two for two
@@ -211,22 +233,38 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
         }
         // the pair of the wave's round D ahead into the registers just used
         if (q + D * RPR < q1) load(q + D * RPR, cur);
-        // the 16 streams of each (row, column) are lanes c, c + 4, ..., c + 60:
-        // a DPP tree within each 16-lane row, then across rows; lanes 0..3
-        // write the wave's sums of rows 0..3 of column c
+        // The 16 streams of each (row r, column c) are lanes c, c + 4, ...,
+        // c + 60: a DPP tree within each 16-lane row (every lane of the row
+        // then holds its column's row sums for all four r), then across the
+        // rows with the four values shared out: rows 0 and 1 (2 and 3) trade
+        // halves so that each keeps two of the r, then the two halves of the
+        // wave so that row R keeps one, r = 2 (R & 1) + (R >> 1).  Lanes 0..3
+        // of each row write it.
+        float *const pw = part + ps * (WPG * CG * 16);
+        const int R = lane >> 4;
+        const bool odd = (R & 1) != 0;
+        const bool upper = R >= 2;
 #pragma unroll
         for (int cg = 0; cg < CG; ++cg) {
+            float v4[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float sm = acc[cg][0][r] + acc[cg][1][r];
                 if constexpr (CH == 4) sm += acc[cg][2][r] + acc[cg][3][r];
                 sm += dpp<0x124>(sm);  // row_ror:4
                 sm += dpp<0x128>(sm);  // row_ror:8
-                sm += __shfl_xor(sm, 16);
-                sm += __shfl_xor(sm, 32);
-                if (g == 0) part[((wave * CG + cg) * 4 + c) * 4 + r] = sm;
+                v4[r] = sm;
             }
+            // the pair this row keeps (r = 2 (R & 1) + {0, 1}) and the pair it hands over
+            const float k0 = odd ? v4[2] : v4[0], k1 = odd ? v4[3] : v4[1];
+            const float s0 = odd ? v4[0] : v4[2], s1 = odd ? v4[1] : v4[3];
+            const float t0 = k0 + lane_xor16(s0, odd), t1 = k1 + lane_xor16(s1, odd);
+            const float sm = (upper ? t1 : t0) + lane_xor32(upper ? t0 : t1, upper);
+            if ((lane & 15) < 4) part_at(pw, wave, cg, c, 2 * (R & 1) + (R >> 1)) = sm;
         }
+        // one barrier per round: a set of slots is written again two rounds
+        // later, after every wave has passed the next round's barrier, by
+        // which time its readers are done with it
         __syncthreads();
         // the KQ waves of a row-quad in order: the first one adds and stores
         if (kq == 0 && q < q1 && lane < 16 * CG) {
@@ -234,18 +272,18 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
             const int cc = (lane >> 2) & 3;
             const int cg = lane >> 4;
             const int col = cg * 4 + cc;
-            float sm = part[((wave * CG + cg) * 4 + cc) * 4 + r];
+            float sm = part_at(pw, wave, cg, cc, r);
 #pragma unroll
-            for (int k2 = 1; k2 < KQ; ++k2) sm += part[(((wave + k2) * CG + cg) * 4 + cc) * 4 + r];
+            for (int k2 = 1; k2 < KQ; ++k2) sm += part_at(pw, wave + k2, cg, cc, r);
             const int ro = 4 * q + r;
             if (col < NC && ro < it.m) it.y[col * it.ldy + ro] = sm;
         }
-        __syncthreads();  // the partial slots are reused by the next round
     };
+    static_assert(D == 2, "the rounds alternate between the two sets of partial slots");
     for (int qb = q0; qb < q1; qb += D * RPR) {
 #pragma unroll
         for (int r = 0; r < D; ++r)
-            if (qb + r * RPR < q1) round(qb + r * RPR, v[r]);  // (uniform across the workgroup)
+            if (qb + r * RPR < q1) round(qb + r * RPR, v[r], r);  // (uniform across the workgroup)
     }
 }
 
@@ -259,7 +297,7 @@ template <int NC> struct MfShape {
 template <int FMT, int NC, int KQ>
 int gemv_mfma_run(const GemvItem &it, hipStream_t stream) {
     constexpr int WPG = MfShape<NC>::kWPG;
-    const size_t lds = ((size_t)NC * kMfPitch + (size_t)WPG * ((NC + 3) / 4) * 16) * sizeof(float);
+    const size_t lds = ((size_t)NC * kMfPitch + 2 * (size_t)WPG * ((NC + 3) / 4) * 16) * sizeof(float);
     const int per_cu = max(1, (int)((160 * 1024) / lds));
     const int64_t quads = ((int64_t)it.m + 3) / 4;
     if (quads > INT32_MAX) return QK_ERR_INVALID_ARG;
