@@ -226,24 +226,29 @@ __device__ __forceinline__ void pair_codes(const uint32_t (&v)[Pair<FMT>::kDword
 // 4i..4i+3 (i < 8).  xa / xb are the matching activations.
 // ---------------------------------------------------------------------------
 
-// Q4_0 group: sum over the 8 elements of (q - 8) * x, added to s.
+// Q4_0 group: sum over the 8 elements of (q - 8) * x, added to s.  Each
+// fp16 pair is masked straight out of the quant word into the mantissas of
+// 0x6400 6400 (one and-or): the low nibbles of bytes 0 and 2 (elements 0
+// and 2) and, from the word shifted by a byte, of bytes 1 and 3 give
+// 1024 + c, and c - 8 after subtracting 1032; the high nibbles are taken in
+// place (1024 + 16c), and (1024 + 16c) / 16 - 72 = c - 8 is one fused,
+// exact operation.
 __device__ __forceinline__ float group_q4_0(uint32_t qw, const float4 &xa, const float4 &xb, float s) {
-    // low nibbles: 1024 + c - 1032 = c - 8; high nibbles left in place:
-    // (1024 + 16c) / 16 - 72 = c - 8 (one fused, exact operation)
-    const uint32_t lo = qw & 0x0F0F0F0Fu;
-    const uint32_t hi = qw & 0xF0F0F0F0u;
-    const uint32_t l01 = pk_add_f16(bytes_to_f16_lo(lo), -1032.0f);
-    const uint32_t l23 = pk_add_f16(bytes_to_f16_hi(lo), -1032.0f);
-    const uint32_t h01 = pk_fma_f16(bytes_to_f16_lo(hi), 0.0625f, -72.0f);
-    const uint32_t h23 = pk_fma_f16(bytes_to_f16_hi(hi), 0.0625f, -72.0f);
-    s = fma_mix_lo(l01, xa.x, s);
-    s = fma_mix_hi(l01, xa.y, s);
-    s = fma_mix_lo(l23, xa.z, s);
-    s = fma_mix_hi(l23, xa.w, s);
-    s = fma_mix_lo(h01, xb.x, s);
-    s = fma_mix_hi(h01, xb.y, s);
-    s = fma_mix_lo(h23, xb.z, s);
-    s = fma_mix_hi(h23, xb.w, s);
+    // (v_bitop3 with truth table 0xEA is (a & b) | c: one instruction)
+    auto mask_or = [](uint32_t a, uint32_t m) { return __builtin_amdgcn_bitop3_b32(a, m, 0x64006400u, 0xEA); };
+    const uint32_t qs = qw >> 8;
+    const uint32_t l02 = pk_add_f16(mask_or(qw, 0x000F000Fu), -1032.0f);
+    const uint32_t l13 = pk_add_f16(mask_or(qs, 0x000F000Fu), -1032.0f);
+    const uint32_t h02 = pk_fma_f16(mask_or(qw, 0x00F000F0u), 0.0625f, -72.0f);
+    const uint32_t h13 = pk_fma_f16(mask_or(qs, 0x00F000F0u), 0.0625f, -72.0f);
+    s = fma_mix_lo(l02, xa.x, s);
+    s = fma_mix_lo(l13, xa.y, s);
+    s = fma_mix_hi(l02, xa.z, s);
+    s = fma_mix_hi(l13, xa.w, s);
+    s = fma_mix_lo(h02, xb.x, s);
+    s = fma_mix_lo(h13, xb.y, s);
+    s = fma_mix_hi(h02, xb.z, s);
+    s = fma_mix_hi(h13, xb.w, s);
     return s;
 }
 
