@@ -111,7 +111,9 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // (made uniform for two column groups: the round's branches are then
+    // scalar; measured 19.7 -> 19.1 us at 8 columns, 14.7 -> 15.0 at 4)
+    const int wave = CG == 2 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
     const int kq = wave % KQ;    // which pair of the row this wave's lanes take
     const int slot = wave / KQ;  // which row-quad of the round
     const int g = lane >> 2;     // k-stream (lane group)
@@ -187,11 +189,16 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
         // CH independent accumulation chains per column group (element
         // t % CH), added at the end: four for one group, two for two
         constexpr int CH = CG == 1 ? 4 : 2;
+        // (with two column groups each chain's first product takes a zero
+        // accumulator operand instead of registers cleared beforehand; with
+        // one, clearing them first measured faster)
+        const f32x4m_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
         f32x4m_t acc[CG][CH];
+        if constexpr (CG == 1) {
 #pragma unroll
-        for (int cg = 0; cg < CG; ++cg)
-#pragma unroll
-            for (int u = 0; u < CH; ++u) acc[cg][u] = f32x4m_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int u = 0; u < CH; ++u) acc[0][u] = zero4;
+        }
+        float *const pw = part + ps * (WPG * CG * 16);
         if (q < q1) {
 #pragma unroll
             for (int bk = 0; bk < 2; ++bk) {
@@ -219,11 +226,13 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
                         for (int cg = 0; cg < CG; ++cg)
                             xb[cg] = *reinterpret_cast<const f32x4m_t *>(xs + colo[cg] + eo);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u)
+                        for (int u = 0; u < 4; ++u) {
+                            const bool first = CG == 2 && bk == 0 && wi == 0 && h == 0 && u < CH;
 #pragma unroll
                             for (int cg = 0; cg < CG; ++cg)
-                                acc[cg][u % CH] = __builtin_amdgcn_mfma_f32_4x4x1f32(wt[4 * h + u], xb[cg][u],
-                                                                                     acc[cg][u % CH], 0, 0, 0);
+                                acc[cg][u % CH] = __builtin_amdgcn_mfma_f32_4x4x1f32(
+                                    wt[4 * h + u], xb[cg][u], first ? zero4 : acc[cg][u % CH], 0, 0, 0);
+                        }
                     }
                     // keep the next word's LDS reads from being hoisted above
                     // this one (bounds the live activations)
@@ -233,34 +242,38 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
         }
         // the pair of the wave's round D ahead into the registers just used
         if (q + D * RPR < q1) load(q + D * RPR, cur);
-        // The 16 streams of each (row r, column c) are lanes c, c + 4, ...,
-        // c + 60: a DPP tree within each 16-lane row (every lane of the row
-        // then holds its column's row sums for all four r), then across the
-        // rows with the four values shared out: rows 0 and 1 (2 and 3) trade
-        // halves so that each keeps two of the r, then the two halves of the
-        // wave so that row R keeps one, r = 2 (R & 1) + (R >> 1).  Lanes 0..3
-        // of each row write it.
-        float *const pw = part + ps * (WPG * CG * 16);
-        const int R = lane >> 4;
-        const bool odd = (R & 1) != 0;
-        const bool upper = R >= 2;
+        // a row-quad past the range has no sums, and none are read: with two
+        // column groups its reduction is skipped (with one, running it on
+        // the cleared accumulators measured faster than the branch)
+        if (CG == 1 || q < q1) {
+            // The 16 streams of each (row r, column c) are lanes c, c + 4, ...,
+            // c + 60: a DPP tree within each 16-lane row (every lane of the row
+            // then holds its column's row sums for all four r), then across the
+            // rows with the four values shared out: rows 0 and 1 (2 and 3) trade
+            // halves so that each keeps two of the r, then the two halves of the
+            // wave so that row R keeps one, r = 2 (R & 1) + (R >> 1).  Lanes 0..3
+            // of each row write it.
+            const int R = lane >> 4;
+            const bool odd = (R & 1) != 0;
+            const bool upper = R >= 2;
 #pragma unroll
-        for (int cg = 0; cg < CG; ++cg) {
-            float v4[4];
+            for (int cg = 0; cg < CG; ++cg) {
+                float v4[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float sm = acc[cg][0][r] + acc[cg][1][r];
-                if constexpr (CH == 4) sm += acc[cg][2][r] + acc[cg][3][r];
-                sm += dpp<0x124>(sm);  // row_ror:4
-                sm += dpp<0x128>(sm);  // row_ror:8
-                v4[r] = sm;
+                for (int r = 0; r < 4; ++r) {
+                    float sm = acc[cg][0][r] + acc[cg][1][r];
+                    if constexpr (CH == 4) sm += acc[cg][2][r] + acc[cg][3][r];
+                    sm += dpp<0x124>(sm);  // row_ror:4
+                    sm += dpp<0x128>(sm);  // row_ror:8
+                    v4[r] = sm;
+                }
+                // the pair this row keeps (r = 2 (R & 1) + {0, 1}) and the pair it hands over
+                const float k0 = odd ? v4[2] : v4[0], k1 = odd ? v4[3] : v4[1];
+                const float s0 = odd ? v4[0] : v4[2], s1 = odd ? v4[1] : v4[3];
+                const float t0 = k0 + lane_xor16(s0, odd), t1 = k1 + lane_xor16(s1, odd);
+                const float sm = (upper ? t1 : t0) + lane_xor32(upper ? t0 : t1, upper);
+                if ((lane & 15) < 4) part_at(pw, wave, cg, c, 2 * (R & 1) + (R >> 1)) = sm;
             }
-            // the pair this row keeps (r = 2 (R & 1) + {0, 1}) and the pair it hands over
-            const float k0 = odd ? v4[2] : v4[0], k1 = odd ? v4[3] : v4[1];
-            const float s0 = odd ? v4[0] : v4[2], s1 = odd ? v4[1] : v4[3];
-            const float t0 = k0 + lane_xor16(s0, odd), t1 = k1 + lane_xor16(s1, odd);
-            const float sm = (upper ? t1 : t0) + lane_xor32(upper ? t0 : t1, upper);
-            if ((lane & 15) < 4) part_at(pw, wave, cg, c, 2 * (R & 1) + (R >> 1)) = sm;
         }
         // one barrier per round: a set of slots is written again two rounds
         // later, after every wave has passed the next round's barrier, by
