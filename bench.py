@@ -530,6 +530,16 @@ def run_layer(c, name, with_cpu=True):
         sec = t["us"] / 1e6
         out[label] = {**timing_fields(t), "weight_GBps": rnd(wtot / sec / 1e9, 1),
                       "pct_of_hbm_peak": rnd(100 * wtot / sec / 1e9 / HBM_PEAK_GBPS, 2)}
+        if label == "grouped_launch":
+            # practical ceiling: one plain streaming read of as many bytes per
+            # step, one launch, over as many cold copies
+            span = (wtot + 255) // 256 * 256
+            big = torch.empty(R * span, dtype=torch.uint8, device="cuda")
+            cs, _ = c.run.time_steps([[c.run.stream_read(big.data_ptr() + r * span, wtot)] for r in range(R)],
+                                     c.warmup, c.steps)
+            out[label]["stream_read_us"] = rnd(cs / c.steps * 1e6)
+            out[label]["pct_of_stream_read"] = rnd(100 * (cs / c.steps) / sec, 1)
+            del big
     # each matrix alone: the median of its own launches
     med = {}
     for i, p in enumerate(probs):
