@@ -31,7 +31,7 @@ Measurement
     78.6 TFLOP/s (256 CUs x 64 lanes x 2 flops per FMA x 2.4 GHz: the build
     keeps packed fp32 instructions off).  The Q4_1 GEMV is reported against
     max(HBM time, ALU time); the GEMM against the MFMA peak.
-  * cpu_baseline: the oracle (plain C, fp64) timed on this host: one thread on
+  * cpu_baseline: the oracle (plain C++, fp64) timed on this host: one thread on
     a bounded row sample (scaled), and T threads (T = CPUs in the affinity
     mask) over the whole workload, which is also the parity reference.
 

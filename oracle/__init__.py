@@ -4,9 +4,9 @@ TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
 the benchmark's CPU-baseline leg import this module.  The GPU library never
 does, and the two share no code.
 
-The arithmetic lives in ``qk_oracle.c`` (plain C, fp64 accumulation, no FMA
-contraction); this module is numpy marshalling around it.  Function by
-function, the C file cites the passages of the "llama_cpp 0.12.1 -> 0.12.2"
+The arithmetic lives in ``qk_oracle.cpp`` (plain C++ with a C interface,
+fp64 accumulation, no FMA contraction); this module is numpy marshalling
+around it.  Function by function, the source cites the passages of the "llama_cpp 0.12.1 -> 0.12.2"
 ggml-cuda.cu diff page that each step follows.
 
 Layout conventions (ggml's: ne0 is the contiguous dimension):

@@ -1,4 +1,4 @@
-"""Compile the CPU oracle (qk_oracle.c) into oracle/liboracle.so.
+"""Compile the CPU oracle (qk_oracle.cpp, g++) into oracle/liboracle.so.
 
 Test infrastructure: the oracle is the correctness reference for the GPU
 library and is never linked into it.
@@ -8,17 +8,17 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "qk_oracle.c")
+SRC = os.path.join(HERE, "qk_oracle.cpp")
 LIB = os.path.join(HERE, "liboracle.so")
 
-# -ffp-contract=off: gcc contracts a*b+c into an FMA by default on hosts that
+# -ffp-contract=off: g++ contracts a*b+c into an FMA by default on hosts that
 # have one; the oracle rounds every multiply and add on its own.
-CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+CFLAGS = ["-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
           "-fPIC", "-shared", "-Wall", "-Wextra"]
 
 
 def build(verbose=False):
-    cmd = ["gcc", *CFLAGS, SRC, "-o", LIB + ".tmp", "-lm"]
+    cmd = ["g++", *CFLAGS, SRC, "-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

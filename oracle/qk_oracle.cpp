@@ -1,6 +1,7 @@
 /*
- * qk_oracle.c - plain, slow CPU oracle for ggml block-quantized dequantize,
- * GEMV and GEMM (formats Q4_0, Q4_1, Q8_0, Q5_0, Q5_1).
+ * qk_oracle.cpp - plain, slow CPU oracle for ggml block-quantized
+ * dequantize, GEMV and GEMM (formats Q4_0, Q4_1, Q8_0, Q5_0, Q5_1), in plain
+ * C++ (loops over arrays, no templates or containers) with a C interface.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference the GPU
  * library is checked against.  Only the test suite, the package smoke check
@@ -8,7 +9,7 @@
  * header, table or constant with the GPU library, and the GPU library never
  * calls it.
  *
- * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * Build: g++ -std=c++17 -O2 -ffp-contract=off -fno-fast-math -shared -fPIC
  * (contraction off: every fp32 multiply and add below is rounded on its own,
  * in the order written).
  *
@@ -39,12 +40,15 @@
 #include <string.h>
 #include <math.h>
 
-/* Format ids used by this oracle's C entry points (its own numbering). */
+/* Format ids used by this oracle's entry points (its own numbering). */
 #define ORC_Q4_0 0
 #define ORC_Q4_1 1
 #define ORC_Q8_0 2
 #define ORC_Q5_0 3
 #define ORC_Q5_1 4
+
+/* Entry points with C linkage, so that they load by name through ctypes. */
+extern "C" {
 
 /* ---------------------------------------------------------------------
  * IEEE-754 binary16 codec, written from the format definition:
@@ -396,3 +400,5 @@ void orc_dot_x8(int fmt, const uint8_t *w, int64_t m, int64_t k, const float *x,
         }
     }
 }
+
+}  /* extern "C" */
