@@ -68,6 +68,23 @@ __global__ __launch_bounds__(512) void mfma_loop_kernel(int iters, float *sink) 
     if (s == 1.2345f) sink[0] = s;
 }
 
+// Plain fp32 FMAs (no packed instructions): 32 independent chains per lane,
+// so issue, not latency, sets the rate.
+__global__ __launch_bounds__(1024) void valu_loop_kernel(int iters, float *sink) {
+    float a[32];
+    const float b = 0.999f, c = 0.001f * (float)threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) a[i] = (float)threadIdx.x * 0.001f + (float)i;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) a[i] = __builtin_fmaf(a[i], b, c);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) s += a[i];
+    if (s == 1.2345f) sink[0] = s;
+}
+
 int stream_read(const void *p, size_t bytes, float *sink, hipStream_t stream) {
     if (((uintptr_t)p & 15) != 0) return 1;
     int dev = 0, cus = 256;
@@ -97,6 +114,14 @@ int qkc_mfma_loop(int workgroups, int iters, float *sink, void *stream) {
     void *args[] = {&iters, &sink};
     return hipLaunchKernel(reinterpret_cast<const void *>(mfma_loop_kernel), dim3((unsigned)workgroups),
                            dim3(512), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : 1;
+}
+
+// Runs `workgroups` x 16 waves of the fp32 FMA loop for `iters` iterations;
+// flops = workgroups * 1024 * iters * 32 * 2.
+int qkc_valu_loop(int workgroups, int iters, float *sink, void *stream) {
+    void *args[] = {&iters, &sink};
+    return hipLaunchKernel(reinterpret_cast<const void *>(valu_loop_kernel), dim3((unsigned)workgroups),
+                           dim3(1024), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : 1;
 }
 
 // One call of the qk C ABI with its arguments.  Every field is 8 bytes wide
