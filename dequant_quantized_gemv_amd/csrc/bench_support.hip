@@ -26,25 +26,43 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kReadThreads = 256;
-constexpr int kReadUnroll = 4;  // independent 16-byte loads in flight per lane
 
-// Every lane reads kReadUnroll 16-byte pieces per iteration, grid-stride
-// over the buffer, and folds them into a value that is stored only if it
-// equals a constant (so the loads cannot be dropped and nothing is written).
+// One 16-byte piece per lane per iteration, grid-stride over the buffer with
+// streaming (nontemporal) loads, folded into a value that is stored only if
+// it equals a constant (so the loads cannot be dropped and nothing is
+// written).  Of the plain reads timed on this chip (1, 2, 4 or 8 pieces per
+// lane per iteration, 256-1024 threads, 4-16 workgroups per CU, grid-stride
+// or a contiguous range per workgroup, with and without the streaming hint)
+// this one is the fastest: the whole grid sweeps the buffer together, a few
+// MB at a time.
 __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4_t *__restrict__ p,
+                                                                   size_t n16, float *sink) {
+    const size_t nt = (size_t)gridDim.x * kReadThreads;
+    uint32_t acc = 0;
+    for (size_t i = (size_t)blockIdx.x * kReadThreads + threadIdx.x; i < n16; i += nt) {
+        const u32x4_t v = __builtin_nontemporal_load(p + i);
+        acc ^= v.x + v.y + v.z + v.w;
+    }
+    if (acc == 0x9E3779B9u) sink[0] = 1.0f;
+}
+
+// The clock settle's read: four plain 16-byte loads per lane per iteration
+// (what the settle was tuned with; the streaming hint above changes what
+// state the first launches after it find).
+__global__ __launch_bounds__(kReadThreads) void settle_read_kernel(const u32x4_t *__restrict__ p,
                                                                    size_t n16, float *sink) {
     const size_t nt = (size_t)gridDim.x * kReadThreads;
     const size_t tid = (size_t)blockIdx.x * kReadThreads + threadIdx.x;
     uint32_t acc = 0;
-    for (size_t i = tid; i < n16; i += nt * kReadUnroll) {
-        u32x4_t v[kReadUnroll];
+    for (size_t i = tid; i < n16; i += nt * 4) {
+        u32x4_t v[4];
 #pragma unroll
-        for (int u = 0; u < kReadUnroll; ++u) {
+        for (int u = 0; u < 4; ++u) {
             const size_t j = i + u * nt;
             v[u] = j < n16 ? p[j] : u32x4_t{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x + v[u].y + v[u].z + v[u].w;
+        for (int u = 0; u < 4; ++u) acc ^= v[u].x + v[u].y + v[u].z + v[u].w;
     }
     if (acc == 0x9E3779B9u) sink[0] = 1.0f;
 }
@@ -85,7 +103,7 @@ __global__ __launch_bounds__(1024) void valu_loop_kernel(int iters, float *sink)
     if (s == 1.2345f) sink[0] = s;
 }
 
-int stream_read(const void *p, size_t bytes, float *sink, hipStream_t stream) {
+int read_launch(const void *kern, const void *p, size_t bytes, float *sink, hipStream_t stream) {
     if (((uintptr_t)p & 15) != 0) return 1;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -94,8 +112,11 @@ int stream_read(const void *p, size_t bytes, float *sink, hipStream_t stream) {
     const unsigned grid = (unsigned)cus * 8;
     size_t n16 = bytes / 16;
     void *args[] = {&p, &n16, &sink};
-    return hipLaunchKernel(reinterpret_cast<const void *>(stream_read_kernel), dim3(grid),
-                           dim3(kReadThreads), args, 0, stream) == hipSuccess ? 0 : 1;
+    return hipLaunchKernel(kern, dim3(grid), dim3(kReadThreads), args, 0, stream) == hipSuccess ? 0 : 1;
+}
+
+int stream_read(const void *p, size_t bytes, float *sink, hipStream_t stream) {
+    return read_launch(reinterpret_cast<const void *>(stream_read_kernel), p, bytes, sink, stream);
 }
 
 }  // namespace
@@ -251,7 +272,7 @@ int qkb_settle(const void *buf, size_t bytes, float *sink, double ms, void *stre
     for (;;) {
         // a few launches between clock reads; at most 64 in flight at once
         for (int i = 0; i < 4; ++i)
-            if (stream_read(buf, bytes, sink, s) != 0) return 1;
+            if (read_launch(reinterpret_cast<const void *>(settle_read_kernel), buf, bytes, sink, s) != 0) return 1;
         launched += 4;
         if (launched % 64 == 0 && hipStreamSynchronize(s) != hipSuccess) return 1;
         const double el = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
