@@ -764,7 +764,7 @@ def main():
                     help="also run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:

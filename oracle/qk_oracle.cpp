@@ -308,9 +308,10 @@ void orc_dot_id(int fmt, const uint8_t *w, int64_t n_experts, int64_t expert_str
 /* ---------------------------------------------------------------------
  * Products with 8-bit activations (integer dot products).
  *
- * The gem diff names the integer-dot kernels (mul_mat_vec_q / MMQ, fed by a
- * quantize_q8_1 step) but prints neither their activation layout nor their
- * rounding.  Reading taken here (this build's own design, stated as such):
+ * The "llama_cpp 0.12.1 -> 0.12.2" diff names the integer-dot kernels
+ * (mul_mat_vec_q / MMQ, fed by a quantize_q8_1 step) but prints neither their
+ * activation layout nor their rounding.  Reading taken here (a design choice
+ * of this library, stated as such):
  * each 32-element block of an activation column is quantized with a
  * power-of-two scale d = 2^e, e the smallest integer with 127 * 2^e >= amax
  * (amax = max |x| over the block), but at least -126; the codes are
