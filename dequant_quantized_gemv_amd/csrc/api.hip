@@ -192,8 +192,7 @@ int qk_mul_mat_vec_id(int fmt, const void *w, int64_t n_experts, int64_t expert_
 
 int qk_mul_mat(int fmt, const void *w, int64_t m, int64_t k, const void *x_f16, int64_t n,
                int64_t ldx, float *y, int64_t ldy, void *stream) {
-    // (the GEMM's tile layouts exist for Q4_0, Q4_1 and Q8_0)
-    if (!fmt_ok(fmt) || fmt == QK_Q5_0 || fmt == QK_Q5_1) return QK_ERR_UNSUPPORTED;
+    if (!fmt_ok(fmt)) return QK_ERR_UNSUPPORTED;
     if (m < 0 || k < 0 || k % 32 != 0 || n < 0) return QK_ERR_INVALID_ARG;
     if (m == 0 || n == 0) return QK_OK;
     if (m > kMaxDim || k > kMaxDim || n > kMaxDim || ldx < k || ldy < m) return QK_ERR_INVALID_ARG;

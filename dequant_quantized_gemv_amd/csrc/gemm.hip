@@ -83,10 +83,17 @@ constexpr int kGmSmallBatchMax = 128;
 //     one from the partner lane's registers, not from LDS (gm_partner_scale)
 //   Q4_1 (40-byte pair): 0 | 4+8h, 8+8h | 20 | 24+8h, 28+8h
 //   Q8_0 (68-byte pair): 8g, 8g+4, 8g+8 | 36+8g, 40+8g | 0 | 32
+//   Q5_0 (44-byte pair; block 0 = d at 0, qh at 2-5, quant bytes 6-21; block
+//     1 = d at 22, qh 24-27, quant bytes 28-43): 0, 4, 4+8h, 8+8h, 12+8h |
+//     20, 24, 28+8h, 32+8h
+//   Q5_1 (48-byte pair; d, m, qh, quant bytes at 0, 2, 4, 8 and 24, 26, 28,
+//     32): 0, 4, 8+8h, 12+8h | 24, 28, 32+8h, 36+8h
 template <int FMT> struct GmQ;
 template <> struct GmQ<QK_Q4_0> { static constexpr int kN = 6; };
 template <> struct GmQ<QK_Q4_1> { static constexpr int kN = 6; };
 template <> struct GmQ<QK_Q8_0> { static constexpr int kN = 7; };
+template <> struct GmQ<QK_Q5_0> { static constexpr int kN = 9; };
+template <> struct GmQ<QK_Q5_1> { static constexpr int kN = 8; };
 
 template <int FMT>
 __device__ __forceinline__ int gm_offset(int slot, int g) {
@@ -97,6 +104,14 @@ __device__ __forceinline__ int gm_offset(int slot, int g) {
     } else if constexpr (FMT == QK_Q4_1) {
         constexpr int base[6] = {0, 4, 8, 20, 24, 28};
         return (slot == 0 || slot == 3) ? base[slot] : base[slot] + 8 * h;
+    } else if constexpr (FMT == QK_Q5_0) {
+        constexpr int base[9] = {0, 4, 4, 8, 12, 20, 24, 28, 32};
+        constexpr bool by_half[9] = {false, false, true, true, true, false, false, true, true};
+        return base[slot] + (by_half[slot] ? 8 * h : 0);
+    } else if constexpr (FMT == QK_Q5_1) {
+        constexpr int base[8] = {0, 4, 8, 12, 24, 28, 32, 36};
+        constexpr bool by_half[8] = {false, false, true, true, false, false, true, true};
+        return base[slot] + (by_half[slot] ? 8 * h : 0);
     } else {
         constexpr int base[7] = {0, 4, 8, 36, 40, 0, 32};
         return slot < 5 ? base[slot] + 8 * g : base[slot];
@@ -146,6 +161,8 @@ struct GmLaneConst {
     uint32_t sel0;   // Q4_0: perm selector giving (d, d) of block 0
     uint32_t sel1;   // Q4_0: perm selector giving (d, d) of block 1
     float dscale;    // Q4_1: 1, or 1/16 for high nibbles kept in place (16q)
+    uint32_t nsh;    // Q5: shift bringing this lane's nibbles to the low four bits (0 or 4)
+    uint32_t qsh;    // Q5: shift bringing this lane's eight qh bits (elements 8g..8g+7) to bits 0-7
 };
 
 template <int FMT>
@@ -163,6 +180,8 @@ __device__ __forceinline__ GmLaneConst gm_lane_const(int g) {
     c.sel0 = h ? 0x05040504u : 0x01000100u;  // perm(q5, q0)
     c.sel1 = h ? 0x07060706u : 0x03020302u;  // perm(q2, q5)
     c.dscale = hi ? 0.0625f : 1.0f;
+    c.nsh = hi ? 4u : 0u;
+    c.qsh = 8u * (uint32_t)g;
     return c;
 }
 
@@ -195,6 +214,32 @@ __device__ __forceinline__ u32x4g_t gm_decode8(uint32_t qa, uint32_t qb, uint32_
     }
 }
 
+// Q5: two quant dwords and the block's qh word -> 4 packed fp16 (one A
+// operand).  The lane's nibbles are brought to the low four bits of each
+// byte and bit 4 of each code comes from its qh bit (elements 8g..8g+7 are
+// qh bits 8g..8g+7), so each byte is the 5-bit code q.  Q5_0: 1024 + q as
+// fp16, minus 1040 is q - 16 exactly, times (d, d) is the one rounding of the
+// exact weight; Q5_1: the fp32 weight d*q + m, then its fp16 (as Q4_1).
+template <int FMT>
+__device__ __forceinline__ u32x4g_t gm_decode8_q5(uint32_t qa, uint32_t qb, uint32_t qh, uint32_t dd, float d,
+                                                  float mm, const GmLaneConst &c) {
+    const uint32_t hb = (qh >> c.qsh) & 0xFFu;
+    const uint32_t ua = ((qa >> c.nsh) & 0x0F0F0F0Fu) | q5_high4(hb & 0xFu);
+    const uint32_t ub = ((qb >> c.nsh) & 0x0F0F0F0Fu) | q5_high4(hb >> 4);
+    if constexpr (FMT == QK_Q5_0) {
+        const uint32_t bias = 0xE410E410u;  // (-1040, -1040)
+        return u32x4g_t{gm_pk_mul(gm_pk_add(gm_perm_lo(ua), bias), dd),
+                        gm_pk_mul(gm_pk_add(gm_perm_hi(ua), bias), dd),
+                        gm_pk_mul(gm_pk_add(gm_perm_lo(ub), bias), dd),
+                        gm_pk_mul(gm_pk_add(gm_perm_hi(ub), bias), dd)};
+    } else {
+        return u32x4g_t{gm_pack2(gm_q41_weight(d, ubyte_f<0>(ua), mm), gm_q41_weight(d, ubyte_f<1>(ua), mm)),
+                        gm_pack2(gm_q41_weight(d, ubyte_f<2>(ua), mm), gm_q41_weight(d, ubyte_f<3>(ua), mm)),
+                        gm_pack2(gm_q41_weight(d, ubyte_f<0>(ub), mm), gm_q41_weight(d, ubyte_f<1>(ub), mm)),
+                        gm_pack2(gm_q41_weight(d, ubyte_f<2>(ub), mm), gm_q41_weight(d, ubyte_f<3>(ub), mm))};
+    }
+}
+
 // The lane's A operands of one 16-row tile and step: block 0 -> a0, block 1 -> a1.
 template <int FMT>
 __device__ __forceinline__ void gm_decode(const uint32_t (&q)[GmQ<FMT>::kN], const GmLaneConst &c,
@@ -211,6 +256,20 @@ __device__ __forceinline__ void gm_decode(const uint32_t (&q)[GmQ<FMT>::kN], con
         a0 = gm_decode8<FMT>(__builtin_amdgcn_alignbyte(q[1], q[0], 2), __builtin_amdgcn_alignbyte(q[2], q[1], 2),
                              dd0, 0.0f, 0.0f, c);
         a1 = gm_decode8<FMT>(q[3], q[4], dd1, 0.0f, 0.0f, c);
+    } else if constexpr (FMT == QK_Q5_0) {
+        // block 0: d in the low half of dword 0, qh two bytes further, its
+        // quant half 2 bytes past dwords 4+8h..; block 1: d in the high half
+        // of dword 20, qh and quant bytes aligned
+        const uint32_t dd0 = __builtin_amdgcn_perm(0u, q[0], 0x01000100u);
+        const uint32_t dd1 = __builtin_amdgcn_perm(0u, q[5], 0x03020302u);
+        a0 = gm_decode8_q5<FMT>(__builtin_amdgcn_alignbyte(q[3], q[2], 2), __builtin_amdgcn_alignbyte(q[4], q[3], 2),
+                                __builtin_amdgcn_alignbyte(q[1], q[0], 2), dd0, 0.0f, 0.0f, c);
+        a1 = gm_decode8_q5<FMT>(q[7], q[8], q[6], dd1, 0.0f, 0.0f, c);
+    } else if constexpr (FMT == QK_Q5_1) {
+        const float d0 = h2f(q[0] & 0xFFFFu), m0 = h2f(q[0] >> 16);
+        const float d1 = h2f(q[4] & 0xFFFFu), m1 = h2f(q[4] >> 16);
+        a0 = gm_decode8_q5<FMT>(q[2], q[3], q[1], 0u, d0, m0, c);
+        a1 = gm_decode8_q5<FMT>(q[6], q[7], q[5], 0u, d1, m1, c);
     } else {
         const float d0 = h2f(q[0] & 0xFFFFu) * c.dscale, m0 = h2f(q[0] >> 16);
         const float d1 = h2f(q[3] & 0xFFFFu) * c.dscale, m1 = h2f(q[3] >> 16);
@@ -363,6 +422,8 @@ template <int FMT> struct GmStage;
 template <> struct GmStage<QK_Q4_0> { static constexpr int kPitch = 48; };
 template <> struct GmStage<QK_Q4_1> { static constexpr int kPitch = 48; };
 template <> struct GmStage<QK_Q8_0> { static constexpr int kPitch = 80; };
+template <> struct GmStage<QK_Q5_0> { static constexpr int kPitch = 48; };
+template <> struct GmStage<QK_Q5_1> { static constexpr int kPitch = 48; };
 
 template <int FMT>
 constexpr size_t gm_group_lds() {
@@ -459,10 +520,11 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
                 const u32x4g_a4 t = *reinterpret_cast<const u32x4g_a4 *>(arow[u] + off);
                 qa[4 * u] = t.x; qa[4 * u + 1] = t.y; qa[4 * u + 2] = t.z; qa[4 * u + 3] = t.w;
             }
-            if constexpr (kTail == 8) {
+            if constexpr (kTail >= 8) {
                 const u32x2g_a4 t = *reinterpret_cast<const u32x2g_a4 *>(arow[kNC] + off);
                 qa[4 * kNC] = t.x; qa[4 * kNC + 1] = t.y;
-            } else {
+                if constexpr (kTail == 12) qa[4 * kNC + 2] = *reinterpret_cast<const uint32_t *>(arow[kNC] + off + 8);
+            } else if constexpr (kTail == 4) {
                 qa[4 * kNC] = *reinterpret_cast<const uint32_t *>(arow[kNC] + off);
             }
         } else {
@@ -476,7 +538,7 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
             // missing bytes reading as zeros (scale 0, weights 0).
             const bool second = 2 * pair + 1 < nb;
 #pragma unroll
-            for (int u = 0; u <= kNC; ++u) {
+            for (int u = 0; u < kNC + (kTail > 0 ? 1 : 0); ++u) {
                 const int nd = u < kNC ? 4 : kTail / 4;
                 const int pos0 = u < kNC ? 16 * ((gtid + 256 * u) % kNC) : 16 * kNC;
                 const uint8_t *a = arow[u] + off;
@@ -488,6 +550,9 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
                     if (nd == 4) {
                         const u32x4g_a4 t = *reinterpret_cast<const u32x4g_a4 *>(base);
                         d[0] = t.x; d[1] = t.y; d[2] = t.z; d[3] = t.w;
+                    } else if (nd == 3) {
+                        const u32x2g_a4 t = *reinterpret_cast<const u32x2g_a4 *>(base);
+                        d[0] = t.x; d[1] = t.y; d[2] = base[2]; d[3] = 0u;
                     } else if (nd == 2) {
                         const u32x2g_a4 t = *reinterpret_cast<const u32x2g_a4 *>(base);
                         d[0] = t.x; d[1] = t.y; d[2] = 0u; d[3] = 0u;
@@ -522,10 +587,12 @@ __global__ __launch_bounds__(kGmThreads) void gemm_kernel(
             *reinterpret_cast<u32x4g_t *>(st + (e / kNC) * kAP + 16 * (e % kNC)) =
                 u32x4g_t{qa[4 * u], qa[4 * u + 1], qa[4 * u + 2], qa[4 * u + 3]};
         }
-        if constexpr (kTail == 8)
+        if constexpr (kTail >= 8) {
             *reinterpret_cast<u32x2g_t *>(st + gtid * kAP + 16 * kNC) = u32x2g_t{qa[4 * kNC], qa[4 * kNC + 1]};
-        else
+            if constexpr (kTail == 12) *reinterpret_cast<uint32_t *>(st + gtid * kAP + 16 * kNC + 8) = qa[4 * kNC + 2];
+        } else if constexpr (kTail == 4) {
             *reinterpret_cast<uint32_t *>(st + gtid * kAP + 16 * kNC) = qa[4 * kNC];
+        }
     };
 
     auto load_b = [&](int s, XSet &xb) __attribute__((always_inline)) {
@@ -976,25 +1043,29 @@ static int dispatch_gemm(const uint8_t *w, int m, int nb, const uint16_t *x, int
     const bool xfast = ((uintptr_t)x % 16) == 0 && (ldx % 8) == 0;
     const bool ya = ((uintptr_t)y % 16) == 0 && (ldy % 4) == 0;
     // the direct-load path moves whole super-steps (two pairs, or eight for
-    // the small-batch tile): k % 128 == 0, or k % 512 == 0
-    const bool dma = fast && xfast && (nb % 4) == 0;
+    // the small-batch tile): k % 128 == 0, or k % 512 == 0; its stage layouts
+    // exist for Q4_0, Q4_1 and Q8_0 (Q5_0 / Q5_1 take the register-staged tile)
+    constexpr bool kDmaFormat = FMT == QK_Q4_0 || FMT == QK_Q4_1 || FMT == QK_Q8_0;
+    const bool dma = kDmaFormat && fast && xfast && (nb % 4) == 0;
     const bool small = dma && nb >= 16 &&
                        (n <= kGmSmallBatch || (n <= kGmSmallBatchMax && mtiles * ntiles < device_cus()));
-    if (small) {
-        // the small-batch tile takes whole eight-pair super-steps; the 4, 8 or
-        // 12 blocks left over go to a second launch that adds its products
-        const int nb16 = nb - nb % 16;
-        int st = ya ? launch_gemm_dma<FMT, true, 8>(w, m, nb16, x, ldx, n, y, ldy, stream, nb)
-                    : launch_gemm_dma<FMT, false, 8>(w, m, nb16, x, ldx, n, y, ldy, stream, nb);
-        if (st != QK_OK || nb16 == nb) return st;
-        const uint8_t *wr = w + (size_t)nb16 * Format<FMT>::kBytes;
-        const uint16_t *xr = x + (size_t)nb16 * kBlockElems;
-        return ya ? launch_gemm_dma<FMT, true, 2, true>(wr, m, nb - nb16, xr, ldx, n, y, ldy, stream, nb)
-                  : launch_gemm_dma<FMT, false, 2, true>(wr, m, nb - nb16, xr, ldx, n, y, ldy, stream, nb);
+    if constexpr (kDmaFormat) {
+        if (small) {
+            // the small-batch tile takes whole eight-pair super-steps; the 4, 8 or
+            // 12 blocks left over go to a second launch that adds its products
+            const int nb16 = nb - nb % 16;
+            int st = ya ? launch_gemm_dma<FMT, true, 8>(w, m, nb16, x, ldx, n, y, ldy, stream, nb)
+                        : launch_gemm_dma<FMT, false, 8>(w, m, nb16, x, ldx, n, y, ldy, stream, nb);
+            if (st != QK_OK || nb16 == nb) return st;
+            const uint8_t *wr = w + (size_t)nb16 * Format<FMT>::kBytes;
+            const uint16_t *xr = x + (size_t)nb16 * kBlockElems;
+            return ya ? launch_gemm_dma<FMT, true, 2, true>(wr, m, nb - nb16, xr, ldx, n, y, ldy, stream, nb)
+                      : launch_gemm_dma<FMT, false, 2, true>(wr, m, nb - nb16, xr, ldx, n, y, ldy, stream, nb);
+        }
+        if (dma)
+            return ya ? launch_gemm_dma<FMT, true, 2>(w, m, nb, x, ldx, n, y, ldy, stream, nb)
+                      : launch_gemm_dma<FMT, false, 2>(w, m, nb, x, ldx, n, y, ldy, stream, nb);
     }
-    if (dma)
-        return ya ? launch_gemm_dma<FMT, true, 2>(w, m, nb, x, ldx, n, y, ldy, stream, nb)
-                  : launch_gemm_dma<FMT, false, 2>(w, m, nb, x, ldx, n, y, ldy, stream, nb);
     auto run = [&](auto fw, auto fx) {
         if (ya) return launch_gemm<FMT, decltype(fw)::value, decltype(fx)::value, true>(w, m, nb, x, ldx, n, y, ldy,
                                                                                         mtiles, ntiles, stream);
@@ -1015,6 +1086,8 @@ int launch_mul_mat(int fmt, const void *w, int64_t m, int64_t k, const uint16_t 
     case QK_Q4_0: return dispatch_gemm<QK_Q4_0>(wb, (int)m, nb, x, ldx, (int)n, y, ldy, stream);
     case QK_Q4_1: return dispatch_gemm<QK_Q4_1>(wb, (int)m, nb, x, ldx, (int)n, y, ldy, stream);
     case QK_Q8_0: return dispatch_gemm<QK_Q8_0>(wb, (int)m, nb, x, ldx, (int)n, y, ldy, stream);
+    case QK_Q5_0: return dispatch_gemm<QK_Q5_0>(wb, (int)m, nb, x, ldx, (int)n, y, ldy, stream);
+    case QK_Q5_1: return dispatch_gemm<QK_Q5_1>(wb, (int)m, nb, x, ldx, (int)n, y, ldy, stream);
     default: return QK_ERR_UNSUPPORTED;
     }
 }

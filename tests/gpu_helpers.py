@@ -10,7 +10,7 @@ from dequant_quantized_gemv_amd import synth
 
 # formats of the dequantize and GEMV entry points; the GEMM takes the first three
 FMTS = ["q4_0", "q4_1", "q8_0", "q5_0", "q5_1"]
-GEMM_FMTS = ["q4_0", "q4_1", "q8_0"]
+GEMM_FMTS = list(FMTS)  # (Q5_0 / Q5_1 through the register-staged tile)
 # fp16 scale ranges of the synthetic weights per format
 D_RANGE = {"q4_0": synth.D_Q4, "q4_1": synth.D_Q4, "q8_0": synth.D_Q8, "q5_0": synth.D_Q8,
            "q5_1": synth.D_Q8}

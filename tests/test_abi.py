@@ -111,8 +111,8 @@ def test_mul_mat_vec_validation(args, want):
 
 @pytest.mark.parametrize("args,want", [
     ((99, W, 8, 64, X, 16, 64, Y, 8), E.QK_ERR_UNSUPPORTED),
-    ((E.QK_Q5_0, W, 8, 64, X, 16, 64, Y, 8), E.QK_ERR_UNSUPPORTED),  # no Q5 GEMM
-    ((E.QK_Q5_1, W, 8, 64, X, 16, 64, Y, 8), E.QK_ERR_UNSUPPORTED),
+    ((E.QK_Q5_0, W, 8, 40, X, 16, 64, Y, 8), E.QK_ERR_INVALID_ARG),
+    ((E.QK_Q5_1, W + 1, 8, 64, X, 16, 64, Y, 8), E.QK_ERR_ALIGNMENT),
     ((E.QK_Q4_0, W, 8, 40, X, 16, 64, Y, 8), E.QK_ERR_INVALID_ARG),
     ((E.QK_Q4_0, W, 8, 64, X, -3, 64, Y, 8), E.QK_ERR_INVALID_ARG),
     ((E.QK_Q4_0, W, 8, 64, X, 16, 32, Y, 8), E.QK_ERR_INVALID_ARG),

@@ -466,21 +466,6 @@ def test_gemm_strides_and_unaligned(fmt):
         assert_within(y, yref, s, GEMM_TOL, f"gemm strided {fmt} {ldx} {ldy} {x_off}")
 
 
-@pytest.mark.parametrize("fmt", ["q5_0", "q5_1"])
-def test_gemm_q5_is_unsupported(fmt):
-    """The GEMM has no Q5 tile layout: QK_ERR_UNSUPPORTED, output untouched."""
-    m, k, n = 64, 256, 16
-    w = _weights(fmt, m, k, seed=45)
-    hw, wp = to_dev_bytes(w)
-    hx, xp = x_dev(synth.activations(k, n, seed=45, tensor_id=2, dtype=np.float16).view(np.uint16), k,
-                   np.uint16)
-    out = Guarded(n * m * 4)
-    st = qk.qk_mul_mat(fmt, wp, m, k, xp, n, k, out.ptr, m, _stream())
-    assert st == qk.QK_ERR_UNSUPPORTED
-    assert np.all(out.host(np.uint32) == 0xA5A5A5A5) and out.guards_intact()
-    del hw, hx
-
-
 def test_gemm_matches_exact_fp16_weight_products():
     """Each term uses the fp16 dequantized weight: with one-hot activations
     the GEMM returns exactly the fp16 weights (as fp32)."""

@@ -100,8 +100,8 @@ GEMV += _as_q5(_cases(0xE1, 20, _draw_gemv), 0xE1)
 GEMV_X8 += _as_q5(_cases(0xE2, 10, _draw_gemv), 0xE2)
 BATCHED += _as_q5(_cases(0xE3, 6, _draw_batched), 0xE3)
 EXPERT += _as_q5(_cases(0xE4, 6, _draw_expert), 0xE4)
-GEMM = _cases(0xD5, 16, _draw_gemm)
-GEMM_SMALL = _cases(0xD6, 12, _draw_gemm_small)
+GEMM = _cases(0xD5, 16, _draw_gemm) + _as_q5(_cases(0xE5, 8, _draw_gemm), 0xE5)
+GEMM_SMALL = _cases(0xD6, 12, _draw_gemm_small) + _as_q5(_cases(0xE6, 4, _draw_gemm_small), 0xE6)
 
 
 @pytest.mark.parametrize("c", DEQUANT, ids=[f"dq{i}" for i in range(len(DEQUANT))])
