@@ -758,9 +758,11 @@ template <int FMT, int KG = 2> struct GmDma {
     // Rows that fill their chunks exactly get one more chunk, which gives the
     // spare bytes for the row shift below: Q4_1 at KG = 2 (80 bytes, at the
     // price of a 2-stage ring: measured 2-6 % faster than 3 stages without the
-    // shift), and every format at KG = 8 (288 / 320 / 544 bytes; the ring keeps
-    // its depth: Q4_1's three stages take 162 816 of the 163 840 bytes).
-    static constexpr int kChunks = (kRow + 15) / 16 + (((kRow % 16) == 0 && (KG == 8 || FMT == QK_Q4_1)) ? 1 : 0);
+    // shift), Q5_1 at KG = 2 (96 bytes; two stages either way), and every
+    // format at KG = 8 (288 / 320 / 544 / 352 / 384 bytes; Q4_1's three stages
+    // take 162 816 of the 163 840 bytes, Q5's take two).
+    static constexpr int kChunks =
+        (kRow + 15) / 16 + (((kRow % 16) == 0 && (KG == 8 || FMT == QK_Q4_1 || FMT == QK_Q5_1)) ? 1 : 0);
     static constexpr int kPad = 16 * kChunks - kRow;
     // Rows 8-15 of every 16-row tile are stored 4 bytes later in their LDS
     // row (their chunks are loaded from 4 bytes earlier), so that the dwords
@@ -1043,9 +1045,8 @@ static int dispatch_gemm(const uint8_t *w, int m, int nb, const uint16_t *x, int
     const bool xfast = ((uintptr_t)x % 16) == 0 && (ldx % 8) == 0;
     const bool ya = ((uintptr_t)y % 16) == 0 && (ldy % 4) == 0;
     // the direct-load path moves whole super-steps (two pairs, or eight for
-    // the small-batch tile): k % 128 == 0, or k % 512 == 0; its stage layouts
-    // exist for Q4_0, Q4_1 and Q8_0 (Q5_0 / Q5_1 take the register-staged tile)
-    constexpr bool kDmaFormat = FMT == QK_Q4_0 || FMT == QK_Q4_1 || FMT == QK_Q8_0;
+    // the small-batch tile): k % 128 == 0, or k % 512 == 0
+    constexpr bool kDmaFormat = true;
     const bool dma = kDmaFormat && fast && xfast && (nb % 4) == 0;
     const bool small = dma && nb >= 16 &&
                        (n <= kGmSmallBatch || (n <= kGmSmallBatchMax && mtiles * ntiles < device_cus()));

@@ -253,7 +253,7 @@ int qk_mul_mat_vec_id(int fmt, const void *w, int64_t n_experts, int64_t expert_
  *   y[j*ldy + i] = sum_c f16(W[i, c]) * x[j*ldx + c]   for i < m, j < n
  *
  * f16(W) is the qk_dequantize fp16 value (one RNE of the fp32 weight).
- * Every format (QK_Q5_0 / QK_Q5_1 through the register-staged tile only).
+ * Every format.
  * Source: the dequantize-to-fp16 then GEMM path (ggml_get_to_fp16_cuda feeding
  * the BLAS mul_mat) and ggml_cuda_mul_mat's choice of a batched kernel when
  * the right operand has more than one column, in the same diff.
