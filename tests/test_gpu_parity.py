@@ -244,6 +244,21 @@ def test_gemv_within_tolerance(fmt, m, k, n):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k,n", [(70, 4224, 3), (100, 9216, 5), (33, 8320, 8), (9, 12288, 4)])
+def test_gemv_restaged_windows(fmt, m, k, n):
+    """Aligned rows longer than one 4096-weight activation window with 3..8
+    columns: the first window is staged through registers, each later one in
+    batches of columns; the last window is partial (128 or 1024 weights: fewer
+    float4s than threads) except at k = 12288."""
+    _say("gemv restaged windows", fmt, m, k, n)
+    w = _weights(fmt, m, k, seed=47)
+    x = synth.activations(k, n, seed=47, tensor_id=2)
+    y = _gpu_gemv(fmt, w, m, k, x)
+    yref, s = oracle.dot(fmt, w, m, k, x, n)
+    assert_within(y, yref, s, GEMV_TOL, f"gemv restaged {fmt} {m}x{k} n={n}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("w_off,x_off,ldx,ldy", [(2, 0, None, None), (0, 1, None, None),
                                                  (0, 0, 4100, 70), (6, 3, 4133, 65)])
 def test_gemv_strides_and_unaligned(fmt, w_off, x_off, ldx, ldy):
