@@ -951,6 +951,10 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
                 }
             }
             load_step(P, cur);
+            // (keeps this step's weight loads ahead of the prefetch: the
+            // scheduler interleaved the two sets in the one-row Q8_0 kernel,
+            // so the first products waited for most of the prefetch too)
+            asm volatile("" ::: "memory");
             if constexpr (PREFETCH) load_step(PF, nxt);
             // unconditional stores (a tail lane rewrites the last float4 with
             // the same value), so no load is moved behind the weight loads
