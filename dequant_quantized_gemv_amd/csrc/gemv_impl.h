@@ -334,6 +334,19 @@ __device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDw
     for (int b = 0; b < 2; ++b) {
         if (!FAST && b == 1 && !second) break;
         if constexpr (kHasM<FMT>) {
+            // d and m converted to fp32 once per block and held opaque, so each
+            // weight is one fp32 FMA (left to itself the compiler folded the
+            // conversions into a mixed-precision FMA per weight, a slower
+            // instruction); the code words are opaque too, so each nibble
+            // converts with one byte-select convert instead of a field extract
+            // and a convert.  The weights are the same exact fp32 values.
+            float dd[RWV], mv[RWV];
+#pragma unroll
+            for (int r = 0; r < RWV; ++r) {
+                dd[r] = h2f(pair_d<FMT>(v[r], b));
+                mv[r] = h2f(pair_m<FMT>(v[r], b));
+                asm volatile("" : "+v"(dd[r]), "+v"(mv[r]));
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float4 xa[NC], xb[NC];
@@ -345,10 +358,11 @@ __device__ __forceinline__ void pair_dot(const uint32_t (&v)[RWV][Pair<FMT>::kDw
 #pragma unroll
                 for (int r = 0; r < RWV; ++r) {
                     if (FAST || r < nrows) {  // fast path: rows clamped, stores guarded
-                        const float d = h2f(pair_d<FMT>(v[r], b));
-                        const float mm = h2f(pair_m<FMT>(v[r], b));
+                        const float d = dd[r];
+                        const float mm = mv[r];
                         uint32_t lo, hi;
                         pair_codes<FMT>(v[r], b, i, lo, hi);
+                        asm volatile("" : "+v"(lo), "+v"(hi));
                         const float w0 = wval(d, ubyte_f<0>(lo), mm), w1 = wval(d, ubyte_f<1>(lo), mm);
                         const float w2 = wval(d, ubyte_f<2>(lo), mm), w3 = wval(d, ubyte_f<3>(lo), mm);
                         const float w4 = wval(d, ubyte_f<0>(hi), mm), w5 = wval(d, ubyte_f<1>(hi), mm);
