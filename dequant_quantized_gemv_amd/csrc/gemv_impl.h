@@ -1200,8 +1200,25 @@ int gemv_mfma_launch(const GemvItem &it, hipStream_t stream);
 template <int FMT, int NC, bool X8>
 int gemv_table_fmt(GemvArgs &a, bool fast, hipStream_t stream) {
     if constexpr (NC >= 4 && !X8) {
-        if (a.count == 1 && fast && a.item[0].nb * kBlockElems <= kGvWindow)
-            return gemv_mfma_launch<FMT, NC>(a.item[0], stream);
+        if (a.count == 1 && fast && a.item[0].nb * kBlockElems <= kGvWindow) {
+            // At 4 columns the vector-ALU kernel is the faster one when its
+            // launch has a row group for every CU and at most one per resident
+            // workgroup (each workgroup then takes a single step): 4096 x 4096
+            // Q4_1 7.9 -> 6.9 us, Q5_1 8.2 -> 7.3, Q8_0 10.2 -> 9.2; 8192
+            // rows Q4_1 11.4 -> 10.1, Q5_0 12.6 -> 11.1 us.  Outside that
+            // range (fewer rows, or more row groups than workgroup slots) the
+            // matrix cores measured as fast or faster.
+            bool vector_alu = false;
+            if constexpr (NC == 4) {
+                constexpr int RG = GemvShape<FMT, NC, 0, true, false>::kRowsPerGroup;
+                const int64_t groups = ((int64_t)a.item[0].m + RG - 1) / RG;
+                const int slots =
+                    max(1, min(kGvMaxWgPerCu, (int)((160 * 1024) / ((size_t)NC * kGvPitch * sizeof(float)))));
+                const int64_t cus = device_cus();
+                vector_alu = groups >= cus && groups <= slots * cus;
+            }
+            if (!vector_alu) return gemv_mfma_launch<FMT, NC>(a.item[0], stream);
+        }
     }
     if constexpr (NC == 1) {
         int npairs = 0;

@@ -244,6 +244,23 @@ def test_gemv_within_tolerance(fmt, m, k, n):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k", [(4096, 4096), (6000, 2048), (3000, 4096)])
+def test_gemv_four_columns_either_path(fmt, m, k):
+    """Four columns where the dispatcher picks the vector-ALU kernel (a row
+    group for every CU, one step per workgroup) or the matrix cores next to
+    it: 4096 rows take the vector kernel for every format, 6000 rows of 2048
+    the vector kernel for Q4_x / Q5_x and the matrix cores for Q8_0, 3000 rows
+    the reverse.  Every output against the oracle, bitwise repeatable."""
+    _say("gemv four columns", fmt, m, k)
+    w = _weights(fmt, m, k, seed=48)
+    x = synth.activations(k, 4, seed=48, tensor_id=2)
+    y = _gpu_gemv(fmt, w, m, k, x)
+    yref, s = oracle_rows(oracle.dot, fmt, w, m, k, x, 4)
+    assert_within(y, yref, s, GEMV_TOL, f"gemv four columns {fmt} {m}x{k}")
+    assert np.array_equal(y.view(np.uint32), _gpu_gemv(fmt, w, m, k, x).view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m,k,n", [(70, 4224, 3), (100, 9216, 5), (33, 8320, 8), (9, 12288, 4)])
 def test_gemv_restaged_windows(fmt, m, k, n):
     """Aligned rows longer than one 4096-weight activation window with 3..8
