@@ -805,9 +805,12 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
     // too (the counter is in order) and then takes one round trip per float4.
     // Every column on the aligned path (Q4_1 11008 x 4096 at 3 columns 14.0
     // -> 11.9 us, 4096 x 11008 at 4 / 8 columns 21.5 -> 19.1 / 38.4 -> 35.5
-    // us); the unaligned kernels above 2 columns keep the loop (their
-    // registers would cost the Q8_0 ones waves per SIMD).
-    constexpr int XR = NC <= 2 || FAST ? NC : 0;
+    // us) and on the unaligned one except Q8_0, whose registers would cost
+    // it waves per SIMD (unaligned 11008 x 4096 at 3 / 4 / 8 columns: Q4_0
+    // 14.8 -> 13.6 / 16.3 -> 16.4 / 29.2 -> 28.5 us, Q4_1 14.3 -> 14.5 / 19.3
+    // -> 18.1 / 28.4 -> 27.2, Q5_0 16.6 -> 14.9 / 18.4 / 31.5 -> 30.0, Q5_1
+    // 15.7 -> 16.0 / 20.8 -> 19.5 / 30.3 -> 28.2).
+    constexpr int XR = NC <= 2 || FAST || FMT != QK_Q8_0 ? NC : 0;
 
     // 8-bit activations: block bi of the window (columns one after another,
     // nblk blocks each) is read from x and quantized into LDS.
