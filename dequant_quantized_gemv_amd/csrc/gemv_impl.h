@@ -842,13 +842,14 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(NC == 
             return;
         }
         const int ce4 = min(XW, it.nb * 32 - e0) / 4;  // float4s in this window (>= 8)
-        if constexpr (NC >= 3 && FAST) {
+        if constexpr (NC >= 3 && (FAST || FMT != QK_Q8_0)) {
             // a batch of columns' loads at a time (a tail thread repeats the
             // last float4 and skips the store), one round trip per batch
             // instead of one per float4: Q4_1 4096 x 11008 at 3 / 4 / 8
-            // columns 14.8 -> 14.6, 19.1 -> 17.5, 35.5 -> 33.9 us.  (With one
-            // column the registers cost the grouped layer a wave per SIMD; the
-            // unaligned Q8_0 kernels, one to two.)
+            // columns 14.8 -> 14.6, 19.1 -> 17.5, 35.5 -> 33.9 us; unaligned,
+            // 15.9 -> 15.9, 19.7 -> 17.9, 35.5 -> 32.3 us (Q5_1 at 8 columns
+            // 39.9 -> 33.9).  (With one column the registers cost the grouped
+            // layer a wave per SIMD; the unaligned Q8_0 kernels, one to two.)
             constexpr int XU = (XW / 4 + NT - 1) / NT;  // float4s per thread and column
             // columns per batch: up to four, at most 8 float4s per thread
             constexpr int CB = (NC < 4 ? NC : 4) * XU <= 8 ? (NC < 4 ? NC : 4) : (XU < 8 ? 8 / XU : 1);
