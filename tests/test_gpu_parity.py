@@ -260,17 +260,19 @@ def test_gemv_four_columns_either_path(fmt, m, k):
     assert np.array_equal(y.view(np.uint32), _gpu_gemv(fmt, w, m, k, x).view(np.uint32))
 
 
+@pytest.mark.parametrize("w_off", [0, 2])
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m,k,n", [(70, 4224, 3), (100, 9216, 5), (33, 8320, 8), (9, 12288, 4)])
-def test_gemv_restaged_windows(fmt, m, k, n):
-    """Aligned rows longer than one 4096-weight activation window with 3..8
-    columns: the first window is staged through registers, each later one in
-    batches of columns; the last window is partial (128 or 1024 weights: fewer
-    float4s than threads) except at k = 12288."""
-    _say("gemv restaged windows", fmt, m, k, n)
+def test_gemv_restaged_windows(fmt, m, k, n, w_off):
+    """Rows longer than one 4096-weight activation window with 3..8 columns,
+    aligned and 2 bytes off: the first window is staged through registers,
+    each later one in batches of columns (unaligned Q8_0: the per-float4
+    loop); the last window is partial (128 or 1024 weights: fewer float4s
+    than threads) except at k = 12288."""
+    _say("gemv restaged windows", fmt, m, k, n, w_off)
     w = _weights(fmt, m, k, seed=47)
     x = synth.activations(k, n, seed=47, tensor_id=2)
-    y = _gpu_gemv(fmt, w, m, k, x)
+    y = _gpu_gemv(fmt, w, m, k, x, w_off=w_off)
     yref, s = oracle.dot(fmt, w, m, k, x, n)
     assert_within(y, yref, s, GEMV_TOL, f"gemv restaged {fmt} {m}x{k} n={n}")
 
