@@ -94,7 +94,7 @@ __device__ __forceinline__ void word_weights(const uint32_t (&v)[Pair<FMT>::kDwo
     }
 }
 
-template <int FMT, int NC, int WPG, int KQ>
+template <int FMT, int NC, int WPG, int KQ, bool CNT>
 __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) void gemv_mfma_kernel(
     const GemvItem it, const int qper, const int qrem) {
     static_assert(NC >= 1 && NC <= 8, "1..8 columns");
@@ -108,6 +108,11 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
     // per wave, its partial sums of one round: [cg][column c][row r], in two
     // sets used by alternate rounds
     float *const part = xs + NC * kMfPitch;
+    // CNT: one set of slots per round, never reused, and an LDS counter per
+    // row-quad of each round; the last of the row-quad's KQ waves to arrive
+    // adds the partial sums, so the rounds need no barrier
+    const int nsets = (qper + (qrem > 0 ? 1 : 0) + RPR - 1) / RPR;
+    uint32_t *const cnt = reinterpret_cast<uint32_t *>(part + (CNT ? nsets : 2) * (WPG * CG * 16));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -176,6 +181,8 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
         if (TOT % NT == 0 || idx < TOT)
             *reinterpret_cast<f32x4m_t *>(xs + j * kMfPitch + e + (e >> 6) * 4) = e < kk ? tmp[u] : z;
     }
+    if constexpr (CNT)
+        for (int i = tid; i < nsets * RPR; i += NT) cnt[i] = 0u;
     __syncthreads();
 
     // partial sum of (wave w, column group cg, column c, row r) in a slot set
@@ -282,6 +289,32 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
                 if ((lane & 15) < 4) part_at(pw, wave, cg, c, 2 * (R & 1) + (R >> 1)) = sm;
             }
         }
+        if constexpr (CNT) {
+            // LDS operations of one wave are performed in order, so the
+            // partial sums written above precede this wave's increment; the
+            // wave that sees KQ - 1 comes after every other wave's increment
+            // and reads their sums (in wave order, as below: the same bits
+            // whichever wave adds them)
+            asm volatile("" ::: "memory");
+            uint32_t old = 0;
+            if (lane == 0)
+                old = __hip_atomic_fetch_add(&cnt[ps * RPR + slot], 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_WORKGROUP);
+            old = __builtin_amdgcn_readfirstlane(old);
+            asm volatile("" ::: "memory");
+            if (old == KQ - 1 && q < q1 && lane < 16 * CG) {
+                const int r = lane & 3;
+                const int cc = (lane >> 2) & 3;
+                const int cg = lane >> 4;
+                const int col = cg * 4 + cc;
+                float sm = part_at(pw, slot * KQ, cg, cc, r);
+#pragma unroll
+                for (int k2 = 1; k2 < KQ; ++k2) sm += part_at(pw, slot * KQ + k2, cg, cc, r);
+                const int ro = 4 * q + r;
+                if (col < NC && ro < it.m) it.y[col * it.ldy + ro] = sm;
+            }
+            return;
+        }
         // one barrier per round: a set of slots is written again two rounds
         // later, after every wave has passed the next round's barrier, by
         // which time its readers are done with it
@@ -299,11 +332,12 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
             if (col < NC && ro < it.m) it.y[col * it.ldy + ro] = sm;
         }
     };
-    static_assert(D == 2, "the rounds alternate between the two sets of partial slots");
+    static_assert(D == 2, "without CNT the rounds alternate between two sets of partial slots");
     for (int qb = q0; qb < q1; qb += D * RPR) {
 #pragma unroll
         for (int r = 0; r < D; ++r)
-            if (qb + r * RPR < q1) round(qb + r * RPR, v[r], r);  // (uniform across the workgroup)
+            if (qb + r * RPR < q1)  // (uniform across the workgroup)
+                round(qb + r * RPR, v[r], CNT ? (qb - q0) / RPR + r : r);
     }
 }
 
@@ -317,13 +351,24 @@ template <int NC> struct MfShape {
 template <int FMT, int NC, int KQ>
 int gemv_mfma_run(const GemvItem &it, hipStream_t stream) {
     constexpr int WPG = MfShape<NC>::kWPG;
-    const size_t lds = ((size_t)NC * kMfPitch + 2 * (size_t)WPG * ((NC + 3) / 4) * 16) * sizeof(float);
+    constexpr int RPR = WPG / KQ;
+    const size_t set_floats = (size_t)WPG * ((NC + 3) / 4) * 16;
+    size_t lds = ((size_t)NC * kMfPitch + 2 * set_floats) * sizeof(float);
     const int per_cu = max(1, (int)((160 * 1024) / lds));
     const int64_t quads = ((int64_t)it.m + 3) / 4;
     if (quads > INT32_MAX) return QK_ERR_INVALID_ARG;
     const int64_t cap = (int64_t)device_cus() * per_cu;
     const int nwg = (int)(quads < cap ? quads : cap);
-    auto kern = gemv_mfma_kernel<FMT, NC, WPG, KQ>;
+    // Counters instead of a barrier per round where workgroups run two or
+    // more rounds and the extra slot sets leave as many workgroups per CU
+    // (Q4_1 11008 x 4096 at 4 / 5 / 6 / 8 columns 14.39 -> 14.27, 17.91 ->
+    // 17.56, 17.95 -> 17.34, 17.97 -> 17.77 us, bitwise equal; with a single
+    // round, e.g. 4096 x 4096 at 8 columns, the counter cost 1 % more)
+    const int64_t rounds = ((quads + nwg - 1) / nwg + RPR - 1) / RPR;
+    const size_t lds_cnt = ((size_t)NC * kMfPitch + (size_t)rounds * (set_floats + RPR)) * sizeof(float);
+    const bool use_cnt = rounds >= 2 && lds_cnt * per_cu <= 160 * 1024;
+    if (use_cnt) lds = lds_cnt;
+    auto kern = use_cnt ? gemv_mfma_kernel<FMT, NC, WPG, KQ, true> : gemv_mfma_kernel<FMT, NC, WPG, KQ, false>;
     if (lds > 64 * 1024 &&
         hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)

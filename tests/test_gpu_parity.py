@@ -260,6 +260,25 @@ def test_gemv_four_columns_either_path(fmt, m, k):
     assert np.array_equal(y.view(np.uint32), _gpu_gemv(fmt, w, m, k, x).view(np.uint32))
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k,n", [(11001, 4096, 5), (20003, 1024, 6), (9000, 2048, 8), (5000, 4096, 7),
+                                   (20001, 4096, 4)])
+def test_gemv_matrix_cores_many_rounds(fmt, m, k, n):
+    """Matrix-core launches whose workgroups run two or more rounds of
+    row-quads (the partial sums of a row-quad's waves then meet through a
+    per-round LDS counter, no barrier): the pairs of a row split over 4, 1, 2
+    and 4 waves, uneven row-quad counts per workgroup, a last round with
+    fewer row-quads than slots and a partial last row-quad.  Every output
+    against the oracle, bitwise repeatable."""
+    _say("gemv matrix cores many rounds", fmt, m, k, n)
+    w = _weights(fmt, m, k, seed=49)
+    x = synth.activations(k, n, seed=49, tensor_id=2)
+    y = _gpu_gemv(fmt, w, m, k, x)
+    yref, s = oracle_rows(oracle.dot, fmt, w, m, k, x, n)
+    assert_within(y, yref, s, GEMV_TOL, f"gemv many rounds {fmt} {m}x{k} n={n}")
+    assert np.array_equal(y.view(np.uint32), _gpu_gemv(fmt, w, m, k, x).view(np.uint32))
+
+
 @pytest.mark.parametrize("w_off", [0, 2])
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m,k,n", [(70, 4224, 3), (100, 9216, 5), (33, 8320, 8), (9, 12288, 4)])
