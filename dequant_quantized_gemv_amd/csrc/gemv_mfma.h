@@ -158,10 +158,14 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     // the wave's pairs of its first D rounds (unconditional, clamped, so the
     // waits that follow are counted exactly); each round then requests the
-    // round D ahead into the registers it has just used.  (Deeper prefetch
-    // measured slower: most workgroups have only one to three rounds, and
-    // the clamped extra loads of the first rounds are then wasted.)
-    constexpr int D = 2;
+    // round D ahead into the registers it has just used.  Two rounds ahead;
+    // three for Q4_1 at four columns with each row-quad over four waves and
+    // counters between the rounds (11008 x 4096: 14.26-14.33 -> 13.58-13.67
+    // us, 12000 x 3072: 14.29 -> 13.74-13.83 us).  Elsewhere three measured
+    // slower: with a barrier per round, at 8 columns (the extra registers:
+    // 6-19 %), for Q8_0 and with two waves per row-quad (1-2 %), and for
+    // Q4_0 / Q5_0 / Q5_1 it was within -2..+2 %.
+    constexpr int D = CNT && CG == 1 && KQ == 4 && FMT == QK_Q4_1 ? 3 : 2;
     uint32_t v[D][ND];
 #pragma unroll
     for (int r = 0; r < D; ++r) load(min(q0 + slot + r * RPR, q1 - 1), v[r]);
@@ -332,7 +336,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
             if (col < NC && ro < it.m) it.y[col * it.ldy + ro] = sm;
         }
     };
-    static_assert(D == 2, "without CNT the rounds alternate between two sets of partial slots");
+    static_assert(CNT || D == 2, "without CNT the rounds alternate between two sets of partial slots");
     for (int qb = q0; qb < q1; qb += D * RPR) {
 #pragma unroll
         for (int r = 0; r < D; ++r)
