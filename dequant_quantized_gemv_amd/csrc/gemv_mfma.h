@@ -100,6 +100,13 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
     static_assert(NC >= 1 && NC <= 8, "1..8 columns");
     static_assert((KQ == 1 || KQ == 2 || KQ == 4) && WPG % KQ == 0, "K split");
     constexpr int CG = (NC + 3) / 4;  // column groups of 4 (one MFMA each per k)
+    // At 5 or 6 columns the columns past the fourth go to the vector ALU (one
+    // FMA per weight and column, fused like the MFMA's updates) instead of a
+    // second, mostly idle MFMA group: Q4_1 11008 x 4096 at 5 / 6 columns
+    // 17.5 -> 15.5 / 17.3 -> 16.7 us, Q5_1 at 6 19.4 -> 17.8, Q8_0 21.6 ->
+    // 21.0; at 7 columns it measured 17.8 -> 21.9 us, so 7 and 8 keep it.
+    constexpr int NV = (NC == 5 || NC == 6) ? NC - 4 : 0;
+    constexpr int CGM = NV > 0 ? 1 : CG;  // column groups on the matrix cores
     constexpr int ND = Pair<FMT>::kDwords;
     constexpr int BS = Format<FMT>::kBytes;
     constexpr int NT = 64 * WPG;
@@ -206,16 +213,20 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
         const int q = qb + slot;
         // CH independent accumulation chains per column group (element
         // t % CH), added at the end: four for one group, two for two
-        constexpr int CH = CG == 1 ? 4 : 2;
+        constexpr int CH = CGM == 1 ? 4 : 2;
         // (with two column groups each chain's first product takes a zero
         // accumulator operand instead of registers cleared beforehand; with
         // one, clearing them first measured faster)
         const f32x4m_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-        f32x4m_t acc[CG][CH];
-        if constexpr (CG == 1) {
+        f32x4m_t acc[CGM][CH];
+        if constexpr (CGM == 1) {
 #pragma unroll
             for (int u = 0; u < CH; ++u) acc[0][u] = zero4;
         }
+        // the vector-ALU columns: two chains per column (element t % 2)
+        float accv[NV > 0 ? NV : 1][2];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) accv[j][0] = accv[j][1] = 0.0f;
         float *const pw = part + ps * (WPG * CG * 16);
         if (q < q1) {
 #pragma unroll
@@ -239,17 +250,25 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
                         // elements 4wi..4wi+3 (h = 0) or 16+4wi.. (h = 1) of the block
                         const int e = 64 * p + 32 * bk + 16 * h + 4 * wi;
                         const int eo = e + (e >> 6) * 4;
-                        f32x4m_t xb[CG];
+                        f32x4m_t xb[CGM];
 #pragma unroll
-                        for (int cg = 0; cg < CG; ++cg)
+                        for (int cg = 0; cg < CGM; ++cg)
                             xb[cg] = *reinterpret_cast<const f32x4m_t *>(xs + colo[cg] + eo);
+                        // (column 4 + j at the lane's own k, as for its row's weight)
+                        f32x4m_t xv[NV > 0 ? NV : 1];
+#pragma unroll
+                        for (int j = 0; j < NV; ++j)
+                            xv[j] = *reinterpret_cast<const f32x4m_t *>(xs + (4 + j) * kMfPitch + eo);
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            const bool first = CG == 2 && bk == 0 && wi == 0 && h == 0 && u < CH;
+                            const bool first = CGM == 2 && bk == 0 && wi == 0 && h == 0 && u < CH;
 #pragma unroll
-                            for (int cg = 0; cg < CG; ++cg)
+                            for (int cg = 0; cg < CGM; ++cg)
                                 acc[cg][u % CH] = __builtin_amdgcn_mfma_f32_4x4x1f32(
                                     wt[4 * h + u], xb[cg][u], first ? zero4 : acc[cg][u % CH], 0, 0, 0);
+#pragma unroll
+                            for (int j = 0; j < NV; ++j)
+                                accv[j][u & 1] = __builtin_fmaf(wt[4 * h + u], xv[j][u], accv[j][u & 1]);
                         }
                     }
                     // keep the next word's LDS reads from being hoisted above
@@ -275,7 +294,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
             const bool odd = (R & 1) != 0;
             const bool upper = R >= 2;
 #pragma unroll
-            for (int cg = 0; cg < CG; ++cg) {
+            for (int cg = 0; cg < CGM; ++cg) {
                 float v4[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -291,6 +310,18 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(4))) v
                 const float t0 = k0 + lane_xor16(s0, odd), t1 = k1 + lane_xor16(s1, odd);
                 const float sm = (upper ? t1 : t0) + lane_xor32(upper ? t0 : t1, upper);
                 if ((lane & 15) < 4) part_at(pw, wave, cg, c, 2 * (R & 1) + (R >> 1)) = sm;
+            }
+            // a vector-ALU column: lane (g, c) holds row c's sum over its
+            // k-stream g; the same tree adds the 16 streams (lanes c, c + 4,
+            // ..., c + 60), every lane ends with its row's sum, lanes 0..3 write
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                float sm = accv[j][0] + accv[j][1];
+                sm += dpp<0x124>(sm);  // row_ror:4
+                sm += dpp<0x128>(sm);  // row_ror:8
+                sm += lane_xor16(sm, odd);
+                sm += lane_xor32(sm, upper);
+                if (lane < 4) part_at(pw, wave, 1, j, c) = sm;
             }
         }
         if constexpr (CNT) {
